@@ -1,0 +1,229 @@
+// Q-outer (query-stationary) sparse attention: the low-reuse schedule.
+//
+// "Sparse Attention" (Chapter 2): a query tile walks selected_indices[base + slot] for
+// slot < selected_count, running the usual load K/V, QK, online-softmax, PV step per block.
+// "Kernel optimization for MiniMax M3 on NVIDIA Blackwell" (section 1): this structure
+// re-reads blocks through the cache instead of writing partials, and wins when few queries
+// share each block (high nsb/N, e.g. decode).
+//
+// A workgroup owns the rows that share one list: the 128 queries of a Q tile for one head
+// (per-tile lists), or the G heads of one query (per-query lists). The rows' Q stays in
+// registers; each listed block is staged in LDS and folded in with an online softmax.
+// Per-query lists may be split over `splits` workgroups, each writing a partial that the
+// combine kernel merges.
+#include "attn_tile.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+struct QArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* descale;
+  float scale_log2;
+  const int32_t* lists;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  uint16_t* o;
+  float* lse;
+  int32_t* counters;
+  int32_t* cmap;
+  float* part_lse;
+  uint16_t* part_o;
+  int total_q, total_k, max_q, max_k;
+  int batch, hq, hkv, topk, list_q, tiles_max, causal, splits;
+};
+
+__device__ __forceinline__ int seq_of_row(const int32_t* cu_q, int batch, int t) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool FP8, int G>
+__global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
+  constexpr int EB = FP8 ? 1 : 2;
+  __shared__ KVLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int r = wave * 32 + col;
+
+  // --- the rows of this workgroup and their list
+  int s, h, hh, t, split;
+  bool valid;
+  const int32_t* list;
+  if (a.list_q > 1) {
+    const int tile = blockIdx.x;
+    hh = blockIdx.y;
+    h = hh / G;
+    s = blockIdx.z;
+    split = 0;
+    const Seq sq0 = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+    if (tile * a.list_q >= sq0.nq) return;
+    const int il = tile * a.list_q + r;
+    valid = r < a.list_q && il < sq0.nq;
+    t = sq0.q0 + (valid ? il : 0);
+    list = a.lists + (((size_t)s * a.tiles_max + tile) * a.hkv + h) * a.topk;
+  } else {
+    const int tq = blockIdx.x;
+    h = blockIdx.y;
+    split = blockIdx.z;
+    if (tq >= a.total_q) return;
+    s = seq_of_row(a.cu_q, a.batch, tq);
+    valid = r < G;
+    hh = h * G + (valid ? r : 0);
+    t = tq;
+    list = a.lists + ((size_t)tq * a.hkv + h) * a.topk;
+  }
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  if (t - sq.q0 >= sq.nq) valid = false;      // row past a clamped sequence
+  const int pos = sq.nk - sq.nq + (t - sq.q0);
+  const int nb = (sq.nk + kBlock - 1) / kBlock;
+  // the workgroup's largest position (rows are in query order) for whole-block skipping
+  int pos_max;
+  if (a.list_q > 1) {
+    const int il_last = min(blockIdx.x * a.list_q + a.list_q - 1, sq.nq - 1);
+    pos_max = sq.nk - sq.nq + il_last;
+  } else {
+    pos_max = pos;
+  }
+  const bool wave_rows = a.list_q > 1 ? true : (wave * 32 < G);
+
+  float sl2 = a.scale_log2, dv = 1.f;
+  if constexpr (FP8) {
+    sl2 *= a.descale[0] * a.descale[1];
+    dv = a.descale[2];
+  }
+  const char* qb = reinterpret_cast<const char*>(a.q);
+  const char* kb = reinterpret_cast<const char*>(a.k);
+  const char* vb = reinterpret_cast<const char*>(a.v);
+  const uint32_t kv_row = (uint32_t)a.hkv * kD;
+
+  bf16x8 bq[8];
+  load_q_operand<FP8>(bq, qb + ((size_t)t * a.hq + hh) * kD * EB, valid, hf);
+
+  const float ninf = -__builtin_inff();
+  float m_run = ninf, l_run = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+
+  const int per = (a.topk + a.splits - 1) / a.splits;
+  const int slot0 = split * per, slot1 = min(a.topk, slot0 + per);
+  for (int slot = slot0; slot < slot1; ++slot) {
+    const int b = list[slot];
+    bool use = b >= 0 && b < nb;
+    if (use && a.causal && b * kBlock > pos_max) use = false;
+    for (int p = 0; p < slot && use; ++p)
+      if (list[p] == b) use = false;
+    if (!use) continue;                      // uniform across the workgroup
+    const int u0 = b * kBlock;
+    const int nk_rel = sq.nk - u0;
+    __syncthreads();
+    stage_kv<FP8>(L, kb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB,
+                  vb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB, kv_row, nk_rel);
+    __syncthreads();
+    if (wave_rows) {
+      f32x16 sacc[4];
+      qk_block(L, bq, sacc, col, hf);
+      int kmax = min(127, nk_rel - 1);
+      if (a.causal) kmax = min(kmax, pos - u0);
+      const float mb = scale_mask_max(sacc, sl2, kmax, hf);
+      const float m_new = fmaxf(m_run, mb);
+      const float ms = m_new > ninf ? m_new : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - ms);
+      const float lb = exp_sum(sacc, ms);
+      l_run = l_run * alpha + lb;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      m_run = m_new;
+      pv_block(L, sacc, oacc, col, hf);
+    }
+  }
+
+  if (a.splits > 1 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0)
+    a.counters[0] = a.total_q * a.hkv * a.splits;
+  if (!valid) return;
+  const bool any = l_run > 0.f;
+  const float inv = any ? dv / l_run : 0.f;
+  const float lse_v = any ? (m_run + log2f(l_run)) * 0.69314718055994531f : ninf;
+  const int g = hh - h * G;
+  if (a.splits == 1) {
+    store_o_row(a.o + ((size_t)t * a.hq + hh) * kD, oacc, inv, hf);
+    if (hf == 0 && a.lse) a.lse[(size_t)t * a.hq + hh] = lse_v;
+  } else {
+    const size_t pe = ((size_t)t * a.hkv + h) * a.splits + split;
+    store_o_row(a.part_o + (pe * G + g) * kD, oacc, inv, hf);
+    if (hf == 0) {
+      a.part_lse[pe * G + g] = lse_v;
+      if (g == 0) a.cmap[pe] = (int)pe;
+    }
+  }
+}
+
+template <bool FP8>
+hipError_t launch_q_g(const QArgs& a, int group, dim3 grid, hipStream_t st) {
+  dim3 blk(256);
+  switch (group) {
+    case 1: hipLaunchKernelGGL((attn_q_kernel<FP8, 1>), grid, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((attn_q_kernel<FP8, 2>), grid, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((attn_q_kernel<FP8, 4>), grid, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((attn_q_kernel<FP8, 8>), grid, blk, 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_q_kernel<FP8, 16>), grid, blk, 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
+                         const void* q, const void* k, const void* v, const float* descale,
+                         float scale, const int32_t* lists, const int32_t* cu_q,
+                         const int32_t* cu_k, char* ws, void* o, float* lse, hipStream_t st) {
+  QArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.descale = descale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.lists = lists;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.o = reinterpret_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.counters = g.splits > 1 ? reinterpret_cast<int32_t*>(ws + L.counters) : nullptr;
+  a.cmap = g.splits > 1 ? reinterpret_cast<int32_t*>(ws + L.cmap) : nullptr;
+  a.part_lse = g.splits > 1 ? reinterpret_cast<float*>(ws + L.part_lse) : nullptr;
+  a.part_o = g.splits > 1 ? reinterpret_cast<uint16_t*>(ws + L.part_o) : nullptr;
+  a.total_q = s.total_q;
+  a.total_k = s.total_k;
+  a.max_q = s.max_q;
+  a.max_k = s.max_k;
+  a.batch = s.batch;
+  a.hq = s.hq;
+  a.hkv = s.hkv;
+  a.topk = s.topk;
+  a.list_q = s.list_q;
+  a.tiles_max = (int)g.tiles_max;
+  a.causal = s.causal;
+  a.splits = g.splits;
+  dim3 grid;
+  if (s.list_q > 1) {
+    if (g.tiles_max == 0) return hipSuccess;
+    grid = dim3((unsigned)g.tiles_max, s.hq, s.batch);
+  } else {
+    if (s.total_q == 0) return hipSuccess;
+    grid = dim3((unsigned)s.total_q, s.hkv, g.splits);
+  }
+  return s.dtype == MSA_FP8_E4M3 ? launch_q_g<true>(a, g.group, grid, st)
+                                 : launch_q_g<false>(a, g.group, grid, st);
+}
+
+}  // namespace msa

@@ -1,0 +1,234 @@
+// One 128-key block of attention for up to 32 query rows per wave, on bf16 MFMA.
+//
+// The block's K (row = key) and V^T (row = head dim) live in LDS as 128 rows of 256 bytes
+// with 16-byte chunks XOR-swizzled by swz(row). A wave owns 32 rows (one per lane column):
+//   S^T[key][row] = sum_d K[key][d] Q[row][d]        (A = K from LDS, B = Q from registers)
+//   O^T[dim][row] += sum_key V^T[dim][key] P[row][key] (A = V^T from LDS, B = P in registers)
+// Lane l holds keys 32*kt + 16*(l/32) + r of its row in s[kt][r], and dims
+// 32*dt + 16*(l/32) + r in o[dt][r].
+#pragma once
+#include "msa_device.h"
+
+namespace msa {
+
+struct KVLds {
+  u32x4 k[128 * 16];
+  u32x4 vt[128 * 16];
+};
+
+// Stage block rows [u0, u0 + 128) of one KV head into LDS. Rows at or past `nk_rel` (keys
+// past the end of the sequence) are zero. `row_stride`: elements between consecutive keys
+// (127 * row_stride must fit in 32 bits, i.e. hkv * d < 2^24). 256 threads.
+template <bool FP8>
+__device__ __forceinline__ void stage_kv(KVLds& L, const void* kbase, const void* vbase,
+                                         uint32_t row_stride, int nk_rel) {
+  const int tid = threadIdx.x;
+  if constexpr (!FP8) {
+    const uint16_t* kp = reinterpret_cast<const uint16_t*>(kbase);
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(vbase);
+    // K: 2048 chunks of 16 B, 8 per thread; 16 consecutive threads read one row.
+    u32x4 kr[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int i = tid + 256 * p;
+      const int row = i >> 4, cc = i & 15;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < nk_rel) v = *reinterpret_cast<const u32x4*>(kp + (uint32_t)row * row_stride + cc * 8);
+      kr[p] = v;
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int i = tid + 256 * p;
+      const int row = i >> 4, cc = i & 15;
+      L.k[row * 16 + (cc ^ swz(row))] = kr[p];
+    }
+    // V: thread owns keys 8*kg..+7 and dims 8*dg..+7, transposed in registers.
+    const int kg = tid >> 4, dg = tid & 15;
+    u32x4 vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * kg + i;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < nk_rel) v = *reinterpret_cast<const u32x4*>(vp + (uint32_t)row * row_stride + dg * 8);
+      vr[i] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = vr[2 * q][j >> 1], b = vr[2 * q + 1][j >> 1];
+        o[q] = (j & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      }
+      const int row = 8 * dg + j;
+      L.vt[row * 16 + (kg ^ swz(row))] = o;
+    }
+  } else {
+    const uint8_t* kp = reinterpret_cast<const uint8_t*>(kbase);
+    const uint8_t* vp = reinterpret_cast<const uint8_t*>(vbase);
+    // K: 1024 chunks of 16 fp8 (= 2 bf16 chunks), 4 per thread.
+    u32x4 kr[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = tid + 256 * p;
+      const int row = i >> 3, c8 = i & 7;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < nk_rel) v = *reinterpret_cast<const u32x4*>(kp + (uint32_t)row * row_stride + c8 * 16);
+      kr[p] = v;
+    }
+    const int kg = tid >> 4, dg = tid & 15;
+    u32x2 vr8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * kg + i;
+      u32x2 v = {0u, 0u};
+      if (row < nk_rel) v = *reinterpret_cast<const u32x2*>(vp + (uint32_t)row * row_stride + dg * 8);
+      vr8[i] = v;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int i = tid + 256 * p;
+      const int row = i >> 3, c8 = i & 7;
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const u32x2 lo = fp8x4_to_bf16x4(kr[p][2 * hlf]);
+        const u32x2 hi = fp8x4_to_bf16x4(kr[p][2 * hlf + 1]);
+        u32x4 o = {lo[0], lo[1], hi[0], hi[1]};
+        const int cc = 2 * c8 + hlf;
+        L.k[row * 16 + (cc ^ swz(row))] = o;
+      }
+    }
+    u32x4 vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x2 lo = fp8x4_to_bf16x4(vr8[i][0]);
+      const u32x2 hi = fp8x4_to_bf16x4(vr8[i][1]);
+      vr[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = vr[2 * q][j >> 1], b = vr[2 * q + 1][j >> 1];
+        o[q] = (j & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+      }
+      const int row = 8 * dg + j;
+      L.vt[row * 16 + (kg ^ swz(row))] = o;
+    }
+  }
+}
+
+// B operand of S^T: the lane's Q row, d = 16*st + 8*(l/32) + i in bq[st].
+template <bool FP8>
+__device__ __forceinline__ void load_q_operand(bf16x8 bq[8], const void* qrow, bool valid,
+                                               int hf) {
+  if constexpr (!FP8) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(qrow);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (valid) v = *reinterpret_cast<const u32x4*>(p + 16 * st + 8 * hf);
+      bq[st] = as_bf16x8(v);
+    }
+  } else {
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(qrow);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      u32x2 v = {0u, 0u};
+      if (valid) v = *reinterpret_cast<const u32x2*>(p + 16 * st + 8 * hf);
+      const u32x2 lo = fp8x4_to_bf16x4(v[0]);
+      const u32x2 hi = fp8x4_to_bf16x4(v[1]);
+      bq[st] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+  }
+}
+
+__device__ __forceinline__ void qk_block(const KVLds& L, const bf16x8 bq[8], f32x16 s[4],
+                                         int col, int hf) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) s[kt] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int row = kt * 32 + rowperm(col);
+      const bf16x8 a = as_bf16x8(L.k[row * 16 + ((2 * st + hf) ^ swz(row))]);
+      s[kt] = mfma32(a, bq[st], s[kt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+__device__ __forceinline__ void pv_block(const KVLds& L, const f32x16 p[4], f32x16 o[4],
+                                         int col, int hf) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(p[kt][8 * ks + 2 * i], p[kt][8 * ks + 2 * i + 1]);
+      const bf16x8 bp = as_bf16x8(pk);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int row = dt * 32 + rowperm(col);
+        const bf16x8 a = as_bf16x8(L.vt[row * 16 + ((4 * kt + 2 * hf + ks) ^ swz(row))]);
+        o[dt] = mfma32(a, bp, o[dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Scale scores into the log2 domain and mask keys past `kmax` (block-relative index of the
+// last visible key; -1 masks the whole block). Returns the row max over the block (both
+// lanes of the row agree).
+__device__ __forceinline__ float scale_mask_max(f32x16 s[4], float sl2, int kmax, int hf) {
+  const float ninf = -__builtin_inff();
+  float m = ninf;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + 16 * hf + r;
+      float x = s[kt][r] * sl2;
+      x = key <= kmax ? x : ninf;
+      s[kt][r] = x;
+      m = fmaxf(m, x);
+    }
+  }
+  return fmaxf(m, shfl_xor_f(m, 32));
+}
+
+// p = 2^(x - m) in place; returns the row sum (both lanes agree). m must be finite.
+__device__ __forceinline__ float exp_sum(f32x16 s[4], float m) {
+  float l = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[kt][r] - m);
+      s[kt][r] = p;
+      l += p;
+    }
+  }
+  return l + shfl_xor_f(l, 32);
+}
+
+// Write 16 consecutive output dims per dt (scaled by `mul`) as bf16 to orow[0..128).
+__device__ __forceinline__ void store_o_row(uint16_t* orow, const f32x16 o[4], float mul, int hf) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = pack_bf16x2(o[dt][8 * h2 + 2 * i] * mul, o[dt][8 * h2 + 2 * i + 1] * mul);
+      *reinterpret_cast<u32x4*>(orow + dt * 32 + 16 * hf + 8 * h2) = w;
+    }
+  }
+}
+
+}  // namespace msa

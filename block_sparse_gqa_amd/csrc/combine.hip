@@ -1,0 +1,108 @@
+// Log-sum-exp combine of per-slot partial outputs.
+//
+// "Sparse Attention" (Chapter 5, partial outputs and combine): combine weights each partial
+// by its LSE relative to the others; "Kernel optimization for MiniMax M3 on NVIDIA
+// Blackwell" (section 2): the combine kernel is bandwidth-bound and gathers the partials
+// through the (query, kv head, slot) -> location map.
+//
+// A thread owns 8 output dims (16 bytes) of one (query, head): it reads the slot LSEs, then
+// issues all of its slot loads before accumulating, so each wave keeps 16 independent
+// 1 KiB gathers in flight.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+template <int G>
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ cmap,
+                                                      const int32_t* __restrict__ counters,
+                                                      const float* __restrict__ part_lse,
+                                                      const uint16_t* __restrict__ part_o,
+                                                      uint16_t* __restrict__ o,
+                                                      float* __restrict__ lse, int total_q,
+                                                      int hkv, int slots) {
+  constexpr int TPB = G * 16;               // threads per (query, group) box
+  constexpr int BOXES = 256 / TPB;
+  const int tid = threadIdx.x;
+  const int box = blockIdx.x * BOXES + tid / TPB;
+  const int g = (tid / 16) % G, c = tid % 16;
+  const int t = box / hkv, h = box % hkv;
+  if (t >= total_q) return;
+  const int n_ent = counters[0];
+  const int hq = hkv * G;
+  const int32_t* cm = cmap + ((size_t)t * hkv + h) * slots;
+
+  float ls[kMaxTopK];
+  int es[kMaxTopK];
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    int e = -1;
+    if (k < slots) e = cm[k];
+    if (e >= n_ent) e = -1;
+    es[k] = e;
+    ls[k] = e >= 0 ? part_lse[(size_t)e * G + g] : -__builtin_inff();
+    m = fmaxf(m, ls[k]);
+  }
+  uint16_t* orow = o + ((size_t)t * hq + h * G + g) * kD + 8 * c;
+  if (!(m > -__builtin_inff())) {
+    *reinterpret_cast<u32x4*>(orow) = u32x4{0u, 0u, 0u, 0u};
+    if (lse && c == 0) lse[(size_t)t * hq + h * G + g] = -__builtin_inff();
+    return;
+  }
+  u32x4 vals[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (es[k] >= 0 && ls[k] > -__builtin_inff())
+      v = *reinterpret_cast<const u32x4*>(part_o + ((size_t)es[k] * G + g) * kD + 8 * c);
+    vals[k] = v;
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float wsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    const float w = __builtin_amdgcn_exp2f((ls[k] - m) * 1.4426950408889634f);  // 0 for -inf
+    wsum += w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(w, bf16_bits_to_f32(vals[k][i] & 0xFFFFu), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(w, bf16_bits_to_f32(vals[k][i] >> 16), acc[2 * i + 1]);
+    }
+  }
+  const float inv = 1.f / wsum;
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  *reinterpret_cast<u32x4*>(orow) = out;
+  if (lse && c == 0) lse[(size_t)t * hq + h * G + g] = m + logf(wsum);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L,
+                          const char* ws, void* o, float* lse, hipStream_t st) {
+  if (s.total_q == 0) return hipSuccess;
+  const int tpb = g.group * 16;
+  const int boxes = 256 / tpb;
+  const int64_t n_boxes = (int64_t)s.total_q * s.hkv;
+  dim3 grid((unsigned)((n_boxes + boxes - 1) / boxes));
+  const int32_t* cmap = reinterpret_cast<const int32_t*>(ws + L.cmap);
+  const int32_t* cnt = reinterpret_cast<const int32_t*>(ws + L.counters);
+  const float* pl = reinterpret_cast<const float*>(ws + L.part_lse);
+  const uint16_t* po = reinterpret_cast<const uint16_t*>(ws + L.part_o);
+  uint16_t* oo = reinterpret_cast<uint16_t*>(o);
+  switch (g.group) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    default: hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

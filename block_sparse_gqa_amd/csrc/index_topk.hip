@@ -1,0 +1,425 @@
+// Index branch: max-pooled proxy block scores and streaming top-K with the local block forced.
+//
+// "Flash-MSA: accelerating million-token training" (proxy forward): as each tile of proxy
+// scores is produced, the causal max of each 128-key chunk is inserted into a per-row top-K
+// kept in registers, and the query's local block gets an infinite score. "Kernel
+// optimization for MiniMax M3 on NVIDIA Blackwell" (summary): one selection per GQA group.
+//
+// Two kernels compute the same result:
+//  - index_tile_kernel (prefill): a workgroup owns 128 queries of one group and streams the
+//    proxy key blocks through LDS; S^T = K_idx Q_idx^T on bf16 MFMA puts one query per lane
+//    column, so a block max is an in-register max plus one cross-lane exchange.
+//  - index_split_kernel + index_merge_kernel (few queries, e.g. decode): the key range is
+//    cut into chunks of blocks scored by separate workgroups (a bandwidth-bound scan of the
+//    proxy keys); their top-K lists are merged by (score desc, block asc).
+// Blocks are always visited in ascending order and inserted only on a strictly greater
+// score, so equal scores keep the lower block index first.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
+
+// Running top list of (score, block) sorted by score descending; a new block goes after
+// equal scores. Fully unrolled so that the list lives in registers.
+struct TopList {
+  float sc[kMaxTopK];
+  int id[kMaxTopK];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) { sc[k] = kNegInf; id[k] = -1; }
+  }
+  __device__ __forceinline__ void insert(float v, int j) {
+#pragma unroll
+    for (int k = kMaxTopK - 1; k >= 1; --k) {
+      const bool gp = v > sc[k - 1];
+      const bool gc = v > sc[k];
+      sc[k] = gp ? sc[k - 1] : (gc ? v : sc[k]);
+      id[k] = gp ? id[k - 1] : (gc ? j : id[k]);
+    }
+    const bool g0 = v > sc[0];
+    sc[0] = g0 ? v : sc[0];
+    id[0] = g0 ? j : id[0];
+  }
+};
+
+// (a beats b) in the order score desc, block asc; empty entries (-1) lose to everything.
+__device__ __forceinline__ bool beats(float sa, int ia, float sb, int ib) {
+  if (ia < 0) return false;
+  if (ib < 0) return true;
+  return sa > sb || (sa == sb && ia < ib);
+}
+
+__device__ __forceinline__ void write_list(int32_t* out_idx, float* out_sc, int topk,
+                                           bool has_local, int local, const float* sc,
+                                           const int* id) {
+  int base = 0;
+  if (has_local) {
+    out_idx[0] = local;
+    if (out_sc) out_sc[0] = kPosInf;
+    base = 1;
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (base + k < topk) {
+      out_idx[base + k] = id[k];
+      if (out_sc) out_sc[base + k] = id[k] >= 0 ? sc[k] : kNegInf;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------ tile kernel
+template <int DP>
+__global__ __launch_bounds__(256) void index_tile_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int hkv, int topk,
+    int causal, int total_q, int total_k, int max_q, int max_k) {
+  constexpr int CH = DP / 8;       // 16-byte chunks per proxy key row
+  constexpr int STEPS = DP / 16;   // MFMA k-steps over the proxy dim
+  constexpr int PER_T = 128 * CH / 256;
+  __shared__ u32x4 kl[2][128 * CH];
+
+  const int s = blockIdx.z, h = blockIdx.y;
+  const int tile = gridDim.x - 1 - blockIdx.x;  // late (heavier, causal) tiles first
+  const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
+  if (tile * 128 >= sq.nq) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int il = tile * 128 + wave * 32 + col;
+  const bool qvalid = il < sq.nq;
+  const int pos = sq.nk - sq.nq + il;
+  const int c = floordiv(pos, kBlock);
+  const int nb = (sq.nk + kBlock - 1) / kBlock;
+
+  int jend;
+  if (causal) {
+    const int il_last = min(tile * 128 + 127, sq.nq - 1);
+    jend = min(floordiv(sq.nk - sq.nq + il_last, kBlock), nb);
+  } else {
+    jend = nb;
+  }
+
+  bf16x8 bq[STEPS];
+  {
+    const uint16_t* qrow = q_idx + ((size_t)(sq.q0 + (qvalid ? il : 0)) * hkv + h) * DP;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qvalid) v = *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hf);
+      bq[st] = as_bf16x8(v);
+    }
+  }
+
+  TopList tl;
+  tl.init();
+
+  u32x4 stage[PER_T];
+  auto load_block = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < PER_T; ++p) {
+      const int i = tid + 256 * p;
+      const int row = i / CH, cc = i % CH;
+      const int u = j * kBlock + row;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (u < sq.nk)
+        v = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + cc * 8);
+      stage[p] = v;
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < PER_T; ++p) {
+      const int i = tid + 256 * p;
+      const int row = i / CH, cc = i % CH;
+      kl[buf][row * CH + (cc ^ ((row >> 1) & (CH - 1)))] = stage[p];
+    }
+  };
+
+  if (jend > 0) {
+    load_block(0);
+    store_block(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < jend; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < jend) load_block(j + 1);
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      acc[kt] = f32x16{};
+      const int row = kt * 32 + col;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        const int cc = 2 * st + hf;
+        const bf16x8 a = as_bf16x8(kl[buf][row * CH + (cc ^ ((row >> 1) & (CH - 1)))]);
+        acc[kt] = mfma32(a, bq[st], acc[kt]);
+      }
+    }
+    float mx = kNegInf;
+    const bool partial = (j + 1) * kBlock > sq.nk;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = acc[kt][r];
+        if (partial) {
+          const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (j * kBlock + key >= sq.nk) x = kNegInf;
+        }
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const bool ins = qvalid && (causal ? (j < c) : (j != c));
+    if (ins) tl.insert(mx, j);
+
+    if (j + 1 < jend) store_block(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qvalid && hf == 0) {
+    const size_t o = ((size_t)(sq.q0 + il) * hkv + h) * topk;
+    write_list(topk_idx + o, topk_score ? topk_score + o : nullptr, topk, pos >= 0, c, tl.sc,
+               tl.id);
+  }
+}
+
+// ------------------------------------------------------------------------ split kernels
+// Grid: x = key chunk, y = group, z = sequence * max_q + query. Each wave scores blocks
+// j0 + wave, j0 + wave + 4, ... of the chunk with VALU dot products (the proxy keys are read
+// once, so the scan is bound by HBM bandwidth); the four wave lists are merged in LDS and the
+// chunk's list is written to the workspace.
+template <int DP>
+__global__ __launch_bounds__(256) void index_split_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    float* __restrict__ part_sc, int32_t* __restrict__ part_id, int hkv, int max_q,
+    int causal, int n_chunks, int total_q, int total_k, int max_k) {
+  constexpr int LPK = DP / 8;      // lanes per key row (16 bytes each)
+  constexpr int KPI = 64 / LPK;    // keys per wave instruction
+  __shared__ float lsc[4][kMaxTopK];
+  __shared__ int lid[4][kMaxTopK];
+
+  const int chunk = blockIdx.x, h = blockIdx.y;
+  const int s = blockIdx.z / max_q, il = blockIdx.z % max_q;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
+  const bool qvalid = il < sq.nq;
+  const int pos = sq.nk - sq.nq + il;
+  const int c = floordiv(pos, kBlock);
+  const int nb = (sq.nk + kBlock - 1) / kBlock;
+  const int jend = qvalid ? (causal ? min(max(c, 0), nb) : nb) : 0;
+  const int j0 = chunk * kSplitIndexChunk;
+  const int j1 = min(j0 + kSplitIndexChunk, jend);
+
+  const int kk = lane / LPK, dc = lane % LPK;
+  float qv[8];
+  {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (qvalid)
+      w = *reinterpret_cast<const u32x4*>(q_idx + ((size_t)(sq.q0 + il) * hkv + h) * DP + dc * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      qv[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  }
+
+  TopList tl;
+  tl.init();
+  for (int j = j0 + wave; j < j1; j += 4) {
+    if (!causal && j == c) continue;
+    float mx = kNegInf;
+    constexpr int IT = kBlock / KPI;
+    u32x4 kvv[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int u = j * kBlock + it * KPI + kk;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (u < sq.nk)
+        w = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + dc * 8);
+      kvv[it] = w;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dot = fmaf(qv[2 * i], bf16_bits_to_f32(kvv[it][i] & 0xFFFFu), dot);
+        dot = fmaf(qv[2 * i + 1], bf16_bits_to_f32(kvv[it][i] >> 16), dot);
+      }
+#pragma unroll
+      for (int m = 1; m < LPK; m <<= 1) dot += shfl_xor_f(dot, m);
+      const int u = j * kBlock + it * KPI + kk;
+      if (u >= sq.nk) dot = kNegInf;
+      mx = fmaxf(mx, dot);
+    }
+#pragma unroll
+    for (int m = LPK; m < 64; m <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+    tl.insert(mx, j);
+  }
+
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+      lsc[wave][k] = tl.sc[k];
+      lid[wave][k] = tl.id[k];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // 64 candidates, one per lane: rank = number of candidates that beat it.
+    const float sc = lsc[lane >> 4][lane & 15];
+    const int id = lid[lane >> 4][lane & 15];
+    int rank = 0;
+    for (int o = 0; o < 64; ++o) {
+      if (beats(lsc[o >> 4][o & 15], lid[o >> 4][o & 15], sc, id)) ++rank;
+    }
+    const size_t base = ((((size_t)s * max_q + il) * hkv + h) * n_chunks + chunk) * kMaxTopK;
+    if (id >= 0 && rank < kMaxTopK) {
+      part_sc[base + rank] = sc;
+      part_id[base + rank] = id;
+    }
+    // slots past the number of real candidates are empty
+    int n_real = 0;
+    for (int o = 0; o < 64; ++o) n_real += lid[o >> 4][o & 15] >= 0 ? 1 : 0;
+    if (lane < kMaxTopK && lane >= n_real) {
+      part_sc[base + lane] = kNegInf;
+      part_id[base + lane] = -1;
+    }
+  }
+}
+
+// One wave per (sequence, query, group): K rounds of a tournament over the chunk lists.
+__global__ __launch_bounds__(64) void index_merge_kernel(
+    const float* __restrict__ part_sc, const int32_t* __restrict__ part_id,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int hkv, int max_q,
+    int topk, int n_chunks, int total_q, int total_k, int max_k) {
+  const int h = blockIdx.x;
+  const int s = blockIdx.y / max_q, il = blockIdx.y % max_q;
+  const int lane = threadIdx.x;
+  const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
+  if (il >= sq.nq) return;
+  const int pos = sq.nk - sq.nq + il;
+  const int c = floordiv(pos, kBlock);
+  const bool has_local = pos >= 0;
+  const size_t base = (((size_t)s * max_q + il) * hkv + h) * n_chunks;
+
+  constexpr int MAXOWN = 8;   // lists per lane: n_chunks <= 512
+  int head[MAXOWN];
+#pragma unroll
+  for (int o = 0; o < MAXOWN; ++o) head[o] = 0;
+
+  float out_sc[kMaxTopK];
+  int out_id[kMaxTopK];
+  const int need = topk - (has_local ? 1 : 0);
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    // best head among this lane's lists
+    float bs = kNegInf;
+    int bi = -1, bo = -1;
+#pragma unroll
+    for (int o = 0; o < MAXOWN; ++o) {
+      const int li = lane + 64 * o;
+      if (li < n_chunks && head[o] < kMaxTopK) {
+        const size_t p = (base + li) * kMaxTopK + head[o];
+        const float sv = part_sc[p];
+        const int iv = part_id[p];
+        if (beats(sv, iv, bs, bi)) { bs = sv; bi = iv; bo = o; }
+      }
+    }
+    // wave arg-best
+    float ws = bs;
+    int wi = bi;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float os = shfl_xor_f(ws, m);
+      const int oi = shfl_xor_i(wi, m);
+      if (beats(os, oi, ws, wi)) { ws = os; wi = oi; }
+    }
+    out_sc[k] = ws;
+    out_id[k] = wi;
+    // the lane holding the winner advances that list (block ids are unique across lists)
+    if (wi >= 0 && bi == wi) {
+#pragma unroll
+      for (int o = 0; o < MAXOWN; ++o) head[o] += (o == bo) ? 1 : 0;
+    }
+    if (k + 1 >= need) break;
+  }
+  if (lane == 0) {
+    const size_t o = ((size_t)(sq.q0 + il) * hkv + h) * topk;
+    write_list(topk_idx + o, topk_score ? topk_score + o : nullptr, topk, has_local, c, out_sc,
+               out_id);
+  }
+}
+
+}  // namespace
+
+size_t index_workspace_bytes(const msa_shape& s) {
+  if (s.max_q > kSplitIndexMaxQ) return 0;
+  const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
+  const int64_t n_chunks = (nb_max + kSplitIndexChunk - 1) / kSplitIndexChunk;
+  const int64_t n = (int64_t)s.batch * s.max_q * s.hkv * n_chunks * kMaxTopK;
+  return (size_t)n * 8 + 256;
+}
+
+hipError_t launch_index_tile(const msa_shape& s, const void* q_idx, const void* k_idx,
+                             const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                             float* topk_score, hipStream_t st) {
+  const int tiles = (s.max_q + 127) / 128;
+  if (tiles == 0) return hipSuccess;
+  dim3 grid(tiles, s.hkv, s.batch);
+  if (s.dp == 64) {
+    hipLaunchKernelGGL(index_tile_kernel<64>, grid, dim3(256), 0, st,
+                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
+                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k,
+                       s.max_q, s.max_k);
+  } else {
+    hipLaunchKernelGGL(index_tile_kernel<32>, grid, dim3(256), 0, st,
+                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
+                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k,
+                       s.max_q, s.max_k);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_index_split(const msa_shape& s, const void* q_idx, const void* k_idx,
+                              const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                              float* topk_score, void* ws, hipStream_t st) {
+  if (s.max_q == 0) return hipSuccess;
+  const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
+  const int n_chunks = (int)((nb_max + kSplitIndexChunk - 1) / kSplitIndexChunk);
+  const int64_t n = (int64_t)s.batch * s.max_q * s.hkv * n_chunks * kMaxTopK;
+  float* part_sc = reinterpret_cast<float*>(ws);
+  int32_t* part_id = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + n * 4);
+  if (n_chunks > 0) {
+    dim3 grid(n_chunks, s.hkv, s.batch * s.max_q);
+    if (s.dp == 64) {
+      hipLaunchKernelGGL(index_split_kernel<64>, grid, dim3(256), 0, st,
+                         (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, part_sc,
+                         part_id, s.hkv, s.max_q, s.causal, n_chunks, s.total_q, s.total_k,
+                         s.max_k);
+    } else {
+      hipLaunchKernelGGL(index_split_kernel<32>, grid, dim3(256), 0, st,
+                         (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, part_sc,
+                         part_id, s.hkv, s.max_q, s.causal, n_chunks, s.total_q, s.total_k,
+                         s.max_k);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid2(s.hkv, s.batch * s.max_q);
+  hipLaunchKernelGGL(index_merge_kernel, grid2, dim3(64), 0, st, part_sc, part_id, cu_q, cu_k,
+                     topk_idx, topk_score, s.hkv, s.max_q, s.topk, n_chunks, s.total_q, s.total_k,
+                     s.max_k);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,361 @@
+// C ABI of libmsa: argument checks, workspace plan, schedule choice, kernel dispatch.
+// Host code only; every check runs before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kInt32Max = 2147483647LL;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+msa_status check_shape(const msa_shape* s) {
+  if (!s) return MSA_ERR_NULL;
+  if (s->dtype != MSA_BF16 && s->dtype != MSA_FP8_E4M3) return MSA_ERR_DTYPE;
+  if (s->batch < 1 || s->batch > 65535) return MSA_ERR_SHAPE;
+  if (s->total_q < 0 || s->total_k < 0 || s->max_q < 0 || s->max_k < 0) return MSA_ERR_SHAPE;
+  if (s->hq < 1 || s->hkv < 1 || s->hq % s->hkv != 0 || s->hq > 65535) return MSA_ERR_SHAPE;
+  const int g = s->hq / s->hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return MSA_ERR_SHAPE;
+  if (s->d != kD || s->block != kBlock) return MSA_ERR_SHAPE;
+  if (s->topk < 1 || s->topk > kMaxTopK) return MSA_ERR_SHAPE;
+  if (s->causal != 0 && s->causal != 1) return MSA_ERR_SHAPE;
+  if (s->list_q != 1 && s->list_q != 128) return MSA_ERR_SHAPE;
+  if (s->max_q > s->total_q || s->max_k > s->total_k) return MSA_ERR_SHAPE;
+  // 32-bit indexing of entries, partial rows and token rows
+  if ((int64_t)s->total_q * s->hkv * s->topk * g > kInt32Max) return MSA_ERR_SHAPE;
+  if ((int64_t)s->total_q * s->hq > kInt32Max || (int64_t)s->total_k * s->hkv > kInt32Max)
+    return MSA_ERR_SHAPE;
+  return MSA_OK;
+}
+
+int choose_splits(const msa_shape& s) {
+  int ns = 1;
+  while (ns * 2 <= s.topk && (int64_t)s.total_q * s.hkv * ns < 2048) ns *= 2;
+  return ns;
+}
+
+double crossover_x(const msa_shape& s, double bw_hbm, double bw_cache) {
+  const double e = s.dtype == MSA_FP8_E4M3 ? 1.0 : 2.0;
+  const double hq = s.hq, hkv = s.hkv, d = s.d, k = s.topk, bk = s.block;
+  const double kv_per_n = hq * d * e + hq * k * (2.0 * 2.0 * d + 2.0 * 4.0) + hq * d * 2.0;
+  const double q_per_n = hkv * k * 2.0 * bk * d * e + hq * d * (e + 2.0);
+  const double beta = bw_cache / bw_hbm;
+  return (q_per_n / beta - kv_per_n) / (2.0 * bk * d * e);
+}
+
+msa_mode resolve(const msa_shape& s, msa_mode mode) {
+  if (mode != MSA_AUTO) return mode;
+  if (s.list_q > 1) return MSA_Q_OUTER;
+  const int64_t nb_max = cdiv(s.max_k, s.block);
+  const double nsb = (double)std::min<int64_t>((int64_t)s.batch * s.hkv * nb_max,
+                                               (int64_t)s.total_q * s.hkv * s.topk);
+  if (s.total_q == 0) return MSA_KV_OUTER;
+  const double x = crossover_x(s, 8.0, 16.0);
+  return (nsb / s.total_q < x) ? MSA_KV_OUTER : MSA_Q_OUTER;
+}
+
+msa_status check_mode(const msa_shape& s, msa_mode mode, msa_mode* out) {
+  if (mode != MSA_AUTO && mode != MSA_KV_OUTER && mode != MSA_Q_OUTER) return MSA_ERR_MODE;
+  const msa_mode m = resolve(s, mode);
+  if (m == MSA_KV_OUTER) {
+    const int64_t nb_max = cdiv(s.max_k, s.block);
+    if (nb_max > 8192) return MSA_ERR_SHAPE;           // LDS bitmap tile of the plan
+    const int64_t words = (int64_t)s.batch * s.hkv * nb_max * cdiv(s.max_q, kWordQ);
+    if (words + 1 > kInt32Max) return MSA_ERR_SHAPE;
+  }
+  *out = m;
+  return MSA_OK;
+}
+
+void fail_launch(hipError_t e) { g_last_error = hipGetErrorString(e); }
+
+}  // namespace
+
+Geometry geometry(const msa_shape& s, msa_mode mode) {
+  Geometry g{};
+  g.group = s.hq / s.hkv;
+  g.nb_max = cdiv(s.max_k, s.block);
+  g.tiles_max = cdiv(s.max_q, s.list_q);
+  g.n_lists = s.list_q == 1 ? s.total_q : (int64_t)s.batch * g.tiles_max;
+  g.splits = 1;
+  if (mode == MSA_KV_OUTER) {
+    g.w_max = cdiv(s.max_q, kWordQ);
+    g.n_buckets = (int64_t)s.batch * s.hkv * g.nb_max;
+    g.n_words = g.n_buckets * g.w_max;
+    g.e_max = (int64_t)s.total_q * s.hkv * s.topk;
+    g.n_scan_blocks = cdiv(g.n_words, kScanTile);
+  } else {
+    g.splits = s.list_q == 1 ? choose_splits(s) : 1;
+    g.e_max = g.splits > 1 ? (int64_t)s.total_q * s.hkv * g.splits : 0;
+  }
+  return g;
+}
+
+Layout layout(const msa_shape& s, msa_mode mode) {
+  const Geometry g = geometry(s, mode);
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  L.counters = take(64 * 4);
+  if (mode == MSA_KV_OUTER) {
+    L.slots = s.topk;
+    L.masks = take((size_t)g.n_words * 8);
+    L.offsets = take((size_t)(g.n_words + 1) * 4);
+    L.scan_sums = take((size_t)(g.n_scan_blocks + 1) * 4);
+    L.entry_q = take((size_t)g.e_max * 4);
+    L.cmap = take((size_t)s.total_q * s.hkv * s.topk * 4);
+  } else {
+    L.slots = g.splits;
+    L.masks = L.offsets = L.scan_sums = L.entry_q = off;
+    L.cmap = take(g.splits > 1 ? (size_t)s.total_q * s.hkv * g.splits * 4 : 0);
+  }
+  L.part_lse = take((size_t)g.e_max * g.group * 4);
+  L.part_o = take((size_t)g.e_max * g.group * s.d * 2);
+  L.total = off;
+  return L;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+const char* msa_status_string(msa_status st) {
+  switch (st) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_NULL: return "null pointer argument";
+    case MSA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case MSA_ERR_DTYPE: return "unknown dtype";
+    case MSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MSA_ERR_MODE: return "mode not allowed";
+    case MSA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+msa_status msa_resolve_mode(const msa_shape* shape, msa_mode mode, msa_mode* chosen) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!chosen) return MSA_ERR_NULL;
+  return check_mode(*shape, mode, chosen);
+}
+
+msa_status msa_crossover(const msa_shape* shape, double bw_hbm, double bw_cache, double* x) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!x) return MSA_ERR_NULL;
+  if (!(bw_hbm > 0)) return MSA_ERR_SHAPE;
+  if (bw_cache <= 0) bw_cache = 2.0 * bw_hbm;
+  *x = crossover_x(*shape, bw_hbm, bw_cache);
+  return MSA_OK;
+}
+
+msa_status msa_workspace_layout_of(const msa_shape* shape, msa_mode mode,
+                                   msa_workspace_layout* out) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!out) return MSA_ERR_NULL;
+  msa_mode m;
+  st = check_mode(*shape, mode, &m);
+  if (st != MSA_OK) return st;
+  const Layout L = layout(*shape, m);
+  const Geometry g = geometry(*shape, m);
+  out->counters = L.counters;
+  out->masks = L.masks;
+  out->offsets = L.offsets;
+  out->scan_sums = L.scan_sums;
+  out->entry_q = L.entry_q;
+  out->cmap = L.cmap;
+  out->part_lse = L.part_lse;
+  out->part_o = L.part_o;
+  out->total = L.total;
+  out->slots = L.slots;
+  out->n_words = (int32_t)g.n_words;
+  out->w_max = (int32_t)g.w_max;
+  out->nb_max = (int32_t)g.nb_max;
+  return MSA_OK;
+}
+
+msa_status msa_workspace_size(const msa_shape* shape, msa_mode mode, size_t* bytes) {
+  if (!bytes) return MSA_ERR_NULL;
+  msa_workspace_layout L;
+  msa_status st = msa_workspace_layout_of(shape, mode, &L);
+  if (st != MSA_OK) return st;
+  *bytes = L.total;
+  return MSA_OK;
+}
+
+msa_status msa_index_workspace_size(const msa_shape* shape, size_t* bytes) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  *bytes = index_workspace_bytes(*shape);
+  return MSA_OK;
+}
+
+msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                          const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                          float* topk_score, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (s.list_q != 1 || (s.dp != 32 && s.dp != 64)) return MSA_ERR_SHAPE;
+  if ((int64_t)s.total_q * s.hkv * s.dp > kInt32Max * 2LL) return MSA_ERR_SHAPE;
+  if (!cu_q || !cu_k || !topk_idx) return MSA_ERR_NULL;
+  if (s.total_q > 0 && !q_idx) return MSA_ERR_NULL;
+  if (s.total_k > 0 && !k_idx) return MSA_ERR_NULL;
+  hipError_t e;
+  if (s.max_q <= kSplitIndexMaxQ) {
+    const int64_t nb_max = cdiv(s.max_k, s.block);
+    if (cdiv(nb_max, kSplitIndexChunk) > 512) return MSA_ERR_SHAPE;
+    if ((int64_t)s.batch * s.max_q > 65535) return MSA_ERR_SHAPE;
+    const size_t need = index_workspace_bytes(s);
+    if (!workspace || ws_bytes < need) return MSA_ERR_WORKSPACE;
+    e = launch_index_split(s, q_idx, k_idx, cu_q, cu_k, topk_idx, topk_score, workspace, stream);
+  } else {
+    e = launch_index_tile(s, q_idx, k_idx, cu_q, cu_k, topk_idx, topk_score, stream);
+  }
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
+static msa_status prep(const msa_shape* shape, msa_mode mode, const void* workspace,
+                       size_t ws_bytes, msa_mode* m, Geometry* g, Layout* L) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  st = check_mode(*shape, mode, m);
+  if (st != MSA_OK) return st;
+  *g = geometry(*shape, *m);
+  *L = layout(*shape, *m);
+  if (!workspace || ws_bytes < L->total) return MSA_ERR_WORKSPACE;
+  return MSA_OK;
+}
+
+msa_status msa_plan(const msa_shape* shape, const int32_t* topk_idx, const int32_t* cu_q,
+                    const int32_t* cu_k, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  msa_mode m;
+  Geometry g;
+  Layout L;
+  msa_status st = prep(shape, MSA_KV_OUTER, workspace, ws_bytes, &m, &g, &L);
+  if (st != MSA_OK) return st;
+  if (!topk_idx || !cu_q || !cu_k) return MSA_ERR_NULL;
+  hipError_t e = launch_plan(*shape, g, L, topk_idx, cu_q, cu_k, (char*)workspace, stream);
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
+msa_status msa_attn_main(const msa_shape* shape, const void* q, const void* k, const void* v,
+                         const float* descale_qkv, float softmax_scale, const int32_t* cu_q,
+                         const int32_t* cu_k, void* workspace, size_t ws_bytes,
+                         hipStream_t stream) {
+  msa_mode m;
+  Geometry g;
+  Layout L;
+  msa_status st = prep(shape, MSA_KV_OUTER, workspace, ws_bytes, &m, &g, &L);
+  if (st != MSA_OK) return st;
+  if (!cu_q || !cu_k) return MSA_ERR_NULL;
+  if ((shape->total_q > 0 && !q) || (shape->total_k > 0 && (!k || !v))) return MSA_ERR_NULL;
+  if (shape->dtype == MSA_FP8_E4M3 && !descale_qkv) return MSA_ERR_NULL;
+  hipError_t e = launch_attn_kv(*shape, g, L, q, k, v, descale_qkv, softmax_scale, cu_q, cu_k,
+                                (char*)workspace, stream);
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
+msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void* k,
+                               const void* v, const float* descale_qkv, float softmax_scale,
+                               const int32_t* topk_idx, const int32_t* cu_q,
+                               const int32_t* cu_k, msa_mode mode, void* workspace,
+                               size_t ws_bytes, void* o, float* lse, hipStream_t stream) {
+  msa_mode m;
+  Geometry g;
+  Layout L;
+  msa_status st = prep(shape, mode, workspace, ws_bytes, &m, &g, &L);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (!topk_idx || !cu_q || !cu_k) return MSA_ERR_NULL;
+  if ((s.total_q > 0 && !q) || (s.total_k > 0 && (!k || !v))) return MSA_ERR_NULL;
+  if (s.dtype == MSA_FP8_E4M3 && !descale_qkv) return MSA_ERR_NULL;
+  hipError_t e;
+  if (m == MSA_KV_OUTER) {
+    e = launch_plan(s, g, L, topk_idx, cu_q, cu_k, (char*)workspace, stream);
+    if (e == hipSuccess)
+      e = launch_attn_kv(s, g, L, q, k, v, descale_qkv, softmax_scale, cu_q, cu_k,
+                         (char*)workspace, stream);
+  } else {
+    if (g.splits == 1 && s.total_q > 0 && !o) return MSA_ERR_NULL;
+    e = launch_attn_q(s, g, L, q, k, v, descale_qkv, softmax_scale, topk_idx, cu_q, cu_k,
+                      (char*)workspace, o, lse, stream);
+  }
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
+msa_status msa_combine(const msa_shape* shape, msa_mode mode, const void* workspace,
+                       size_t ws_bytes, void* o, float* lse, hipStream_t stream) {
+  msa_mode m;
+  Geometry g;
+  Layout L;
+  msa_status st = prep(shape, mode, workspace, ws_bytes, &m, &g, &L);
+  if (st != MSA_OK) return st;
+  if (m == MSA_Q_OUTER && g.splits == 1) return MSA_OK;
+  if (shape->total_q > 0 && !o) return MSA_ERR_NULL;
+  hipError_t e = launch_combine(*shape, g, L, (const char*)workspace, o, lse, stream);
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
+}  // extern "C"

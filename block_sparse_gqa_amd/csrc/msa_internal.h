@@ -1,0 +1,77 @@
+// Host-side internals of libmsa: workspace plan and kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/msa.h"
+
+namespace msa {
+
+// Threshold below which the index branch splits the key range across workgroups instead of
+// tiling queries (decode and other short-query calls).
+constexpr int kSplitIndexMaxQ = 16;
+// Blocks of keys scored by one workgroup of the split index kernel.
+constexpr int kSplitIndexChunk = 32;
+// Queries per inverted-index bitmap word.
+constexpr int kWordQ = 64;
+// Elements per workgroup in the scan kernels.
+constexpr int kScanTile = 4096;
+
+struct Geometry {
+  int64_t nb_max;        // ceil(max_k / block)
+  int64_t w_max;         // ceil(max_q / 64): bitmap words per bucket
+  int64_t n_buckets;     // batch * hkv * nb_max
+  int64_t n_words;       // n_buckets * w_max
+  int64_t e_max;         // total_q * hkv * topk (upper bound on entries)
+  int64_t n_scan_blocks; // ceil(n_words / kScanTile)
+  int64_t n_lists;       // rows of topk_idx: total_q, or batch * tiles_max for tile lists
+  int64_t tiles_max;     // ceil(max_q / list_q)
+  int group;             // hq / hkv
+  int splits;            // Q-outer: splits of each list (1 = output written directly)
+  int64_t index_chunks;  // split index kernel: key chunks per sequence
+};
+
+// Offsets (bytes) of each region of the caller's workspace.
+struct Layout {
+  size_t counters;      // int32[64]: [0] = number of entries
+  size_t masks;         // uint64 [n_words]
+  size_t offsets;       // int32  [n_words + 1]
+  size_t scan_sums;     // int32  [n_scan_blocks + 1]
+  size_t entry_q;       // int32  [e_max]
+  size_t cmap;          // int32  [total_q * hkv * slots]
+  size_t part_lse;      // float  [e_max * group]
+  size_t part_o;        // bf16   [e_max * group * d]
+  size_t total;
+  int slots;            // combine slots per (query, group): topk or splits
+};
+
+Geometry geometry(const msa_shape& s, msa_mode mode);
+Layout layout(const msa_shape& s, msa_mode mode);
+size_t index_workspace_bytes(const msa_shape& s);
+
+// ----- launchers (return hipSuccess or the launch error)
+hipError_t launch_index_tile(const msa_shape& s, const void* q_idx, const void* k_idx,
+                             const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                             float* topk_score, hipStream_t st);
+hipError_t launch_index_split(const msa_shape& s, const void* q_idx, const void* k_idx,
+                              const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                              float* topk_score, void* ws, hipStream_t st);
+
+hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
+                       const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k,
+                       char* ws, hipStream_t st);
+hipError_t launch_attn_kv(const msa_shape& s, const Geometry& g, const Layout& L,
+                          const void* q, const void* k, const void* v, const float* descale,
+                          float scale, const int32_t* cu_q, const int32_t* cu_k, char* ws,
+                          hipStream_t st);
+hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
+                         const void* q, const void* k, const void* v, const float* descale,
+                         float scale, const int32_t* lists, const int32_t* cu_q,
+                         const int32_t* cu_k, char* ws, void* o, float* lse, hipStream_t st);
+hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L,
+                          const char* ws, void* o, float* lse, hipStream_t st);
+
+int device_cu_count();
+
+}  // namespace msa

@@ -1,0 +1,241 @@
+// Block -> query inverted index and combine map for the KV-outer schedule.
+//
+// "Kernel optimization for MiniMax M3 on NVIDIA Blackwell" (section 2): the attention kernel
+// writes partial outputs contiguously in work order and an index (query, kv head, slot) ->
+// location lets the combine kernel gather them; a deterministic, atomic-free scheduler
+// flattens all (kv head, kv block, query) work into one sequence. "Sparse Attention"
+// (Chapter 5, reverse index): for each block, the queries that chose it, and each one's
+// place in the query's list.
+//
+// Entries are the valid (query, group, block) triples, ordered by (sequence, group, block,
+// query). The order is fixed by bitmaps rather than by atomics:
+//  1. plan_mask: bucket (s, g, b) gets one 64-bit word per 64 queries, bit i set when query
+//     64w + i listed block b (LDS atomics only set bits, so the result is order-free);
+//  2. a three-pass exclusive scan of the word popcounts gives every word's first entry;
+//  3. plan_scatter: an entry's index is its word's offset plus the popcount of the lower
+//     bits; it records the query row and fills the combine map.
+#include <algorithm>
+
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+struct PlanArgs {
+  const int32_t* lists;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  unsigned long long* masks;
+  const int32_t* offsets;
+  int32_t* entry_q;
+  int32_t* cmap;
+  int total_q, total_k, max_q, max_k;
+  int hkv, topk, list_q, tiles_max, nb_max, w_max, wpb, causal;
+};
+
+// Block b of list slot `slot` is a real entry for this query: in range, first occurrence,
+// and (causal) holding at least one key at or before the query's position.
+__device__ __forceinline__ int entry_block(const PlanArgs& a, const Seq& sq, int il, int slot,
+                                           const int32_t* L) {
+  const int b = L[slot];
+  const int nb = min((sq.nk + kBlock - 1) / kBlock, a.nb_max);
+  if (b < 0 || b >= nb) return -1;
+  if (a.causal && b * kBlock > sq.nk - sq.nq + il) return -1;
+  for (int p = 0; p < slot; ++p)
+    if (L[p] == b) return -1;
+  return b;
+}
+
+__device__ __forceinline__ const int32_t* list_of(const PlanArgs& a, int s, const Seq& sq,
+                                                  int il, int h) {
+  const int64_t row = a.list_q == 1 ? (int64_t)(sq.q0 + il)
+                                    : (int64_t)s * a.tiles_max + il / a.list_q;
+  return a.lists + (row * a.hkv + h) * a.topk;
+}
+
+__global__ __launch_bounds__(256) void plan_mask_kernel(PlanArgs a) {
+  extern __shared__ unsigned long long lm[];   // [nb_max][wpb]
+  const int s = blockIdx.z, h = blockIdx.y;
+  const int w0 = blockIdx.x * a.wpb;
+  const int tid = threadIdx.x;
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  const int n_lm = a.nb_max * a.wpb;
+  for (int i = tid; i < n_lm; i += 256) lm[i] = 0ull;
+  __syncthreads();
+  const int qa = w0 * kWordQ;
+  const int qb = min((w0 + a.wpb) * kWordQ, sq.nq);
+  const int n = max(qb - qa, 0) * a.topk;
+  for (int i = tid; i < n; i += 256) {
+    const int il = qa + i / a.topk, slot = i % a.topk;
+    const int32_t* L = list_of(a, s, sq, il, h);
+    const int b = entry_block(a, sq, il, slot, L);
+    if (b >= 0) atomicOr(&lm[b * a.wpb + (il / kWordQ - w0)], 1ull << (il % kWordQ));
+  }
+  __syncthreads();
+  const size_t bucket0 = ((size_t)s * a.hkv + h) * a.nb_max;
+  for (int i = tid; i < n_lm; i += 256) {
+    const int b = i / a.wpb, wl = i % a.wpb;
+    const int w = w0 + wl;
+    if (w < a.w_max) a.masks[(bucket0 + b) * a.w_max + w] = lm[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void plan_scatter_kernel(PlanArgs a) {
+  const int s = blockIdx.z, h = blockIdx.y;
+  const int w0 = blockIdx.x * a.wpb;
+  const int tid = threadIdx.x;
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  const int qa = w0 * kWordQ;
+  const int qb = min((w0 + a.wpb) * kWordQ, sq.nq);
+  const int n = max(qb - qa, 0) * a.topk;
+  const size_t bucket0 = ((size_t)s * a.hkv + h) * a.nb_max;
+  for (int i = tid; i < n; i += 256) {
+    const int il = qa + i / a.topk, slot = i % a.topk;
+    const int32_t* L = list_of(a, s, sq, il, h);
+    const int b = entry_block(a, sq, il, slot, L);
+    int e = -1;
+    if (b >= 0) {
+      const size_t wi = (bucket0 + b) * a.w_max + il / kWordQ;
+      const unsigned long long m = a.masks[wi];
+      const unsigned long long below = (1ull << (il % kWordQ)) - 1ull;
+      e = a.offsets[wi] + __popcll(m & below);
+      a.entry_q[e] = sq.q0 + il;
+    }
+    a.cmap[((size_t)(sq.q0 + il) * a.hkv + h) * a.topk + slot] = e;
+  }
+}
+
+// ---- three-pass exclusive scan of popcounts (kScanTile words per workgroup)
+constexpr int kPer = kScanTile / 256;
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    pre += (w < wave) ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return pre + x - v;
+}
+
+__global__ __launch_bounds__(256) void scan_reduce_kernel(const unsigned long long* __restrict__ masks,
+                                                          int64_t n_words, int32_t* __restrict__ sums) {
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kPer;
+  int v = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (base + i < n_words) v += __popcll(masks[base + i]);
+  int tot;
+  block_exclusive_scan(v, &tot);
+  if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(256) void scan_top_kernel(int32_t* __restrict__ sums, int64_t n_blocks,
+                                                       int32_t* __restrict__ counters,
+                                                       int32_t* __restrict__ offsets_end) {
+  int carry = 0;
+  for (int64_t b0 = 0; b0 < n_blocks; b0 += 256) {
+    const int64_t i = b0 + threadIdx.x;
+    const int v = i < n_blocks ? sums[i] : 0;
+    int tot;
+    const int ex = block_exclusive_scan(v, &tot);
+    if (i < n_blocks) sums[i] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) {
+    counters[0] = carry;
+    *offsets_end = carry;
+  }
+}
+
+__global__ __launch_bounds__(256) void scan_down_kernel(const unsigned long long* __restrict__ masks,
+                                                        int64_t n_words, const int32_t* __restrict__ sums,
+                                                        int32_t* __restrict__ offsets) {
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kPer;
+  int cnt[kPer];
+  int v = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    cnt[i] = (base + i < n_words) ? __popcll(masks[base + i]) : 0;
+    v += cnt[i];
+  }
+  int tot;
+  int run = block_exclusive_scan(v, &tot) + sums[blockIdx.x];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (base + i < n_words) offsets[base + i] = run;
+    run += cnt[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
+                       const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k,
+                       char* ws, hipStream_t st) {
+  PlanArgs a;
+  a.lists = lists;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.masks = reinterpret_cast<unsigned long long*>(ws + L.masks);
+  a.offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
+  a.entry_q = reinterpret_cast<int32_t*>(ws + L.entry_q);
+  a.cmap = reinterpret_cast<int32_t*>(ws + L.cmap);
+  a.total_q = s.total_q;
+  a.total_k = s.total_k;
+  a.max_q = s.max_q;
+  a.max_k = s.max_k;
+  a.hkv = s.hkv;
+  a.topk = s.topk;
+  a.list_q = s.list_q;
+  a.tiles_max = (int)g.tiles_max;
+  a.nb_max = (int)g.nb_max;
+  a.w_max = (int)g.w_max;
+  a.causal = s.causal;
+  int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sums = reinterpret_cast<int32_t*>(ws + L.scan_sums);
+
+  if (g.n_words == 0) {
+    // nothing can be selected: zero entries
+    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, sums, (int64_t)0, counters,
+                       offsets);
+    return hipGetLastError();
+  }
+  // words per workgroup: keep the LDS bitmap tile at <= 64 KiB
+  int wpb = (int)std::max<int64_t>(1, std::min<int64_t>(8, 8192 / std::max<int64_t>(1, g.nb_max)));
+  wpb = (int)std::min<int64_t>(wpb, g.w_max);
+  a.wpb = wpb;
+  const size_t lds = (size_t)g.nb_max * wpb * 8;
+  dim3 grid((unsigned)((g.w_max + wpb - 1) / wpb), s.hkv, s.batch);
+  hipLaunchKernelGGL(plan_mask_kernel, grid, dim3(256), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned nblk = (unsigned)g.n_scan_blocks;
+  hipLaunchKernelGGL(scan_reduce_kernel, dim3(nblk), dim3(256), 0, st,
+                     (const unsigned long long*)a.masks, (int64_t)g.n_words, sums);
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, sums, (int64_t)nblk, counters,
+                     offsets + g.n_words);
+  hipLaunchKernelGGL(scan_down_kernel, dim3(nblk), dim3(256), 0, st,
+                     (const unsigned long long*)a.masks, (int64_t)g.n_words,
+                     (const int32_t*)sums, offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_scatter_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,201 @@
+/*
+ * msa.h - C ABI of libmsa: MiniMax-style block-sparse GQA attention on AMD MI355X (gfx950).
+ *
+ * The operator ("Kernel optimization for MiniMax M3 on NVIDIA Blackwell", summary section)
+ * cuts the KV sequence into 128-token blocks; an index branch scores the blocks for every
+ * GQA group and keeps the top-K; a main branch computes exact attention over only the
+ * selected blocks. This library runs the three steps as separate calls:
+ *
+ *   msa_index_topk       index branch: max-pooled proxy scores + top-K, local block forced
+ *   msa_sparse_attn_fwd  main branch: KV-outer partials (or Q-outer output) over the lists
+ *   msa_combine          log-sum-exp merge of the per-slot partials into O and LSE
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers allocated and owned by the caller; the library never
+ *    allocates, frees, synchronises, or copies device memory to the host. Work is enqueued on
+ *    `stream` (NULL = the default stream) and the call returns without waiting.
+ *  - Layouts are dense row-major. Q is [total_q, hq, d]; K and V are [total_k, hkv, d];
+ *    q_idx is [total_q, hkv, dp]; k_idx is [total_k, hkv, dp]. Query head h belongs to KV
+ *    group h / (hq / hkv), so the heads of one group are adjacent.
+ *  - Variable-length batches: cu_q and cu_k are DEVICE int32 arrays of batch + 1
+ *    non-decreasing offsets (cu[0] = 0, cu[batch] = total). Sequence s owns query rows
+ *    [cu_q[s], cu_q[s+1]) and key rows [cu_k[s], cu_k[s+1]). Query i of a sequence with N
+ *    queries and Nk keys sits at position pos = Nk - N + i (bottom-right alignment), and its
+ *    local block is floor(pos / block). Each sequence must satisfy N <= max_q and
+ *    Nk <= max_k; the library cannot check device-side values (no device-to-host copy).
+ *  - Errors: argument checks run on the host before anything is enqueued; a non-OK status
+ *    means nothing was launched. MSA_ERR_LAUNCH means a kernel launch failed (the HIP error
+ *    text is in msa_last_error(), kept per thread).
+ *  - Determinism: identical inputs give bitwise-identical outputs (no floating-point atomics;
+ *    fixed reduction orders).
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_NULL = 1,       /* a required pointer is NULL */
+  MSA_ERR_SHAPE = 2,      /* sizes outside what this build supports, or inconsistent */
+  MSA_ERR_DTYPE = 3,      /* unknown dtype */
+  MSA_ERR_WORKSPACE = 4,  /* workspace pointer NULL or smaller than msa_workspace_size() */
+  MSA_ERR_MODE = 5,       /* mode value unknown or not allowed for these shapes */
+  MSA_ERR_LAUNCH = 6      /* a HIP kernel launch failed */
+} msa_status;
+
+typedef enum {
+  MSA_BF16 = 0,       /* Q, K, V in bfloat16 */
+  MSA_FP8_E4M3 = 1    /* Q, K, V in OCP fp8 e4m3fn with per-tensor fp32 descales */
+} msa_dtype;
+
+/* Schedule of the main branch ("Kernel optimization ...", section 1: the two structures).
+ * KV_OUTER: each selected KV block is loaded once and every query that chose it is gathered
+ * in; partial outputs are written and msa_combine merges them. Q_OUTER: each group of rows
+ * that shares a list walks its blocks with an online softmax. AUTO picks by the nsb/N
+ * bandwidth crossover (see msa_crossover). */
+typedef enum { MSA_AUTO = 0, MSA_KV_OUTER = 1, MSA_Q_OUTER = 2 } msa_mode;
+
+typedef struct {
+  int32_t batch;    /* number of sequences, >= 1 */
+  int32_t total_q;  /* rows of Q / q_idx: sum of per-sequence query counts, >= 0 */
+  int32_t total_k;  /* rows of K / V / k_idx */
+  int32_t max_q;    /* upper bound on any sequence's query count (sizes the schedule) */
+  int32_t max_k;    /* upper bound on any sequence's key count */
+  int32_t hq;       /* query heads */
+  int32_t hkv;      /* KV heads (GQA groups); hq % hkv == 0, hq / hkv in {1, 2, 4, 8, 16} */
+  int32_t d;        /* head dim: 128 */
+  int32_t dp;       /* proxy (index) dim: 32 or 64; ignored when the index branch is unused */
+  int32_t block;    /* KV block size: 128 */
+  int32_t topk;     /* selected blocks per list: 1..16 */
+  int32_t causal;   /* 1: key u visible to a query at position pos iff u <= pos */
+  int32_t dtype;    /* msa_dtype of Q/K/V; proxies are always bf16 */
+  int32_t list_q;   /* 1: per-query lists topk_idx [total_q, hkv, topk];
+                       128: per-Q-tile lists [batch * ceil(max_q/128), hkv, topk], row
+                       s * ceil(max_q/128) + t holds the list of queries [128t, 128t+128)
+                       of sequence s ("Sparse Attention", Chapter 1, per-Q-tile selection) */
+} msa_shape;
+
+/* Layout of the workspace regions, for tests and tools. Offsets are in bytes from the start
+ * of the workspace; a region of size 0 is unused. */
+typedef struct {
+  size_t counters;     /* int32[64]; [0] = number of (query-group, block) entries E */
+  size_t masks;        /* uint64 bitmaps, bucket-major: bucket (s, g, b), word w of 64 queries */
+  size_t offsets;      /* int32 exclusive scan of the bitmap popcounts, n_words + 1 values */
+  size_t scan_sums;    /* int32 scratch of the scan */
+  size_t entry_q;      /* int32 [E]: query row of entry e (entries sorted by s, g, b, query) */
+  size_t cmap;         /* int32 [total_q, hkv, slots]: partial index of each slot, -1 = none */
+  size_t part_lse;     /* float [E, hq/hkv]: log-sum-exp of each partial */
+  size_t part_o;       /* bf16 [E, hq/hkv, d]: normalised partial output */
+  size_t total;        /* bytes needed */
+  int32_t slots;       /* slots per (query, group) in cmap */
+  int32_t n_words;     /* bitmap words (0 for Q-outer) */
+  int32_t w_max;       /* bitmap words per bucket */
+  int32_t nb_max;      /* blocks per sequence bound */
+} msa_workspace_layout;
+
+/* ---- host-only queries (no GPU needed) ---------------------------------------------- */
+
+/* Bytes of workspace msa_sparse_attn_fwd and msa_combine need for `shape` under `mode`.
+ * KV-outer holds the inverted index (bitmaps, scan, entry list, combine map) and E bf16
+ * partials of (hq/hkv) x d plus fp32 LSEs, E <= total_q * hkv * topk. Errors: NULL, SHAPE,
+ * DTYPE, MODE. */
+msa_status msa_workspace_size(const msa_shape* shape, msa_mode mode, size_t* bytes);
+
+/* Region offsets of that workspace (same errors). */
+msa_status msa_workspace_layout_of(const msa_shape* shape, msa_mode mode,
+                                   msa_workspace_layout* out);
+
+/* Bytes of workspace msa_index_topk needs (non-zero only for short-query calls, where the key
+ * range is split across workgroups and the partial top-K lists are merged). */
+msa_status msa_index_workspace_size(const msa_shape* shape, size_t* bytes);
+
+/* The schedule msa_sparse_attn_fwd runs for `mode` (AUTO resolved). Per-Q-tile lists always
+ * run Q-outer; otherwise AUTO runs KV-outer iff nsb_max / total_q < msa_crossover(), where
+ * nsb_max = min(batch * hkv * ceil(max_k/block), total_q * hkv * topk) bounds the distinct
+ * selected blocks from the shape alone. */
+msa_status msa_resolve_mode(const msa_shape* shape, msa_mode mode, msa_mode* chosen);
+
+/* Bandwidth-roofline crossover X ("Kernel optimization ...", section 1 and appendix):
+ * KV-outer is the faster schedule when nsb / N < X. KV-outer moves each selected block once
+ * plus, per query, Q, its partials (written and read back) and O through HBM; Q-outer
+ * re-reads every list's blocks through the cache at bw_cache. With e = bytes per Q/K/V
+ * element, partials bf16 and LSE fp32, per query token:
+ *   kv_per_n = hq*d*e + hq*topk*(2*2*d + 2*4) + hq*d*2 ;  q_per_n = hkv*topk*2*block*d*e + hq*d*(e+2)
+ *   X = (q_per_n * bw_hbm / bw_cache - kv_per_n) / (2*block*d*e).
+ * bw_* in any common unit; bw_cache = 0 selects the MI355X default ratio (2.0). */
+msa_status msa_crossover(const msa_shape* shape, double bw_hbm, double bw_cache, double* x);
+
+const char* msa_status_string(msa_status st);
+const char* msa_last_error(void);
+
+/* ---- device calls ----------------------------------------------------------------------- */
+
+/* Index branch ("Flash-MSA: accelerating million-token training", proxy forward; "Kernel
+ * optimization ...", summary). For every query row i and group g: for each visible block j
+ * other than the local block c, s_j = max over keys u of block j (u < Nk; u <= pos if causal)
+ * of the fp32 dot product q_idx[i,g,:] . k_idx[u,g,:]; s_c = +inf. topk_idx[i,g,:] receives
+ * the first min(topk, #visible) blocks by (s descending, block index ascending) - the local
+ * block in slot 0 - and -1 in unused slots. topk_score (nullable) receives the matching
+ * scores (+inf for the local block, -inf for unused slots).
+ * In: q_idx, k_idx bf16 (layouts above), cu_q, cu_k. Out: topk_idx [total_q, hkv, topk]
+ * int32, topk_score [total_q, hkv, topk] fp32. workspace: msa_index_workspace_size() bytes
+ * (may be NULL when that size is 0). Requires list_q == 1, dp in {32, 64}. */
+msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                          const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                          float* topk_score, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Main branch ("Kernel optimization ...", summary and section 2; "Sparse Attention",
+ * Chapters 1 and 5). Every query head attends, with its own softmax, to the union of the
+ * keys of its group's selected blocks (key u of block b is u = block*b + offset, u < Nk, and
+ * u <= pos if causal); scores are softmax_scale * q.k (times descale_q * descale_k for fp8),
+ * values are scaled by descale_v. Lists: topk_idx as described for list_q; entries outside
+ * [0, ceil(Nk/block)), repeated entries, and (causal) blocks wholly after the query are
+ * ignored.
+ * KV_OUTER: builds the block -> query inverted index in the workspace, then one kernel loads
+ * each selected block once and writes, for every (query-group, block) entry, the normalised
+ * partial output (bf16) and its LSE (fp32) contiguously in entry order; msa_combine must
+ * follow on the same stream. `o` and `lse` are not touched.
+ * Q_OUTER: writes O (same dtype as the result of msa_combine: bf16 [total_q, hq, d]) and LSE
+ * (fp32 [total_q, hq]) directly, or - when the schedule splits long lists - partials that
+ * msa_combine merges. Calling msa_combine after Q_OUTER is always valid.
+ * descale_qkv: DEVICE float[3] (dq, dk, dv) for fp8; NULL for bf16. The workspace must hold
+ * msa_workspace_size(shape, mode) bytes and stay untouched until msa_combine has run. */
+msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void* k,
+                               const void* v, const float* descale_qkv, float softmax_scale,
+                               const int32_t* topk_idx, const int32_t* cu_q,
+                               const int32_t* cu_k, msa_mode mode, void* workspace,
+                               size_t ws_bytes, void* o, float* lse, hipStream_t stream);
+
+/* KV-outer halves of msa_sparse_attn_fwd, for timing the inverted-index build and the
+ * attention kernel separately. msa_plan(...) followed by msa_attn_main(...) with the same
+ * arguments is exactly msa_sparse_attn_fwd(..., MSA_KV_OUTER, ...). */
+msa_status msa_plan(const msa_shape* shape, const int32_t* topk_idx, const int32_t* cu_q,
+                    const int32_t* cu_k, void* workspace, size_t ws_bytes, hipStream_t stream);
+msa_status msa_attn_main(const msa_shape* shape, const void* q, const void* k, const void* v,
+                         const float* descale_qkv, float softmax_scale, const int32_t* cu_q,
+                         const int32_t* cu_k, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Combine ("Sparse Attention", Chapter 5, partial outputs and combine; "Kernel optimization
+ * ...", section 2: the combine kernel gathers through the index map). For every query row and
+ * head: LSE = log sum_slot exp(lse_slot) over the valid slots (max-shifted), O = sum_slot
+ * exp(lse_slot - LSE) * O_slot; with no valid slot, O = 0 and LSE = -inf. Reads the
+ * workspace written by msa_sparse_attn_fwd with the same shape and mode. Out: o bf16
+ * [total_q, hq, d], lse fp32 [total_q, hq] (lse may be NULL). A no-op when the Q-outer
+ * schedule already wrote O. */
+msa_status msa_combine(const msa_shape* shape, msa_mode mode, const void* workspace,
+                       size_t ws_bytes, void* o, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -37,8 +37,9 @@ def seq_rows(case: Case, rows: np.ndarray | None):
 
 
 def tile_base(case: Case, s: int) -> int:
-    lq = case.cfg.list_q
-    return sum(-(-int(case.cu_q[r + 1] - case.cu_q[r]) // lq) for r in range(s))
+    """Row of sequence s's first tile list: lists are laid out [B * tiles_max, Hkv, K]."""
+    tiles_max = -(-case.max_q // case.cfg.list_q)
+    return s * tiles_max
 
 
 def run(case: Case, rows: np.ndarray | None = None, lists: np.ndarray | None = None,

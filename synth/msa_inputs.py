@@ -310,11 +310,16 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
 def tile_lists(cfg: Config, cu_q: np.ndarray, seed: int) -> np.ndarray:
     """Per-(Q tile, KV head) block lists: ``topk`` distinct blocks drawn uniformly without
     replacement from ``range(list_pool)``, sorted ascending (the "Sparse Attention" page,
-    Chapter 3, draws independent lists per Q128 tile). Shape [sum ceil(N_s/list_q), Hkv, K]."""
+    Chapter 3, draws independent lists per Q128 tile). Shape [B * tiles_max, Hkv, K] with
+    tiles_max = ceil(max_q / list_q); row s * tiles_max + t is tile t of sequence s (rows past
+    a sequence's last tile hold -1)."""
     rng = np.random.default_rng(_stream(seed, "lists"))
-    n_tiles = sum(-(-int(cu_q[s + 1] - cu_q[s]) // cfg.list_q) for s in range(len(cu_q) - 1))
-    out = np.empty((n_tiles, cfg.hkv, cfg.topk), dtype=np.int32)
-    for t in range(n_tiles):
-        for h in range(cfg.hkv):
-            out[t, h] = np.sort(rng.choice(cfg.list_pool, cfg.topk, replace=False))
+    nq = np.diff(cu_q)
+    tiles_max = -(-int(nq.max()) // cfg.list_q) if nq.size else 0
+    out = np.full((len(nq) * tiles_max, cfg.hkv, cfg.topk), -1, dtype=np.int32)
+    for s in range(len(nq)):
+        for t in range(-(-int(nq[s]) // cfg.list_q)):
+            for h in range(cfg.hkv):
+                out[s * tiles_max + t, h] = np.sort(rng.choice(cfg.list_pool, cfg.topk,
+                                                               replace=False))
     return out
