@@ -1,0 +1,322 @@
+"""Benchmark of the MSA layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of seeded synthetic input already
+resident in HBM: index branch (msa_index_topk) -> inverted index (msa_plan) -> KV-outer
+attention (msa_attn_main) -> LSE combine (msa_combine); Q-outer workloads run
+msa_sparse_attn_fwd in place of the two middle calls. Prints one JSON line.
+
+value = useful FLOPs (4*D per unmasked selected (query, head, key) triple: QK^T and PV only,
+"Sparse Attention", Chapter 3) / whole-step time. Each kernel is also timed with HIP events
+recorded on the stream the library launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_gqa_amd import msa  # noqa: E402
+from synth import msa_inputs as mi    # noqa: E402
+
+PEAK_HBM = 8.0e12            # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15           # dense bf16 MFMA FLOP/s
+KERNEL_SOURCES = ("block_sparse_gqa_amd/csrc/attn_kv.hip", "block_sparse_gqa_amd/csrc/attn_tile.h",
+                  "block_sparse_gqa_amd/csrc/msa_device.h")
+
+WORKLOADS = {
+    # name -> (config key, description)
+    "m3": ("m3", "M3-shape MSA prefill: B=1, N=32768 causal, Hq=64, Hkv=4, D=128, block 128, "
+                 "top-16, proxy dim 64, rank-8 block-reuse bias, bf16"),
+    "tiny": ("tiny", "tiny MSA prefill: B=1, N=2048 causal, Hq=16, Hkv=1, top-4, proxy dim 32, bf16"),
+    "qtile": ("qtile", "per-Q-tile block-sparse fwd: N=8192 non-causal, Hq=Hkv=16, 16 of 64 blocks "
+                       "per Q128 tile, bf16"),
+    "m3_fp8_long": ("m3_fp8_long", "long-context fp8 MSA prefill: N=131072 causal, Hq=64, Hkv=4, "
+                                   "top-16, fp8 e4m3 Q/K/V, bf16 proxies and partials"),
+    "decode": ("decode", "MSA decode: 64 requests x 1 query, Nk uniform over multiples of 128 in "
+                         "[16384, 131072], Hq=64, Hkv=4, top-16, bf16"),
+}
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def useful_pairs(cfg, cu_q, cu_k, lists_np: np.ndarray, list_q: int) -> tuple[int, int]:
+    """(useful (query, head, key) triples, distinct selected (seq, group, block) buckets)."""
+    g = cfg.hq // cfg.hkv
+    total, buckets = 0, 0
+    tiles_max = -(-int(np.max(np.diff(cu_q))) // list_q) if list_q > 1 else 0
+    for s in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[s]), int(cu_q[s + 1])
+        nk = int(cu_k[s + 1] - cu_k[s])
+        nq = q1 - q0
+        if nq == 0:
+            continue
+        nb = -(-nk // 128)
+        pos = nk - nq + np.arange(nq)
+        lst = lists_np[s * tiles_max + np.arange(nq) // list_q] if list_q > 1 else lists_np[q0:q1]
+        for h in range(cfg.hkv):
+            l = lst[:, h, :].astype(np.int64)
+            srt = np.sort(np.where((l >= 0) & (l < nb), l, -1), axis=1)
+            dup = np.zeros_like(srt, dtype=bool)
+            dup[:, 1:] = (srt[:, 1:] == srt[:, :-1]) & (srt[:, 1:] >= 0)
+            b = np.where(dup, -1, srt)
+            start = b * 128
+            end = np.minimum(start + 128, nk)
+            if cfg.causal:
+                end = np.minimum(end, pos[:, None] + 1)
+                b = np.where(start <= pos[:, None], b, -1)
+            ok = b >= 0
+            total += int(np.where(ok, np.maximum(end - start, 0), 0).sum()) * g
+            buckets += int(np.unique(b[ok]).size)
+    return total, buckets
+
+
+class Timer:
+    """HIP events on the current stream around each call of a step."""
+
+    def __init__(self, names):
+        self.names = names
+        self.ev = []
+
+    def step(self):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+        self.ev.append(evs)
+        return evs
+
+    def ms(self):
+        out = {n: 0.0 for n in self.names}
+        for evs in self.ev:
+            for i, n in enumerate(self.names):
+                out[n] += evs[i].elapsed_time(evs[i + 1])
+        return {n: v / max(1, len(self.ev)) for n, v in out.items()}
+
+
+def cpu_baseline(case, budget_s: float) -> dict:
+    """The oracle, untuned, on a bounded sample of the same workload (whole 128-query blocks,
+    index branch + sparse attention for their rows), scaled to useful TFLOP/s."""
+    from oracle import msa_case
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    nqb = -(-case.max_q // 128)
+    rows_done, flops, t_used = [], 0, 0.0
+    rng = np.random.default_rng(0)
+    blocks = rng.permutation(max(1, nqb))
+    t0 = time.perf_counter()
+    for b in blocks:
+        rows = np.arange(b * 128, min(case.total_q, (b + 1) * 128))
+        if case.cfg.length_seed_draw is not None:      # decode: one query per request
+            rows = np.arange(min(case.total_q, 8)) + 8 * (len(rows_done))
+            rows = rows[rows < case.total_q]
+        if rows.size == 0:
+            break
+        out = msa_case.run(case, rows=rows)
+        lists = np.full((case.total_q, case.cfg.hkv, case.cfg.topk), -1, dtype=np.int32)
+        lists[out.rows] = out.topk_idx
+        p, _ = useful_pairs(case.cfg, case.cu_q, case.cu_k, lists, 1)
+        flops += 4 * 128 * p
+        rows_done.append(rows.size)
+        t_used = time.perf_counter() - t0
+        if t_used >= budget_s:
+            break
+    n_rows = int(sum(rows_done))
+    return {"value": flops / max(t_used, 1e-9) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_rows} query rows ({len(rows_done)} groups of whole 128-query blocks, "
+                      f"all heads) of the same workload, index branch + sparse attention, "
+                      f"fp64 NumPy, {t_used:.1f} s wall on {platform.processor() or 'host'}"}
+
+
+def load_traffic(workload: str, launches_bytes_alg: float):
+    path = os.path.join(ROOT, "profiles", f"attn_kv_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="m3", choices=sorted(WORKLOADS))
+    ap.add_argument("--mode", default="auto", choices=["auto", "kv", "q"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also time a plain device copy of this many MiB (counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    cfg_key, desc = WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    case = mi.make_case(cfg_key, seed=args.seed)
+    t_gen = time.perf_counter() - t_gen
+    cfg = case.cfg
+    dtype = msa.MSA_FP8_E4M3 if cfg.dtype == "fp8" else msa.MSA_BF16
+    shape = msa.make_shape(batch=len(case.cu_q) - 1, total_q=case.total_q, total_k=case.total_k,
+                           max_q=case.max_q, max_k=case.max_k, hq=cfg.hq, hkv=cfg.hkv,
+                           topk=cfg.topk, dp=cfg.dp, causal=cfg.causal, dtype=dtype,
+                           list_q=cfg.list_q)
+    mode = {"auto": msa.MSA_AUTO, "kv": msa.MSA_KV_OUTER, "q": msa.MSA_Q_OUTER}[args.mode]
+    chosen = msa.msa_resolve_mode(shape, mode)
+
+    up = lambda t: None if t is None else t.contiguous().to(dev)
+    q, k, v = up(case.q), up(case.k), up(case.v)
+    q_idx, k_idx = up(case.q_idx), up(case.k_idx)
+    cu_q = torch.from_numpy(case.cu_q).to(dev)
+    cu_k = torch.from_numpy(case.cu_k).to(dev)
+    descale = torch.tensor(case.descale, dtype=torch.float32, device=dev) if dtype else None
+    given = torch.from_numpy(case.lists).to(dev) if case.lists is not None else None
+    n_lists = case.total_q
+    topk = given if given is not None else torch.empty((n_lists, cfg.hkv, cfg.topk),
+                                                      dtype=torch.int32, device=dev)
+    iws = torch.empty(max(msa.msa_index_workspace_size(shape) if given is None else 0, 256),
+                      dtype=torch.uint8, device=dev)
+    ws = torch.empty(msa.msa_workspace_size(shape, chosen), dtype=torch.uint8, device=dev)
+    o = torch.empty((case.total_q, cfg.hq, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.total_q, cfg.hq), dtype=torch.float32, device=dev)
+    scale = case.softmax_scale
+
+    kv = chosen == msa.MSA_KV_OUTER
+    names = (["index"] if given is None else []) + (["plan", "attn_main"] if kv else ["attn_q"]) \
+        + ["combine"]
+    timer = Timer(names)
+
+    def step(evs=None):
+        i = 0
+        rec = (lambda: evs[i].record()) if evs else (lambda: None)
+        if evs:
+            evs[0].record()
+        if given is None:
+            msa.msa_index_topk(shape, q_idx, k_idx, cu_q, cu_k, topk, None, iws)
+            if evs:
+                i += 1
+                evs[i].record()
+        if kv:
+            msa.msa_plan(shape, topk, cu_q, cu_k, ws)
+            if evs:
+                i += 1
+                evs[i].record()
+            msa.msa_attn_main(shape, q, k, v, descale, scale, cu_q, cu_k, ws)
+        else:
+            msa.msa_sparse_attn_fwd(shape, q, k, v, descale, scale, topk, cu_q, cu_k, chosen, ws,
+                                    o, lse)
+        if evs:
+            i += 1
+            evs[i].record()
+        msa.msa_combine(shape, chosen, ws, o, lse)
+        if evs:
+            i += 1
+            evs[i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # per-kernel times from events (separate pass so events do not perturb the timed loop)
+    for _ in range(max(3, min(args.steps, 10))):
+        step(timer.step())
+    torch.cuda.synchronize()
+    kms = timer.ms()
+
+    lists_np = topk.cpu().numpy()
+    pairs, nsb = useful_pairs(cfg, case.cu_q, case.cu_k, lists_np, cfg.list_q)
+    flops = 4.0 * 128 * pairs
+    g = cfg.hq // cfg.hkv
+    eb = 1 if dtype else 2
+    n_ent = int(ws[:4].view(torch.int32)[0].item()) if kv else 0
+    res = {
+        "metric": "main-attn TFLOP/s (useful pairs) + % MFMA/HBM roofline; ms per layer call",
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if dtype else "bf16",
+        "data": "synthetic (seeded NumPy draws, see DESIGN.md input recipe)",
+        "config": {"workload": args.workload, "description": desc, "mode": {1: "kv_outer", 2: "q_outer"}[chosen],
+                   "global_batch": len(case.cu_q) - 1, "seq_len": case.max_q,
+                   "hq": cfg.hq, "hkv": cfg.hkv, "d": 128, "block": 128, "topk": cfg.topk,
+                   "dp": cfg.dp, "causal": cfg.causal, "parallelism": "single GPU"},
+        "kernel_ms": kms,
+        "useful_gflop": flops / 1e9,
+        "nsb": nsb, "nsb_over_n": nsb / max(1, case.total_q), "entries": n_ent,
+    }
+    main_name = "attn_main" if kv else "attn_q"
+    t_main = kms[main_name] * 1e-3
+    res["main_attn_tflops"] = flops / t_main / 1e12
+    res["main_attn_mfma_frac"] = flops / t_main / PEAK_BF16
+    if kv:
+        alg = (case.total_q * cfg.hq * 128 * eb            # Q, each query once
+               + nsb * 2 * 128 * 128 * eb                   # selected K and V blocks once
+               + n_ent * g * 128 * 2                        # bf16 partial O written
+               + n_ent * g * 4)                             # fp32 partial LSE written
+        res["roofline"] = {"bound": "hbm", "kernel": "attn_kv_kernel", "achieved": alg / t_main / 1e9,
+                           "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": alg / t_main / PEAK_HBM,
+                           "traffic": load_traffic(args.workload, alg),
+                           "algorithmic_bytes": alg}
+        comb_alg = n_ent * g * (128 * 2 + 4) + case.total_q * cfg.hkv * cfg.topk * 4 \
+            + case.total_q * cfg.hq * (128 * 2 + 4)
+        res["combine_gbps"] = comb_alg / (kms["combine"] * 1e-3) / 1e9
+    else:
+        res["roofline"] = {"bound": "mfma", "kernel": "attn_q_kernel",
+                           "achieved": flops / t_main / 1e12, "peak": PEAK_BF16 / 1e12,
+                           "unit": "TFLOP/s", "frac": flops / t_main / PEAK_BF16, "traffic": None}
+    res["kernel_sha"] = kernel_sha()
+    res["gen_seconds"] = round(t_gen, 1)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        res["copy_probe"] = {"bytes_each_way": n, "gbps": 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

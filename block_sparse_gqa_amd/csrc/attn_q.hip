@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   const uint32_t kv_row = (uint32_t)a.hkv * kD;
 
   bf16x8 bq[8];
-  load_q_operand<FP8>(bq, qb + ((size_t)t * a.hq + hh) * kD * EB, valid, hf);
+  load_q_operand<FP8>(bq, qb + ((size_t)t * a.hq + hh) * kD * EB, hf);
 
   const float ninf = -__builtin_inff();
   float m_run = ninf, l_run = 0.f;
@@ -133,18 +133,19 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
       qk_block(L, bq, sacc, col, hf);
       int kmax = min(127, nk_rel - 1);
       if (a.causal) kmax = min(kmax, pos - u0);
-      const float mb = scale_mask_max(sacc, sl2, kmax, hf);
-      const float m_new = fmaxf(m_run, mb);
-      const float ms = m_new > ninf ? m_new : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - ms);
-      const float lb = exp_sum(sacc, ms);
+      const float mb = mask_max(sacc, kmax, __any(kmax < 127), hf);
+      const float m_new = fmaxf(m_run, mb);          // raw-score units
+      const float c = m_new > ninf ? m_new * sl2 : 0.f;
+      const float alpha = m_run > ninf ? __builtin_amdgcn_exp2f(m_run * sl2 - c) : 0.f;
+      u32x4 pk[4][2];
+      const float lb = exp_pack(sacc, sl2, c, pk);
       l_run = l_run * alpha + lb;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       m_run = m_new;
-      pv_block(L, sacc, oacc, col, hf);
+      pv_block<false>(L, pk, oacc, col, hf);
     }
   }
 
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   if (!valid) return;
   const bool any = l_run > 0.f;
   const float inv = any ? dv / l_run : 0.f;
-  const float lse_v = any ? (m_run + log2f(l_run)) * 0.69314718055994531f : ninf;
+  const float lse_v = any ? (m_run * sl2 + log2f(l_run)) * 0.69314718055994531f : ninf;
   const int g = hh - h * G;
   if (a.splits == 1) {
     store_o_row(a.o + ((size_t)t * a.hq + hh) * kD, oacc, inv, hf);

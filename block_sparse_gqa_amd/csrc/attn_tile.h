@@ -22,7 +22,10 @@ struct KVLds {
 template <bool FP8>
 __device__ __forceinline__ void stage_kv(KVLds& L, const void* kbase, const void* vbase,
                                          uint32_t row_stride, int nk_rel) {
-  const int tid = threadIdx.x;
+  // Opaque copy of the thread id: keeps the compiler from hoisting the 16 per-thread row
+  // offsets out of the caller's loops (they would stay live, or spill, for the whole kernel).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   if constexpr (!FP8) {
     const uint16_t* kp = reinterpret_cast<const uint16_t*>(kbase);
     const uint16_t* vp = reinterpret_cast<const uint16_t*>(vbase);
@@ -119,24 +122,21 @@ __device__ __forceinline__ void stage_kv(KVLds& L, const void* kbase, const void
   }
 }
 
-// B operand of S^T: the lane's Q row, d = 16*st + 8*(l/32) + i in bq[st].
+// B operand of S^T: the lane's Q row, d = 16*st + 8*(l/32) + i in bq[st]. The loads are
+// unconditional (padding rows point at a valid row), which keeps them free of exec-masked
+// branches so the compiler can leave them in flight across a whole tile of work.
 template <bool FP8>
-__device__ __forceinline__ void load_q_operand(bf16x8 bq[8], const void* qrow, bool valid,
-                                               int hf) {
+__device__ __forceinline__ void load_q_operand(bf16x8 bq[8], const void* qrow, int hf) {
   if constexpr (!FP8) {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(qrow);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4*>(p + 16 * st + 8 * hf);
-      bq[st] = as_bf16x8(v);
-    }
+    for (int st = 0; st < 8; ++st)
+      bq[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(p + 16 * st + 8 * hf));
   } else {
     const uint8_t* p = reinterpret_cast<const uint8_t*>(qrow);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      u32x2 v = {0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x2*>(p + 16 * st + 8 * hf);
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p + 16 * st + 8 * hf);
       const u32x2 lo = fp8x4_to_bf16x4(v[0]);
       const u32x2 hi = fp8x4_to_bf16x4(v[1]);
       bq[st] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
@@ -144,76 +144,107 @@ __device__ __forceinline__ void load_q_operand(bf16x8 bq[8], const void* qrow, b
   }
 }
 
+// S^T for the wave's 32 rows over the block's 128 keys: 32 MFMAs. The K operands of step
+// st+1 are read from LDS while the MFMAs of step st run.
 __device__ __forceinline__ void qk_block(const KVLds& L, const bf16x8 bq[8], f32x16 s[4],
                                          int col, int hf) {
+  const int rp = rowperm(col);
+  const int sw = swz(rp);                 // swz(32*kt + rp) == swz(rp)
+  bf16x8 a[2][4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) s[kt] = f32x16{};
+  for (int kt = 0; kt < 4; ++kt) a[0][kt] = as_bf16x8(L.k[(kt * 32 + rp) * 16 + (hf ^ sw)]);
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
+    if (st + 1 < 8) {
+      const int cc = (2 * (st + 1) + hf) ^ sw;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int row = kt * 32 + rowperm(col);
-      const bf16x8 a = as_bf16x8(L.k[row * 16 + ((2 * st + hf) ^ swz(row))]);
-      s[kt] = mfma32(a, bq[st], s[kt]);
+      for (int kt = 0; kt < 4; ++kt) a[(st + 1) & 1][kt] = as_bf16x8(L.k[(kt * 32 + rp) * 16 + cc]);
     }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      s[kt] = mfma32(a[st & 1][kt], bq[st], st == 0 ? f32x16{} : s[kt]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-__device__ __forceinline__ void pv_block(const KVLds& L, const f32x16 p[4], f32x16 o[4],
+// O^T (+)= V^T P^T over the block: 32 MFMAs; p holds the row's probabilities as packed
+// bf16 pairs, p[kt][ks][i] = keys 32*kt + 16*(l/32) + 8*ks + 2i, +1. With `init`, o starts
+// from zero instead of accumulating.
+template <bool INIT>
+__device__ __forceinline__ void pv_block(const KVLds& L, const u32x4 p[4][2], f32x16 o[4],
                                          int col, int hf) {
+  const int rp = rowperm(col);
+  const int sw = swz(rp);                 // swz(32*dt + rp) == swz(rp)
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int step = 0; step < 8; ++step) {
+    const int kt = step >> 1, ks = step & 1;
+    const int cc = (4 * kt + 2 * hf + ks) ^ sw;
+    bf16x8 a[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 pk;
+    for (int dt = 0; dt < 4; ++dt) a[dt] = as_bf16x8(L.vt[(dt * 32 + rp) * 16 + cc]);
+    const bf16x8 bp = as_bf16x8(p[kt][ks]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(p[kt][8 * ks + 2 * i], p[kt][8 * ks + 2 * i + 1]);
-      const bf16x8 bp = as_bf16x8(pk);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int row = dt * 32 + rowperm(col);
-        const bf16x8 a = as_bf16x8(L.vt[row * 16 + ((4 * kt + 2 * hf + ks) ^ swz(row))]);
-        o[dt] = mfma32(a, bp, o[dt]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int dt = 0; dt < 4; ++dt)
+      o[dt] = mfma32(a[dt], bp, (INIT && step == 0) ? f32x16{} : o[dt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Scale scores into the log2 domain and mask keys past `kmax` (block-relative index of the
-// last visible key; -1 masks the whole block). Returns the row max over the block (both
-// lanes of the row agree).
-__device__ __forceinline__ float scale_mask_max(f32x16 s[4], float sl2, int kmax, int hf) {
+// Row max of raw scores over the block, keys past `kmax` (block-relative index of the last
+// visible key) set to -inf first when `need_mask`. Both lanes of the row agree.
+__device__ __forceinline__ float mask_max(f32x16 s[4], int kmax, bool need_mask, int hf) {
   const float ninf = -__builtin_inff();
+  if (need_mask) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[kt][r] = (kt * 32 + 16 * hf + r <= kmax) ? s[kt][r] : ninf;
+  }
   float m = ninf;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kt * 32 + 16 * hf + r;
-      float x = s[kt][r] * sl2;
-      x = key <= kmax ? x : ninf;
-      s[kt][r] = x;
-      m = fmaxf(m, x);
-    }
-  }
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, s[kt][r]);
   return fmaxf(m, shfl_xor_f(m, 32));
 }
 
-// p = 2^(x - m) in place; returns the row sum (both lanes agree). m must be finite.
-__device__ __forceinline__ float exp_sum(f32x16 s[4], float m) {
+// p = 2^(s * sl2 - c) packed to bf16 pairs; returns the fp32 row sum (both lanes agree).
+// c = row max * sl2 (finite); masked scores (-inf) give 0.
+__device__ __forceinline__ float exp_pack(const f32x16 s[4], float sl2, float c, u32x4 p[4][2]) {
   float l = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[kt][r] - m);
-      s[kt][r] = p;
-      l += p;
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * ks + 2 * i], sl2, -c));
+        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * ks + 2 * i + 1], sl2, -c));
+        l += x0 + x1;
+        p[kt][ks][i] = pack_bf16x2(x0, x1);
+      }
     }
   }
   return l + shfl_xor_f(l, 32);
+}
+
+// Pack 16 consecutive output dims per dt (scaled by `mul`) as bf16: w[2*dt + h2] holds dims
+// 32*dt + 16*(l/32) + 8*h2 .. +8.
+__device__ __forceinline__ void pack_o_row(u32x4 w[8], const f32x16 o[4], float mul) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[2 * dt + h2][i] = pack_bf16x2(o[dt][8 * h2 + 2 * i] * mul, o[dt][8 * h2 + 2 * i + 1] * mul);
+}
+
+__device__ __forceinline__ void store_packed_row(uint16_t* orow, const u32x4 w[8], int hf) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<u32x4*>(orow + (j >> 1) * 32 + 16 * hf + 8 * (j & 1)) = w[j];
 }
 
 // Write 16 consecutive output dims per dt (scaled by `mul`) as bf16 to orow[0..128).

@@ -33,31 +33,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int hq = hkv * G;
   const int32_t* cm = cmap + ((size_t)t * hkv + h) * slots;
 
-  float ls[kMaxTopK];
+  // Slot indices first; then the LSE loads and the 16-byte partial loads of every valid
+  // slot are all issued before any of them is used.
   int es[kMaxTopK];
-  float m = -__builtin_inff();
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
     int e = -1;
     if (k < slots) e = cm[k];
-    if (e >= n_ent) e = -1;
-    es[k] = e;
-    ls[k] = e >= 0 ? part_lse[(size_t)e * G + g] : -__builtin_inff();
-    m = fmaxf(m, ls[k]);
+    es[k] = (e >= n_ent) ? -1 : e;
   }
+  float ls[kMaxTopK];
+  u32x4 vals[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    float l = -__builtin_inff();
+    if (es[k] >= 0) {
+      l = part_lse[(size_t)es[k] * G + g];
+      v = *reinterpret_cast<const u32x4*>(part_o + ((size_t)es[k] * G + g) * kD + 8 * c);
+    }
+    ls[k] = l;
+    vals[k] = v;
+  }
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) m = fmaxf(m, ls[k]);
   uint16_t* orow = o + ((size_t)t * hq + h * G + g) * kD + 8 * c;
   if (!(m > -__builtin_inff())) {
     *reinterpret_cast<u32x4*>(orow) = u32x4{0u, 0u, 0u, 0u};
     if (lse && c == 0) lse[(size_t)t * hq + h * G + g] = -__builtin_inff();
     return;
-  }
-  u32x4 vals[kMaxTopK];
-#pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (es[k] >= 0 && ls[k] > -__builtin_inff())
-      v = *reinterpret_cast<const u32x4*>(part_o + ((size_t)es[k] * G + g) * kD + 8 * c);
-    vals[k] = v;
   }
   float acc[8];
 #pragma unroll

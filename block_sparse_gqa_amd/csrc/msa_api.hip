@@ -74,7 +74,7 @@ msa_status check_mode(const msa_shape& s, msa_mode mode, msa_mode* out) {
   if (m == MSA_KV_OUTER) {
     const int64_t nb_max = cdiv(s.max_k, s.block);
     if (nb_max > 8192) return MSA_ERR_SHAPE;           // LDS bitmap tile of the plan
-    const int64_t words = (int64_t)s.batch * s.hkv * nb_max * cdiv(s.max_q, kWordQ);
+    const int64_t words = (int64_t)s.batch * s.hkv * nb_max * (cdiv(s.max_q, kRangeQ) * (kRangeQ / kWordQ));
     if (words + 1 > kInt32Max) return MSA_ERR_SHAPE;
   }
   *out = m;
@@ -94,8 +94,11 @@ Geometry geometry(const msa_shape& s, msa_mode mode) {
   g.splits = 1;
   if (mode == MSA_KV_OUTER) {
     g.w_max = cdiv(s.max_q, kWordQ);
-    g.n_buckets = (int64_t)s.batch * s.hkv * g.nb_max;
-    g.n_words = g.n_buckets * g.w_max;
+    g.wr = 1;
+    while (g.wr < g.w_max && g.wr < kRangeQ / kWordQ) g.wr *= 2;
+    g.n_r = cdiv(g.w_max, g.wr);
+    g.n_buckets = (int64_t)s.batch * s.hkv * g.n_r * g.nb_max;
+    g.n_words = g.n_buckets * g.wr;
     g.e_max = (int64_t)s.total_q * s.hkv * s.topk;
     g.n_scan_blocks = cdiv(g.n_words, kScanTile);
   } else {
@@ -121,14 +124,16 @@ Layout layout(const msa_shape& s, msa_mode mode) {
     L.offsets = take((size_t)(g.n_words + 1) * 4);
     L.scan_sums = take((size_t)(g.n_scan_blocks + 1) * 4);
     L.entry_q = take((size_t)g.e_max * 4);
+    L.entry_bucket = take((size_t)g.e_max * 4);
     L.cmap = take((size_t)s.total_q * s.hkv * s.topk * 4);
   } else {
     L.slots = g.splits;
-    L.masks = L.offsets = L.scan_sums = L.entry_q = off;
+    L.masks = L.offsets = L.scan_sums = L.entry_q = L.entry_bucket = off;
     L.cmap = take(g.splits > 1 ? (size_t)s.total_q * s.hkv * g.splits * 4 : 0);
   }
   L.part_lse = take((size_t)g.e_max * g.group * 4);
   L.part_o = take((size_t)g.e_max * g.group * s.d * 2);
+  L.dummy = take(mode == MSA_KV_OUTER ? 65536 : 0);
   L.total = off;
   return L;
 }
@@ -202,6 +207,7 @@ msa_status msa_workspace_layout_of(const msa_shape* shape, msa_mode mode,
   out->offsets = L.offsets;
   out->scan_sums = L.scan_sums;
   out->entry_q = L.entry_q;
+  out->entry_bucket = L.entry_bucket;
   out->cmap = L.cmap;
   out->part_lse = L.part_lse;
   out->part_o = L.part_o;
@@ -209,6 +215,8 @@ msa_status msa_workspace_layout_of(const msa_shape* shape, msa_mode mode,
   out->slots = L.slots;
   out->n_words = (int32_t)g.n_words;
   out->w_max = (int32_t)g.w_max;
+  out->words_per_bucket = (int32_t)g.wr;
+  out->n_ranges = (int32_t)g.n_r;
   out->nb_max = (int32_t)g.nb_max;
   return MSA_OK;
 }

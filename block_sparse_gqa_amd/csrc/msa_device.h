@@ -51,8 +51,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two round-to-nearest-even bf16 in one dword (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // OCP fp8 e4m3fn byte -> float (exact). Subnormals at exponent 0; 0x7f/0xff are NaN.

@@ -4,7 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/msa.h"
+#include "msa.h"
 
 namespace msa {
 
@@ -15,13 +15,20 @@ constexpr int kSplitIndexMaxQ = 16;
 constexpr int kSplitIndexChunk = 32;
 // Queries per inverted-index bitmap word.
 constexpr int kWordQ = 64;
+// Queries per range of the entry order (s, group, range, block, query): the queries of one
+// range are re-read from cache by all of their blocks while the range is being processed.
+constexpr int kRangeQ = 2048;
+// Tiles per chunk handed round-robin to the persistent attention workgroups.
+constexpr int kChunkTiles = 8;
 // Elements per workgroup in the scan kernels.
 constexpr int kScanTile = 4096;
 
 struct Geometry {
   int64_t nb_max;        // ceil(max_k / block)
-  int64_t w_max;         // ceil(max_q / 64): bitmap words per bucket
-  int64_t n_buckets;     // batch * hkv * nb_max
+  int64_t w_max;         // ceil(max_q / 64): bitmap words per (sequence, group, block)
+  int64_t wr;            // bitmap words per bucket (power of two, <= kRangeQ / 64)
+  int64_t n_r;           // query ranges per sequence: ceil(w_max / wr)
+  int64_t n_buckets;     // batch * hkv * n_r * nb_max
   int64_t n_words;       // n_buckets * w_max
   int64_t e_max;         // total_q * hkv * topk (upper bound on entries)
   int64_t n_scan_blocks; // ceil(n_words / kScanTile)
@@ -39,9 +46,11 @@ struct Layout {
   size_t offsets;       // int32  [n_words + 1]
   size_t scan_sums;     // int32  [n_scan_blocks + 1]
   size_t entry_q;       // int32  [e_max]
+  size_t entry_bucket;  // int32  [e_max]
   size_t cmap;          // int32  [total_q * hkv * slots]
   size_t part_lse;      // float  [e_max * group]
   size_t part_o;        // bf16   [e_max * group * d]
+  size_t dummy;         // 64 KiB sink for the stores of padding rows (KV-outer)
   size_t total;
   int slots;            // combine slots per (query, group): topk or splits
 };

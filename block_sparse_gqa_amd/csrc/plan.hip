@@ -29,10 +29,19 @@ struct PlanArgs {
   unsigned long long* masks;
   const int32_t* offsets;
   int32_t* entry_q;
+  int32_t* entry_bucket;
   int32_t* cmap;
   int total_q, total_k, max_q, max_k;
-  int hkv, topk, list_q, tiles_max, nb_max, w_max, wpb, causal;
+  int hkv, topk, list_q, tiles_max, nb_max, w_max, wr, n_r, wpb, causal;
 };
+
+// Bucket (s, h, r, b) of query word w (r = w / wr) and the word's index in the mask array.
+__device__ __forceinline__ size_t bucket_of(const PlanArgs& a, int s, int h, int w, int b) {
+  return (((size_t)s * a.hkv + h) * a.n_r + w / a.wr) * a.nb_max + b;
+}
+__device__ __forceinline__ size_t word_index(const PlanArgs& a, int s, int h, int w, int b) {
+  return bucket_of(a, s, h, w, b) * a.wr + (w % a.wr);
+}
 
 // Block b of list slot `slot` is a real entry for this query: in range, first occurrence,
 // and (causal) holding at least one key at or before the query's position.
@@ -73,11 +82,11 @@ __global__ __launch_bounds__(256) void plan_mask_kernel(PlanArgs a) {
     if (b >= 0) atomicOr(&lm[b * a.wpb + (il / kWordQ - w0)], 1ull << (il % kWordQ));
   }
   __syncthreads();
-  const size_t bucket0 = ((size_t)s * a.hkv + h) * a.nb_max;
+  // a workgroup's words lie in one range (wpb divides wr), so each block's words are contiguous
   for (int i = tid; i < n_lm; i += 256) {
     const int b = i / a.wpb, wl = i % a.wpb;
     const int w = w0 + wl;
-    if (w < a.w_max) a.masks[(bucket0 + b) * a.w_max + w] = lm[i];
+    if (w < a.n_r * a.wr) a.masks[word_index(a, s, h, w, b)] = lm[i];
   }
 }
 
@@ -89,18 +98,19 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(PlanArgs a) {
   const int qa = w0 * kWordQ;
   const int qb = min((w0 + a.wpb) * kWordQ, sq.nq);
   const int n = max(qb - qa, 0) * a.topk;
-  const size_t bucket0 = ((size_t)s * a.hkv + h) * a.nb_max;
   for (int i = tid; i < n; i += 256) {
     const int il = qa + i / a.topk, slot = i % a.topk;
     const int32_t* L = list_of(a, s, sq, il, h);
     const int b = entry_block(a, sq, il, slot, L);
     int e = -1;
     if (b >= 0) {
-      const size_t wi = (bucket0 + b) * a.w_max + il / kWordQ;
+      const int w = il / kWordQ;
+      const size_t wi = word_index(a, s, h, w, b);
       const unsigned long long m = a.masks[wi];
       const unsigned long long below = (1ull << (il % kWordQ)) - 1ull;
       e = a.offsets[wi] + __popcll(m & below);
       a.entry_q[e] = sq.q0 + il;
+      a.entry_bucket[e] = (int)bucket_of(a, s, h, w, b);
     }
     a.cmap[((size_t)(sq.q0 + il) * a.hkv + h) * a.topk + slot] = e;
   }
@@ -193,6 +203,7 @@ hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
   a.masks = reinterpret_cast<unsigned long long*>(ws + L.masks);
   a.offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
   a.entry_q = reinterpret_cast<int32_t*>(ws + L.entry_q);
+  a.entry_bucket = reinterpret_cast<int32_t*>(ws + L.entry_bucket);
   a.cmap = reinterpret_cast<int32_t*>(ws + L.cmap);
   a.total_q = s.total_q;
   a.total_k = s.total_k;
@@ -204,6 +215,8 @@ hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
   a.tiles_max = (int)g.tiles_max;
   a.nb_max = (int)g.nb_max;
   a.w_max = (int)g.w_max;
+  a.wr = (int)g.wr;
+  a.n_r = (int)g.n_r;
   a.causal = s.causal;
   int32_t* counters = reinterpret_cast<int32_t*>(ws + L.counters);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -216,11 +229,13 @@ hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
     return hipGetLastError();
   }
   // words per workgroup: keep the LDS bitmap tile at <= 64 KiB
-  int wpb = (int)std::max<int64_t>(1, std::min<int64_t>(8, 8192 / std::max<int64_t>(1, g.nb_max)));
-  wpb = (int)std::min<int64_t>(wpb, g.w_max);
+  // (powers of two, so that wpb divides wr and a workgroup stays inside one range)
+  int wpb = 8;
+  while (wpb > 1 && (int64_t)wpb * g.nb_max > 8192) wpb >>= 1;
+  while (wpb > g.wr) wpb >>= 1;
   a.wpb = wpb;
   const size_t lds = (size_t)g.nb_max * wpb * 8;
-  dim3 grid((unsigned)((g.w_max + wpb - 1) / wpb), s.hkv, s.batch);
+  dim3 grid((unsigned)((g.n_r * g.wr) / wpb), s.hkv, s.batch);
   hipLaunchKernelGGL(plan_mask_kernel, grid, dim3(256), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -86,18 +86,25 @@ typedef struct {
  * of the workspace; a region of size 0 is unused. */
 typedef struct {
   size_t counters;     /* int32[64]; [0] = number of (query-group, block) entries E */
-  size_t masks;        /* uint64 bitmaps, bucket-major: bucket (s, g, b), word w of 64 queries */
+  size_t masks;        /* uint64 bitmaps, bucket-major. Bucket (s, g, r, b) covers the
+                          queries [64 W r, 64 W (r + 1)) of sequence s for group g and block b
+                          (W = words_per_bucket); its word w has bit i set when query
+                          64 (W r + w) + i listed block b */
   size_t offsets;      /* int32 exclusive scan of the bitmap popcounts, n_words + 1 values */
   size_t scan_sums;    /* int32 scratch of the scan */
-  size_t entry_q;      /* int32 [E]: query row of entry e (entries sorted by s, g, b, query) */
+  size_t entry_q;      /* int32 [E]: query row of entry e; entries are sorted by
+                          (sequence, group, query range r, block, query) */
+  size_t entry_bucket; /* int32 [E]: bucket ((s * hkv + g) * n_ranges + r) * nb_max + b */
   size_t cmap;         /* int32 [total_q, hkv, slots]: partial index of each slot, -1 = none */
   size_t part_lse;     /* float [E, hq/hkv]: log-sum-exp of each partial */
   size_t part_o;       /* bf16 [E, hq/hkv, d]: normalised partial output */
   size_t total;        /* bytes needed */
   int32_t slots;       /* slots per (query, group) in cmap */
   int32_t n_words;     /* bitmap words (0 for Q-outer) */
-  int32_t w_max;       /* bitmap words per bucket */
+  int32_t w_max;       /* bitmap words per (sequence, group, block): ceil(max_q / 64) */
   int32_t nb_max;      /* blocks per sequence bound */
+  int32_t words_per_bucket; /* bitmap words per bucket */
+  int32_t n_ranges;    /* query ranges per sequence */
 } msa_workspace_layout;
 
 /* ---- host-only queries (no GPU needed) ---------------------------------------------- */

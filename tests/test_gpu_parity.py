@@ -103,6 +103,8 @@ LAYER_CASES = [
                                dp=32, causal=False), 0),
     ("fp8_small", mi.custom(name="fp8", n_q=(1024,), hq=32, hkv=2, topk=6, dp=64, dtype="fp8",
                             lowrank=True), 0),
+    ("multi_range", mi.custom(name="mr", n_q=(4500, 700), n_k=(4500, 5000), hq=4, hkv=2, topk=5,
+                              dp=32, lowrank=True), 0),
 ]
 
 
@@ -177,13 +179,18 @@ def test_partials_match_oracle_partials():
                     heads = slice(g * G, (g + 1) * G)
                     assert np.max(np.abs(po[e] - o_s[i, heads, slot])) <= 2e-2
                     assert np.max(np.abs(plse[e] - l_s[i, heads, slot])) <= 1e-2
-    # entries are sorted by (group, block, query) inside each sequence
+    # entries are sorted by (sequence, group, query range, block, query) and carry their bucket
+    ebk = wsn[L.entry_bucket:L.entry_bucket + n_ent * 4].view(torch.int32).numpy()
+    qr = 64 * L.words_per_bucket
     key = []
     for e in range(n_ent):
         t = entry_q[e]
         i_g, i_slot = np.argwhere(cmap[t] == e)[0]
         si = int(np.searchsorted(case.cu_q, t, side="right") - 1)
-        key.append((si, i_g, out.topk_idx[t, i_g, i_slot], t))
+        rr = (t - case.cu_q[si]) // qr
+        blk = out.topk_idx[t, i_g, i_slot]
+        key.append((si, i_g, rr, blk, t))
+        assert ebk[e] == ((si * case.cfg.hkv + i_g) * L.n_ranges + rr) * L.nb_max + blk
     assert key == sorted(key)
 
 
