@@ -8,20 +8,18 @@
 //
 // The entry list built by the plan kernels is cut into equal contiguous slices, one per
 // persistent workgroup (deterministic, no atomics; heavy blocks are split between
-// workgroups automatically). A workgroup walks its slice bucket by bucket: it stages the
-// bucket's K and V^T in LDS once, then processes tiles of 128 rows = 128/G entries x G heads
-// with four waves of 32 rows. Each entry's G x D partial lands in rows e*G .. e*G+G-1 of the
-// partial buffer, so a tile's stores form one contiguous 32 KiB range.
+// workgroups automatically). A workgroup of eight waves walks its slice bucket by bucket: it
+// stages the bucket's K and V^T in LDS once, then processes tiles of 256 rows = 256/G entries
+// x G heads, 32 rows per wave, two waves per SIMD. Each entry's G x D partial lands in rows
+// e*G .. e*G+G-1 of the partial buffer, so a wave's 32 output rows are one contiguous 8 KiB
+// range; they are written through a per-wave LDS buffer so that every store instruction
+// covers 1 KiB of consecutive bytes.
 #include "attn_tile.h"
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
-// vmcnt[5:4] << 14); expcnt and lgkmcnt left at their maxima (no wait).
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVm27 = 0x0F70 | (27 & 15) | ((27 >> 4) << 14);
 
 struct KvArgs {
   const void* q;
@@ -42,27 +40,111 @@ struct KvArgs {
   int hq, hkv, nb_max, wr, n_r, n_buckets, n_wg, causal;
 };
 
+// --------------------------------------------------------------------------------------
+// Per-wave tile step. The MFMA pipe and the VALU of a SIMD run concurrently when MFMAs and
+// independent VALU work alternate in the instruction stream, so each tile is done in two
+// interleaved phases:
+//   phase A, step st: 4 MFMAs of QK^T(j) (d-step st)  | O(j-1): bf16 packing into the wave's
+//                                                      |   LDS buffer (steps 0-3), coalesced
+//                                                      |   read-back and stores (steps 4-7)
+//   row max of S(j)
+//   phase B, step s:  4 MFMAs of PV(j) (key-step s)    | exp2 + packing of key-step s+1
+// LDS operands are double-buffered over the 16 steps; everything else stays in VGPRs.
+
+// K operands (A) of d-step st for the 4 key tiles.
+__device__ __forceinline__ void k_frags(const KVLds& L, bf16x8 a[4], int st, int rp, int sw,
+                                        int hf) {
+  const int cc = (2 * st + hf) ^ sw;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) a[kt] = as_bf16x8(L.k[(kt * 32 + rp) * 16 + cc]);
+}
+
+// V^T operands (A) of key-step s for the 4 output-dim tiles.
+__device__ __forceinline__ void v_frags(const KVLds& L, bf16x8 a[4], int s, int rp, int sw,
+                                        int hf) {
+  const int cc = (4 * (s >> 1) + 2 * hf + (s & 1)) ^ sw;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) a[dt] = as_bf16x8(L.vt[(dt * 32 + rp) * 16 + cc]);
+}
+
+// exp2 of the 8 scores of key-step s, packed to bf16 into pk; returns their sum.
+__device__ __forceinline__ float exp_step(const f32x16 sc[4], int s, float sl2, float c,
+                                          u32x4& pk) {
+  const int kt = s >> 1, base = 8 * (s & 1);
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[kt][base + 2 * i], sl2, -c));
+    const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[kt][base + 2 * i + 1], sl2, -c));
+    l += x0 + x1;
+    pk[i] = pack_bf16x2(x0, x1);
+  }
+  return l;
+}
+
+// Output staging: the wave's 32 rows x 256 B, 16-byte chunk c of row R at R*16 + (c ^ (R%16)).
+// Lane (col, hf) deposits dims 32*dt + 16*hf .. +15 of row col (chunks 4dt+2hf, +1).
+__device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, float mul,
+                                        int col, int hf) {
+  // opaque copy: the addresses are recomputed here instead of being held (or spilled) across
+  // the caller's loop
+  asm volatile("" : "+v"(col));
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack_bf16x2(o[8 * h2 + 2 * i] * mul, o[8 * h2 + 2 * i + 1] * mul);
+    const int c = 4 * dt + 2 * hf + h2;
+    buf[col * 16 + (c ^ (col & 15))] = w;
+  }
+}
+
+// Read-back i (0..7): lane l takes chunk l%16 of row 4i + l/16, so the 64 lanes hold
+// 1 KiB of consecutive output bytes.
+__device__ __forceinline__ u32x4 unstage_o(const u32x4* buf, int i, int lane) {
+  asm volatile("" : "+v"(lane));
+  const int R = 4 * i + (lane >> 4);
+  return buf[R * 16 + ((lane & 15) ^ (R & 15))];
+}
+
+// Destination of read-back i: the wave's output rows start at o_row0 (a row of the partial
+// buffer); rows at or past o_rows are padding and go to the sink.
+__device__ __forceinline__ uint16_t* o_dest(uint16_t* part_o, uint16_t* sink, size_t o_row0,
+                                            int o_rows, int i, int lane) {
+  const int R = 4 * i + (lane >> 4);
+  return R < o_rows ? part_o + (o_row0 + R) * kD + (lane & 15) * 8 : sink;
+}
+
+// Scheduling request for one phase-A step: the first MFMA, the 4 LDS reads of the next
+// step's operands, then MFMAs each followed by NVALU VALU instructions.
+#define MSA_INTERLEAVE(ID, NVALU)                                 \
+  do {                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);           \
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, ID);           \
+    __builtin_amdgcn_sched_group_barrier(0x002, NVALU, ID);       \
+    _Pragma("unroll") for (int q_ = 0; q_ < 3; ++q_) {            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);         \
+      __builtin_amdgcn_sched_group_barrier(0x002, NVALU, ID);     \
+    }                                                             \
+    __builtin_amdgcn_sched_barrier(0);                            \
+  } while (0)
+
 template <bool FP8, int G>
-__global__ __launch_bounds__(256, 2) void attn_kv_kernel(KvArgs a) {
-  constexpr int MQ = 128 / G;          // entries per tile
+__global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
+  constexpr int MQ = 256 / G;          // entries per tile
   constexpr int EB = FP8 ? 1 : 2;      // bytes per Q/K/V element
   __shared__ KVLds L;
+  __shared__ u32x4 obuf_all[8][32 * 16];
 
   const int E = a.counters[0];
-  // Chunks of kChunkTiles tiles go round-robin to the workgroups, so that at any time the
-  // whole grid works on one window of the entry order (one query range of one group: its Q
-  // rows are then re-read from cache). Workgroup ids are dispatched round-robin over the 8
-  // XCDs; renumbering them XCD-major gives each XCD runs of consecutive chunks, which share
-  // K/V blocks in that XCD's L2.
-  const int n_xcd = 8;
-  const int per_xcd = a.n_wg / n_xcd;
-  const int lw = (int)(blockIdx.x % n_xcd) * per_xcd + (int)(blockIdx.x / n_xcd);
-  constexpr int CHUNK = kChunkTiles * MQ;
-
+  if (E == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
   const int r = wave * 32 + col;       // row of the tile
   const int rent = r / G, g = r % G;
+  const int rp = rowperm(col), sw = swz(rp);
+  u32x4* const obuf = obuf_all[wave];
 
   float sl2 = a.scale_log2, dv = 1.f;
   if constexpr (FP8) {
@@ -73,111 +155,152 @@ __global__ __launch_bounds__(256, 2) void attn_kv_kernel(KvArgs a) {
   const char* kb = reinterpret_cast<const char*>(a.k);
   const char* vb = reinterpret_cast<const char*>(a.v);
   const uint32_t kv_row = (uint32_t)a.hkv * kD;    // elements between consecutive keys
+  const int last = E - 1;
+  // Sinks for the stores of padding rows (contents never read).
+  uint16_t* const o_sink = a.dummy + lane * 8;
+  float* const lse_sink = reinterpret_cast<float*>(a.dummy + 64 * 8) + lane;
 
-  int staged = -1;                     // bucket whose K/V sit in LDS
-  // Packed output of the last tile, stored during the next tile. Until a first tile exists
-  // it points at the sink.
-  u32x4 wout[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) wout[j] = u32x4{0u, 0u, 0u, 0u};
-  uint16_t* pend_o = a.dummy + (size_t)r * kD;
-  float* pend_lse_ptr = reinterpret_cast<float*>(a.dummy + 128 * kD) + r;
-  float pend_lse = 0.f;
-  for (int64_t c0 = (int64_t)lw * CHUNK; c0 < E; c0 += (int64_t)a.n_wg * CHUNK) {
-  const int c1 = (int)min<int64_t>(E, c0 + CHUNK);
-  int cur = (int)c0;
-  while (cur < c1) {
+  // Phases (sequence, group, query range) in entry order; this workgroup's share of each.
+  const int n_phase = a.n_buckets / a.nb_max;
+  for (int ph = 0; ph < n_phase; ++ph) {
+  const int p_begin = a.offsets[(size_t)ph * a.nb_max * a.wr];
+  const int p_end = (ph + 1 < n_phase) ? a.offsets[(size_t)(ph + 1) * a.nb_max * a.wr] : E;
+  const int e_begin = p_begin + (int)((int64_t)(p_end - p_begin) * blockIdx.x / a.n_wg);
+  const int e_end = p_begin + (int)((int64_t)(p_end - p_begin) * (blockIdx.x + 1) / a.n_wg);
+  int cur = e_begin;
+  while (cur < e_end) {
     const int bk = a.entry_bucket[cur];
     if ((unsigned)bk >= (unsigned)a.n_buckets) break;   // never for a planned workspace
     const int bend = (bk + 1 < a.n_buckets) ? a.offsets[(size_t)(bk + 1) * a.wr] : E;
-    const int run_end = min(c1, bend);
+    const int run_end = min(e_end, bend);
     const int b = bk % a.nb_max;
     const int h = (bk / (a.nb_max * a.n_r)) % a.hkv;
     const int s = bk / (a.nb_max * a.n_r * a.hkv);
     const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
     const int u0 = b * kBlock;
     const int nk_rel = sq.nk - u0;
-    const int kvkey = (s * a.hkv + h) * a.nb_max + b;
 
-    if (kvkey != staged) {
-      __syncthreads();   // LDS of the previous block no longer read
+    __syncthreads();   // LDS of the previous block no longer read
+    if (tid < 256)
       stage_kv<FP8>(L, kb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB,
                     vb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB, kv_row, nk_rel);
-      __syncthreads();
-      staged = kvkey;
-    }
+    __syncthreads();
 
-    // Tile pipeline. Per tile, in issue order: the entry index of the tile three steps ahead
-    // (1 load), the Q rows of the tile two steps ahead (8 loads), the QK^T MFMAs, the 9
-    // stores of the previous tile's output (its registers are not reused before they are
-    // read), softmax and PV. Every one of these memory operations is issued by every lane
-    // (padding rows read a valid row and write to a sink), so the explicit wait at the end of
-    // a tile is exact: the next tile's Q rows (loaded one tile earlier) must have arrived;
-    // the 27 operations issued after them may stay in flight.
-    const int last = E - 1;
-    int e0 = cur + rent, e1 = e0 + MQ, e2 = e1 + MQ;
-    int t0v = a.entry_q[min(e0, last)], t1v = a.entry_q[min(e1, last)];
-    int t2v = a.entry_q[min(e2, last)];
     auto qrow = [&](int e, int tv) {
       return qb + ((size_t)(e < run_end ? tv : sq.q0) * a.hq + h * G + g) * kD * EB;
     };
-    bf16x8 bq[8], bq1[8];
+
+    int e0 = cur + rent, e1 = e0 + MQ;
+    int t0v = a.entry_q[min(e0, last)];
+    int t1v = a.entry_q[min(e1, last)];
+    bf16x8 bq[8];
     load_q_operand<FP8>(bq, qrow(e0, t0v), hf);
-    load_q_operand<FP8>(bq1, qrow(e1, t1v), hf);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // LDS operands, double-buffered over the 16 steps of a tile (8 K steps, then 8 V steps):
+    // step i reads fr[i & 1] while the reads of step i + 1 are in flight.
+    bf16x8 fr[2][4];
+    k_frags(L, fr[0], 0, rp, sw, hf);
+    // output of the previous tile: none yet (its rows all count as padding)
+    f32x16 oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+    float o_mul = 0.f, o_lse = 0.f;
+    size_t o_row0 = 0;
+    int o_rows = 0;
+    float* lse_ptr = lse_sink;
+
     for (int tile0 = cur; tile0 < run_end; tile0 += MQ) {
-      const int e3 = e2 + MQ;
-      const int t3v = a.entry_q[min(e3, last)];
-      bf16x8 bq2[8];
-      load_q_operand<FP8>(bq2, qrow(e2, t2v), hf);
-
-      f32x16 sacc[4];
-      qk_block(L, bq, sacc, col, hf);
-      store_packed_row(pend_o, wout, hf);
-      *pend_lse_ptr = pend_lse;
-      const int t = t0v;
-      const bool valid = e0 < run_end;
-      const int pos = sq.nk - sq.nq + (t - sq.q0);
+      const int e2 = e1 + MQ;
+      const int t2v = a.entry_q[min(e2, last)];
       int kmax = min(127, nk_rel - 1);
-      if (a.causal) kmax = min(kmax, pos - u0);
+      if (a.causal) kmax = min(kmax, sq.nk - sq.nq + (t0v - sq.q0) - u0);
       const bool need_mask = __any(kmax < 127);
-      const float m = mask_max(sacc, kmax, need_mask, hf);
-      const bool any = m > -__builtin_inff();
-      const float c = any ? m * sl2 : 0.f;
-      u32x4 pk[4][2];
-      const float l = exp_pack(sacc, sl2, c, pk);
+      const bool valid = e0 < run_end;
 
-      f32x16 oacc[4];
-      pv_block<true>(L, pk, oacc, col, hf);
-
-      pack_o_row(wout, oacc, any ? dv / l : 0.f);
-      const size_t prow = valid ? (size_t)e0 * G + g : (size_t)r;
-      pend_o = (valid ? a.part_o : a.dummy) + prow * kD;
-      pend_lse_ptr = (valid ? a.part_lse : reinterpret_cast<float*>(a.dummy + 128 * kD)) + prow;
-      pend_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-      __builtin_amdgcn_s_waitcnt(kWaitVm27);
+      // ---- phase A: QK^T(j) | O(j-1) through LDS to memory
+      f32x16 sc[4];
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        bq[st] = bq1[st];
-        bq1[st] = bq2[st];
+        if (st < 7) k_frags(L, fr[(st + 1) & 1], st + 1, rp, sw, hf);
+        else v_frags(L, fr[0], 0, rp, sw, hf);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
+        if (st < 4) {
+          stage_o(obuf, oacc[st], st, o_mul, col, hf);
+        } else {
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2) {
+            const int i = 2 * (st - 4) + i2;
+            const u32x4 w = unstage_o(obuf, i, lane);
+            *reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)) = w;
+          }
+          if (st == 7) *lse_ptr = o_lse;
+        }
+        MSA_INTERLEAVE(1, 6);
       }
+      // Q of the next tile goes straight into bq, whose last use was the step above
+      load_q_operand<FP8>(bq, qrow(e1, t1v), hf);
+      // ---- row max of S(j)
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sc[kt][i] = (kt * 32 + 16 * hf + i <= kmax) ? sc[kt][i] : -__builtin_inff();
+      }
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      const bool any = m > -__builtin_inff();
+      const float c = any ? m * sl2 : 0.f;
+      // ---- phase B: PV(j) | exp of the next key-step
+      u32x4 pk[8];
+      float l = exp_step(sc, 0, sl2, c, pk[0]);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        // the last step fetches the first K operands of the next tile (discarded after the
+        // run's last tile)
+        if (st < 7) v_frags(L, fr[(st + 1) & 1], st + 1, rp, sw, hf);
+        else k_frags(L, fr[0], 0, rp, sw, hf);
+        const bf16x8 bp = as_bf16x8(pk[st]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
+        if (st + 1 < 8) l += exp_step(sc, st + 1, sl2, c, pk[st + 1]);
+        MSA_INTERLEAVE(2, 7);
+      }
+      l += shfl_xor_f(l, 32);
+      // the output of tile j is stored during the next tile's phase A
+      o_mul = any ? dv / l : 0.f;
+      o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+      o_row0 = (size_t)tile0 * G + wave * 32;
+      o_rows = (run_end - tile0) * G - wave * 32;
+      lse_ptr = valid ? a.part_lse + (size_t)e0 * G + g : lse_sink;
       e0 = e1;
       e1 = e2;
-      e2 = e3;
       t0v = t1v;
       t1v = t2v;
-      t2v = t3v;
     }
+    // output of the run's last tile
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) stage_o(obuf, oacc[dt], dt, o_mul, col, hf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 w = unstage_o(obuf, i, lane);
+      *reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)) = w;
+    }
+    *lse_ptr = o_lse;
     cur = run_end;
   }
   }
-  store_packed_row(pend_o, wout, hf);
-  *pend_lse_ptr = pend_lse;
 }
 
 template <bool FP8>
 hipError_t launch_kv_g(const KvArgs& a, int group, int n_wg, hipStream_t st) {
-  dim3 grid(n_wg), blk(256);
+  dim3 grid(n_wg), blk(512);
   switch (group) {
     case 1: hipLaunchKernelGGL((attn_kv_kernel<FP8, 1>), grid, blk, 0, st, a); break;
     case 2: hipLaunchKernelGGL((attn_kv_kernel<FP8, 2>), grid, blk, 0, st, a); break;
@@ -221,7 +344,7 @@ hipError_t launch_attn_kv(const msa_shape& s, const Geometry& g, const Layout& L
   a.n_buckets = (int)g.n_buckets;
   a.causal = s.causal;
   if (g.n_words == 0) return hipSuccess;
-  const int n_wg = 2 * ((device_cu_count() + 7) / 8) * 8;
+  const int n_wg = device_cu_count();   // one workgroup (eight waves) per CU
   a.n_wg = n_wg;
   return s.dtype == MSA_FP8_E4M3 ? launch_kv_g<true>(a, g.group, n_wg, st)
                                  : launch_kv_g<false>(a, g.group, n_wg, st);

@@ -15,9 +15,12 @@ constexpr int kSplitIndexMaxQ = 16;
 constexpr int kSplitIndexChunk = 32;
 // Queries per inverted-index bitmap word.
 constexpr int kWordQ = 64;
-// Queries per range of the entry order (s, group, range, block, query): the queries of one
-// range are re-read from cache by all of their blocks while the range is being processed.
-constexpr int kRangeQ = 2048;
+// Queries per range of the entry order (s, group, range, block, query). The attention
+// kernel works through the (s, group, range) phases one after the other, every workgroup
+// taking an equal share of each. Measured on the 32K-query layer, one range per sequence
+// (plain contiguous slices of the whole entry list) is fastest: shorter ranges keep the Q
+// rows in use within the memory-side cache but cost more K/V restaging and ragged tiles.
+constexpr int kRangeQ = 1 << 24;
 // Tiles per chunk handed round-robin to the persistent attention workgroups.
 constexpr int kChunkTiles = 8;
 // Elements per workgroup in the scan kernels.
