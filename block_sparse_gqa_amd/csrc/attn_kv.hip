@@ -86,17 +86,18 @@ __device__ __forceinline__ float exp_step(const f32x16 sc[4], int s, float sl2, 
 // Lane (col, hf) deposits dims 32*dt + 16*hf .. +15 of row col (chunks 4dt+2hf, +1).
 __device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, float mul,
                                         int col, int hf) {
-  // opaque copy: the addresses are recomputed here instead of being held (or spilled) across
-  // the caller's loop
-  asm volatile("" : "+v"(col));
+  // opaque copies: the addresses are recomputed here instead of being held (or spilled)
+  // across the caller's loop
+  asm volatile("" : "+v"(col), "+v"(hf));
+  const int x = (2 * hf) ^ (col & 15);   // c ^ (col % 16) == (4dt + h2) ^ x
+  u32x4* const row = buf + col * 16;
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = pack_bf16x2(o[8 * h2 + 2 * i] * mul, o[8 * h2 + 2 * i + 1] * mul);
-    const int c = 4 * dt + 2 * hf + h2;
-    buf[col * 16 + (c ^ (col & 15))] = w;
+    row[(4 * dt + h2) ^ x] = w;
   }
 }
 
@@ -112,9 +113,39 @@ __device__ __forceinline__ u32x4 unstage_o(const u32x4* buf, int i, int lane) {
 // buffer); rows at or past o_rows are padding and go to the sink.
 __device__ __forceinline__ uint16_t* o_dest(uint16_t* part_o, uint16_t* sink, size_t o_row0,
                                             int o_rows, int i, int lane) {
+  asm volatile("" : "+v"(lane));
   const int R = 4 * i + (lane >> 4);
   return R < o_rows ? part_o + (o_row0 + R) * kD + (lane & 15) * 8 : sink;
 }
+
+// bf16 Q rows of the wave's next tile into its staging buffer with direct-to-LDS loads, in
+// the staging layout. `rowidx` is the lane's own Q row index (query * hq + head); load i
+// brings rows 4i .. 4i+3, lane l fetching the chunk that belongs in slot l%16 of row 4i + l/16,
+// so each load reads 1 KiB of whole rows.
+__device__ __forceinline__ void dma_q(u32x4* buf, const uint16_t* q, int rowidx, int lane) {
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int R = 4 * i + (lane >> 4);
+    const int src_row = __shfl(rowidx, R);
+    const int c = (lane & 15) ^ (R & 15);
+    __builtin_amdgcn_global_load_lds(
+        q + (size_t)src_row * kD + c * 8,
+        (__attribute__((address_space(3))) void*)(buf + 64 * i), 16, 0, 0);
+  }
+}
+
+// B operand of S^T from the staging buffer: chunk 2st + hf of the lane's row.
+__device__ __forceinline__ void read_q(const u32x4* buf, bf16x8 bq[8], int col, int hf) {
+  asm volatile("" : "+v"(col), "+v"(hf));
+  const int x = hf ^ (col & 15);          // (2st + hf) ^ (col % 16) == 2st ^ x
+  const u32x4* const row = buf + col * 16;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) bq[st] = as_bf16x8(row[(2 * st) ^ x]);
+}
+
+// s_waitcnt vmcnt(0): direct-to-LDS loads are not tracked by the compiler's own waits.
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Scheduling request for one phase-A step: the first MFMA, the 4 LDS reads of the next
 // step's operands, then MFMAs each followed by NVALU VALU instructions.
@@ -186,15 +217,15 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
                     vb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB, kv_row, nk_rel);
     __syncthreads();
 
-    auto qrow = [&](int e, int tv) {
-      return qb + ((size_t)(e < run_end ? tv : sq.q0) * a.hq + h * G + g) * kD * EB;
-    };
+    auto qidx = [&](int e, int tv) { return (e < run_end ? tv : sq.q0) * a.hq + h * G + g; };
+    auto qrow = [&](int e, int tv) { return qb + (size_t)qidx(e, tv) * kD * EB; };
 
     int e0 = cur + rent, e1 = e0 + MQ;
     int t0v = a.entry_q[min(e0, last)];
     int t1v = a.entry_q[min(e1, last)];
     bf16x8 bq[8];
-    load_q_operand<FP8>(bq, qrow(e0, t0v), hf);
+    if constexpr (FP8) load_q_operand<FP8>(bq, qrow(e0, t0v), hf);
+    else dma_q(obuf, reinterpret_cast<const uint16_t*>(a.q), qidx(e0, t0v), lane);
     // LDS operands, double-buffered over the 16 steps of a tile (8 K steps, then 8 V steps):
     // step i reads fr[i & 1] while the reads of step i + 1 are in flight.
     bf16x8 fr[2][4];
@@ -215,6 +246,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
       if (a.causal) kmax = min(kmax, sq.nk - sq.nq + (t0v - sq.q0) - u0);
       const bool need_mask = __any(kmax < 127);
       const bool valid = e0 < run_end;
+      if constexpr (!FP8) {
+        wait_vm0();               // this tile's Q rows have landed in the staging buffer
+        read_q(obuf, bq, col, hf);
+      }
 
       // ---- phase A: QK^T(j) | O(j-1) through LDS to memory
       f32x16 sc[4];
@@ -232,14 +267,18 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
           for (int i2 = 0; i2 < 2; ++i2) {
             const int i = 2 * (st - 4) + i2;
             const u32x4 w = unstage_o(obuf, i, lane);
-            *reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)) = w;
+            // streaming store: the partials are read once, by the combine kernel
+            __builtin_nontemporal_store(
+                w, reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)));
           }
           if (st == 7) *lse_ptr = o_lse;
         }
         MSA_INTERLEAVE(1, 6);
       }
-      // Q of the next tile goes straight into bq, whose last use was the step above
-      load_q_operand<FP8>(bq, qrow(e1, t1v), hf);
+      // Q of the next tile: straight into bq (fp8: converted on load) or into the staging
+      // buffer, whose read-back for the stores above is complete
+      if constexpr (FP8) load_q_operand<FP8>(bq, qrow(e1, t1v), hf);
+      else dma_q(obuf, reinterpret_cast<const uint16_t*>(a.q), qidx(e1, t1v), lane);
       // ---- row max of S(j)
       if (need_mask) {
 #pragma unroll
@@ -284,13 +323,15 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
       t0v = t1v;
       t1v = t2v;
     }
-    // output of the run's last tile
+    // output of the run's last tile (after the last, unused, Q load into the buffer)
+    wait_vm0();
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) stage_o(obuf, oacc[dt], dt, o_mul, col, hf);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4 w = unstage_o(obuf, i, lane);
-      *reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)) = w;
+      __builtin_nontemporal_store(
+          w, reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)));
     }
     *lse_ptr = o_lse;
     cur = run_end;
