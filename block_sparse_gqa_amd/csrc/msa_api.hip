@@ -74,8 +74,7 @@ msa_status check_mode(const msa_shape& s, msa_mode mode, msa_mode* out) {
   if (m == MSA_KV_OUTER) {
     const int64_t nb_max = cdiv(s.max_k, s.block);
     if (nb_max > 8192) return MSA_ERR_SHAPE;           // LDS bitmap tile of the plan
-    const int64_t words = (int64_t)s.batch * s.hkv * nb_max * (cdiv(s.max_q, kRangeQ) * (kRangeQ / kWordQ));
-    if (words + 1 > kInt32Max) return MSA_ERR_SHAPE;
+    if (geometry(s, m).n_words + 1 > kInt32Max) return MSA_ERR_SHAPE;   // 32-bit scan
   }
   *out = m;
   return MSA_OK;

@@ -1,0 +1,240 @@
+"""Host side of libmsa's C ABI, with no GPU: the library loads, exports every function that
+include/msa.h declares, validates arguments before anything is enqueued, sizes its
+workspace as documented, and applies the schedule rule and the crossover model.
+
+Nothing here launches a kernel: every device entry point is called with arguments that the
+host checks reject, so the calls return before touching the HIP runtime.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from block_sparse_gqa_amd import msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "pages_figures.json")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(msa.LIB_PATH):
+        from block_sparse_gqa_amd import build
+        build.build()
+    return msa.lib()
+
+
+def m3_shape(**kw):
+    base = dict(batch=1, total_q=32768, total_k=32768, max_q=32768, max_k=32768, hq=64, hkv=4,
+                topk=16, dp=64)
+    base.update(kw)
+    return msa.make_shape(**base)
+
+
+def decode_shape():
+    # 64 requests of one query each over KV caches of up to 131072 keys
+    return msa.make_shape(batch=64, total_q=64, total_k=64 * 70000, max_q=1, max_k=131072,
+                          hq=64, hkv=4, topk=16, dp=64)
+
+
+# ------------------------------------------------------------------ symbols
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(msa.SYMBOLS)
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings(L):
+    seen = set()
+    for st in range(7):
+        s = msa.lib().msa_status_string(st).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert msa.lib().msa_status_string(99).decode() == "unknown status"
+
+
+# ------------------------------------------------------------------ shape checks
+
+BAD_SHAPES = [
+    ("d", dict(d=64), msa.MSA_ERR_SHAPE),
+    ("block", dict(block=64), msa.MSA_ERR_SHAPE),
+    ("topk0", dict(topk=0), msa.MSA_ERR_SHAPE),
+    ("topk17", dict(topk=17), msa.MSA_ERR_SHAPE),
+    ("group3", dict(hq=12, hkv=4), msa.MSA_ERR_SHAPE),
+    ("group32", dict(hq=64, hkv=2), msa.MSA_ERR_SHAPE),
+    ("hq_not_multiple", dict(hq=10, hkv=4), msa.MSA_ERR_SHAPE),
+    ("list_q", dict(list_q=64), msa.MSA_ERR_SHAPE),
+    ("causal", dict(causal=2), msa.MSA_ERR_SHAPE),
+    ("max_q_gt_total", dict(max_q=40000), msa.MSA_ERR_SHAPE),
+    ("negative", dict(total_k=-1), msa.MSA_ERR_SHAPE),
+    ("batch0", dict(batch=0), msa.MSA_ERR_SHAPE),
+    ("dtype", dict(dtype=7), msa.MSA_ERR_DTYPE),
+    ("int32_entries", dict(total_q=1 << 24, max_q=1 << 24, total_k=1 << 24, max_k=1 << 24),
+     msa.MSA_ERR_SHAPE),
+]
+
+
+@pytest.mark.parametrize("name,kw,status", BAD_SHAPES, ids=[b[0] for b in BAD_SHAPES])
+def test_bad_shapes_are_rejected_by_every_entry_point(L, name, kw, status):
+    s = m3_shape(**kw)
+    if name == "causal":
+        s.causal = 2
+    n = ctypes.c_size_t(0)
+    assert L.msa_workspace_size(ctypes.byref(s), msa.MSA_AUTO, ctypes.byref(n)) == status
+    m = ctypes.c_int(0)
+    assert L.msa_resolve_mode(ctypes.byref(s), msa.MSA_AUTO, ctypes.byref(m)) == status
+    # device entry points: rejected before any launch
+    fake = ctypes.c_void_p(0x1000)
+    assert L.msa_index_topk(ctypes.byref(s), fake, fake, fake, fake, fake, None, None, 0,
+                            None) == status
+    assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
+                                 msa.MSA_AUTO, fake, 1 << 40, fake, None, None) == status
+    assert L.msa_combine(ctypes.byref(s), msa.MSA_AUTO, fake, 1 << 40, fake, None,
+                         None) == status
+
+
+def test_null_shape_and_outputs(L):
+    n = ctypes.c_size_t(0)
+    assert L.msa_workspace_size(None, msa.MSA_AUTO, ctypes.byref(n)) == msa.MSA_ERR_NULL
+    s = m3_shape()
+    assert L.msa_workspace_size(ctypes.byref(s), msa.MSA_AUTO, None) == msa.MSA_ERR_NULL
+    assert L.msa_resolve_mode(ctypes.byref(s), msa.MSA_AUTO, None) == msa.MSA_ERR_NULL
+    assert L.msa_crossover(ctypes.byref(s), 8.0, 16.0, None) == msa.MSA_ERR_NULL
+
+
+def test_null_device_pointers_and_small_workspace(L):
+    s = m3_shape()
+    fake = ctypes.c_void_p(0x1000)
+    need = msa.msa_workspace_size(s, msa.MSA_AUTO)
+    # index branch: missing lists / inputs
+    assert L.msa_index_topk(ctypes.byref(s), fake, fake, fake, fake, None, None, None, 0,
+                            None) == msa.MSA_ERR_NULL
+    assert L.msa_index_topk(ctypes.byref(s), None, fake, fake, fake, fake, None, None, 0,
+                            None) == msa.MSA_ERR_NULL
+    # unsupported proxy width
+    s_dp = m3_shape(dp=48)
+    assert L.msa_index_topk(ctypes.byref(s_dp), fake, fake, fake, fake, fake, None, None, 0,
+                            None) == msa.MSA_ERR_SHAPE
+    # main branch: workspace checks come first, then pointers
+    assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
+                                 msa.MSA_AUTO, fake, need - 1, fake, None,
+                                 None) == msa.MSA_ERR_WORKSPACE
+    assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
+                                 msa.MSA_AUTO, None, need, fake, None,
+                                 None) == msa.MSA_ERR_WORKSPACE
+    assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, None, fake, None, 0.1, fake, fake, fake,
+                                 msa.MSA_AUTO, fake, need, fake, None,
+                                 None) == msa.MSA_ERR_NULL
+    assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, None, fake, fake,
+                                 msa.MSA_AUTO, fake, need, fake, None,
+                                 None) == msa.MSA_ERR_NULL
+    s8 = m3_shape(dtype=msa.MSA_FP8_E4M3)
+    need8 = msa.msa_workspace_size(s8, msa.MSA_AUTO)
+    assert L.msa_sparse_attn_fwd(ctypes.byref(s8), fake, fake, fake, None, 0.1, fake, fake, fake,
+                                 msa.MSA_AUTO, fake, need8, fake, None,
+                                 None) == msa.MSA_ERR_NULL
+    assert L.msa_combine(ctypes.byref(s), msa.MSA_AUTO, fake, need, None, None,
+                         None) == msa.MSA_ERR_NULL
+    assert L.msa_combine(ctypes.byref(s), msa.MSA_AUTO, fake, need - 1, fake, None,
+                         None) == msa.MSA_ERR_WORKSPACE
+    assert L.msa_plan(ctypes.byref(s), None, fake, fake, fake, need, None) == msa.MSA_ERR_NULL
+    assert L.msa_attn_main(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake, 16,
+                           None) == msa.MSA_ERR_WORKSPACE
+    # a mode outside the enum
+    assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
+                                 5, fake, need, fake, None, None) == msa.MSA_ERR_MODE
+
+
+def test_python_binding_raises_on_error(L):
+    with pytest.raises(msa.MSAError) as ei:
+        msa.msa_workspace_size(m3_shape(d=64), msa.MSA_AUTO)
+    assert ei.value.status == msa.MSA_ERR_SHAPE
+
+
+# ------------------------------------------------------------------ workspace layout
+
+
+def test_kv_outer_workspace_layout_m3():
+    s = m3_shape()
+    lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
+    e_max = 32768 * 4 * 16
+    G = 16
+    regions = [lay.counters, lay.masks, lay.offsets, lay.scan_sums, lay.entry_q,
+               lay.entry_bucket, lay.cmap, lay.part_lse, lay.part_o]
+    assert regions == sorted(regions) and all(r % 256 == 0 for r in regions)
+    assert lay.part_o - lay.part_lse >= e_max * G * 4
+    assert lay.total - lay.part_o >= e_max * G * 128 * 2
+    assert lay.slots == 16 and lay.nb_max == 256
+    assert lay.n_words == lay.words_per_bucket * lay.n_ranges * 4 * lay.nb_max
+    assert msa.msa_workspace_size(s, msa.MSA_KV_OUTER) == lay.total
+
+
+def test_partial_memory_ratio_matches_the_pages():
+    """bf16 partials of every selected block take topk times the bf16 output."""
+    g = json.load(open(GOLDEN))["partial_memory_ratio"]
+    s = m3_shape(topk=g["topk"])
+    lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
+    part_o_bytes = lay.total - lay.part_o - 65536       # partials, then the padding sink
+    out_bytes = 32768 * 64 * 128 * 2
+    assert part_o_bytes - out_bytes * g["bf16_partials_over_bf16_output"] in range(0, 256)
+
+
+def test_q_outer_workspace():
+    s = decode_shape()
+    lay = msa.msa_workspace_layout_of(s, msa.MSA_Q_OUTER)
+    assert lay.slots >= 2                       # decode splits each list
+    assert lay.part_o - lay.part_lse >= 64 * 4 * lay.slots * 16 * 4
+    tiles = msa.make_shape(batch=1, total_q=8192, total_k=8192, max_q=8192, max_k=8192, hq=16,
+                           hkv=16, topk=16, causal=False, list_q=128)
+    lt = msa.msa_workspace_layout_of(tiles, msa.MSA_Q_OUTER)
+    assert lt.slots == 1 and lt.total <= 1024  # output written directly, nothing else
+
+
+# ------------------------------------------------------------------ schedule rule
+
+
+def test_dispatch_rule():
+    assert msa.msa_resolve_mode(m3_shape(), msa.MSA_AUTO) == msa.MSA_KV_OUTER
+    assert msa.msa_resolve_mode(m3_shape(dtype=msa.MSA_FP8_E4M3, total_q=131072, max_q=131072,
+                                         total_k=131072, max_k=131072),
+                                msa.MSA_AUTO) == msa.MSA_KV_OUTER
+    assert msa.msa_resolve_mode(decode_shape(), msa.MSA_AUTO) == msa.MSA_Q_OUTER
+    tiles = msa.make_shape(batch=1, total_q=8192, total_k=8192, max_q=8192, max_k=8192, hq=16,
+                           hkv=16, topk=16, causal=False, list_q=128)
+    assert msa.msa_resolve_mode(tiles, msa.MSA_AUTO) == msa.MSA_Q_OUTER
+    # explicit modes are honoured
+    assert msa.msa_resolve_mode(decode_shape(), msa.MSA_KV_OUTER) == msa.MSA_KV_OUTER
+    assert msa.msa_resolve_mode(m3_shape(), msa.MSA_Q_OUTER) == msa.MSA_Q_OUTER
+
+
+def test_crossover_reproduces_the_pages_figure():
+    g = json.load(open(GOLDEN))["crossover"]
+    s = msa.make_shape(batch=1, total_q=1024, total_k=1024, max_q=1024, max_k=1024, hq=g["hq"],
+                       hkv=g["hkv"], topk=g["topk"], dtype=msa.MSA_FP8_E4M3)
+    x = msa.msa_crossover(s, g["hbm_tbps"], g["l2_tbps"])
+    assert abs(x / g["nsb_over_n"] - 1) <= g["relative_tolerance"], x
+
+
+def test_crossover_is_monotone_in_cache_bandwidth():
+    s = m3_shape()
+    xs = [msa.msa_crossover(s, 8.0, b) for b in (10.0, 16.0, 24.0)]
+    assert xs[0] > xs[1] > xs[2]
+    s8 = m3_shape(dtype=msa.MSA_FP8_E4M3)
+    # fp8 data halves the K/V bytes Q-outer re-reads: the crossover moves down
+    assert msa.msa_crossover(s8, 8.0, 16.0) < xs[1]
