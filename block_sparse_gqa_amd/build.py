@@ -25,6 +25,13 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source extra flags. The index kernel's MFMA results feed VALU max-reductions directly:
+# the VGPR form of MFMA spares the accumulator-register reads the default form would need.
+EXTRA_FLAGS = {
+    "index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -34,7 +41,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -72,6 +72,14 @@ __device__ __forceinline__ void write_list(int32_t* out_idx, float* out_sc, int 
 }
 
 // ------------------------------------------------------------------------ tile kernel
+// s_waitcnt vmcnt(n) for the direct-to-LDS loads of the block ring (not tracked by the
+// compiler's own waits).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 template <int DP>
 __global__ __launch_bounds__(256) void index_tile_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
@@ -80,8 +88,9 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     int causal, int total_q, int total_k, int max_q, int max_k) {
   constexpr int CH = DP / 8;       // 16-byte chunks per proxy key row
   constexpr int STEPS = DP / 16;   // MFMA k-steps over the proxy dim
-  constexpr int PER_T = 128 * CH / 256;
-  __shared__ u32x4 kl[2][128 * CH];
+  constexpr int PER_T = 128 * CH / 256;   // direct-to-LDS loads per thread per block
+  constexpr int NBUF = 4;          // ring of key blocks: three in flight while one is scored
+  __shared__ u32x4 kl[NBUF][128 * CH];
 
   const int s = blockIdx.z, h = blockIdx.y;
   const int tile = gridDim.x - 1 - blockIdx.x;  // late (heavier, causal) tiles first
@@ -118,36 +127,37 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   TopList tl;
   tl.init();
 
-  u32x4 stage[PER_T];
-  auto load_block = [&](int j) {
+  // Block j into ring slot j % NBUF. Slot i of the buffer (16 bytes) holds chunk
+  // (i % CH) ^ f(row) of key row i / CH, f(row) = (row / 2) % CH: lane l of each load fetches
+  // the chunk that belongs in the slot it writes, so a load covers whole rows. Rows past the
+  // end of the sequence repeat its last key, which belongs to the same (last) block: the
+  // repeats cannot change the block's maximum, so no masking is needed.
+  auto dma_block = [&](int j) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
-      const int i = tid + 256 * p;
-      const int row = i / CH, cc = i % CH;
-      const int u = j * kBlock + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (u < sq.nk)
-        v = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + cc * 8);
-      stage[p] = v;
-    }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PER_T; ++p) {
-      const int i = tid + 256 * p;
-      const int row = i / CH, cc = i % CH;
-      kl[buf][row * CH + (cc ^ ((row >> 1) & (CH - 1)))] = stage[p];
+      const int i = p * 256 + t;
+      const int row = i / CH;
+      const int cc = (i % CH) ^ ((row >> 1) & (CH - 1));
+      const int u = min(j * kBlock + row, sq.nk - 1);
+      __builtin_amdgcn_global_load_lds(
+          k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + cc * 8,
+          (__attribute__((address_space(3))) void*)(&kl[j % NBUF][p * 256 + wave * 64]), 16, 0,
+          0);
     }
   };
 
-  if (jend > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  __syncthreads();
+  for (int j = 0; j < min(jend, NBUF - 1); ++j) dma_block(j);
   for (int j = 0; j < jend; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < jend) load_block(j + 1);
+    // block j has landed once at most the later blocks' loads are outstanding
+    const int later = min(jend - 1 - j, NBUF - 2);
+    if (later >= 2) wait_vm<2 * PER_T>();
+    else if (later == 1) wait_vm<PER_T>();
+    else wait_vm<0>();
+    __syncthreads();   // every thread's part of block j is in LDS; slot (j-1) % NBUF is free
+    if (j + NBUF - 1 < jend) dma_block(j + NBUF - 1);
+    const int buf = j % NBUF;
 
     f32x16 acc[4];
 #pragma unroll
@@ -162,25 +172,16 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
       }
     }
     float mx = kNegInf;
-    const bool partial = (j + 1) * kBlock > sq.nk;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = acc[kt][r];
-        if (partial) {
-          const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (j * kBlock + key >= sq.nk) x = kNegInf;
-        }
-        mx = fmaxf(mx, x);
-      }
-    }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kt][r]);
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const bool ins = qvalid && (causal ? (j < c) : (j != c));
-    if (ins) tl.insert(mx, j);
-
-    if (j + 1 < jend) store_block(buf ^ 1);
-    __syncthreads();
+    // insertion only where the block beats the current last entry (wave-uniform skip)
+    const bool ins = qvalid && (causal ? (j < c) : (j != c)) && mx > tl.sc[kMaxTopK - 1];
+    if (__any(ins)) {
+      if (ins) tl.insert(mx, j);
+    }
   }
 
   if (qvalid && hf == 0) {
