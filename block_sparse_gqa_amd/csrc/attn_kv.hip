@@ -118,30 +118,48 @@ __device__ __forceinline__ uint16_t* o_dest(uint16_t* part_o, uint16_t* sink, si
   return R < o_rows ? part_o + (o_row0 + R) * kD + (lane & 15) * 8 : sink;
 }
 
-// bf16 Q rows of the wave's next tile into its staging buffer with direct-to-LDS loads, in
-// the staging layout. `rowidx` is the lane's own Q row index (query * hq + head); load i
-// brings rows 4i .. 4i+3, lane l fetching the chunk that belongs in slot l%16 of row 4i + l/16,
-// so each load reads 1 KiB of whole rows.
-__device__ __forceinline__ void dma_q(u32x4* buf, const uint16_t* q, int rowidx, int lane) {
+// Q rows of the wave's next tile into its staging buffer with direct-to-LDS loads. `rowidx`
+// is the lane's own Q row index (query * hq + head). A row is RB = 128 * EB bytes = RB / 16
+// chunks; load i brings rows (64 / CPR) i .. +(64 / CPR - 1), lane l fetching the chunk that
+// belongs in slot l % CPR of its row (chunk c of row R sits in slot c ^ (R % CPR)), so each
+// load reads 1 KiB of whole rows.
+template <bool FP8>
+__device__ __forceinline__ void dma_q(u32x4* buf, const void* q, int rowidx, int lane) {
+  constexpr int RB = FP8 ? 128 : 256;    // bytes per Q row
+  constexpr int CPR = RB / 16;           // chunks per row
+  constexpr int RPL = 64 / CPR;          // rows per load
   asm volatile("" : "+v"(lane));
+  const char* qb = reinterpret_cast<const char*>(q);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int R = 4 * i + (lane >> 4);
+  for (int i = 0; i < 32 / RPL; ++i) {
+    const int R = RPL * i + lane / CPR;
     const int src_row = __shfl(rowidx, R);
-    const int c = (lane & 15) ^ (R & 15);
+    const int c = (lane % CPR) ^ (R % CPR);
     __builtin_amdgcn_global_load_lds(
-        q + (size_t)src_row * kD + c * 8,
+        qb + (size_t)src_row * RB + c * 16,
         (__attribute__((address_space(3))) void*)(buf + 64 * i), 16, 0, 0);
   }
 }
 
-// B operand of S^T from the staging buffer: chunk 2st + hf of the lane's row.
+// B operand of S^T from the staging buffer: elements 16*st + 8*hf .. +7 of the lane's row.
+template <bool FP8>
 __device__ __forceinline__ void read_q(const u32x4* buf, bf16x8 bq[8], int col, int hf) {
   asm volatile("" : "+v"(col), "+v"(hf));
-  const int x = hf ^ (col & 15);          // (2st + hf) ^ (col % 16) == 2st ^ x
-  const u32x4* const row = buf + col * 16;
+  if constexpr (!FP8) {
+    const int x = hf ^ (col & 15);          // (2st + hf) ^ (col % 16) == 2st ^ x
+    const u32x4* const row = buf + col * 16;
 #pragma unroll
-  for (int st = 0; st < 8; ++st) bq[st] = as_bf16x8(row[(2 * st) ^ x]);
+    for (int st = 0; st < 8; ++st) bq[st] = as_bf16x8(row[(2 * st) ^ x]);
+  } else {
+    const u32x2* const row = reinterpret_cast<const u32x2*>(buf + col * 8);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const u32x2 v = row[2 * (st ^ (col & 7)) + hf];
+      const u32x2 lo = fp8x4_to_bf16x4(v[0]);
+      const u32x2 hi = fp8x4_to_bf16x4(v[1]);
+      bq[st] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+  }
 }
 
 // s_waitcnt vmcnt(0): direct-to-LDS loads are not tracked by the compiler's own waits.
@@ -182,7 +200,6 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
     sl2 *= a.descale[0] * a.descale[1];
     dv = a.descale[2];
   }
-  const char* qb = reinterpret_cast<const char*>(a.q);
   const char* kb = reinterpret_cast<const char*>(a.k);
   const char* vb = reinterpret_cast<const char*>(a.v);
   const uint32_t kv_row = (uint32_t)a.hkv * kD;    // elements between consecutive keys
@@ -218,14 +235,12 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
     __syncthreads();
 
     auto qidx = [&](int e, int tv) { return (e < run_end ? tv : sq.q0) * a.hq + h * G + g; };
-    auto qrow = [&](int e, int tv) { return qb + (size_t)qidx(e, tv) * kD * EB; };
 
     int e0 = cur + rent, e1 = e0 + MQ;
     int t0v = a.entry_q[min(e0, last)];
     int t1v = a.entry_q[min(e1, last)];
     bf16x8 bq[8];
-    if constexpr (FP8) load_q_operand<FP8>(bq, qrow(e0, t0v), hf);
-    else dma_q(obuf, reinterpret_cast<const uint16_t*>(a.q), qidx(e0, t0v), lane);
+    dma_q<FP8>(obuf, a.q, qidx(e0, t0v), lane);
     // LDS operands, double-buffered over the 16 steps of a tile (8 K steps, then 8 V steps):
     // step i reads fr[i & 1] while the reads of step i + 1 are in flight.
     bf16x8 fr[2][4];
@@ -246,10 +261,8 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
       if (a.causal) kmax = min(kmax, sq.nk - sq.nq + (t0v - sq.q0) - u0);
       const bool need_mask = __any(kmax < 127);
       const bool valid = e0 < run_end;
-      if constexpr (!FP8) {
-        wait_vm0();               // this tile's Q rows have landed in the staging buffer
-        read_q(obuf, bq, col, hf);
-      }
+      wait_vm0();               // this tile's Q rows have landed in the staging buffer
+      read_q<FP8>(obuf, bq, col, hf);
 
       // ---- phase A: QK^T(j) | O(j-1) through LDS to memory
       f32x16 sc[4];
@@ -275,10 +288,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
         }
         MSA_INTERLEAVE(1, 6);
       }
-      // Q of the next tile: straight into bq (fp8: converted on load) or into the staging
-      // buffer, whose read-back for the stores above is complete
-      if constexpr (FP8) load_q_operand<FP8>(bq, qrow(e1, t1v), hf);
-      else dma_q(obuf, reinterpret_cast<const uint16_t*>(a.q), qidx(e1, t1v), lane);
+      // Q of the next tile into the staging buffer, whose read-back for the stores above is
+      // complete
+      dma_q<FP8>(obuf, a.q, qidx(e1, t1v), lane);
       // ---- row max of S(j)
       if (need_mask) {
 #pragma unroll
