@@ -45,6 +45,19 @@ __device__ __forceinline__ int seq_of_row(const int32_t* cu_q, int batch, int t)
   return lo;
 }
 
+// Per-tile lists: (tile, head) of linear workgroup id `id` over a tiles x heads grid. The
+// hardware hands ids to the 8 XCDs round-robin; XCD x = id % 8 takes the (id / 8)-th pair of
+// its own contiguous run of head-major (head, tile) pairs, so the workgroups running together
+// on one XCD share heads and their K/V blocks stay in that XCD's L2.
+__device__ __forceinline__ void xcd_tile_head(int id, int tiles, int heads, int* tile,
+                                              int* head) {
+  const int n = tiles * heads;
+  int pair = id;
+  if (n % 8 == 0) pair = (id % 8) * (n / 8) + id / 8;   // a bijection of [0, n)
+  *head = pair / tiles;
+  *tile = pair % tiles;
+}
+
 template <bool FP8, int G>
 __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   constexpr int EB = FP8 ? 1 : 2;
@@ -54,12 +67,13 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   const int r = wave * 32 + col;
 
   // --- the rows of this workgroup and their list
-  int s, h, hh, t, split;
+  int s, h, hh, t, split, tile = 0;
   bool valid;
   const int32_t* list;
   if (a.list_q > 1) {
-    const int tile = blockIdx.x;
-    hh = blockIdx.y;
+    // Workgroup ids go round-robin over the XCDs; remap them so that the tiles of one head
+    // run together on one XCD, whose L2 then holds that head's K/V blocks.
+    xcd_tile_head(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x, gridDim.y, &tile, &hh);
     h = hh / G;
     s = blockIdx.z;
     split = 0;
@@ -87,7 +101,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   // the workgroup's largest position (rows are in query order) for whole-block skipping
   int pos_max;
   if (a.list_q > 1) {
-    const int il_last = min(blockIdx.x * a.list_q + a.list_q - 1, sq.nq - 1);
+    const int il_last = min(tile * a.list_q + a.list_q - 1, sq.nq - 1);
     pos_max = sq.nk - sq.nq + il_last;
   } else {
     pos_max = pos;
@@ -115,37 +129,107 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
 
   const int per = (a.topk + a.splits - 1) / a.splits;
   const int slot0 = split * per, slot1 = min(a.topk, slot0 + per);
-  for (int slot = slot0; slot < slot1; ++slot) {
-    const int b = list[slot];
-    bool use = b >= 0 && b < nb;
-    if (use && a.causal && b * kBlock > pos_max) use = false;
-    for (int p = 0; p < slot && use; ++p)
-      if (list[p] == b) use = false;
-    if (!use) continue;                      // uniform across the workgroup
-    const int u0 = b * kBlock;
-    const int nk_rel = sq.nk - u0;
-    __syncthreads();
-    stage_kv<FP8>(L, kb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB,
-                  vb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB, kv_row, nk_rel);
-    __syncthreads();
-    if (wave_rows) {
+  // The blocks this workgroup visits (uniform): valid, visible to some row, first occurrence.
+  __shared__ int vis[kMaxTopK];
+  __shared__ int n_vis;
+  if (tid == 0) {
+    int n = 0;
+    for (int slot = slot0; slot < slot1; ++slot) {
+      const int b = list[slot];
+      bool use = b >= 0 && b < nb;
+      if (use && a.causal && b * kBlock > pos_max) use = false;
+      for (int p = 0; p < slot && use; ++p)
+        if (list[p] == b) use = false;
+      if (use) vis[n++] = b;
+    }
+    n_vis = n;
+  }
+  __syncthreads();
+  const int nv = n_vis;
+  const size_t kv_head = (size_t)sq.k0 * a.hkv + h;     // row of key 0 of the sequence, head h
+
+  auto fold = [&](int u0, int nk_rel, auto&& pv) {
+    f32x16 sacc[4];
+    qk_block(L, bq, sacc, col, hf);
+    int kmax = min(127, nk_rel - 1);
+    if (a.causal) kmax = min(kmax, pos - u0);
+    const float mb = mask_max(sacc, kmax, __any(kmax < 127), hf);
+    const float m_new = fmaxf(m_run, mb);          // raw-score units
+    const float c = m_new > ninf ? m_new * sl2 : 0.f;
+    const float alpha = m_run > ninf ? __builtin_amdgcn_exp2f(m_run * sl2 - c) : 0.f;
+    u32x4 pk[4][2];
+    const float lb = exp_pack(sacc, sl2, c, pk);
+    l_run = l_run * alpha + lb;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    m_run = m_new;
+    pv(pk);
+  };
+
+  if constexpr (FP8) {
+    // fp8 K/V are widened to bf16 while staging (through registers), one block at a time
+    for (int j = 0; j < nv; ++j) {
+      const int u0 = vis[j] * kBlock;
+      const int nk_rel = sq.nk - u0;
+      __syncthreads();
+      stage_kv<FP8>(L, kb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB,
+                    vb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB, kv_row, nk_rel);
+      __syncthreads();
+      if (wave_rows) fold(u0, nk_rel, [&](const u32x4 (&pk)[4][2]) {
+        pv_block<false>(L, pk, oacc, col, hf);
+      });
+    }
+  } else {
+    // bf16: K and V of block j+1 stream into LDS by direct loads while block j is computed.
+    // K(j+1) is issued once every wave has finished QK(j); V(j+1) once PV(j) is done.
+    const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k);
+    const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v);
+    auto dma_k = [&](int j) {
+      const int u0 = vis[j] * kBlock;
+      dma_rows<false>(L.k, kp + (kv_head + (size_t)u0 * a.hkv) * kD, kv_row, sq.nk - u0);
+    };
+    auto dma_v = [&](int j) {
+      const int u0 = vis[j] * kBlock;
+      dma_rows<true>(L.vt, vp + (kv_head + (size_t)u0 * a.hkv) * kD, kv_row, sq.nk - u0);
+    };
+    if (nv > 0) {
+      dma_k(0);
+      dma_v(0);
+    }
+    for (int j = 0; j < nv; ++j) {
+      const int u0 = vis[j] * kBlock;
+      const int nk_rel = sq.nk - u0;
+      wait_vm<8>();          // K(j) landed (only V(j), 8 loads, may still be in flight)
+      __syncthreads();
       f32x16 sacc[4];
-      qk_block(L, bq, sacc, col, hf);
-      int kmax = min(127, nk_rel - 1);
-      if (a.causal) kmax = min(kmax, pos - u0);
-      const float mb = mask_max(sacc, kmax, __any(kmax < 127), hf);
-      const float m_new = fmaxf(m_run, mb);          // raw-score units
-      const float c = m_new > ninf ? m_new * sl2 : 0.f;
-      const float alpha = m_run > ninf ? __builtin_amdgcn_exp2f(m_run * sl2 - c) : 0.f;
+      if (wave_rows) qk_block(L, bq, sacc, col, hf);
+      __syncthreads();       // K buffer free
+      const bool more = j + 1 < nv;
+      if (more) dma_k(j + 1);
       u32x4 pk[4][2];
-      const float lb = exp_pack(sacc, sl2, c, pk);
-      l_run = l_run * alpha + lb;
+      if (wave_rows) {
+        int kmax = min(127, nk_rel - 1);
+        if (a.causal) kmax = min(kmax, pos - u0);
+        const float mb = mask_max(sacc, kmax, __any(kmax < 127), hf);
+        const float m_new = fmaxf(m_run, mb);          // raw-score units
+        const float c = m_new > ninf ? m_new * sl2 : 0.f;
+        const float alpha = m_run > ninf ? __builtin_amdgcn_exp2f(m_run * sl2 - c) : 0.f;
+        const float lb = exp_pack(sacc, sl2, c, pk);
+        l_run = l_run * alpha + lb;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-      m_run = m_new;
-      pv_block<false>(L, pk, oacc, col, hf);
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        m_run = m_new;
+      }
+      if (more) wait_vm<8>();   // V(j) landed (K(j+1) may still be in flight)
+      else wait_vm<0>();
+      __syncthreads();
+      if (wave_rows) pv_block_tr<false>(L, pk, oacc, lane);
+      __syncthreads();       // V buffer free
+      if (more) dma_v(j + 1);
     }
   }
 

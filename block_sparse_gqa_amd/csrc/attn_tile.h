@@ -190,6 +190,81 @@ __device__ __forceinline__ void pv_block(const KVLds& L, const u32x4 p[4][2], f3
   }
 }
 
+// ---- row-major staging by direct-to-LDS loads (bf16), for pipelined block loops
+// K keeps the layout above (chunk c of key row r at slot c ^ swz(r)); V is stored row-major
+// too, chunk c of key row r at slot c ^ swz_v(r), and read transposed with the LDS transpose
+// load. swz_v depends on r % 4 only, so every transposed read of a lane is its fixed base
+// address plus a compile-time offset.
+__device__ __forceinline__ int swz_v(int key) { return (key & 3) << 2; }
+
+// s_waitcnt vmcnt(n): direct-to-LDS loads are not tracked by the compiler's own waits.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// One 128-row x 256-byte block (rows at or past nk_rel repeat row nk_rel - 1; the caller masks
+// or zero-weights them) into `dst`, 256 threads, 8 loads each: slot i of the block holds chunk
+// (i % 16) ^ f(i / 16) of row i / 16, lane l fetching exactly the chunk its slot needs.
+template <bool V>
+__device__ __forceinline__ void dma_rows(u32x4* dst, const uint16_t* base, uint32_t row_stride,
+                                         int nk_rel) {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  const int wave = t >> 6, row0 = t >> 4, slot = t & 15;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int row = 16 * p + row0;        // swz(row) and swz_v(row) from row0 and p
+    const int f = V ? swz_v(row0)
+                    : ((row0 & 3) | ((p & 1) << 2) | (((row0 >> 2) & 1) << 3));
+    const uint32_t r = (uint32_t)min(row, nk_rel - 1);
+    __builtin_amdgcn_global_load_lds(
+        base + r * row_stride + (uint32_t)((slot ^ f) * 8),
+        (__attribute__((address_space(3))) void*)(dst + p * 256 + wave * 64), 16, 0, 0);
+  }
+}
+
+// O^T (+)= V^T P^T with V row-major in LDS. The LDS transpose load gives lane j of each
+// 16-lane group elements from the 16 rows x 4 columns its group's lanes address: lane s of
+// the group addresses key row k0 + s/4 at dims D(s%4) .. +3 with D = {0, 16, 4, 20} (+8 for
+// the group of lanes 16..31), and lane j receives dims D(j/4) + j%4 = rowperm(j) of keys
+// k0 .. k0+3, i.e. its A-operand row for four consecutive keys.
+template <bool INIT>
+__device__ __forceinline__ void pv_block_tr(const KVLds& L, const u32x4 p[4][2], f32x16 o[4],
+                                            int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  asm volatile("" : "+v"(lane));
+  const int s = lane & 15, grp = (lane >> 4) & 1, hf = lane >> 5;
+  const int dsel = s & 3, k_lane = s >> 2;
+  const int d_lane = ((dsel & 1) << 4) + ((dsel >> 1) << 2) + 8 * grp;   // D(s%4) + 8*grp
+  // element (key 16*hf + k_lane, dim 32*dt + d_lane); chunk (dim / 8) ^ (4 * k_lane)
+  const unsigned short* vrow = reinterpret_cast<const unsigned short*>(L.vt);
+  const unsigned short* base[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    base[dt] = vrow + (16 * hf + k_lane) * 128 + (4 * (dt ^ k_lane) + (d_lane >> 3)) * 8 +
+               (d_lane & 7);
+#pragma unroll
+  for (int step = 0; step < 8; ++step) {
+    const int kt = step >> 1, ks = step & 1;
+    bf16x8 a[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      s4 r[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(base[dt] + (32 * kt + 8 * ks + 4 * h2) * 128));
+      a[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    const bf16x8 bp = as_bf16x8(p[kt][ks]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      o[dt] = mfma32(a[dt], bp, (INIT && step == 0) ? f32x16{} : o[dt]);
+  }
+}
+
 // Row max of raw scores over the block, keys past `kmax` (block-relative index of the last
 // visible key) set to -inf first when `need_mask`. Both lanes of the row agree.
 __device__ __forceinline__ float mask_max(f32x16 s[4], int kmax, bool need_mask, int hf) {
