@@ -87,6 +87,40 @@ def useful_pairs(cfg, cu_q, cu_k, lists_np: np.ndarray, list_q: int) -> tuple[in
     return total, buckets
 
 
+def index_work(cfg, cu_q, cu_k) -> tuple[float, float]:
+    """(proxy FLOPs, proxy bytes) the index branch must do: 2*dp per (query, group, key) over
+    the keys of every visible block other than the local one; q_idx and those k_idx rows once,
+    plus the lists written."""
+    flops, kbytes = 0.0, 0.0
+    for s in range(len(cu_q) - 1):
+        nq = int(cu_q[s + 1] - cu_q[s])
+        nk = int(cu_k[s + 1] - cu_k[s])
+        if nq == 0:
+            continue
+        pos = nk - nq + np.arange(nq)
+        nb = -(-nk // 128)
+        if cfg.causal:
+            keys = 128.0 * np.maximum(pos // 128, 0)            # blocks 0 .. c-1, all full
+            kread = min(nk, 128 * (int(pos[-1]) // 128))
+        else:
+            keys = np.full(nq, float(nk - min(128, nk)))         # all but the local block
+            kread = nk
+        flops += 2.0 * cfg.dp * cfg.hkv * float(np.sum(keys))
+        kbytes += 2.0 * cfg.dp * cfg.hkv * kread
+    tq = int(cu_q[-1])
+    return flops, kbytes + 2.0 * cfg.dp * cfg.hkv * tq + 4.0 * cfg.hkv * cfg.topk * tq
+
+
+def roof(ms, bound, amount):
+    """Roofline entry of one kernel: amount = bytes (hbm) or FLOPs (mfma) per call."""
+    t = ms * 1e-3
+    if bound == "hbm":
+        return {"ms": ms, "bound": "hbm", "achieved": amount / t / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": amount / t / PEAK_HBM, "algorithmic": amount}
+    return {"ms": ms, "bound": "mfma", "achieved": amount / t / 1e12, "peak": PEAK_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": amount / t / PEAK_BF16, "algorithmic": amount}
+
+
 class Timer:
     """HIP events on the current stream around each call of a step."""
 
@@ -292,9 +326,35 @@ def main():
             + case.total_q * cfg.hq * (128 * 2 + 4)
         res["combine_gbps"] = comb_alg / (kms["combine"] * 1e-3) / 1e9
     else:
-        res["roofline"] = {"bound": "mfma", "kernel": "attn_q_kernel",
-                           "achieved": flops / t_main / 1e12, "peak": PEAK_BF16 / 1e12,
-                           "unit": "TFLOP/s", "frac": flops / t_main / PEAK_BF16, "traffic": None}
+        qbytes = nsb * 2 * 128 * 128 * eb + case.total_q * cfg.hq * 128 * (eb + 2)
+        if flops / qbytes > PEAK_BF16 / PEAK_HBM:
+            res["roofline"] = {"bound": "mfma", "kernel": "attn_q_kernel",
+                               "achieved": flops / t_main / 1e12, "peak": PEAK_BF16 / 1e12,
+                               "unit": "TFLOP/s", "frac": flops / t_main / PEAK_BF16,
+                               "traffic": None}
+        else:
+            res["roofline"] = {"bound": "hbm", "kernel": "attn_q_kernel",
+                               "achieved": qbytes / t_main / 1e9, "peak": PEAK_HBM / 1e9,
+                               "unit": "GB/s", "frac": qbytes / t_main / PEAK_HBM,
+                               "traffic": None, "algorithmic_bytes": qbytes}
+    # every call of the step against its own roofline
+    kr = {}
+    if given is None:
+        ifl, ib = index_work(cfg, case.cu_q, case.cu_k)
+        ridge = PEAK_BF16 / PEAK_HBM
+        kr["index"] = roof(kms["index"], "mfma", ifl) if ifl / ib > ridge else \
+            roof(kms["index"], "hbm", ib)
+    if kv:
+        e_max = case.total_q * cfg.hkv * cfg.topk
+        kr["plan"] = roof(kms["plan"], "hbm", e_max * 4 + n_ent * 8 + e_max * 4)
+        kr["attn_main"] = roof(kms["attn_main"], "hbm", alg)
+        kr["combine"] = roof(kms["combine"], "hbm", comb_alg)
+    else:
+        qbytes = nsb * 2 * 128 * 128 * eb + case.total_q * cfg.hq * 128 * (eb + 2)
+        kr["attn_q"] = roof(kms["attn_q"], "mfma", flops) if flops / qbytes > PEAK_BF16 / PEAK_HBM \
+            else roof(kms["attn_q"], "hbm", qbytes)
+        kr["combine"] = {"ms": kms["combine"]}
+    res["kernels"] = kr
     res["kernel_sha"] = kernel_sha()
     res["gen_seconds"] = round(t_gen, 1)
     if args.copy_probe:
