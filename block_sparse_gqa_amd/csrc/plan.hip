@@ -43,19 +43,6 @@ __device__ __forceinline__ size_t word_index(const PlanArgs& a, int s, int h, in
   return bucket_of(a, s, h, w, b) * a.wr + (w % a.wr);
 }
 
-// Block b of list slot `slot` is a real entry for this query: in range, first occurrence,
-// and (causal) holding at least one key at or before the query's position.
-__device__ __forceinline__ int entry_block(const PlanArgs& a, const Seq& sq, int il, int slot,
-                                           const int32_t* L) {
-  const int b = L[slot];
-  const int nb = min((sq.nk + kBlock - 1) / kBlock, a.nb_max);
-  if (b < 0 || b >= nb) return -1;
-  if (a.causal && b * kBlock > sq.nk - sq.nq + il) return -1;
-  for (int p = 0; p < slot; ++p)
-    if (L[p] == b) return -1;
-  return b;
-}
-
 __device__ __forceinline__ const int32_t* list_of(const PlanArgs& a, int s, const Seq& sq,
                                                   int il, int h) {
   const int64_t row = a.list_q == 1 ? (int64_t)(sq.q0 + il)
@@ -63,6 +50,28 @@ __device__ __forceinline__ const int32_t* list_of(const PlanArgs& a, int s, cons
   return a.lists + (row * a.hkv + h) * a.topk;
 }
 
+// The entry blocks of one (query, group) list: blk[k] = the block of slot k when it is a real
+// entry (in range, first occurrence in the list, and, causally, holding at least one key at or
+// before the query's position), else -1. One read of the list row per query.
+__device__ __forceinline__ void entry_blocks(const PlanArgs& a, const Seq& sq, int s, int il,
+                                             int h, int blk[kMaxTopK]) {
+  const int32_t* L = list_of(a, s, sq, il, h);
+  const int nb = min((sq.nk + kBlock - 1) / kBlock, a.nb_max);
+  const int pos = sq.nk - sq.nq + il;
+  int raw[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) raw[k] = k < a.topk ? L[k] : -1;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    const int b = raw[k];
+    bool ok = b >= 0 && b < nb && !(a.causal && b * kBlock > pos);
+#pragma unroll
+    for (int p = 0; p < k; ++p) ok = ok && raw[p] != b;
+    blk[k] = ok ? b : -1;
+  }
+}
+
+// One thread per query of the workgroup's wpb words.
 __global__ __launch_bounds__(256) void plan_mask_kernel(PlanArgs a) {
   extern __shared__ unsigned long long lm[];   // [nb_max][wpb]
   const int s = blockIdx.z, h = blockIdx.y;
@@ -74,12 +83,14 @@ __global__ __launch_bounds__(256) void plan_mask_kernel(PlanArgs a) {
   __syncthreads();
   const int qa = w0 * kWordQ;
   const int qb = min((w0 + a.wpb) * kWordQ, sq.nq);
-  const int n = max(qb - qa, 0) * a.topk;
-  for (int i = tid; i < n; i += 256) {
-    const int il = qa + i / a.topk, slot = i % a.topk;
-    const int32_t* L = list_of(a, s, sq, il, h);
-    const int b = entry_block(a, sq, il, slot, L);
-    if (b >= 0) atomicOr(&lm[b * a.wpb + (il / kWordQ - w0)], 1ull << (il % kWordQ));
+  for (int il = qa + tid; il < qb; il += 256) {
+    int blk[kMaxTopK];
+    entry_blocks(a, sq, s, il, h, blk);
+    const unsigned long long bit = 1ull << (il % kWordQ);
+    const int wl = il / kWordQ - w0;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+      if (blk[k] >= 0) atomicOr(&lm[blk[k] * a.wpb + wl], bit);
   }
   __syncthreads();
   // a workgroup's words lie in one range (wpb divides wr), so each block's words are contiguous
@@ -97,22 +108,24 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(PlanArgs a) {
   const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
   const int qa = w0 * kWordQ;
   const int qb = min((w0 + a.wpb) * kWordQ, sq.nq);
-  const int n = max(qb - qa, 0) * a.topk;
-  for (int i = tid; i < n; i += 256) {
-    const int il = qa + i / a.topk, slot = i % a.topk;
-    const int32_t* L = list_of(a, s, sq, il, h);
-    const int b = entry_block(a, sq, il, slot, L);
-    int e = -1;
-    if (b >= 0) {
-      const int w = il / kWordQ;
-      const size_t wi = word_index(a, s, h, w, b);
-      const unsigned long long m = a.masks[wi];
-      const unsigned long long below = (1ull << (il % kWordQ)) - 1ull;
-      e = a.offsets[wi] + __popcll(m & below);
-      a.entry_q[e] = sq.q0 + il;
-      a.entry_bucket[e] = (int)bucket_of(a, s, h, w, b);
+  for (int il = qa + tid; il < qb; il += 256) {
+    int blk[kMaxTopK];
+    entry_blocks(a, sq, s, il, h, blk);
+    const int w = il / kWordQ;
+    const unsigned long long below = (1ull << (il % kWordQ)) - 1ull;
+    int32_t* cm = a.cmap + ((size_t)(sq.q0 + il) * a.hkv + h) * a.topk;
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+      if (k >= a.topk) break;
+      int e = -1;
+      if (blk[k] >= 0) {
+        const size_t wi = word_index(a, s, h, w, blk[k]);
+        e = a.offsets[wi] + __popcll(a.masks[wi] & below);
+        a.entry_q[e] = sq.q0 + il;
+        a.entry_bucket[e] = (int)bucket_of(a, s, h, w, blk[k]);
+      }
+      cm[k] = e;
     }
-    a.cmap[((size_t)(sq.q0 + il) * a.hkv + h) * a.topk + slot] = e;
   }
 }
 
