@@ -101,21 +101,14 @@ __device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, flo
   }
 }
 
-// Read-back i (0..7): lane l takes chunk l%16 of row 4i + l/16, so the 64 lanes hold
-// 1 KiB of consecutive output bytes.
-__device__ __forceinline__ u32x4 unstage_o(const u32x4* buf, int i, int lane) {
+// Read-back i (0..7): lane l takes chunk l%16 of row R = 4i + l/16, so the 64 lanes hold
+// 1 KiB of consecutive output bytes. With R % 16 = 4 (i % 4) + l/16 the slot is
+// (l%16) ^ (l/16) ^ 4 (i % 4): the lane's address for read-back i is ub[i % 4] + 256 (i / 4).
+__device__ __forceinline__ void unstage_bases(int lane, int ub[4]) {
   asm volatile("" : "+v"(lane));
-  const int R = 4 * i + (lane >> 4);
-  return buf[R * 16 + ((lane & 15) ^ (R & 15))];
-}
-
-// Destination of read-back i: the wave's output rows start at o_row0 (a row of the partial
-// buffer); rows at or past o_rows are padding and go to the sink.
-__device__ __forceinline__ uint16_t* o_dest(uint16_t* part_o, uint16_t* sink, size_t o_row0,
-                                            int o_rows, int i, int lane) {
-  asm volatile("" : "+v"(lane));
-  const int R = 4 * i + (lane >> 4);
-  return R < o_rows ? part_o + (o_row0 + R) * kD + (lane & 15) * 8 : sink;
+  const int lq = lane >> 4, x = (lane & 15) ^ lq;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ub[j] = (4 * j + lq) * 16 + (x ^ (4 * j));
 }
 
 // Q rows of the wave's next tile into its staging buffer with direct-to-LDS loads. `rowidx`
@@ -123,18 +116,26 @@ __device__ __forceinline__ uint16_t* o_dest(uint16_t* part_o, uint16_t* sink, si
 // chunks; load i brings rows (64 / CPR) i .. +(64 / CPR - 1), lane l fetching the chunk that
 // belongs in slot l % CPR of its row (chunk c of row R sits in slot c ^ (R % CPR)), so each
 // load reads 1 KiB of whole rows.
-template <bool FP8>
+template <bool FP8, int G>
 __device__ __forceinline__ void dma_q(u32x4* buf, const void* q, int rowidx, int lane) {
   constexpr int RB = FP8 ? 128 : 256;    // bytes per Q row
   constexpr int CPR = RB / 16;           // chunks per row
   constexpr int RPL = 64 / CPR;          // rows per load
   asm volatile("" : "+v"(lane));
   const char* qb = reinterpret_cast<const char*>(q);
+  const int lr = lane / CPR, lc = lane % CPR;
 #pragma unroll
   for (int i = 0; i < 32 / RPL; ++i) {
-    const int R = RPL * i + lane / CPR;
-    const int src_row = __shfl(rowidx, R);
-    const int c = (lane % CPR) ^ (R % CPR);
+    const int R = RPL * i + lr;
+    int src_row;
+    if constexpr (G >= RPL) {
+      // the load's rows are consecutive heads of one query: Q rows row0 .. row0 + RPL - 1,
+      // row0 being the row index held by the lane of row RPL * i
+      src_row = __builtin_amdgcn_readlane(rowidx, RPL * i) + lr;
+    } else {
+      src_row = __shfl(rowidx, R);
+    }
+    const int c = lc ^ (R % CPR);
     __builtin_amdgcn_global_load_lds(
         qb + (size_t)src_row * RB + c * 16,
         (__attribute__((address_space(3))) void*)(buf + 64 * i), 16, 0, 0);
@@ -240,7 +241,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
     int t0v = a.entry_q[min(e0, last)];
     int t1v = a.entry_q[min(e1, last)];
     bf16x8 bq[8];
-    dma_q<FP8>(obuf, a.q, qidx(e0, t0v), lane);
+    int ub[4];
+    unstage_bases(lane, ub);
+    dma_q<FP8, G>(obuf, a.q, qidx(e0, t0v), lane);
     // LDS operands, double-buffered over the 16 steps of a tile (8 K steps, then 8 V steps):
     // step i reads fr[i & 1] while the reads of step i + 1 are in flight.
     bf16x8 fr[2][4];
@@ -250,8 +253,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
     float o_mul = 0.f, o_lse = 0.f;
-    size_t o_row0 = 0;
-    int o_rows = 0;
+    // stores of the previous tile: rows 4i + lane/16 of the wave at o_base + 4i rows, valid
+    // while 4i < o_nv (none yet)
+    uint16_t* o_base = o_sink;
+    int o_nv = 0;
     float* lse_ptr = lse_sink;
 
     for (int tile0 = cur; tile0 < run_end; tile0 += MQ) {
@@ -279,10 +284,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2) {
             const int i = 2 * (st - 4) + i2;
-            const u32x4 w = unstage_o(obuf, i, lane);
+            const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
             // streaming store: the partials are read once, by the combine kernel
             __builtin_nontemporal_store(
-                w, reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)));
+                w, reinterpret_cast<u32x4*>(4 * i < o_nv ? o_base + i * 4 * kD : o_sink));
           }
           if (st == 7) *lse_ptr = o_lse;
         }
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
       }
       // Q of the next tile into the staging buffer, whose read-back for the stores above is
       // complete
-      dma_q<FP8>(obuf, a.q, qidx(e1, t1v), lane);
+      dma_q<FP8, G>(obuf, a.q, qidx(e1, t1v), lane);
       // ---- row max of S(j)
       if (need_mask) {
 #pragma unroll
@@ -327,8 +332,12 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
       // the output of tile j is stored during the next tile's phase A
       o_mul = any ? dv / l : 0.f;
       o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-      o_row0 = (size_t)tile0 * G + wave * 32;
-      o_rows = (run_end - tile0) * G - wave * 32;
+      {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        o_base = a.part_o + ((size_t)tile0 * G + wave * 32 + (ln >> 4)) * kD + (ln & 15) * 8;
+        o_nv = (run_end - tile0) * G - wave * 32 - (ln >> 4);
+      }
       lse_ptr = valid ? a.part_lse + (size_t)e0 * G + g : lse_sink;
       e0 = e1;
       e1 = e2;
@@ -341,9 +350,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
     for (int dt = 0; dt < 4; ++dt) stage_o(obuf, oacc[dt], dt, o_mul, col, hf);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const u32x4 w = unstage_o(obuf, i, lane);
+      const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
       __builtin_nontemporal_store(
-          w, reinterpret_cast<u32x4*>(o_dest(a.part_o, o_sink, o_row0, o_rows, i, lane)));
+          w, reinterpret_cast<u32x4*>(4 * i < o_nv ? o_base + i * 4 * kD : o_sink));
     }
     *lse_ptr = o_lse;
     cur = run_end;
