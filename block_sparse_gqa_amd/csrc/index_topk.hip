@@ -6,7 +6,7 @@
 // optimization for MiniMax M3 on NVIDIA Blackwell" (summary): one selection per GQA group.
 //
 // Two kernels compute the same result:
-//  - index_tile_kernel (prefill): a workgroup owns 128 queries of one group and streams the
+//  - index_tile_kernel (prefill): a workgroup owns 256 queries of one group and streams the
 //    proxy key blocks through LDS; S^T = K_idx Q_idx^T on bf16 MFMA puts one query per lane
 //    column, so a block max is an in-register max plus one cross-lane exchange.
 //  - index_split_kernel + index_merge_kernel (few queries, e.g. decode): the key range is
@@ -14,6 +14,8 @@
 //    proxy keys); their top-K lists are merged by (score desc, block asc).
 // Blocks are always visited in ascending order and inserted only on a strictly greater
 // score, so equal scores keep the lower block index first.
+#include <algorithm>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -21,6 +23,16 @@ namespace msa {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kIndexTileQ = 256;   // queries per workgroup of the tile kernel (64 per wave)
+
+// Blocks the tile kernel scores for query tile `tile` of a sequence: those before the local
+// block of the tile's last query (causal), or all of them.
+__device__ __forceinline__ int tile_blocks(const Seq& sq, int tile, int causal) {
+  const int nb = (sq.nk + kBlock - 1) / kBlock;
+  if (!causal) return nb;
+  const int il_last = min(tile * kIndexTileQ + kIndexTileQ - 1, sq.nq - 1);
+  return max(0, min(floordiv(sq.nk - sq.nq + il_last, kBlock), nb));
+}
 constexpr float kPosInf = __builtin_inff();
 
 // Running top list of (score, block) sorted by score descending; a new block goes after
@@ -80,6 +92,9 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// A workgroup scores one 256-query tile of one group against every block it can see,
+// heavy (late, causal) tiles first. (Splitting long tiles' key ranges over several
+// workgroups, with a merge of the partial lists, measured slower at 32K and 128K keys.)
 template <int DP>
 __global__ __launch_bounds__(256) void index_tile_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
@@ -93,34 +108,35 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   __shared__ u32x4 kl[NBUF][128 * CH];
 
   const int s = blockIdx.z, h = blockIdx.y;
-  const int tile = gridDim.x - 1 - blockIdx.x;  // late (heavier, causal) tiles first
+  const int tile = gridDim.x - 1 - blockIdx.x;   // late (heavier) tiles first
   const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
-  if (tile * 128 >= sq.nq) return;
+  if (tile * kIndexTileQ >= sq.nq) return;
 
+  // A wave scores 64 queries as two 32-query halves (one per MFMA B operand), so each K
+  // operand read from LDS feeds two MFMAs. Lane (col, hf) keeps the top list of query
+  // col of half hf.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
-  const int il = tile * 128 + wave * 32 + col;
+  const int q_wave = tile * kIndexTileQ + wave * 64;
+  const int il = q_wave + hf * 32 + col;
   const bool qvalid = il < sq.nq;
   const int pos = sq.nk - sq.nq + il;
   const int c = floordiv(pos, kBlock);
   const int nb = (sq.nk + kBlock - 1) / kBlock;
 
-  int jend;
-  if (causal) {
-    const int il_last = min(tile * 128 + 127, sq.nq - 1);
-    jend = min(floordiv(sq.nk - sq.nq + il_last, kBlock), nb);
-  } else {
-    jend = nb;
-  }
+  const int jbeg = 0, jend = tile_blocks(sq, tile, causal);
 
-  bf16x8 bq[STEPS];
-  {
-    const uint16_t* qrow = q_idx + ((size_t)(sq.q0 + (qvalid ? il : 0)) * hkv + h) * DP;
+  bf16x8 bq[2][STEPS];
+#pragma unroll
+  for (int qh = 0; qh < 2; ++qh) {
+    const int iq = q_wave + qh * 32 + col;
+    const bool ok = iq < sq.nq;
+    const uint16_t* qrow = q_idx + ((size_t)(sq.q0 + (ok ? iq : 0)) * hkv + h) * DP;
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (qvalid) v = *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hf);
-      bq[st] = as_bf16x8(v);
+      if (ok) v = *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hf);
+      bq[qh][st] = as_bf16x8(v);
     }
   }
 
@@ -132,24 +148,26 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   // the chunk that belongs in the slot it writes, so a load covers whole rows. Rows past the
   // end of the sequence repeat its last key, which belongs to the same (last) block: the
   // repeats cannot change the block's maximum, so no masking is needed.
+  // Thread t covers rows t / CH + (256 / CH) p, p < PER_T, all at chunk slot t % CH; the
+  // swizzle term (row / 2) % CH is the same for all of them.
+  const unsigned row0 = (unsigned)tid / CH;
+  const unsigned cc0 = ((unsigned)tid % CH) ^ ((row0 >> 1) & (CH - 1));
+  const size_t krow = (size_t)hkv * DP;                 // elements between consecutive keys
+  const uint16_t* const kh = k_idx + (size_t)h * DP + cc0 * 8;
   auto dma_block = [&](int j) {
-    int t = tid;
-    asm volatile("" : "+v"(t));
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
-      const int i = p * 256 + t;
-      const int row = i / CH;
-      const int cc = (i % CH) ^ ((row >> 1) & (CH - 1));
-      const int u = min(j * kBlock + row, sq.nk - 1);
+      const unsigned row = row0 + (256 / CH) * p;
+      const unsigned u = min(j * kBlock + (int)row, sq.nk - 1);
       __builtin_amdgcn_global_load_lds(
-          k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + cc * 8,
+          kh + (size_t)(sq.k0 + u) * krow,
           (__attribute__((address_space(3))) void*)(&kl[j % NBUF][p * 256 + wave * 64]), 16, 0,
           0);
     }
   };
 
-  for (int j = 0; j < min(jend, NBUF - 1); ++j) dma_block(j);
-  for (int j = 0; j < jend; ++j) {
+  for (int j = jbeg; j < min(jend, jbeg + NBUF - 1); ++j) dma_block(j);
+  for (int j = jbeg; j < jend; ++j) {
     // block j has landed once at most the later blocks' loads are outstanding
     const int later = min(jend - 1 - j, NBUF - 2);
     if (later >= 2) wait_vm<2 * PER_T>();
@@ -159,24 +177,36 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     if (j + NBUF - 1 < jend) dma_block(j + NBUF - 1);
     const int buf = j % NBUF;
 
-    f32x16 acc[4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      acc[kt] = f32x16{};
-      const int row = kt * 32 + col;
+    for (int st = 0; st < STEPS; ++st) {
+      bf16x8 ka[4];
 #pragma unroll
-      for (int st = 0; st < STEPS; ++st) {
+      for (int kt = 0; kt < 4; ++kt) {
+        const int row = kt * 32 + col;
         const int cc = 2 * st + hf;
-        const bf16x8 a = as_bf16x8(kl[buf][row * CH + (cc ^ ((row >> 1) & (CH - 1)))]);
-        acc[kt] = mfma32(a, bq[st], acc[kt]);
+        ka[kt] = as_bf16x8(kl[buf][row * CH + (cc ^ ((row >> 1) & (CH - 1)))]);
       }
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          acc[qh][kt] = mfma32(ka[kt], bq[qh][st], st == 0 ? f32x16{} : acc[qh][kt]);
     }
-    float mx = kNegInf;
+    float mq[2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int qh = 0; qh < 2; ++qh) {
+      float m4[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kt][r]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      for (int kt = 0; kt < 4; ++kt) {
+        m4[kt] = acc[qh][kt][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m4[kt] = fmaxf(m4[kt], acc[qh][kt][r]);
+      }
+      mq[qh] = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      mq[qh] = fmaxf(mq[qh], shfl_xor_f(mq[qh], 32));   // both lanes of the column
+    }
+    const float mx = hf ? mq[1] : mq[0];
     // insertion only where the block beats the current last entry (wave-uniform skip)
     const bool ins = qvalid && (causal ? (j < c) : (j != c)) && mx > tl.sc[kMaxTopK - 1];
     if (__any(ins)) {
@@ -184,7 +214,7 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     }
   }
 
-  if (qvalid && hf == 0) {
+  if (qvalid) {
     const size_t o = ((size_t)(sq.q0 + il) * hkv + h) * topk;
     write_list(topk_idx + o, topk_score ? topk_score + o : nullptr, topk, pos >= 0, c, tl.sc,
                tl.id);
@@ -303,8 +333,8 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int hkv, int max_q,
     int topk, int n_chunks, int total_q, int total_k, int max_k) {
-  const int h = blockIdx.x;
-  const int s = blockIdx.y / max_q, il = blockIdx.y % max_q;
+  const int h = blockIdx.y;
+  const int s = blockIdx.x / max_q, il = blockIdx.x % max_q;
   const int lane = threadIdx.x;
   const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
   if (il >= sq.nq) return;
@@ -363,30 +393,45 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
 
 }  // namespace
 
+// Key chunks of the split kernel (short-query calls) per (sequence, query, group).
+static int64_t index_chunks(const msa_shape& s) {
+  const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
+  return std::max<int64_t>(1, (nb_max + kSplitIndexChunk - 1) / kSplitIndexChunk);
+}
+
 size_t index_workspace_bytes(const msa_shape& s) {
   if (s.max_q > kSplitIndexMaxQ) return 0;
-  const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
-  const int64_t n_chunks = (nb_max + kSplitIndexChunk - 1) / kSplitIndexChunk;
-  const int64_t n = (int64_t)s.batch * s.max_q * s.hkv * n_chunks * kMaxTopK;
+  const int64_t n = (int64_t)s.batch * s.max_q * s.hkv * index_chunks(s) * kMaxTopK;
   return (size_t)n * 8 + 256;
+}
+
+static hipError_t launch_index_merge(const msa_shape& s, const float* part_sc,
+                                     const int32_t* part_id, int n_chunks, const int32_t* cu_q,
+                                     const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
+                                     hipStream_t st) {
+  dim3 grid2(s.batch * s.max_q, s.hkv);
+  hipLaunchKernelGGL(index_merge_kernel, grid2, dim3(64), 0, st, part_sc, part_id, cu_q, cu_k,
+                     topk_idx, topk_score, s.hkv, s.max_q, s.topk, n_chunks, s.total_q,
+                     s.total_k, s.max_k);
+  return hipGetLastError();
 }
 
 hipError_t launch_index_tile(const msa_shape& s, const void* q_idx, const void* k_idx,
                              const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
                              float* topk_score, hipStream_t st) {
-  const int tiles = (s.max_q + 127) / 128;
+  const int tiles = (s.max_q + kIndexTileQ - 1) / kIndexTileQ;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, s.hkv, s.batch);
   if (s.dp == 64) {
     hipLaunchKernelGGL(index_tile_kernel<64>, grid, dim3(256), 0, st,
                        (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
-                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k,
-                       s.max_q, s.max_k);
+                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k, s.max_q,
+                       s.max_k);
   } else {
     hipLaunchKernelGGL(index_tile_kernel<32>, grid, dim3(256), 0, st,
                        (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
-                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k,
-                       s.max_q, s.max_k);
+                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k, s.max_q,
+                       s.max_k);
   }
   return hipGetLastError();
 }
@@ -416,11 +461,7 @@ hipError_t launch_index_split(const msa_shape& s, const void* q_idx, const void*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid2(s.hkv, s.batch * s.max_q);
-  hipLaunchKernelGGL(index_merge_kernel, grid2, dim3(64), 0, st, part_sc, part_id, cu_q, cu_k,
-                     topk_idx, topk_score, s.hkv, s.max_q, s.topk, n_chunks, s.total_q, s.total_k,
-                     s.max_k);
-  return hipGetLastError();
+  return launch_index_merge(s, part_sc, part_id, n_chunks, cu_q, cu_k, topk_idx, topk_score, st);
 }
 
 }  // namespace msa

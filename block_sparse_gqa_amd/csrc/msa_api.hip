@@ -251,9 +251,9 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
   if (s.total_k > 0 && !k_idx) return MSA_ERR_NULL;
   hipError_t e;
   if (s.max_q <= kSplitIndexMaxQ) {
-    const int64_t nb_max = cdiv(s.max_k, s.block);
-    if (cdiv(nb_max, kSplitIndexChunk) > 512) return MSA_ERR_SHAPE;
-    if ((int64_t)s.batch * s.max_q > 65535) return MSA_ERR_SHAPE;
+    // key chunks merged by one wave per (query, group): at most 512 per query
+    if (cdiv(cdiv(s.max_k, s.block), kSplitIndexChunk) > 512) return MSA_ERR_SHAPE;
+    if ((int64_t)s.batch * s.max_q > 65535) return MSA_ERR_SHAPE;      // grid z of the split kernel
     const size_t need = index_workspace_bytes(s);
     if (!workspace || ws_bytes < need) return MSA_ERR_WORKSPACE;
     e = launch_index_split(s, q_idx, k_idx, cu_q, cu_k, topk_idx, topk_score, workspace, stream);

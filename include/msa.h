@@ -119,8 +119,9 @@ msa_status msa_workspace_size(const msa_shape* shape, msa_mode mode, size_t* byt
 msa_status msa_workspace_layout_of(const msa_shape* shape, msa_mode mode,
                                    msa_workspace_layout* out);
 
-/* Bytes of workspace msa_index_topk needs (non-zero only for short-query calls, where the key
- * range is split across workgroups and the partial top-K lists are merged). */
+/* Bytes of workspace msa_index_topk needs: non-zero only for short-query calls (max_q <= 16),
+ * where the key range of every query is scored in chunks by separate workgroups and the
+ * chunks' partial top-K lists (8 bytes per entry, 16 entries per chunk) are merged. */
 msa_status msa_index_workspace_size(const msa_shape* shape, size_t* bytes);
 
 /* The schedule msa_sparse_attn_fwd runs for `mode` (AUTO resolved). Per-Q-tile lists always
@@ -153,7 +154,8 @@ const char* msa_last_error(void);
  * scores (+inf for the local block, -inf for unused slots).
  * In: q_idx, k_idx bf16 (layouts above), cu_q, cu_k. Out: topk_idx [total_q, hkv, topk]
  * int32, topk_score [total_q, hkv, topk] fp32. workspace: msa_index_workspace_size() bytes
- * (may be NULL when that size is 0). Requires list_q == 1, dp in {32, 64}. */
+ * (may be NULL when that size is 0), else MSA_ERR_WORKSPACE. Requires list_q == 1,
+ * dp in {32, 64}; short-query calls (max_q <= 16) take max_k <= 2^21 keys. */
 msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx,
                           const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
                           float* topk_score, void* workspace, size_t ws_bytes,
