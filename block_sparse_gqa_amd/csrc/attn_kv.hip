@@ -34,6 +34,7 @@ struct KvArgs {
   const int32_t* entry_q;
   const int32_t* entry_bucket;
   float* part_lse;
+  float* part_l;
   uint16_t* part_o;
   uint16_t* dummy;
   int total_q, total_k, max_q, max_k;
@@ -67,23 +68,30 @@ __device__ __forceinline__ void v_frags(const KVLds& L, bf16x8 a[4], int s, int 
   for (int dt = 0; dt < 4; ++dt) a[dt] = as_bf16x8(L.vt[(dt * 32 + rp) * 16 + cc]);
 }
 
-// exp2 of the 8 scores of key-step s, packed to bf16 into pk; returns their sum.
+// exp2 of the 8 scores of key-step s, packed to bf16 into pk; their sum is added to l. The
+// sum is taken over the bf16-rounded weights (one bf16 dot product per pair), the exact
+// weights the PV product uses.
 __device__ __forceinline__ float exp_step(const f32x16 sc[4], int s, float sl2, float c,
-                                          u32x4& pk) {
+                                          u32x4& pk, float l) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const int kt = s >> 1, base = 8 * (s & 1);
-  float l = 0.f;
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float x0 = __builtin_amdgcn_exp2f(fmaf(sc[kt][base + 2 * i], sl2, -c));
     const float x1 = __builtin_amdgcn_exp2f(fmaf(sc[kt][base + 2 * i + 1], sl2, -c));
-    l += x0 + x1;
-    pk[i] = pack_bf16x2(x0, x1);
+    // (the packed pair is taken as a value: a bit_cast of the vector element reference pk[i]
+    // has been compiled to read element 0 for every i)
+    const uint32_t pw = pack_bf16x2(x0, x1);
+    pk[i] = pw;
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw), ones, l, false);
   }
   return l;
 }
 
 // Output staging: the wave's 32 rows x 256 B, 16-byte chunk c of row R at R*16 + (c ^ (R%16)).
 // Lane (col, hf) deposits dims 32*dt + 16*hf .. +15 of row col (chunks 4dt+2hf, +1).
+template <bool FP8>
 __device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, float mul,
                                         int col, int hf) {
   // opaque copies: the addresses are recomputed here instead of being held (or spilled)
@@ -95,8 +103,12 @@ __device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, flo
   for (int h2 = 0; h2 < 2; ++h2) {
     u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = pack_bf16x2(o[8 * h2 + 2 * i] * mul, o[8 * h2 + 2 * i + 1] * mul);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (FP8)   // the V descale; bf16 stores the accumulator as it is
+        w[i] = pack_bf16x2(o[8 * h2 + 2 * i] * mul, o[8 * h2 + 2 * i + 1] * mul);
+      else
+        w[i] = pack_bf16x2(o[8 * h2 + 2 * i], o[8 * h2 + 2 * i + 1]);
+    }
     row[(4 * dt + h2) ^ x] = w;
   }
 }
@@ -208,6 +220,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
   // Sinks for the stores of padding rows (contents never read).
   uint16_t* const o_sink = a.dummy + lane * 8;
   float* const lse_sink = reinterpret_cast<float*>(a.dummy + 64 * 8) + lane;
+  float* const l_sink = reinterpret_cast<float*>(a.dummy + 128 * 8) + lane;
 
   // Phases (sequence, group, query range) in entry order; this workgroup's share of each.
   const int n_phase = a.n_buckets / a.nb_max;
@@ -252,12 +265,13 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
     f32x16 oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
-    float o_mul = 0.f, o_lse = 0.f;
+    float o_l = 0.f, o_lse = 0.f;
     // stores of the previous tile: rows 4i + lane/16 of the wave at o_base + 4i rows, valid
     // while 4i < o_nv (none yet)
     uint16_t* o_base = o_sink;
     int o_nv = 0;
     float* lse_ptr = lse_sink;
+    float* l_ptr = l_sink;
 
     for (int tile0 = cur; tile0 < run_end; tile0 += MQ) {
       const int e2 = e1 + MQ;
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
         for (int kt = 0; kt < 4; ++kt)
           sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
         if (st < 4) {
-          stage_o(obuf, oacc[st], st, o_mul, col, hf);
+          stage_o<FP8>(obuf, oacc[st], st, dv, col, hf);
         } else {
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2) {
@@ -289,7 +303,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
             __builtin_nontemporal_store(
                 w, reinterpret_cast<u32x4*>(4 * i < o_nv ? o_base + i * 4 * kD : o_sink));
           }
-          if (st == 7) *lse_ptr = o_lse;
+          if (st == 7) {
+            *lse_ptr = o_lse;
+            *l_ptr = o_l;
+          }
         }
         MSA_INTERLEAVE(1, 6);
       }
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
       const float c = any ? m * sl2 : 0.f;
       // ---- phase B: PV(j) | exp of the next key-step
       u32x4 pk[8];
-      float l = exp_step(sc, 0, sl2, c, pk[0]);
+      float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         // the last step fetches the first K operands of the next tile (discarded after the
@@ -325,12 +342,12 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
           oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
-        if (st + 1 < 8) l += exp_step(sc, st + 1, sl2, c, pk[st + 1]);
+        if (st + 1 < 8) l = exp_step(sc, st + 1, sl2, c, pk[st + 1], l);
         MSA_INTERLEAVE(2, 7);
       }
       l += shfl_xor_f(l, 32);
       // the output of tile j is stored during the next tile's phase A
-      o_mul = any ? dv / l : 0.f;
+      o_l = any ? l : 0.f;
       o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
       {
         int ln = lane;
@@ -339,6 +356,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
         o_nv = (run_end - tile0) * G - wave * 32 - (ln >> 4);
       }
       lse_ptr = valid ? a.part_lse + (size_t)e0 * G + g : lse_sink;
+      l_ptr = valid ? a.part_l + (size_t)e0 * G + g : l_sink;
       e0 = e1;
       e1 = e2;
       t0v = t1v;
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
     // output of the run's last tile (after the last, unused, Q load into the buffer)
     wait_vm0();
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) stage_o(obuf, oacc[dt], dt, o_mul, col, hf);
+    for (int dt = 0; dt < 4; ++dt) stage_o<FP8>(obuf, oacc[dt], dt, dv, col, hf);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
@@ -355,6 +373,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
           w, reinterpret_cast<u32x4*>(4 * i < o_nv ? o_base + i * 4 * kD : o_sink));
     }
     *lse_ptr = o_lse;
+    *l_ptr = o_l;
     cur = run_end;
   }
   }
@@ -392,6 +411,7 @@ hipError_t launch_attn_kv(const msa_shape& s, const Geometry& g, const Layout& L
   a.entry_q = reinterpret_cast<const int32_t*>(ws + L.entry_q);
   a.entry_bucket = reinterpret_cast<const int32_t*>(ws + L.entry_bucket);
   a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  a.part_l = reinterpret_cast<float*>(ws + L.part_l);
   a.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
   a.dummy = reinterpret_cast<uint16_t*>(ws + L.dummy);
   a.total_q = s.total_q;

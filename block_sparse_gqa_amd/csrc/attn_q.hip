@@ -31,6 +31,7 @@ struct QArgs {
   int32_t* counters;
   int32_t* cmap;
   float* part_lse;
+  float* part_l;
   uint16_t* part_o;
   int total_q, total_k, max_q, max_k;
   int batch, hq, hkv, topk, list_q, tiles_max, causal, splits;
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
     store_o_row(a.part_o + (pe * G + g) * kD, oacc, inv, hf);
     if (hf == 0) {
       a.part_lse[pe * G + g] = lse_v;
+      a.part_l[pe * G + g] = 1.f;           // the partial output is already normalised
       if (g == 0) a.cmap[pe] = (int)pe;
     }
   }
@@ -286,6 +288,7 @@ hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
   a.counters = g.splits > 1 ? reinterpret_cast<int32_t*>(ws + L.counters) : nullptr;
   a.cmap = g.splits > 1 ? reinterpret_cast<int32_t*>(ws + L.cmap) : nullptr;
   a.part_lse = g.splits > 1 ? reinterpret_cast<float*>(ws + L.part_lse) : nullptr;
+  a.part_l = g.splits > 1 ? reinterpret_cast<float*>(ws + L.part_l) : nullptr;
   a.part_o = g.splits > 1 ? reinterpret_cast<uint16_t*>(ws + L.part_o) : nullptr;
   a.total_q = s.total_q;
   a.total_k = s.total_k;

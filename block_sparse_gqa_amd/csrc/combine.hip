@@ -5,9 +5,10 @@
 // Blackwell" (section 2): the combine kernel is bandwidth-bound and gathers the partials
 // through the (query, kv head, slot) -> location map.
 //
-// A thread owns 8 output dims (16 bytes) of one (query, head): it reads the slot LSEs, then
-// issues all of its slot loads before accumulating, so each wave keeps 16 independent
-// 1 KiB gathers in flight.
+// A thread owns 8 output dims (16 bytes) of one (query, head): it reads the slot LSEs and
+// weight sums, then issues all of its slot loads before accumulating, so each wave keeps 16
+// independent 1 KiB gathers in flight. A partial is stored unnormalised (its output times its
+// weight sum l), so slot k enters with coefficient exp(lse_k - m) / l_k.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -18,6 +19,7 @@ template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ cmap,
                                                       const int32_t* __restrict__ counters,
                                                       const float* __restrict__ part_lse,
+                                                      const float* __restrict__ part_l,
                                                       const uint16_t* __restrict__ part_o,
                                                       uint16_t* __restrict__ o,
                                                       float* __restrict__ lse, int total_q,
@@ -42,17 +44,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     if (k < slots) e = cm[k];
     es[k] = (e >= n_ent) ? -1 : e;
   }
-  float ls[kMaxTopK];
+  float ls[kMaxTopK], lw[kMaxTopK];
   u32x4 vals[kMaxTopK];
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
     u32x4 v = {0u, 0u, 0u, 0u};
-    float l = -__builtin_inff();
+    float l = -__builtin_inff(), w = 1.f;
     if (es[k] >= 0) {
       l = part_lse[(size_t)es[k] * G + g];
+      w = part_l[(size_t)es[k] * G + g];
       v = *reinterpret_cast<const u32x4*>(part_o + ((size_t)es[k] * G + g) * kD + 8 * c);
     }
     ls[k] = l;
+    lw[k] = w;
     vals[k] = v;
   }
   float m = -__builtin_inff();
@@ -72,10 +76,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   for (int k = 0; k < kMaxTopK; ++k) {
     const float w = __builtin_amdgcn_exp2f((ls[k] - m) * 1.4426950408889634f);  // 0 for -inf
     wsum += w;
+    const float cw = w > 0.f ? w / lw[k] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(w, bf16_bits_to_f32(vals[k][i] & 0xFFFFu), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(w, bf16_bits_to_f32(vals[k][i] >> 16), acc[2 * i + 1]);
+      acc[2 * i] = fmaf(cw, bf16_bits_to_f32(vals[k][i] & 0xFFFFu), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(cw, bf16_bits_to_f32(vals[k][i] >> 16), acc[2 * i + 1]);
     }
   }
   const float inv = 1.f / wsum;
@@ -98,14 +103,15 @@ hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L
   const int32_t* cmap = reinterpret_cast<const int32_t*>(ws + L.cmap);
   const int32_t* cnt = reinterpret_cast<const int32_t*>(ws + L.counters);
   const float* pl = reinterpret_cast<const float*>(ws + L.part_lse);
+  const float* pw = reinterpret_cast<const float*>(ws + L.part_l);
   const uint16_t* po = reinterpret_cast<const uint16_t*>(ws + L.part_o);
   uint16_t* oo = reinterpret_cast<uint16_t*>(o);
   switch (g.group) {
-    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
-    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
-    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
-    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
-    default: hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, st, cmap, cnt, pl, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, st, cmap, cnt, pl, pw, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(256), 0, st, cmap, cnt, pl, pw, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, st, cmap, cnt, pl, pw, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, st, cmap, cnt, pl, pw, po, oo, lse, s.total_q, s.hkv, L.slots); break;
+    default: hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, st, cmap, cnt, pl, pw, po, oo, lse, s.total_q, s.hkv, L.slots); break;
   }
   return hipGetLastError();
 }

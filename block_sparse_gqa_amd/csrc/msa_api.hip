@@ -131,6 +131,7 @@ Layout layout(const msa_shape& s, msa_mode mode) {
     L.cmap = take(g.splits > 1 ? (size_t)s.total_q * s.hkv * g.splits * 4 : 0);
   }
   L.part_lse = take((size_t)g.e_max * g.group * 4);
+  L.part_l = take((size_t)g.e_max * g.group * 4);
   L.part_o = take((size_t)g.e_max * g.group * s.d * 2);
   L.dummy = take(mode == MSA_KV_OUTER ? 65536 : 0);
   L.total = off;
@@ -209,6 +210,7 @@ msa_status msa_workspace_layout_of(const msa_shape* shape, msa_mode mode,
   out->entry_bucket = L.entry_bucket;
   out->cmap = L.cmap;
   out->part_lse = L.part_lse;
+  out->part_l = L.part_l;
   out->part_o = L.part_o;
   out->total = L.total;
   out->slots = L.slots;

@@ -52,6 +52,7 @@ struct Layout {
   size_t entry_bucket;  // int32  [e_max]
   size_t cmap;          // int32  [total_q * hkv * slots]
   size_t part_lse;      // float  [e_max * group]
+  size_t part_l;        // float  [e_max * group]: weight sums (partials are unnormalised)
   size_t part_o;        // bf16   [e_max * group * d]
   size_t dummy;         // 64 KiB sink for the stores of padding rows (KV-outer)
   size_t total;

@@ -97,7 +97,12 @@ typedef struct {
   size_t entry_bucket; /* int32 [E]: bucket ((s * hkv + g) * n_ranges + r) * nb_max + b */
   size_t cmap;         /* int32 [total_q, hkv, slots]: partial index of each slot, -1 = none */
   size_t part_lse;     /* float [E, hq/hkv]: log-sum-exp of each partial */
-  size_t part_o;       /* bf16 [E, hq/hkv, d]: normalised partial output */
+  size_t part_l;       /* float [E, hq/hkv]: sum of each partial's softmax weights (relative
+                          to its maximum); 1 where the partial output is already normalised */
+  size_t part_o;       /* bf16 [E, hq/hkv, d]: partial output before normalisation, i.e. the
+                          partial's attention output times part_l ("Kernel optimization
+                          ...", section 2: unnormalised accumulators, normalised in the
+                          combine) */
   size_t total;        /* bytes needed */
   int32_t slots;       /* slots per (query, group) in cmap */
   int32_t n_words;     /* bitmap words (0 for Q-outer) */

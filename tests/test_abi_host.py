@@ -176,9 +176,10 @@ def test_kv_outer_workspace_layout_m3():
     e_max = 32768 * 4 * 16
     G = 16
     regions = [lay.counters, lay.masks, lay.offsets, lay.scan_sums, lay.entry_q,
-               lay.entry_bucket, lay.cmap, lay.part_lse, lay.part_o]
+               lay.entry_bucket, lay.cmap, lay.part_lse, lay.part_l, lay.part_o]
     assert regions == sorted(regions) and all(r % 256 == 0 for r in regions)
-    assert lay.part_o - lay.part_lse >= e_max * G * 4
+    assert lay.part_l - lay.part_lse >= e_max * G * 4
+    assert lay.part_o - lay.part_l >= e_max * G * 4
     assert lay.total - lay.part_o >= e_max * G * 128 * 2
     assert lay.slots == 16 and lay.nb_max == 256
     assert lay.n_words == lay.words_per_bucket * lay.n_ranges * 4 * lay.nb_max

@@ -154,8 +154,11 @@ def test_partials_match_oracle_partials():
     cmap = wsn[L.cmap:L.cmap + case.total_q * case.cfg.hkv * case.cfg.topk * 4].view(torch.int32)
     cmap = cmap.numpy().reshape(case.total_q, case.cfg.hkv, case.cfg.topk)
     plse = wsn[L.part_lse:L.part_lse + n_ent * G * 4].view(torch.float32).numpy().reshape(n_ent, G)
+    pl = wsn[L.part_l:L.part_l + n_ent * G * 4].view(torch.float32).numpy().reshape(n_ent, G)
     po = wsn[L.part_o:L.part_o + n_ent * G * 256].view(torch.bfloat16).float().numpy()
-    po = po.reshape(n_ent, G, 128)
+    # stored unnormalised: output times the weight sum (a block always has a visible key here)
+    assert np.all(pl >= 1.0)
+    po = po.reshape(n_ent, G, 128) / pl[:, :, None]
     entry_q = wsn[L.entry_q:L.entry_q + n_ent * 4].view(torch.int32).numpy()
     # every valid slot maps to a distinct entry that records its query
     valid = cmap >= 0
