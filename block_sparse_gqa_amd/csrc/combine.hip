@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   for (int k = 0; k < kMaxTopK; ++k) {
     const float w = __builtin_amdgcn_exp2f((ls[k] - m) * 1.4426950408889634f);  // 0 for -inf
     wsum += w;
-    const float cw = w > 0.f ? w / lw[k] : 0.f;
+    const float cw = w > 0.f ? w * __builtin_amdgcn_rcpf(lw[k]) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] = fmaf(cw, bf16_bits_to_f32(vals[k][i] & 0xFFFFu), acc[2 * i]);

@@ -105,6 +105,13 @@ LAYER_CASES = [
                             lowrank=True), 0),
     ("multi_range", mi.custom(name="mr", n_q=(4500, 700), n_k=(4500, 5000), hq=4, hkv=2, topk=5,
                               dp=32, lowrank=True), 0),
+    # group sizes whose Q rows of one 1 KiB load span several queries (bf16: G < 4, fp8: G < 8)
+    ("group2", mi.custom(name="g2", n_q=(700, 130), n_k=(700, 1000), hq=4, hkv=2, topk=5,
+                         dp=32), 1),
+    ("group8", mi.custom(name="g8", n_q=(900,), hq=16, hkv=2, topk=6, dp=64, lowrank=True), 2),
+    ("fp8_group4", mi.custom(name="f4", n_q=(800,), hq=8, hkv=2, topk=5, dp=32, dtype="fp8"), 3),
+    ("fp8_group1_ragged", mi.custom(name="f1", n_q=(600, 300), n_k=(600, 900), hq=2, hkv=2,
+                                    topk=4, dp=32, dtype="fp8"), 4),
 ]
 
 
