@@ -59,6 +59,45 @@ __device__ __forceinline__ void xcd_tile_head(int id, int tiles, int heads, int*
   *tile = pair % tiles;
 }
 
+// The blocks a workgroup visits, in list order: the slots [slot0, slot1) of `list` whose block
+// is valid (0 <= b < nb), visible to some row of the workgroup (causal: 128 b <= pos_max) and
+// not listed in an earlier slot. Built by one wave, one list entry per lane (topk <= 64).
+__device__ __forceinline__ void visit_list(const int32_t* list, int topk, int slot0, int slot1,
+                                           int nb, bool causal, int pos_max, int* vis,
+                                           int* n_vis) {
+  const int lane = threadIdx.x & 63;
+  const int b = lane < topk ? list[lane] : -1;
+  bool use = lane >= slot0 && lane < slot1 && b >= 0 && b < nb &&
+             !(causal && b * kBlock > pos_max);
+#pragma unroll
+  for (int p = 0; p < kMaxTopK; ++p) {
+    const int bp = __shfl(b, p, 64);
+    if (p < lane && bp == b) use = false;
+  }
+  const unsigned long long m = __ballot(use);
+  if (use) vis[__popcll(m & ((1ull << lane) - 1))] = b;
+  if (lane == 0) *n_vis = __popcll(m);
+}
+
+// The same list kept in registers: lane i (< count) of the calling wave receives the i-th
+// visited block. Every wave builds its own copy.
+__device__ __forceinline__ int visit_list_lanes(const int32_t* list, int topk, int nb,
+                                                bool causal, int pos_max, int* count) {
+  const int lane = threadIdx.x & 63;
+  const int b = lane < topk ? list[lane] : -1;
+  bool use = b >= 0 && b < nb && !(causal && b * kBlock > pos_max);
+#pragma unroll
+  for (int p = 0; p < kMaxTopK; ++p) {
+    const int bp = __shfl(b, p, 64);
+    if (p < lane && bp == b) use = false;
+  }
+  const unsigned long long m = __ballot(use);
+  *count = __popcll(m);
+  // forward permute: a used entry goes to lane (its rank); the others to lanes 32..63
+  const int dst = use ? __popcll(m & ((1ull << lane) - 1)) : (32 | (lane & 31));
+  return __builtin_amdgcn_ds_permute(dst * 4, b);
+}
+
 template <bool FP8, int G>
 __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   constexpr int EB = FP8 ? 1 : 2;
@@ -133,18 +172,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   // The blocks this workgroup visits (uniform): valid, visible to some row, first occurrence.
   __shared__ int vis[kMaxTopK];
   __shared__ int n_vis;
-  if (tid == 0) {
-    int n = 0;
-    for (int slot = slot0; slot < slot1; ++slot) {
-      const int b = list[slot];
-      bool use = b >= 0 && b < nb;
-      if (use && a.causal && b * kBlock > pos_max) use = false;
-      for (int p = 0; p < slot && use; ++p)
-        if (list[p] == b) use = false;
-      if (use) vis[n++] = b;
-    }
-    n_vis = n;
-  }
+  if (tid < 64) visit_list(list, a.topk, slot0, slot1, nb, a.causal, pos_max, vis, &n_vis);
   __syncthreads();
   const int nv = n_vis;
   const size_t kv_head = (size_t)sq.k0 * a.hkv + h;     // row of key 0 of the sequence, head h
@@ -255,6 +283,163 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   }
 }
 
+// Per-tile lists, bf16: the 128 rows of one (Q tile, head) on 8 waves. Wave w takes rows
+// 32*(w%4) .. +31 and keys 64*(w/4) .. +63 of every listed block, with its own running max,
+// sum and output; the two key halves of a row are merged once at the end. K and V are
+// double-buffered in LDS (128 KiB): at the top of step j the workgroup waits for block j,
+// crosses its one barrier of the step, and issues block j+1 by direct-to-LDS loads, which then
+// have a whole step to land. The two waves sharing a SIMD overlap one's softmax with the
+// other's MFMAs. The running max is raised only when a block's max exceeds it by more than
+// 2^8 in probability (the output is rescaled then); otherwise the probabilities are taken
+// against the old max, which changes no result beyond rounding.
+struct KVLds2 {
+  u32x4 k[2][128 * 16];
+  u32x4 v[2][128 * 16];
+};
+
+__global__ __launch_bounds__(512, 1) void attn_qt_kernel(QArgs a) {
+  __shared__ KVLds2 L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int rg = wave & 3, kh = wave >> 2, kt0 = 2 * kh;
+  const int r = rg * 32 + col;
+
+  int tile, hh;
+  xcd_tile_head(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x, gridDim.y, &tile, &hh);
+  const int h = hh / (a.hq / a.hkv);
+  const int s = blockIdx.z;
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  if (tile * a.list_q >= sq.nq) return;
+  const int il = tile * a.list_q + r;
+  const bool valid = r < a.list_q && il < sq.nq;
+  const int t = sq.q0 + (valid ? il : 0);
+  const int32_t* list = a.lists + (((size_t)s * a.tiles_max + tile) * a.hkv + h) * a.topk;
+  const int pos = sq.nk - sq.nq + (t - sq.q0);
+  const int nb = (sq.nk + kBlock - 1) / kBlock;
+  const int pos_max = sq.nk - sq.nq + min(tile * a.list_q + a.list_q - 1, sq.nq - 1);
+
+  int nv;
+  const int vis_lane = visit_list_lanes(list, a.topk, nb, a.causal, pos_max, &nv);
+  auto vis = [&](int j) { return __builtin_amdgcn_readlane(vis_lane, j); };
+
+  const float sl2 = a.scale_log2;
+  bf16x8 bq[8];
+  load_q_operand<false>(bq, reinterpret_cast<const char*>(a.q) + ((size_t)t * a.hq + hh) * kD * 2, hf);
+
+  // K/V transfers: waves 0-3 load K rows, waves 4-7 V rows (dma_rows layouts); thread u of
+  // its half issues 8 loads, load p reading row 16p + u/16. A full block's addresses are the
+  // block base (uniform), p times 16 rows (uniform) and one of two per-thread offsets.
+  const char* kvb = reinterpret_cast<const char*>(tid < 256 ? a.k : a.v);
+  const uint32_t row_bytes = (uint32_t)a.hkv * kD * 2;
+  const size_t head_off = ((size_t)sq.k0 * a.hkv + h) * kD * 2;
+  const int u = tid & 255, row0 = u >> 4, slot = u & 15;
+  const int half_wave = __builtin_amdgcn_readfirstlane((tid & 255) >> 6);
+  const bool is_v = tid >= 256;
+  uint32_t col_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int f = is_v ? swz_v(row0) : ((row0 & 3) | (par << 2) | (((row0 >> 2) & 1) << 3));
+    col_off[par] = (uint32_t)row0 * row_bytes + (uint32_t)((slot ^ f) * 16);
+  }
+  auto dma = [&](int j, bool v_part) {
+    const int u0 = vis(j) * kBlock;
+    const int nk_rel = sq.nk - u0;
+    u32x4* dst = v_part ? L.v[j & 1] : L.k[j & 1];
+    if (nk_rel >= kBlock) {
+      const char* src = kvb + head_off + (size_t)u0 * row_bytes;
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        __builtin_amdgcn_global_load_lds(
+            src + p * 16 * row_bytes + col_off[p & 1],
+            (__attribute__((address_space(3))) void*)(dst + p * 256 + half_wave * 64), 16, 0, 0);
+    } else {
+      const uint16_t* base = reinterpret_cast<const uint16_t*>(kvb + head_off + (size_t)u0 * row_bytes);
+      if (v_part) dma_rows_t<true>(dst, base, row_bytes / 2, nk_rel, u);
+      else dma_rows_t<false>(dst, base, row_bytes / 2, nk_rel, u);
+    }
+  };
+  auto dma_k = [&](int j) { if (!is_v) dma(j, false); };
+  auto dma_v = [&](int j) { if (is_v) dma(j, true); };
+
+  const float ninf = -__builtin_inff();
+  // c_run: reference max in scaled (log2) units; l_run: this lane's share of the row sum
+  float c_run = ninf, l_run = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+
+  if (nv > 0) {
+    dma_k(0);
+    dma_v(0);
+  }
+  for (int j = 0; j < nv; ++j) {
+    wait_vm<0>();                            // this thread's K(j) and V(j) landed
+    __syncthreads();                         // ... everyone's; step j-1 done by every wave
+    const int u0 = vis(j) * kBlock;
+    if (j + 1 < nv) {
+      dma_k(j + 1);
+      dma_v(j + 1);
+    }
+    f32x16 sc[2];
+    qk_half(L.k[j & 1], bq, sc, kt0, col, hf);
+    int kmax = min(127, sq.nk - u0 - 1);
+    if (a.causal) kmax = min(kmax, pos - u0);
+    const float mb = mask_max_half(sc, kt0, kmax, __any(kmax < kt0 * 32 + 63), hf);
+    // the reference max is raised only when the block's max exceeds it by more than 2^8
+    const float mbs = mb * sl2;                        // -inf stays -inf (sl2 > 0)
+    const bool grow = mbs > c_run + 8.f;
+    if (__any(grow)) {
+      const float c_new = grow ? mbs : c_run;
+      const float alpha = grow ? (c_run > ninf ? __builtin_amdgcn_exp2f(c_run - c_new) : 0.f) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      c_run = c_new;
+    }
+    u32x4 pk[2][2];
+    l_run += exp_pack_half(sc, sl2, c_run > ninf ? c_run : 0.f, pk);
+    pv_half_tr(L.v[j & 1], pk, oacc, kt0, lane);
+  }
+
+  l_run += shfl_xor_f(l_run, 32);            // the row's sum over the wave's keys
+
+  // merge the key halves: waves 4-7 hand their (max, sum, output) to waves 0-3 through LDS
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(&L);             // [4 rg][4 dt][4][64 lanes][4]
+  float* xc = xo + 4 * 4 * 4 * 64 * 4;                  // [4 rg][64 lanes] max, then sum
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 w = {oacc[dt][4 * q], oacc[dt][4 * q + 1], oacc[dt][4 * q + 2], oacc[dt][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(xo + (((rg * 4 + dt) * 4 + q) * 64 + lane) * 4) = w;
+      }
+    xc[rg * 64 + lane] = c_run;
+    xc[256 + rg * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 1 || !valid) return;
+  const float c1 = xc[rg * 64 + lane], l1 = xc[256 + rg * 64 + lane];
+  const float cm = fmaxf(c_run, c1);
+  const float w0 = c_run > ninf ? __builtin_amdgcn_exp2f(c_run - cm) : 0.f;
+  const float w1 = c1 > ninf ? __builtin_amdgcn_exp2f(c1 - cm) : 0.f;
+  const float l = w0 * l_run + w1 * l1;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(xo + (((rg * 4 + dt) * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[dt][4 * q + i] = w0 * oacc[dt][4 * q + i] + w1 * x[i];
+    }
+  const bool any = l > 0.f;
+  store_o_row(a.o + ((size_t)t * a.hq + hh) * kD, oacc, any ? 1.f / l : 0.f, hf);
+  if (hf == 0 && a.lse) a.lse[(size_t)t * a.hq + hh] = any ? (cm + log2f(l)) * 0.69314718055994531f : ninf;
+}
+
 template <bool FP8>
 hipError_t launch_q_g(const QArgs& a, int group, dim3 grid, hipStream_t st) {
   dim3 blk(256);
@@ -306,6 +491,10 @@ hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
   if (s.list_q > 1) {
     if (g.tiles_max == 0) return hipSuccess;
     grid = dim3((unsigned)g.tiles_max, s.hq, s.batch);
+    if (s.dtype == MSA_BF16) {
+      hipLaunchKernelGGL(attn_qt_kernel, grid, dim3(512), 0, st, a);
+      return hipGetLastError();
+    }
   } else {
     if (s.total_q == 0) return hipSuccess;
     grid = dim3((unsigned)s.total_q, s.hkv, g.splits);

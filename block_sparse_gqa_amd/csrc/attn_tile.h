@@ -205,12 +205,11 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // One 128-row x 256-byte block (rows at or past nk_rel repeat row nk_rel - 1; the caller masks
-// or zero-weights them) into `dst`, 256 threads, 8 loads each: slot i of the block holds chunk
+// or zero-weights them) into `dst` by 256 threads t = 0..255, 8 loads each: slot i of the block holds chunk
 // (i % 16) ^ f(i / 16) of row i / 16, lane l fetching exactly the chunk its slot needs.
 template <bool V>
-__device__ __forceinline__ void dma_rows(u32x4* dst, const uint16_t* base, uint32_t row_stride,
-                                         int nk_rel) {
-  int t = threadIdx.x;
+__device__ __forceinline__ void dma_rows_t(u32x4* dst, const uint16_t* base, uint32_t row_stride,
+                                           int nk_rel, int t) {
   asm volatile("" : "+v"(t));
   const int wave = t >> 6, row0 = t >> 4, slot = t & 15;
 #pragma unroll
@@ -223,6 +222,13 @@ __device__ __forceinline__ void dma_rows(u32x4* dst, const uint16_t* base, uint3
         base + r * row_stride + (uint32_t)((slot ^ f) * 8),
         (__attribute__((address_space(3))) void*)(dst + p * 256 + wave * 64), 16, 0, 0);
   }
+}
+
+// The same with the workgroup's own 256 threads (thread t = threadIdx.x).
+template <bool V>
+__device__ __forceinline__ void dma_rows(u32x4* dst, const uint16_t* base, uint32_t row_stride,
+                                         int nk_rel) {
+  dma_rows_t<V>(dst, base, row_stride, nk_rel, (int)threadIdx.x);
 }
 
 // O^T (+)= V^T P^T with V row-major in LDS. The LDS transpose load gives lane j of each
@@ -265,6 +271,70 @@ __device__ __forceinline__ void pv_block_tr(const KVLds& L, const u32x4 p[4][2],
   }
 }
 
+// ---- half blocks: a wave covering keys [32*kt0, 32*kt0 + 64) of a staged block
+
+// S^T for the wave's 32 rows over keys 32*kt0 .. +63 of the block in `kb` (K layout above):
+// 16 MFMAs, s[i] holding keys 32*(kt0 + i) + 16*(l/32) + r. The K operands are read two
+// steps ahead of their MFMAs (a ring of three steps), so a caller can spread other work
+// between the MFMAs without waiting on LDS.
+__device__ __forceinline__ void qk_half(const u32x4* kb, const bf16x8 bq[8], f32x16 s[2],
+                                        int kt0, int col, int hf) {
+  const int rp = rowperm(col);
+  const int sw = swz(rp);                 // swz(32*kt + rp) == swz(rp)
+  const u32x4* r0 = kb + (kt0 * 32 + rp) * 16;
+  bf16x8 a[3][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int cc = (2 * st + hf) ^ sw;
+    a[st][0] = as_bf16x8(r0[cc]);
+    a[st][1] = as_bf16x8(r0[32 * 16 + cc]);
+  }
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    if (st + 2 < 8) {
+      const int cc = (2 * (st + 2) + hf) ^ sw;
+      a[(st + 2) % 3][0] = as_bf16x8(r0[cc]);
+      a[(st + 2) % 3][1] = as_bf16x8(r0[32 * 16 + cc]);
+    }
+    s[0] = mfma32(a[st % 3][0], bq[st], st == 0 ? f32x16{} : s[0]);
+    s[1] = mfma32(a[st % 3][1], bq[st], st == 0 ? f32x16{} : s[1]);
+  }
+}
+
+// O^T += V^T P^T over keys 32*kt0 .. +63 of the row-major V block in `vb` (layout of
+// dma_rows<true>): 16 MFMAs; p[i][ks] holds keys 32*(kt0 + i) + 16*(l/32) + 8*ks + 2j, +1.
+__device__ __forceinline__ void pv_half_tr(const u32x4* vb, const u32x4 p[2][2], f32x16 o[4],
+                                           int kt0, int lane) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  asm volatile("" : "+v"(lane));
+  const int s = lane & 15, grp = (lane >> 4) & 1, hf = lane >> 5;
+  const int dsel = s & 3, k_lane = s >> 2;
+  const int d_lane = ((dsel & 1) << 4) + ((dsel >> 1) << 2) + 8 * grp;
+  const unsigned short* vrow = reinterpret_cast<const unsigned short*>(vb) + kt0 * 32 * 128;
+  const unsigned short* base[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    base[dt] = vrow + (16 * hf + k_lane) * 128 + (4 * (dt ^ k_lane) + (d_lane >> 3)) * 8 +
+               (d_lane & 7);
+#pragma unroll
+  for (int step = 0; step < 4; ++step) {
+    const int kt = step >> 1, ks = step & 1;
+    bf16x8 a[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      s4 r[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(base[dt] + (32 * kt + 8 * ks + 4 * h2) * 128));
+      a[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    const bf16x8 bp = as_bf16x8(p[kt][ks]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(a[dt], bp, o[dt]);
+  }
+}
+
 // Row max of raw scores over the block, keys past `kmax` (block-relative index of the last
 // visible key) set to -inf first when `need_mask`. Both lanes of the row agree.
 __device__ __forceinline__ float mask_max(f32x16 s[4], int kmax, bool need_mask, int hf) {
@@ -302,6 +372,48 @@ __device__ __forceinline__ float exp_pack(const f32x16 s[4], float sl2, float c,
     }
   }
   return l + shfl_xor_f(l, 32);
+}
+
+// Row max of raw scores over the wave's half block (s[i]: block keys 32*(kt0 + i) + 16*(l/32)
+// + r), keys past `kmax` (block-relative) set to -inf first when `need_mask`.
+__device__ __forceinline__ float mask_max_half(f32x16 s[2], int kt0, int kmax, bool need_mask,
+                                               int hf) {
+  const float ninf = -__builtin_inff();
+  if (need_mask) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        s[i][r] = ((kt0 + i) * 32 + 16 * hf + r <= kmax) ? s[i][r] : ninf;
+  }
+  float m = ninf;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) m = fmaxf(m, s[i][r]);
+  return fmaxf(m, shfl_xor_f(m, 32));
+}
+
+// p = 2^(s * sl2 - c) over the half block as packed bf16 pairs; returns this lane's sum of
+// the rounded p (the row's other 32 keys sit in lane l ^ 32).
+__device__ __forceinline__ float exp_pack_half(const f32x16 s[2], float sl2, float c,
+                                               u32x4 p[2][2]) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[i][8 * ks + 2 * j], sl2, -c));
+        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[i][8 * ks + 2 * j + 1], sl2, -c));
+        const uint32_t w = pack_bf16x2(x0, x1);
+        p[i][ks][j] = w;
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l, false);
+      }
+  return l;
 }
 
 // Pack 16 consecutive output dims per dt (scaled by `mul`) as bf16: w[2*dt + h2] holds dims

@@ -219,6 +219,44 @@ def test_tile_lists_q_outer_and_kv_outer():
         assert st["max_abs"] <= 2e-2 and st["max_dlse"] <= 1e-2
 
 
+TILE_CASES = [
+    # causal, varlen with ragged tails, a one-query sequence, blocks past a sequence's end in
+    # the pool, G = 2
+    ("causal_varlen_g2", mi.custom(name="tc", n_q=(1000, 300, 1), n_k=(1000, 700, 2000), hq=8,
+                                   hkv=4, topk=6, causal=True, list_q=128, list_pool=8), 0),
+    # non-causal, bottom-right aligned, one KV head for four query heads, long lists
+    ("noncausal_g4", mi.custom(name="tn", n_q=(384,), n_k=(2000,), hq=4, hkv=1, topk=12,
+                               causal=False, list_q=128, list_pool=15), 1),
+    # fp8 Q/K/V on per-tile lists
+    ("fp8", mi.custom(name="tf", n_q=(512,), hq=4, hkv=2, topk=4, dtype="fp8", causal=False,
+                      list_q=128, list_pool=4), 2),
+]
+
+
+@pytest.mark.parametrize("name,cfg,seed", TILE_CASES, ids=[c[0] for c in TILE_CASES])
+def test_tile_lists_edge_cases(name, cfg, seed):
+    """Per-tile lists with -1 padding, repeated blocks and out-of-range ids, both schedules."""
+    _say(f"[tile lists] {name}")
+    case = mi.make_case(cfg, seed=seed)
+    rng = np.random.default_rng(seed)
+    lists = case.lists
+    n_rows = lists.shape[0] * lists.shape[1]
+    flat = lists.reshape(n_rows, -1)
+    for i in rng.choice(n_rows, max(1, n_rows // 3), replace=False):
+        flat[i, -1] = -1                                   # shorter list
+    for i in rng.choice(n_rows, max(1, n_rows // 3), replace=False):
+        flat[i, 1] = flat[i, 0]                            # a block listed twice
+    flat[0, 0] = 10_000                                    # out of range: skipped
+    dev = upload(case)
+    out = msa_case.run(case)
+    tol_o, tol_l = TOL[case.cfg.dtype]
+    for mode in (msa.MSA_Q_OUTER, msa.MSA_KV_OUTER):
+        o, lse = gpu_attention(case, dev, dev.lists, mode)
+        st = err_stats(o, out.o, lse, out.lse)
+        _say(mode, st)
+        assert st["max_abs"] <= tol_o and st["max_dlse"] <= tol_l and st["lse_inf_match"]
+
+
 def test_decode_q_outer_splits():
     _say("[decode]")
     cfg = mi.Config(name="dec", batch=6, n_q=(), n_k=(), hq=64, hkv=4, topk=16, dp=64,
