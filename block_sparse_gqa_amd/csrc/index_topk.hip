@@ -222,23 +222,25 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
 }
 
 // ------------------------------------------------------------------------ split kernels
-// Grid: x = key chunk, y = group, z = sequence * max_q + query. Each wave scores blocks
-// j0 + wave, j0 + wave + 4, ... of the chunk with VALU dot products (the proxy keys are read
-// once, so the scan is bound by HBM bandwidth); the four wave lists are merged in LDS and the
-// chunk's list is written to the workspace.
+// Grid: x = key chunk, y = sequence * max_q + query. One workgroup scores the chunk's blocks
+// for every group: with hkv >= 4 wave w takes groups w, w+4, ..., each over all of the chunk's
+// blocks; with hkv < 4 the 4/hkv waves of a group take its blocks in turn. The waves thus read
+// the groups' interleaved proxy-key rows of the same keys together, i.e. one contiguous span
+// of memory (the scan is bound by HBM bandwidth). Dot products on the VALUs; the chunk's list
+// of each group (merged in LDS over the waves sharing the group) goes to the workspace.
 template <int DP>
 __global__ __launch_bounds__(256) void index_split_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     float* __restrict__ part_sc, int32_t* __restrict__ part_id, int hkv, int max_q,
-    int causal, int n_chunks, int total_q, int total_k, int max_k) {
+    int causal, int n_chunks, int chunk_blocks, int total_q, int total_k, int max_k) {
   constexpr int LPK = DP / 8;      // lanes per key row (16 bytes each)
   constexpr int KPI = 64 / LPK;    // keys per wave instruction
   __shared__ float lsc[4][kMaxTopK];
   __shared__ int lid[4][kMaxTopK];
 
-  const int chunk = blockIdx.x, h = blockIdx.y;
-  const int s = blockIdx.z / max_q, il = blockIdx.z % max_q;
+  const int chunk = blockIdx.x;
+  const int s = blockIdx.y / max_q, il = blockIdx.y % max_q;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
   const bool qvalid = il < sq.nq;
@@ -246,56 +248,80 @@ __global__ __launch_bounds__(256) void index_split_kernel(
   const int c = floordiv(pos, kBlock);
   const int nb = (sq.nk + kBlock - 1) / kBlock;
   const int jend = qvalid ? (causal ? min(max(c, 0), nb) : nb) : 0;
-  const int j0 = chunk * kSplitIndexChunk;
-  const int j1 = min(j0 + kSplitIndexChunk, jend);
-
+  const int j0 = chunk * chunk_blocks;
+  const int j1 = min(j0 + chunk_blocks, jend);
+  const int wph = hkv >= 4 ? 1 : 4 / hkv;   // waves per group
   const int kk = lane / LPK, dc = lane % LPK;
-  float qv[8];
-  {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (qvalid)
-      w = *reinterpret_cast<const u32x4*>(q_idx + ((size_t)(sq.q0 + il) * hkv + h) * DP + dc * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qv[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-      qv[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-    }
-  }
 
-  TopList tl;
-  tl.init();
-  for (int j = j0 + wave; j < j1; j += 4) {
-    if (!causal && j == c) continue;
-    float mx = kNegInf;
-    constexpr int IT = kBlock / KPI;
-    u32x4 kvv[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int u = j * kBlock + it * KPI + kk;
+  // this wave's best blocks of group h over blocks j0 + sub, j0 + sub + wph, ...
+  auto scan = [&](int h, int sub, TopList& tl) {
+    float qv[8];
+    {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (u < sq.nk)
-        w = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + dc * 8);
-      kvv[it] = w;
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      float dot = 0.f;
+      if (qvalid)
+        w = *reinterpret_cast<const u32x4*>(q_idx + ((size_t)(sq.q0 + il) * hkv + h) * DP + dc * 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dot = fmaf(qv[2 * i], bf16_bits_to_f32(kvv[it][i] & 0xFFFFu), dot);
-        dot = fmaf(qv[2 * i + 1], bf16_bits_to_f32(kvv[it][i] >> 16), dot);
+        qv[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        qv[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    }
+    tl.init();
+    for (int j = j0 + sub; j < j1; j += wph) {
+      if (!causal && j == c) continue;
+      float mx = kNegInf;
+      constexpr int IT = kBlock / KPI;
+      u32x4 kvv[IT];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int u = j * kBlock + it * KPI + kk;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (u < sq.nk)
+          w = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + dc * 8);
+        kvv[it] = w;
       }
 #pragma unroll
-      for (int m = 1; m < LPK; m <<= 1) dot += shfl_xor_f(dot, m);
-      const int u = j * kBlock + it * KPI + kk;
-      if (u >= sq.nk) dot = kNegInf;
-      mx = fmaxf(mx, dot);
-    }
+      for (int it = 0; it < IT; ++it) {
+        float dot = 0.f;
 #pragma unroll
-    for (int m = LPK; m < 64; m <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
-    tl.insert(mx, j);
-  }
+        for (int i = 0; i < 4; ++i) {
+          dot = fmaf(qv[2 * i], bf16_bits_to_f32(kvv[it][i] & 0xFFFFu), dot);
+          dot = fmaf(qv[2 * i + 1], bf16_bits_to_f32(kvv[it][i] >> 16), dot);
+        }
+#pragma unroll
+        for (int m = 1; m < LPK; m <<= 1) dot += shfl_xor_f(dot, m);
+        const int u = j * kBlock + it * KPI + kk;
+        if (u >= sq.nk) dot = kNegInf;
+        mx = fmaxf(mx, dot);
+      }
+#pragma unroll
+      for (int m = LPK; m < 64; m <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+      tl.insert(mx, j);
+    }
+  };
+  auto out_base = [&](int h) {
+    return ((((size_t)s * max_q + il) * hkv + h) * n_chunks + chunk) * kMaxTopK;
+  };
 
+  if (wph == 1) {
+    // a wave per group: its list is the chunk's list (empty slots are -inf / -1)
+    for (int h = wave; h < hkv; h += 4) {
+      TopList tl;
+      scan(h, 0, tl);
+      if (lane == 0) {
+        const size_t base = out_base(h);
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+          part_sc[base + k] = tl.sc[k];
+          part_id[base + k] = tl.id[k];
+        }
+      }
+    }
+    return;
+  }
+  const int h = wave % hkv, sub = wave / hkv;
+  TopList tl;
+  scan(h, sub, tl);
   if (lane == 0) {
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
@@ -304,22 +330,27 @@ __global__ __launch_bounds__(256) void index_split_kernel(
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    // 64 candidates, one per lane: rank = number of candidates that beat it.
-    const float sc = lsc[lane >> 4][lane & 15];
-    const int id = lid[lane >> 4][lane & 15];
-    int rank = 0;
-    for (int o = 0; o < 64; ++o) {
-      if (beats(lsc[o >> 4][o & 15], lid[o >> 4][o & 15], sc, id)) ++rank;
+  if (sub == 0) {
+    // the group's wph * 16 candidates, one per lane (lists of waves h, h + hkv, ...): rank =
+    // number of candidates that beat it
+    const int n_cand = wph * kMaxTopK;
+    const int lw = h + (lane >> 4) * hkv;
+    const float sc = lane < n_cand ? lsc[lw][lane & 15] : kNegInf;
+    const int id = lane < n_cand ? lid[lw][lane & 15] : -1;
+    int rank = 0, n_real = 0;
+    for (int o = 0; o < n_cand; ++o) {
+      const int ow = h + (o >> 4) * hkv;
+      const float os = lsc[ow][o & 15];
+      const int oi = lid[ow][o & 15];
+      rank += beats(os, oi, sc, id) ? 1 : 0;
+      n_real += oi >= 0 ? 1 : 0;
     }
-    const size_t base = ((((size_t)s * max_q + il) * hkv + h) * n_chunks + chunk) * kMaxTopK;
+    const size_t base = out_base(h);
     if (id >= 0 && rank < kMaxTopK) {
       part_sc[base + rank] = sc;
       part_id[base + rank] = id;
     }
     // slots past the number of real candidates are empty
-    int n_real = 0;
-    for (int o = 0; o < 64; ++o) n_real += lid[o >> 4][o & 15] >= 0 ? 1 : 0;
     if (lane < kMaxTopK && lane >= n_real) {
       part_sc[base + lane] = kNegInf;
       part_id[base + lane] = -1;
@@ -327,7 +358,9 @@ __global__ __launch_bounds__(256) void index_split_kernel(
   }
 }
 
-// One wave per (sequence, query, group): K rounds of a tournament over the chunk lists.
+// One wave per (sequence, query, group): every chunk list is read once into registers (lane
+// l merges lists l, l + 64, ... into one list), then K rounds of a tournament over the lanes'
+// list heads, the winning lane shifting its list.
 __global__ __launch_bounds__(64) void index_merge_kernel(
     const float* __restrict__ part_sc, const int32_t* __restrict__ part_id,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
@@ -343,32 +376,41 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
   const bool has_local = pos >= 0;
   const size_t base = (((size_t)s * max_q + il) * hkv + h) * n_chunks;
 
-  constexpr int MAXOWN = 8;   // lists per lane: n_chunks <= 512
-  int head[MAXOWN];
+  // this lane's lists, in chunk order (ties then keep the lower block, as in one scan)
+  TopList tl;
+  tl.init();
+  for (int li = lane; li < n_chunks; li += 64) {
+    const u32x4* ps = reinterpret_cast<const u32x4*>(part_sc + (base + li) * kMaxTopK);
+    const u32x4* pi = reinterpret_cast<const u32x4*>(part_id + (base + li) * kMaxTopK);
+    u32x4 vs[4], vi[4];
 #pragma unroll
-  for (int o = 0; o < MAXOWN; ++o) head[o] = 0;
+    for (int q = 0; q < 4; ++q) {
+      vs[q] = ps[q];
+      vi[q] = pi[q];
+    }
+    if (li == lane) {
+      // the first list is already sorted: take it as it is
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k) {
+        tl.sc[k] = __uint_as_float(vs[k >> 2][k & 3]);
+        tl.id[k] = (int)vi[k >> 2][k & 3];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k) {
+        const int id = (int)vi[k >> 2][k & 3];
+        if (id >= 0) tl.insert(__uint_as_float(vs[k >> 2][k & 3]), id);
+      }
+    }
+  }
 
   float out_sc[kMaxTopK];
   int out_id[kMaxTopK];
   const int need = topk - (has_local ? 1 : 0);
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
-    // best head among this lane's lists
-    float bs = kNegInf;
-    int bi = -1, bo = -1;
-#pragma unroll
-    for (int o = 0; o < MAXOWN; ++o) {
-      const int li = lane + 64 * o;
-      if (li < n_chunks && head[o] < kMaxTopK) {
-        const size_t p = (base + li) * kMaxTopK + head[o];
-        const float sv = part_sc[p];
-        const int iv = part_id[p];
-        if (beats(sv, iv, bs, bi)) { bs = sv; bi = iv; bo = o; }
-      }
-    }
-    // wave arg-best
-    float ws = bs;
-    int wi = bi;
+    float ws = tl.sc[0];
+    int wi = tl.id[0];
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const float os = shfl_xor_f(ws, m);
@@ -377,10 +419,15 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
     }
     out_sc[k] = ws;
     out_id[k] = wi;
-    // the lane holding the winner advances that list (block ids are unique across lists)
-    if (wi >= 0 && bi == wi) {
+    // the lane holding the winner drops it (block ids are unique across lists)
+    if (wi >= 0 && tl.id[0] == wi) {
 #pragma unroll
-      for (int o = 0; o < MAXOWN; ++o) head[o] += (o == bo) ? 1 : 0;
+      for (int q = 0; q + 1 < kMaxTopK; ++q) {
+        tl.sc[q] = tl.sc[q + 1];
+        tl.id[q] = tl.id[q + 1];
+      }
+      tl.sc[kMaxTopK - 1] = kNegInf;
+      tl.id[kMaxTopK - 1] = -1;
     }
     if (k + 1 >= need) break;
   }
@@ -396,7 +443,8 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
 // Key chunks of the split kernel (short-query calls) per (sequence, query, group).
 static int64_t index_chunks(const msa_shape& s) {
   const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
-  return std::max<int64_t>(1, (nb_max + kSplitIndexChunk - 1) / kSplitIndexChunk);
+  const int cb = split_index_chunk(nb_max);
+  return std::max<int64_t>(1, (nb_max + cb - 1) / cb);
 }
 
 size_t index_workspace_bytes(const msa_shape& s) {
@@ -441,22 +489,23 @@ hipError_t launch_index_split(const msa_shape& s, const void* q_idx, const void*
                               float* topk_score, void* ws, hipStream_t st) {
   if (s.max_q == 0) return hipSuccess;
   const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
-  const int n_chunks = (int)((nb_max + kSplitIndexChunk - 1) / kSplitIndexChunk);
+  const int cb = split_index_chunk(nb_max);
+  const int n_chunks = (int)((nb_max + cb - 1) / cb);
   const int64_t n = (int64_t)s.batch * s.max_q * s.hkv * n_chunks * kMaxTopK;
   float* part_sc = reinterpret_cast<float*>(ws);
   int32_t* part_id = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + n * 4);
   if (n_chunks > 0) {
-    dim3 grid(n_chunks, s.hkv, s.batch * s.max_q);
+    dim3 grid(n_chunks, s.batch * s.max_q);
     if (s.dp == 64) {
       hipLaunchKernelGGL(index_split_kernel<64>, grid, dim3(256), 0, st,
                          (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, part_sc,
-                         part_id, s.hkv, s.max_q, s.causal, n_chunks, s.total_q, s.total_k,
-                         s.max_k);
+                         part_id, s.hkv, s.max_q, s.causal, n_chunks, cb, s.total_q,
+                         s.total_k, s.max_k);
     } else {
       hipLaunchKernelGGL(index_split_kernel<32>, grid, dim3(256), 0, st,
                          (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, part_sc,
-                         part_id, s.hkv, s.max_q, s.causal, n_chunks, s.total_q, s.total_k,
-                         s.max_k);
+                         part_id, s.hkv, s.max_q, s.causal, n_chunks, cb, s.total_q,
+                         s.total_k, s.max_k);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

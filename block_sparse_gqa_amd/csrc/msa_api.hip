@@ -255,7 +255,7 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
   if (s.max_q <= kSplitIndexMaxQ) {
     // key chunks merged by one wave per (query, group): at most 512 per query
     if (cdiv(cdiv(s.max_k, s.block), kSplitIndexChunk) > 512) return MSA_ERR_SHAPE;
-    if ((int64_t)s.batch * s.max_q > 65535) return MSA_ERR_SHAPE;      // grid z of the split kernel
+    if ((int64_t)s.batch * s.max_q > 65535) return MSA_ERR_SHAPE;      // grid y of the split kernel
     const size_t need = index_workspace_bytes(s);
     if (!workspace || ws_bytes < need) return MSA_ERR_WORKSPACE;
     e = launch_index_split(s, q_idx, k_idx, cu_q, cu_k, topk_idx, topk_score, workspace, stream);

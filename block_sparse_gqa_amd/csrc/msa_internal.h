@@ -11,8 +11,10 @@ namespace msa {
 // Threshold below which the index branch splits the key range across workgroups instead of
 // tiling queries (decode and other short-query calls).
 constexpr int kSplitIndexMaxQ = 16;
-// Blocks of keys scored by one workgroup of the split index kernel.
+// Blocks of keys scored by one workgroup of the split index kernel: 16 up to 1024 blocks
+// (64 chunks), 32 beyond (the merge reads at most 512 chunk lists).
 constexpr int kSplitIndexChunk = 32;
+inline int split_index_chunk(int64_t nb_max) { return nb_max <= 1024 ? 16 : kSplitIndexChunk; }
 // Queries per inverted-index bitmap word.
 constexpr int kWordQ = 64;
 // Queries per range of the entry order (s, group, range, block, query). The attention

@@ -58,6 +58,15 @@ INDEX_CASES = [
                             causal=False, proxy="grid")),
     ("decode_grid", dict(n_q=(1, 1, 1, 2), n_k=(130, 4096 + 77, 9000, 256), hq=16, hkv=2,
                          topk=16, dp=64, proxy="grid")),
+    # short-query (key-split) path: one, three and eight groups, non-causal rows, and more
+    # than 64 key chunks per query
+    ("split_g1", dict(n_q=(1, 3), n_k=(5000, 20000), hq=4, hkv=1, topk=16, dp=32, proxy="grid")),
+    ("split_g3", dict(n_q=(2,), n_k=(9000,), hq=6, hkv=3, topk=8, dp=64, proxy="grid")),
+    ("split_g8", dict(n_q=(1, 1), n_k=(3000, 12000), hq=16, hkv=8, topk=16, dp=64, proxy="grid")),
+    ("split_noncausal", dict(n_q=(4, 16), n_k=(3000, 7000), hq=8, hkv=4, topk=10, dp=32,
+                             causal=False, proxy="grid")),
+    ("split_many_chunks", dict(n_q=(1,), n_k=(300000,), hq=2, hkv=1, topk=16, dp=32,
+                               proxy="grid")),
 ]
 
 
