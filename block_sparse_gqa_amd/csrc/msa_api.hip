@@ -42,9 +42,12 @@ msa_status check_shape(const msa_shape* s) {
   return MSA_OK;
 }
 
+// Splits of each per-query list for the Q-outer kernel: the smallest power of two giving about
+// 512 workgroups (two per compute unit of a 256-CU part), so that each workgroup streams a few
+// blocks back to back. Shape-only, so the workspace size depends on the shape alone.
 int choose_splits(const msa_shape& s) {
   int ns = 1;
-  while (ns * 2 <= s.topk && (int64_t)s.total_q * s.hkv * ns < 2048) ns *= 2;
+  while (ns * 2 <= s.topk && (int64_t)s.total_q * s.hkv * ns < 512) ns *= 2;
   return ns;
 }
 
