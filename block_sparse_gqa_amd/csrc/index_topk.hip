@@ -288,14 +288,12 @@ __global__ __launch_bounds__(256) void index_split_kernel(
           dot = fmaf(qv[2 * i], bf16_bits_to_f32(kvv[it][i] & 0xFFFFu), dot);
           dot = fmaf(qv[2 * i + 1], bf16_bits_to_f32(kvv[it][i] >> 16), dot);
         }
-#pragma unroll
-        for (int m = 1; m < LPK; m <<= 1) dot += shfl_xor_f(dot, m);
+        dot = group_sum<LPK>(dot);
         const int u = j * kBlock + it * KPI + kk;
         if (u >= sq.nk) dot = kNegInf;
         mx = fmaxf(mx, dot);
       }
-#pragma unroll
-      for (int m = LPK; m < 64; m <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+      mx = wave_max_from<LPK>(mx);
       tl.insert(mx, j);
     }
   };
@@ -411,12 +409,16 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
   for (int k = 0; k < kMaxTopK; ++k) {
     float ws = tl.sc[0];
     int wi = tl.id[0];
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const float os = shfl_xor_f(ws, m);
-      const int oi = shfl_xor_i(wi, m);
+    // wave arg-best: four levels on the DPP network, then lanes ^ 16 and ^ 32
+    auto take = [&](float os, int oi) {
       if (beats(os, oi, ws, wi)) { ws = os; wi = oi; }
-    }
+    };
+    take(dpp_f<kDppXor1>(ws), dpp_i<kDppXor1>(wi));
+    take(dpp_f<kDppXor2>(ws), dpp_i<kDppXor2>(wi));
+    take(dpp_f<kDppHalfMirror>(ws), dpp_i<kDppHalfMirror>(wi));
+    take(dpp_f<kDppMirror>(ws), dpp_i<kDppMirror>(wi));
+    take(shfl_xor_f(ws, 16), shfl_xor_i(wi, 16));
+    take(shfl_xor_f(ws, 32), shfl_xor_i(wi, 32));
     out_sc[k] = ws;
     out_id[k] = wi;
     // the lane holding the winner drops it (block ids are unique across lists)

@@ -100,6 +100,46 @@ __device__ __forceinline__ int shfl_xor_i(int v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Cross-lane moves on the DPP network (no LDS traffic). gfx9 controls: quad_perm [1,0,3,2]
+// (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror (lane i of 8 reads 7 - i: the
+// other quad), row_mirror (lane i of 16 reads 15 - i: the other half row).
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, 8 or 16); every lane gets its group's sum.
+// Each level adds the other half of the group, so both halves compute the same sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
+// Max over all 64 lanes of values that are already equal within aligned groups of N lanes.
+template <int N>
+__device__ __forceinline__ float wave_max_from(float v) {
+  if constexpr (N <= 1) v = fmaxf(v, dpp_f<kDppXor1>(v));
+  if constexpr (N <= 2) v = fmaxf(v, dpp_f<kDppXor2>(v));
+  if constexpr (N <= 4) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (N <= 8) v = fmaxf(v, dpp_f<kDppMirror>(v));
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  return fmaxf(v, shfl_xor_f(v, 32));
+}
+
 // Per-sequence geometry read from the cumulative length arrays.
 struct Seq {
   int q0, nq, k0, nk;
