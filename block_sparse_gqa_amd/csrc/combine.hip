@@ -53,7 +53,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     if (es[k] >= 0) {
       l = part_lse[(size_t)es[k] * G + g];
       w = part_l[(size_t)es[k] * G + g];
-      v = *reinterpret_cast<const u32x4*>(part_o + ((size_t)es[k] * G + g) * kD + 8 * c);
+      // streaming load: each partial is read exactly once
+      v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(part_o + ((size_t)es[k] * G + g) * kD + 8 * c));
     }
     ls[k] = l;
     lw[k] = w;
