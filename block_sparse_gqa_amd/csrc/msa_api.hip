@@ -77,7 +77,9 @@ msa_status check_mode(const msa_shape& s, msa_mode mode, msa_mode* out) {
   if (m == MSA_KV_OUTER) {
     const int64_t nb_max = cdiv(s.max_k, s.block);
     if (nb_max > 8192) return MSA_ERR_SHAPE;           // LDS bitmap tile of the plan
-    if (geometry(s, m).n_words + 1 > kInt32Max) return MSA_ERR_SHAPE;   // 32-bit scan
+    const Geometry g = geometry(s, m);
+    if (g.n_words + 1 > kInt32Max) return MSA_ERR_SHAPE;   // 32-bit scan
+    if (g.tiled && g.n_tiles_max > kInt32Max) return MSA_ERR_SHAPE;
   }
   *out = m;
   return MSA_OK;
@@ -97,11 +99,15 @@ Geometry geometry(const msa_shape& s, msa_mode mode) {
   if (mode == MSA_KV_OUTER) {
     g.w_max = cdiv(s.max_q, kWordQ);
     g.wr = 1;
-    while (g.wr < g.w_max && g.wr < kRangeQ / kWordQ) g.wr *= 2;
+    while (g.wr < g.w_max && g.wr < range_q(s) / kWordQ) g.wr *= 2;
     g.n_r = cdiv(g.w_max, g.wr);
-    g.n_buckets = (int64_t)s.batch * s.hkv * g.n_r * g.nb_max;
+    g.n_phase = (int64_t)s.batch * s.hkv * g.n_r;
+    g.n_buckets = g.n_phase * g.nb_max;
     g.n_words = g.n_buckets * g.wr;
     g.e_max = (int64_t)s.total_q * s.hkv * s.topk;
+    g.tiled = s.dtype == MSA_BF16;
+    // a bucket of c entries makes ceil(c / (256 / group)) tiles
+    g.n_tiles_max = g.tiled ? std::min(g.e_max, g.e_max / (256 / g.group) + g.n_buckets) + 1 : 0;
     g.n_scan_blocks = cdiv(g.n_words, kScanTile);
   } else {
     g.splits = s.list_q == 1 ? choose_splits(s) : 1;
@@ -128,9 +134,13 @@ Layout layout(const msa_shape& s, msa_mode mode) {
     L.entry_q = take((size_t)g.e_max * 4);
     L.entry_bucket = take((size_t)g.e_max * 4);
     L.cmap = take((size_t)s.total_q * s.hkv * s.topk * 4);
+    L.tile_off = take(g.tiled ? (size_t)g.n_buckets * 4 : 0);
+    L.phase_base = take(g.tiled ? (size_t)(g.n_phase + 1) * 8 : 0);
+    L.tiles = take((size_t)g.n_tiles_max * 8);
   } else {
     L.slots = g.splits;
     L.masks = L.offsets = L.scan_sums = L.entry_q = L.entry_bucket = off;
+    L.tile_off = L.phase_base = L.tiles = off;
     L.cmap = take(g.splits > 1 ? (size_t)s.total_q * s.hkv * g.splits * 4 : 0);
   }
   L.part_lse = take((size_t)g.e_max * g.group * 4);
@@ -139,6 +149,14 @@ Layout layout(const msa_shape& s, msa_mode mode) {
   L.dummy = take(mode == MSA_KV_OUTER ? 65536 : 0);
   L.total = off;
   return L;
+}
+
+// XCDs of the device (chiplets with their own L2). The tiled attention kernel gives each XCD
+// its own query ranges; workgroup i is taken to run on XCD i % n (round-robin dispatch).
+// Only locality depends on this, never the result.
+int device_xcd_count() {
+  const int cu = device_cu_count();
+  return cu % 8 == 0 ? 8 : 1;
 }
 
 int device_cu_count() {

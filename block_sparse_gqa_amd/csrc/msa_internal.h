@@ -17,23 +17,28 @@ constexpr int kSplitIndexChunk = 32;
 inline int split_index_chunk(int64_t nb_max) { return nb_max <= 1024 ? 16 : kSplitIndexChunk; }
 // Queries per inverted-index bitmap word.
 constexpr int kWordQ = 64;
-// Queries per range of the entry order (s, group, range, block, query). The attention
-// kernel works through the (s, group, range) phases one after the other, every workgroup
-// taking an equal share of each. Measured on the 32K-query layer, one range per sequence
-// (plain contiguous slices of the whole entry list) is fastest: shorter ranges keep the Q
-// rows in use within the memory-side cache but cost more K/V restaging and ragged tiles.
-constexpr int kRangeQ = 1 << 24;
-// Tiles per chunk handed round-robin to the persistent attention workgroups.
-constexpr int kChunkTiles = 8;
+// Queries per range of the entry order (s, group, range, block, query). The bf16 attention
+// kernel hands each (s, group, range) phase to one XCD, whose workgroups split the phase's
+// tiles; 512 queries of one group hold 2 MiB of Q rows, half an XCD's L2, so a query's Q rows
+// are fetched from memory once and re-read from L2 for each of its blocks. The fp8 kernel
+// walks one range per sequence, every workgroup taking an equal share of it.
+constexpr int kRangeQBf16 = 512;
+constexpr int kRangeQFp8 = 1 << 24;
+inline int range_q(const msa_shape& s) {
+  return s.dtype == MSA_FP8_E4M3 ? kRangeQFp8 : kRangeQBf16;
+}
 // Elements per workgroup in the scan kernels.
 constexpr int kScanTile = 4096;
 
 struct Geometry {
   int64_t nb_max;        // ceil(max_k / block)
   int64_t w_max;         // ceil(max_q / 64): bitmap words per (sequence, group, block)
-  int64_t wr;            // bitmap words per bucket (power of two, <= kRangeQ / 64)
+  int64_t wr;            // bitmap words per bucket (power of two, <= range_q / 64)
   int64_t n_r;           // query ranges per sequence: ceil(w_max / wr)
   int64_t n_buckets;     // batch * hkv * n_r * nb_max
+  int64_t n_phase;       // batch * hkv * n_r: (sequence, group, range) phases
+  int64_t n_tiles_max;   // bound on attention tiles (entries split per bucket into tiles)
+  bool tiled;            // the bf16 tiled attention kernel (tile records, XCD phases)
   int64_t n_words;       // n_buckets * w_max
   int64_t e_max;         // total_q * hkv * topk (upper bound on entries)
   int64_t n_scan_blocks; // ceil(n_words / kScanTile)
@@ -53,6 +58,10 @@ struct Layout {
   size_t entry_q;       // int32  [e_max]
   size_t entry_bucket;  // int32  [e_max]
   size_t cmap;          // int32  [total_q * hkv * slots]
+  size_t tile_off;      // int32  [n_buckets]: first tile of each bucket, phase-relative
+  size_t phase_base;    // int32  [2 * (n_phase + 1)]: first tile record of each phase,
+                        //   then the tile count of each phase
+  size_t tiles;         // int2   [n_tiles_max]: (first entry, block << 8 | entries - 1)
   size_t part_lse;      // float  [e_max * group]
   size_t part_l;        // float  [e_max * group]: weight sums (partials are unnormalised)
   size_t part_o;        // bf16   [e_max * group * d]
@@ -88,5 +97,6 @@ hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L
                           const char* ws, void* o, float* lse, hipStream_t st);
 
 int device_cu_count();
+int device_xcd_count();
 
 }  // namespace msa

@@ -13,7 +13,10 @@
 //     64w + i listed block b (LDS atomics only set bits, so the result is order-free);
 //  2. a three-pass exclusive scan of the word popcounts gives every word's first entry;
 //  3. plan_scatter: an entry's index is its word's offset plus the popcount of the lower
-//     bits; it records the query row and fills the combine map.
+//     bits; it records the query row and fills the combine map;
+//  4. (bf16 attention) plan_tiles / plan_records: each bucket's entries are cut into tiles of
+//     256 / group entries (one tile = 256 Q rows of one block), numbered per (s, group, range)
+//     phase, and every tile gets a record (first entry, block, entry count) in phase order.
 #include <algorithm>
 
 #include "msa_device.h"
@@ -204,6 +207,74 @@ __global__ __launch_bounds__(256) void scan_down_kernel(const unsigned long long
   }
 }
 
+
+// ---- tiles of the bf16 attention kernel (one workgroup per phase)
+struct TileArgs {
+  const int32_t* offsets;     // entry offset of every bitmap word (+ E at the end)
+  int32_t* tile_off;          // [n_buckets] first tile of each bucket, phase-relative
+  int32_t* phase_base;        // [n_phase + 1] first record of each phase
+  int32_t* phase_n;           // [n_phase] tiles of each phase
+  int2* recs;                 // tile records
+  int wr, nb_max, mq, n_phase;
+};
+
+__device__ __forceinline__ int bucket_entries(const TileArgs& a, int64_t bk, int* e0) {
+  const int b0 = a.offsets[bk * a.wr];
+  *e0 = b0;
+  return a.offsets[(bk + 1) * a.wr] - b0;
+}
+
+// Exclusive scan of the tile counts of the phase's buckets.
+__global__ __launch_bounds__(256) void plan_tiles_kernel(TileArgs a) {
+  const int p = blockIdx.x, tid = threadIdx.x;
+  const int per = (a.nb_max + 255) / 256;          // consecutive buckets per thread (<= 32)
+  const int b0 = tid * per;
+  int v = 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < a.nb_max) {
+      int e0;
+      const int c = bucket_entries(a, (int64_t)p * a.nb_max + b, &e0);
+      v += (c + a.mq - 1) / a.mq;
+    }
+  }
+  int tot;
+  int run = block_exclusive_scan(v, &tot);
+  for (int i = 0; i < per; ++i) {
+    const int b = b0 + i;
+    if (b < a.nb_max) {
+      const int64_t bk = (int64_t)p * a.nb_max + b;
+      int e0;
+      const int c = bucket_entries(a, bk, &e0);
+      a.tile_off[bk] = run;
+      run += (c + a.mq - 1) / a.mq;
+    }
+  }
+  if (tid == 0) a.phase_n[p] = tot;
+}
+
+// Phase bases (sum of the tile counts of the earlier phases) and the tile records.
+__global__ __launch_bounds__(256) void plan_records_kernel(TileArgs a) {
+  const int p = blockIdx.x, tid = threadIdx.x;
+  int v = 0;
+  for (int i = tid; i < p; i += 256) v += a.phase_n[i];
+  int base;
+  block_exclusive_scan(v, &base);                  // base = total over the threads
+  if (tid == 0) {
+    a.phase_base[p] = base;
+    if (p == a.n_phase - 1) a.phase_base[a.n_phase] = base + a.phase_n[p];
+  }
+  for (int b = tid; b < a.nb_max; b += 256) {
+    const int64_t bk = (int64_t)p * a.nb_max + b;
+    int e0;
+    const int c = bucket_entries(a, bk, &e0);
+    const int t0 = base + a.tile_off[bk];
+    for (int i = 0; i * a.mq < c; ++i) {
+      const int n = min(a.mq, c - i * a.mq);
+      a.recs[t0 + i] = make_int2(e0 + i * a.mq, (b << 8) | (n - 1));
+    }
+  }
+}
 }  // namespace
 
 hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
@@ -263,6 +334,20 @@ hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_scatter_kernel, grid, dim3(256), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || !g.tiled) return e;
+  TileArgs t;
+  t.offsets = offsets;
+  t.tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
+  t.phase_base = reinterpret_cast<int32_t*>(ws + L.phase_base);
+  t.phase_n = t.phase_base + g.n_phase + 1;
+  t.recs = reinterpret_cast<int2*>(ws + L.tiles);
+  t.wr = (int)g.wr;
+  t.nb_max = (int)g.nb_max;
+  t.mq = 256 / g.group;
+  t.n_phase = (int)g.n_phase;
+  hipLaunchKernelGGL(plan_tiles_kernel, dim3((unsigned)g.n_phase), dim3(256), 0, st, t);
+  hipLaunchKernelGGL(plan_records_kernel, dim3((unsigned)g.n_phase), dim3(256), 0, st, t);
   return hipGetLastError();
 }
 
