@@ -718,30 +718,42 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
     const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs]);
     k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[0], 0, rp, sw, hf);
 
-    // ---- phase A: QK^T(j) | O(j-1) through LDS to memory
+    // ---- phase A: QK^T(j) | O(j-1) through LDS to memory: packed into LDS in steps 0-1,
+    // read back one step ahead of its stores in steps 2-6; the staging buffer is then free
+    // and the next tile's Q rows are requested in step 6
     f32x16 sc[4];
+    u32x4 wb[2];
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       if (st < 7) k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[(st + 1) & 1], st + 1, rp, sw, hf);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
-      if (st < 4) {
-        stage_o<false>(obuf, oacc[st], st, 1.f, col, hf);
-      } else {
-        const __amdgpu_buffer_rsrc_t ro = srd(a.part_o + o_row0 * kD, o_nrow * kD * 2);
+      if (st < 2) {
+        stage_o<false>(obuf, oacc[2 * st], 2 * st, 1.f, col, hf);
+        stage_o<false>(obuf, oacc[2 * st + 1], 2 * st + 1, 1.f, col, hf);
+      } else if (st < 7) {
+        if (st > 2) {
+          // streaming stores: the partials are read once, by the combine kernel
+          const __amdgpu_buffer_rsrc_t ro = srd(a.part_o + o_row0 * kD, o_nrow * kD * 2);
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const int i = 2 * (st - 4) + i2;
-          const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
-          // streaming store: the partials are read once, by the combine kernel
-          __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_voff + i * 1024, 0, 2);
+          for (int i2 = 0; i2 < 2; ++i2)
+            __builtin_amdgcn_raw_buffer_store_b128(wb[i2], ro, o_voff + (2 * (st - 3) + i2) * 1024, 0, 2);
         }
-        if (st == 7) {
+        if (st < 6) {
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2) {
+            const int i = 2 * (st - 2) + i2;
+            wb[i2] = obuf[ub[i & 3] + 256 * (i >> 2)];
+          }
+        } else {
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
                                                 srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
                                                 srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+          // Q of the next tile into the staging buffer, whose read-back is complete (the
+          // stores above took its data from registers)
+          tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
         }
       }
       MSA_INTERLEAVE(1, 6);
@@ -751,9 +763,6 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
       dma_block<true>(kvs[ks], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock, wave,
                       lane);
     }
-    // Q of the next tile into the staging buffer, whose read-back for the stores above is
-    // complete (the stores took its data from registers)
-    tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
     // ---- row max of S(j)
     if (need_mask) {
 #pragma unroll
