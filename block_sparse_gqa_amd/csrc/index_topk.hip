@@ -108,7 +108,12 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   __shared__ u32x4 kl[NBUF][128 * CH];
 
   const int s = blockIdx.z, h = blockIdx.y;
-  const int tile = gridDim.x - 1 - blockIdx.x;   // late (heavier) tiles first
+  // Causal tiles grow with their position. The first half of the (sequence, group) pairs
+  // takes its tiles heavy first, the second half light first: the workgroups that share a
+  // compute unit (the dispatcher fills every unit once, then again in the same order) then
+  // pair a heavy tile with a light one instead of two of the same size.
+  const bool light_first = (int)(s * gridDim.y + h) >= (int)(gridDim.y * gridDim.z) / 2;
+  const int tile = light_first ? (int)blockIdx.x : (int)(gridDim.x - 1 - blockIdx.x);
   const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
   if (tile * kIndexTileQ >= sq.nq) return;
 
