@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int hkv, int topk,
-    int causal, int total_q, int total_k, int max_q, int max_k) {
+    int causal, int total_q, int total_k, int max_q, int max_k, int one_round) {
   constexpr int CH = DP / 8;       // 16-byte chunks per proxy key row
   constexpr int STEPS = DP / 16;   // MFMA k-steps over the proxy dim
   constexpr int PER_T = 128 * CH / 256;   // direct-to-LDS loads per thread per block
@@ -108,11 +108,13 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   __shared__ u32x4 kl[NBUF][128 * CH];
 
   const int s = blockIdx.z, h = blockIdx.y;
-  // Causal tiles grow with their position. The first half of the (sequence, group) pairs
-  // takes its tiles heavy first, the second half light first: the workgroups that share a
-  // compute unit (the dispatcher fills every unit once, then again in the same order) then
-  // pair a heavy tile with a light one instead of two of the same size.
-  const bool light_first = (int)(s * gridDim.y + h) >= (int)(gridDim.y * gridDim.z) / 2;
+  // Causal tiles grow with their position; heavy tiles go first. When the whole grid runs in
+  // one round (two workgroups per compute unit), the second half of the (sequence, group)
+  // pairs takes its tiles light first instead: the workgroups that share a compute unit (the
+  // dispatcher fills every unit once, then again in the same order) then pair a heavy tile
+  // with a light one instead of two of the same size.
+  const bool light_first =
+      one_round && (int)(s * gridDim.y + h) >= (int)(gridDim.y * gridDim.z) / 2;
   const int tile = light_first ? (int)blockIdx.x : (int)(gridDim.x - 1 - blockIdx.x);
   const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
   if (tile * kIndexTileQ >= sq.nq) return;
@@ -477,16 +479,17 @@ hipError_t launch_index_tile(const msa_shape& s, const void* q_idx, const void* 
   const int tiles = (s.max_q + kIndexTileQ - 1) / kIndexTileQ;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, s.hkv, s.batch);
+  const int one_round = (int64_t)tiles * s.hkv * s.batch <= 2 * (int64_t)device_cu_count();
   if (s.dp == 64) {
     hipLaunchKernelGGL(index_tile_kernel<64>, grid, dim3(256), 0, st,
                        (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
                        topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k, s.max_q,
-                       s.max_k);
+                       s.max_k, one_round);
   } else {
     hipLaunchKernelGGL(index_tile_kernel<32>, grid, dim3(256), 0, st,
                        (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
                        topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k, s.max_q,
-                       s.max_k);
+                       s.max_k, one_round);
   }
   return hipGetLastError();
 }
