@@ -460,8 +460,11 @@ __device__ __forceinline__ void it_enter(TileIt& it, const KvTArgs& a, int j) {
     const int pb0 = a.phase_base[it.p], pb1 = a.phase_base[it.p + 1];
     // n * n_share stays far below 2^31 (a phase holds at most 512 * 16 entries)
     const int n = pb1 - pb0;
-    it.t = pb0 + (int)((uint32_t)(n * j) / (uint32_t)a.n_share);
-    it.t_end = pb0 + (int)((uint32_t)(n * (j + 1)) / (uint32_t)a.n_share);
+    // The share taken rotates with the phase: the last share of a causal phase holds the
+    // range's own blocks, whose tiles need the causal mask; rotating spreads them evenly.
+    const int jj = (j + it.p / a.n_xcd) % a.n_share;
+    it.t = pb0 + (int)((uint32_t)(n * jj) / (uint32_t)a.n_share);
+    it.t_end = pb0 + (int)((uint32_t)(n * (jj + 1)) / (uint32_t)a.n_share);
     if (it.t < it.t_end) return;
     it.p += a.n_xcd;
   }
