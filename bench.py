@@ -318,7 +318,7 @@ def main():
                + nsb * 2 * 128 * 128 * eb                   # selected K and V blocks once
                + n_ent * g * 128 * 2                        # bf16 partial O written
                + n_ent * g * 4)                             # fp32 partial LSE written
-        kname = "attn_kv_kernel" if dtype else "attn_kv_tiled_kernel"
+        kname = "attn_kv_f8_kernel" if dtype else "attn_kv_tiled_kernel"
         res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": alg / t_main / 1e9,
                            "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": alg / t_main / PEAK_HBM,
                            "traffic": load_traffic(args.workload, alg),

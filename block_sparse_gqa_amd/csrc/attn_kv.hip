@@ -1,45 +1,23 @@
-// KV-outer (KV-stationary) main attention kernel.
+// KV-outer (KV-stationary) main attention kernels.
 //
 // "Kernel optimization for MiniMax M3 on NVIDIA Blackwell" (summary and section 2): each
-// selected KV block is loaded once in the outer loop and every query that chose it is
-// gathered in the inner loop; a work unit owns a single block, so there is one softmax step
-// and no rescaling; partial outputs are written contiguously in work order. The GQA heads of
-// one query form a contiguous box of Q rows, gathered with one index read per query-group.
+// selected KV block is loaded once and every query that chose it is gathered in; a work unit
+// owns a single block, so there is one softmax step and no rescaling; partial outputs are
+// written contiguously in work order. The GQA heads of one query form a contiguous box of Q
+// rows, gathered with one index read per query-group.
 //
-// The entry list built by the plan kernels is cut into equal contiguous slices, one per
-// persistent workgroup (deterministic, no atomics; heavy blocks are split between
-// workgroups automatically). A workgroup of eight waves walks its slice bucket by bucket: it
-// stages the bucket's K and V^T in LDS once, then processes tiles of 256 rows = 256/G entries
-// x G heads, 32 rows per wave, two waves per SIMD. Each entry's G x D partial lands in rows
-// e*G .. e*G+G-1 of the partial buffer, so a wave's 32 output rows are one contiguous 8 KiB
-// range; they are written through a per-wave LDS buffer so that every store instruction
-// covers 1 KiB of consecutive bytes.
+// The plan cuts the entry order (sequence, group, query range, block, query) into tiles of
+// 256 rows = 256/G entries of one bucket x G heads, 32 rows per wave, two waves per SIMD, and
+// writes one record per tile. Each entry's G x D partial lands in rows e*G .. e*G+G-1 of the
+// partial buffer, so a wave's 32 output rows are one contiguous range; they are written
+// through a per-wave LDS buffer so that every store instruction covers 1 KiB of consecutive
+// bytes. Two kernels walk the tiles: bf16 Q/K/V on bf16 MFMA, fp8 Q/K/V on fp8 MFMA.
 #include "attn_tile.h"
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-
-struct KvArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const float* descale;
-  float scale_log2;
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  const int32_t* counters;
-  const int32_t* offsets;
-  const int32_t* entry_q;
-  const int32_t* entry_bucket;
-  float* part_lse;
-  float* part_l;
-  uint16_t* part_o;
-  uint16_t* dummy;
-  int total_q, total_k, max_q, max_k;
-  int hq, hkv, nb_max, wr, n_r, n_buckets, n_wg, causal;
-};
 
 // --------------------------------------------------------------------------------------
 // Per-wave tile step. The MFMA pipe and the VALU of a SIMD run concurrently when MFMAs and
@@ -58,14 +36,6 @@ __device__ __forceinline__ void k_frags(const KVLds& L, bf16x8 a[4], int st, int
   const int cc = (2 * st + hf) ^ sw;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) a[kt] = as_bf16x8(L.k[(kt * 32 + rp) * 16 + cc]);
-}
-
-// V^T operands (A) of key-step s for the 4 output-dim tiles.
-__device__ __forceinline__ void v_frags(const KVLds& L, bf16x8 a[4], int s, int rp, int sw,
-                                        int hf) {
-  const int cc = (4 * (s >> 1) + 2 * hf + (s & 1)) ^ sw;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) a[dt] = as_bf16x8(L.vt[(dt * 32 + rp) * 16 + cc]);
 }
 
 // exp2 of the 8 scores of key-step s, packed to bf16 into pk; their sum is added to l. The
@@ -91,9 +61,7 @@ __device__ __forceinline__ float exp_step(const f32x16 sc[4], int s, float sl2, 
 
 // Output staging: the wave's 32 rows x 256 B, 16-byte chunk c of row R at R*16 + (c ^ (R%16)).
 // Lane (col, hf) deposits dims 32*dt + 16*hf .. +15 of row col (chunks 4dt+2hf, +1).
-template <bool FP8>
-__device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, float mul,
-                                        int col, int hf) {
+__device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, int col, int hf) {
   // opaque copies: the addresses are recomputed here instead of being held (or spilled)
   // across the caller's loop
   asm volatile("" : "+v"(col), "+v"(hf));
@@ -103,12 +71,7 @@ __device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, flo
   for (int h2 = 0; h2 < 2; ++h2) {
     u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (FP8)   // the V descale; bf16 stores the accumulator as it is
-        w[i] = pack_bf16x2(o[8 * h2 + 2 * i] * mul, o[8 * h2 + 2 * i + 1] * mul);
-      else
-        w[i] = pack_bf16x2(o[8 * h2 + 2 * i], o[8 * h2 + 2 * i + 1]);
-    }
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[8 * h2 + 2 * i], o[8 * h2 + 2 * i + 1]);
     row[(4 * dt + h2) ^ x] = w;
   }
 }
@@ -123,56 +86,14 @@ __device__ __forceinline__ void unstage_bases(int lane, int ub[4]) {
   for (int j = 0; j < 4; ++j) ub[j] = (4 * j + lq) * 16 + (x ^ (4 * j));
 }
 
-// Q rows of the wave's next tile into its staging buffer with direct-to-LDS loads. `rowidx`
-// is the lane's own Q row index (query * hq + head). A row is RB = 128 * EB bytes = RB / 16
-// chunks; load i brings rows (64 / CPR) i .. +(64 / CPR - 1), lane l fetching the chunk that
-// belongs in slot l % CPR of its row (chunk c of row R sits in slot c ^ (R % CPR)), so each
-// load reads 1 KiB of whole rows.
-template <bool FP8, int G>
-__device__ __forceinline__ void dma_q(u32x4* buf, const void* q, int rowidx, int lane) {
-  constexpr int RB = FP8 ? 128 : 256;    // bytes per Q row
-  constexpr int CPR = RB / 16;           // chunks per row
-  constexpr int RPL = 64 / CPR;          // rows per load
-  asm volatile("" : "+v"(lane));
-  const char* qb = reinterpret_cast<const char*>(q);
-  const int lr = lane / CPR, lc = lane % CPR;
-#pragma unroll
-  for (int i = 0; i < 32 / RPL; ++i) {
-    const int R = RPL * i + lr;
-    int src_row;
-    if constexpr (G >= RPL) {
-      // the load's rows are consecutive heads of one query: Q rows row0 .. row0 + RPL - 1,
-      // row0 being the row index held by the lane of row RPL * i
-      src_row = __builtin_amdgcn_readlane(rowidx, RPL * i) + lr;
-    } else {
-      src_row = __shfl(rowidx, R);
-    }
-    const int c = lc ^ (R % CPR);
-    __builtin_amdgcn_global_load_lds(
-        qb + (size_t)src_row * RB + c * 16,
-        (__attribute__((address_space(3))) void*)(buf + 64 * i), 16, 0, 0);
-  }
-}
-
-// B operand of S^T from the staging buffer: elements 16*st + 8*hf .. +7 of the lane's row.
-template <bool FP8>
+// B operand of S^T from the staging buffer (chunk c of row R in slot c ^ (R % 16)):
+// elements 16*st + 8*hf .. +7 of the lane's row.
 __device__ __forceinline__ void read_q(const u32x4* buf, bf16x8 bq[8], int col, int hf) {
   asm volatile("" : "+v"(col), "+v"(hf));
-  if constexpr (!FP8) {
-    const int x = hf ^ (col & 15);          // (2st + hf) ^ (col % 16) == 2st ^ x
-    const u32x4* const row = buf + col * 16;
+  const int x = hf ^ (col & 15);          // (2st + hf) ^ (col % 16) == 2st ^ x
+  const u32x4* const row = buf + col * 16;
 #pragma unroll
-    for (int st = 0; st < 8; ++st) bq[st] = as_bf16x8(row[(2 * st) ^ x]);
-  } else {
-    const u32x2* const row = reinterpret_cast<const u32x2*>(buf + col * 8);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const u32x2 v = row[2 * (st ^ (col & 7)) + hf];
-      const u32x2 lo = fp8x4_to_bf16x4(v[0]);
-      const u32x2 hi = fp8x4_to_bf16x4(v[1]);
-      bq[st] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-  }
+  for (int st = 0; st < 8; ++st) bq[st] = as_bf16x8(row[(2 * st) ^ x]);
 }
 
 // s_waitcnt vmcnt(0): direct-to-LDS loads are not tracked by the compiler's own waits.
@@ -191,194 +112,6 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
     }                                                             \
     __builtin_amdgcn_sched_barrier(0);                            \
   } while (0)
-
-template <bool FP8, int G>
-__global__ __launch_bounds__(512, 1) void attn_kv_kernel(KvArgs a) {
-  constexpr int MQ = 256 / G;          // entries per tile
-  constexpr int EB = FP8 ? 1 : 2;      // bytes per Q/K/V element
-  __shared__ KVLds L;
-  __shared__ u32x4 obuf_all[8][32 * 16];
-
-  const int E = a.counters[0];
-  if (E == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, hf = lane >> 5;
-  const int r = wave * 32 + col;       // row of the tile
-  const int rent = r / G, g = r % G;
-  const int rp = rowperm(col), sw = swz(rp);
-  u32x4* const obuf = obuf_all[wave];
-
-  float sl2 = a.scale_log2, dv = 1.f;
-  if constexpr (FP8) {
-    sl2 *= a.descale[0] * a.descale[1];
-    dv = a.descale[2];
-  }
-  const char* kb = reinterpret_cast<const char*>(a.k);
-  const char* vb = reinterpret_cast<const char*>(a.v);
-  const uint32_t kv_row = (uint32_t)a.hkv * kD;    // elements between consecutive keys
-  const int last = E - 1;
-  // Sinks for the stores of padding rows (contents never read).
-  uint16_t* const o_sink = a.dummy + lane * 8;
-  float* const lse_sink = reinterpret_cast<float*>(a.dummy + 64 * 8) + lane;
-  float* const l_sink = reinterpret_cast<float*>(a.dummy + 128 * 8) + lane;
-
-  // Phases (sequence, group, query range) in entry order; this workgroup's share of each.
-  const int n_phase = a.n_buckets / a.nb_max;
-  for (int ph = 0; ph < n_phase; ++ph) {
-  const int p_begin = a.offsets[(size_t)ph * a.nb_max * a.wr];
-  const int p_end = (ph + 1 < n_phase) ? a.offsets[(size_t)(ph + 1) * a.nb_max * a.wr] : E;
-  const int e_begin = p_begin + (int)((int64_t)(p_end - p_begin) * blockIdx.x / a.n_wg);
-  const int e_end = p_begin + (int)((int64_t)(p_end - p_begin) * (blockIdx.x + 1) / a.n_wg);
-  int cur = e_begin;
-  while (cur < e_end) {
-    const int bk = a.entry_bucket[cur];
-    if ((unsigned)bk >= (unsigned)a.n_buckets) break;   // never for a planned workspace
-    const int bend = (bk + 1 < a.n_buckets) ? a.offsets[(size_t)(bk + 1) * a.wr] : E;
-    const int run_end = min(e_end, bend);
-    const int b = bk % a.nb_max;
-    const int h = (bk / (a.nb_max * a.n_r)) % a.hkv;
-    const int s = bk / (a.nb_max * a.n_r * a.hkv);
-    const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
-    const int u0 = b * kBlock;
-    const int nk_rel = sq.nk - u0;
-
-    __syncthreads();   // LDS of the previous block no longer read
-    if (tid < 256)
-      stage_kv<FP8>(L, kb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB,
-                    vb + ((size_t)(sq.k0 + u0) * a.hkv + h) * kD * EB, kv_row, nk_rel);
-    __syncthreads();
-
-    auto qidx = [&](int e, int tv) { return (e < run_end ? tv : sq.q0) * a.hq + h * G + g; };
-
-    int e0 = cur + rent, e1 = e0 + MQ;
-    int t0v = a.entry_q[min(e0, last)];
-    int t1v = a.entry_q[min(e1, last)];
-    bf16x8 bq[8];
-    int ub[4];
-    unstage_bases(lane, ub);
-    dma_q<FP8, G>(obuf, a.q, qidx(e0, t0v), lane);
-    // LDS operands, double-buffered over the 16 steps of a tile (8 K steps, then 8 V steps):
-    // step i reads fr[i & 1] while the reads of step i + 1 are in flight.
-    bf16x8 fr[2][4];
-    k_frags(L, fr[0], 0, rp, sw, hf);
-    // output of the previous tile: none yet (its rows all count as padding)
-    f32x16 oacc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
-    float o_l = 0.f, o_lse = 0.f;
-    // stores of the previous tile: rows 4i + lane/16 of the wave at o_base + 4i rows, valid
-    // while 4i < o_nv (none yet)
-    uint16_t* o_base = o_sink;
-    int o_nv = 0;
-    float* lse_ptr = lse_sink;
-    float* l_ptr = l_sink;
-
-    for (int tile0 = cur; tile0 < run_end; tile0 += MQ) {
-      const int e2 = e1 + MQ;
-      const int t2v = a.entry_q[min(e2, last)];
-      int kmax = min(127, nk_rel - 1);
-      if (a.causal) kmax = min(kmax, sq.nk - sq.nq + (t0v - sq.q0) - u0);
-      const bool need_mask = __any(kmax < 127);
-      const bool valid = e0 < run_end;
-      wait_vm0();               // this tile's Q rows have landed in the staging buffer
-      read_q<FP8>(obuf, bq, col, hf);
-
-      // ---- phase A: QK^T(j) | O(j-1) through LDS to memory
-      f32x16 sc[4];
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (st < 7) k_frags(L, fr[(st + 1) & 1], st + 1, rp, sw, hf);
-        else v_frags(L, fr[0], 0, rp, sw, hf);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
-        if (st < 4) {
-          stage_o<FP8>(obuf, oacc[st], st, dv, col, hf);
-        } else {
-#pragma unroll
-          for (int i2 = 0; i2 < 2; ++i2) {
-            const int i = 2 * (st - 4) + i2;
-            const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
-            // streaming store: the partials are read once, by the combine kernel
-            __builtin_nontemporal_store(
-                w, reinterpret_cast<u32x4*>(4 * i < o_nv ? o_base + i * 4 * kD : o_sink));
-          }
-          if (st == 7) {
-            *lse_ptr = o_lse;
-            *l_ptr = o_l;
-          }
-        }
-        MSA_INTERLEAVE(1, 6);
-      }
-      // Q of the next tile into the staging buffer, whose read-back for the stores above is
-      // complete
-      dma_q<FP8, G>(obuf, a.q, qidx(e1, t1v), lane);
-      // ---- row max of S(j)
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            sc[kt][i] = (kt * 32 + 16 * hf + i <= kmax) ? sc[kt][i] : -__builtin_inff();
-      }
-      float m = -__builtin_inff();
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
-      m = fmaxf(m, shfl_xor_f(m, 32));
-      const bool any = m > -__builtin_inff();
-      const float c = any ? m * sl2 : 0.f;
-      // ---- phase B: PV(j) | exp of the next key-step
-      u32x4 pk[8];
-      float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        // the last step fetches the first K operands of the next tile (discarded after the
-        // run's last tile)
-        if (st < 7) v_frags(L, fr[(st + 1) & 1], st + 1, rp, sw, hf);
-        else k_frags(L, fr[0], 0, rp, sw, hf);
-        const bf16x8 bp = as_bf16x8(pk[st]);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
-        if (st + 1 < 8) l = exp_step(sc, st + 1, sl2, c, pk[st + 1], l);
-        MSA_INTERLEAVE(2, 7);
-      }
-      l += shfl_xor_f(l, 32);
-      // the output of tile j is stored during the next tile's phase A
-      o_l = any ? l : 0.f;
-      o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
-      {
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        o_base = a.part_o + ((size_t)tile0 * G + wave * 32 + (ln >> 4)) * kD + (ln & 15) * 8;
-        o_nv = (run_end - tile0) * G - wave * 32 - (ln >> 4);
-      }
-      lse_ptr = valid ? a.part_lse + (size_t)e0 * G + g : lse_sink;
-      l_ptr = valid ? a.part_l + (size_t)e0 * G + g : l_sink;
-      e0 = e1;
-      e1 = e2;
-      t0v = t1v;
-      t1v = t2v;
-    }
-    // output of the run's last tile (after the last, unused, Q load into the buffer)
-    wait_vm0();
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) stage_o<FP8>(obuf, oacc[dt], dt, dv, col, hf);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
-      __builtin_nontemporal_store(
-          w, reinterpret_cast<u32x4*>(4 * i < o_nv ? o_base + i * 4 * kD : o_sink));
-    }
-    *lse_ptr = o_lse;
-    *l_ptr = o_l;
-    cur = run_end;
-  }
-  }
-}
-
 
 // ======================================================================================
 // bf16: tiles of XCD-local query ranges, K/V restaged asynchronously.
@@ -409,6 +142,7 @@ struct KvTArgs {
   const void* q;
   const void* k;
   const void* v;
+  const float* descale;   // fp8: device [q, k, v] descales; bf16: unused
   float scale_log2;
   const int32_t* __restrict__ cu_q;
   const int32_t* __restrict__ cu_k;
@@ -578,8 +312,9 @@ struct TileQ {
       return q[0];
     }
   }
-  // Q rows of the wave into its staging buffer (layout of dma_q); `qo` = lane offsets of
-  // loads i % 4 (G >= 4).
+  // Q rows of the wave into its staging buffer: load i brings rows 4i .. 4i + 3, lane l the
+  // chunk that belongs in slot l % 16 of row 4i + l / 16 (chunk c of row R in slot
+  // c ^ (R % 16)), 1 KiB of whole rows per load; `qo` = lane offsets of loads i % 4 (G >= 4).
   __device__ __forceinline__ void dma(u32x4* buf, const void* qp, int hq, int h, int g,
                                       const int qo[4], int lane) const {
     const char* const qb = reinterpret_cast<const char*>(qp);
@@ -590,7 +325,7 @@ struct TileQ {
         dma16s(qb + (size_t)row0 * 256, (uint32_t)qo[i & 3], lds_addr(buf + 64 * i));
       }
     } else {
-      // rows of a load belong to several entries: per-lane addresses (dma_q's layout)
+      // rows of a load belong to several entries: per-lane addresses
       const int rowidx = q[0] * hq + h * G + g;
       const int lr = lane / 16, lc = lane % 16;
 #pragma unroll
@@ -716,7 +451,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
     if (trans)
       dma_block<false>(kvs[fs], kv_base(kb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock, wave,
                        lane);
-    read_q<false>(obuf, bq, col, hf);
+    read_q(obuf, bq, col, hf);
     const u32x4* const kslot = kvs[ks];
     const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs]);
     k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[0], 0, rp, sw, hf);
@@ -733,8 +468,8 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
       for (int kt = 0; kt < 4; ++kt)
         sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
       if (st < 2) {
-        stage_o<false>(obuf, oacc[2 * st], 2 * st, 1.f, col, hf);
-        stage_o<false>(obuf, oacc[2 * st + 1], 2 * st + 1, 1.f, col, hf);
+        stage_o(obuf, oacc[2 * st], 2 * st, col, hf);
+        stage_o(obuf, oacc[2 * st + 1], 2 * st + 1, col, hf);
       } else if (st < 7) {
         if (st > 2) {
           // streaming stores: the partials are read once, by the combine kernel
@@ -820,7 +555,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   // output of the last tile (after the last, unused, Q load into the buffer)
   wait_vm0();
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) stage_o<false>(obuf, oacc[dt], dt, 1.f, col, hf);
+  for (int dt = 0; dt < 4; ++dt) stage_o(obuf, oacc[dt], dt, col, hf);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
@@ -833,22 +568,404 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
                                         srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
 }
 
+// ======================================================================================
+// fp8: the tiled schedule on fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4)
+//
+// Q, K and V stay OCP e4m3 in LDS (16 KiB per block, 4 KiB of Q rows per wave), half the bytes
+// of the bf16 kernel, and each MFMA covers 64 of the contraction at twice the bf16 rate. For
+// the 32x32x64 8-bit MFMA, lane l supplies row l % 32 of A (and column l % 32 of B) at
+// contraction indices 32 (l / 32) .. +31, 32 bytes; the result has the 32x32 layout of the
+// bf16 MFMA. QK^T: A = K rows (key order rowperm, as in the bf16 kernel), B = Q rows, D = 64
+// per MFMA (two MFMAs per 128 dims). PV: the probabilities (scaled by 2^8, which the weight
+// sum divides out) become two e4m3 operands, hi and the rounded remainder lo, which serve as
+// B with each lane's own 32 keys of a 64-key step, each against the same rows of V^T: those
+// come from four 8-byte transpose loads (ds_read_b64_tr_b8: within a 16-lane group, lane j
+// receives byte j % 8 of the blocks addressed by lanes 2t + j / 8, t = 0..7), one run of 8
+// keys each. An A operand of ones gives the weight sum of exactly the quantised probabilities
+// on the MFMA pipe.
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c,
+                                        int scale_a = 127) {
+  // formats 0/0: e4m3 operands; scales are E8M0 codes (2^(code - 127)), B unscaled
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
+}
+
+// LDS layouts (16-byte chunks, 8 per 128-byte row): chunk c of row r at slot c ^ f(r).
+__device__ __forceinline__ int f8_swz_k(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+__device__ __forceinline__ int f8_swz_v(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int f8_swz_q(int r) { return (r ^ (r >> 3)) & 7; }
+
+// An fp8 K or V block into an LDS slot by the workgroup's 512 threads, 2 direct loads each:
+// load p of wave w fills rows 64p + 8w .. +7. Rows at or past nk_rel repeat the last key.
+template <bool V>
+__device__ __forceinline__ void dma_block8(u32x4* dst, const uint8_t* base, uint32_t row_stride,
+                                           int nk_rel, int wave, int lane) {
+  const int slot = lane & 7;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = 64 * p + 8 * wave + (lane >> 3);
+    const int f = V ? f8_swz_v(row) : f8_swz_k(row);
+    const uint32_t r = (uint32_t)min(row, nk_rel - 1);
+    dma16s(base, r * row_stride + (uint32_t)((slot ^ f) * 16), lds_addr(dst + p * 512 + wave * 64));
+  }
+}
+
+// Entry queries of a wave's 32 rows (fp8: a 1 KiB load brings 8 rows, one entry when G >= 8).
 template <int G>
-hipError_t launch_kv_tiled_g(const KvTArgs& a, int n_wg, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kv_tiled_kernel<G>), dim3(n_wg), dim3(512), 0, st, a);
+struct TileQ8 {
+  static constexpr int EPW = G >= 8 ? 32 / G : 1;
+  int q[EPW];
+
+  __device__ __forceinline__ void load(const int32_t* __restrict__ entry_q, const TileD& d,
+                                       int wave, int rent) {
+    const int last = d.e0 + max(d.n - 1, 0);
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    if constexpr (G >= 8) {
+#pragma unroll
+      for (int i = 0; i < EPW; ++i) q[i] = entry_q[min(d.e0 + wave * EPW + i, last) + z];
+    } else {
+      q[0] = entry_q[min(d.e0 + rent, last) + z];
+    }
+  }
+  __device__ __forceinline__ int lane_query(int col) const {
+    if constexpr (G >= 8) {
+      int v = q[0];
+#pragma unroll
+      for (int i = 1; i < EPW; ++i) v = (col / G == i) ? q[i] : v;
+      return v;
+    } else {
+      return q[0];
+    }
+  }
+  // Q rows of the wave: load i brings rows 8i .. 8i + 7, lane l chunk (l % 8) ^ f8_swz_q(row)
+  // of row 8i + l / 8 into slot l % 8 of that row.
+  __device__ __forceinline__ void dma(u32x4* buf, const void* qp, int hq, int h, int g,
+                                      int lane) const {
+    const char* const qb = reinterpret_cast<const char*>(qp);
+    const int lr = lane >> 3, lc = lane & 7;
+    if constexpr (G >= 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row0 = __builtin_amdgcn_readfirstlane(q[(8 * i) / G]) * hq + h * G + (8 * i) % G;
+        const int R = 8 * i + lr;
+        dma16s(qb + (size_t)row0 * 128, (uint32_t)(lr * 128 + ((lc ^ f8_swz_q(R)) * 16)),
+               lds_addr(buf + 64 * i));
+      }
+    } else {
+      const int rowidx = q[0] * hq + h * G + g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int R = 8 * i + lr;
+        const int src_row = __shfl(rowidx, R);
+        dma16(qb + (size_t)src_row * 128 + (lc ^ f8_swz_q(R)) * 16, lds_addr(buf + 64 * i));
+      }
+    }
+  }
+};
+
+// B operand of S^T for contraction step ds: Q[row col][64 ds + 32 hf .. +31].
+__device__ __forceinline__ i32x8 read_q8(const u32x4* buf, int ds, int col, int hf) {
+  const int f = f8_swz_q(col);
+  const u32x4 lo = buf[col * 8 + ((4 * ds + 2 * hf) ^ f)];
+  const u32x4 hi = buf[col * 8 + ((4 * ds + 2 * hf + 1) ^ f)];
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+// A operand of S^T for key tile kt, contraction step ds: K[32 kt + rowperm(col)][64 ds + 32 hf ..].
+__device__ __forceinline__ i32x8 read_k8(const u32x4* kb, int kt, int ds, int rp, int hf) {
+  const int r = 32 * kt + rp;
+  const int f = f8_swz_k(r);
+  const u32x4 lo = kb[r * 8 + ((4 * ds + 2 * hf) ^ f)];
+  const u32x4 hi = kb[r * 8 + ((4 * ds + 2 * hf + 1) ^ f)];
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+// A operand of O^T for dim tile dt, key step ks: V^T[32 dt + m][keys of run q = 0..3], run q of
+// lane half hf covering keys 32 (2 ks + q / 2) + 16 hf + 8 (q % 2) .. +7, the keys the lane's
+// own probabilities stand for. In 16-lane group gl (= lane / 16), supplier lane i = 2t + p
+// addresses key row k0 + t, dims 32 dt + 16 (gl % 2) + 8 p .. +7; receiving lane j gets dim
+// 32 dt + 16 (gl % 2) + j of keys k0 .. k0 + 7. Lane offsets depend on (q, t, p) only.
+__device__ __forceinline__ i32x8 read_v8(const uint8_t* vb, int dt, int ks, int lane) {
+  const int gl = lane >> 4, j = lane & 15;
+  const int t = j >> 1, p = j & 1, hf = gl >> 1;
+  i32x8 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 32 * (2 * ks + (q >> 1)) + 16 * hf + 8 * (q & 1) + t;
+    const int chunk = (2 * dt + (gl & 1)) ^ f8_swz_v(row);
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2*)(vb + row * 128 + chunk * 16 + 8 * p));
+    out[2 * q] = v[0];
+    out[2 * q + 1] = v[1];
+  }
+  return out;
+}
+
+// Probabilities of key step ks, scaled by 2^8, as a sum of two e4m3 operands: hi = e4m3(x)
+// and lo = e4m3(x - hi), so that hi + lo carries x to about 2^-8 relative (one e4m3 term
+// alone is 2^-4). Byte 8 q + u of the lane is key 32 (2 ks + q / 2) + 16 hf + 8 (q % 2) + u,
+// i.e. sc[2 ks + q / 2][8 (q % 2) + u].
+__device__ __forceinline__ void pack_p8(const f32x16 sc[4], int ks, float sl2, float c, i32x8& hi,
+                                        i32x8& lo) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int kt = 2 * ks + (q >> 1), b = 8 * (q & 1);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x[u] = __builtin_amdgcn_exp2f(fmaf(sc[kt][b + 4 * w + u], sl2, 8.f - c));
+      // the first conversion of a pair writes the low half and keeps the high half of its
+      // third operand, which the second conversion overwrites: any dead value serves there
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(
+          x[0], x[1], __builtin_bit_cast(int, sc[kt][b + 4 * w]), false);
+      d = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], d, true);
+      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+      const float r0 = x[0] - h01[0];
+      int e = __builtin_amdgcn_cvt_pk_fp8_f32(r0, x[1] - h01[1], __builtin_bit_cast(int, r0), false);
+      e = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], e, true);
+      hi[2 * q + w] = d;
+      lo[2 * q + w] = e;
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
+  __shared__ u32x4 kvs[3][128 * 8];    // rotating fp8 K / V slots, 16 KiB each
+  __shared__ u32x4 obuf_all[8][32 * 16];
+
+  const int E = a.counters[0];
+  if (E <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, hf = lane >> 5;
+  const int r = wave * 32 + col;       // row of the tile
+  const int rent = r / G, g = r % G;
+  const int rp = rowperm(col);
+  u32x4* const obuf = obuf_all[wave];
+  const int xcd = blockIdx.x % a.n_xcd, j = blockIdx.x / a.n_xcd;
+  const float sl2 = a.scale_log2 * a.descale[0] * a.descale[1];
+  // V descale dv = sigma * 2^kv, sigma in [1, 2) for normal dv: 2^kv is applied by the PV MFMAs'
+  // A scale, sigma by dividing the stored weight sum (the output over the weight sum carries
+  // dv, the log-sum-exp does not depend on it). dv = 0 gives an infinite weight sum, i.e. a
+  // zero contribution with the right log-sum-exp.
+  const float dv = a.descale[2];
+  const int kv = min((int)((__builtin_bit_cast(uint32_t, dv) >> 23) & 0xff) - 127, 127);
+  const int v_scale = 127 + kv;
+  const float inv_sigma = 1.f / ldexpf(dv, -kv);
+  const uint8_t* const kb = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* const vb = reinterpret_cast<const uint8_t*>(a.v);
+  const uint32_t kv_row = (uint32_t)a.hkv * kD;   // bytes between consecutive keys
+  int ub[4];
+  unstage_bases(lane, ub);
+  const int o_voff = (lane >> 4) * 256 + (lane & 15) * 16;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+
+  auto seq_of = [&](int p, int* h) {
+    *h = (p / a.n_r) % a.hkv;
+    return load_seq_clamped(a.cu_q, a.cu_k, p / (a.n_r * a.hkv), a.total_q, a.total_k, a.max_q,
+                            a.max_k);
+  };
+  auto kv_base = [&](const uint8_t* base, const Seq& sq, int h, int b) {
+    return base + ((size_t)(sq.k0 + b * kBlock) * a.hkv + h) * kD;
+  };
+
+  TileIt it{xcd, 0, 0};
+  it_enter(it, a, j);
+  TileD d0 = it_decode(it_fetch(it, a, j), it, a, E);
+  if (d0.n == 0) return;
+  TileD d1 = it_decode(it_fetch(it, a, j), it, a, E);
+  TileD d2 = it_decode(it_fetch(it, a, j), it, a, E);
+  TileRaw r3 = it_fetch(it, a, j);
+
+  int h0;
+  Seq sq0 = seq_of(d0.p, &h0);
+  int ks_ = 0, vs_ = 1, fs_ = 2;
+  dma_block8<false>(kvs[ks_], kv_base(kb, sq0, h0, d0.b), kv_row, sq0.nk - d0.b * kBlock, wave, lane);
+  dma_block8<true>(kvs[vs_], kv_base(vb, sq0, h0, d0.b), kv_row, sq0.nk - d0.b * kBlock, wave, lane);
+  TileQ8<G> tq0, tq1;
+  tq0.load(a.entry_q, d0, wave, rent);
+  wait_vm0();
+  tq0.dma(obuf, a.q, a.hq, h0, g, lane);
+  bool opened = true;
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+  // weight sum and max of the previous tile, read where its outputs are stored (the weight
+  // sum's MFMA chain then completes under the next tile's QK^T)
+  f32x16 o_lacc = {};
+  float o_c = 0.f;
+  bool o_any = false;
+  size_t o_row0 = 0;
+  int o_nrow = 0;
+
+  while (true) {
+    const bool trans = d1.n != 0 && (d1.b != d0.b || d1.p != d0.p);
+    int h1 = h0;
+    Seq sq1 = sq0;
+    if (d1.n != 0 && d1.p != d0.p) sq1 = seq_of(d1.p, &h1);
+    const int u0 = d0.b * kBlock;
+    const int nk_rel = sq0.nk - u0;
+    int kmax = min(127, nk_rel - 1);
+    if (a.causal) kmax = min(kmax, sq0.nk - sq0.nq + (tq0.lane_query(col) - sq0.q0) - u0);
+    const bool need_mask = __any(kmax < 127);
+
+    wait_vm0();               // Q rows (and, when `opened`, this bucket's K/V) have landed
+    if (opened) __syncthreads();
+    tq1 = tq0;
+    if (d1.n) tq1.load(a.entry_q, d1, wave, rent);
+    const TileD d3 = it_decode(r3, it, a, E);
+    r3 = it_fetch(it, a, j);
+    if (trans)
+      dma_block8<false>(kvs[fs_], kv_base(kb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
+                        wave, lane);
+    const i32x8 bq0 = read_q8(obuf, 0, col, hf);
+    const i32x8 bq1 = read_q8(obuf, 1, col, hf);
+    const u32x4* const kslot = kvs[ks_];
+    const uint8_t* const vslot = reinterpret_cast<const uint8_t*>(kvs[vs_]);
+
+    // ---- phase A: QK^T(j) (8 MFMAs) | O(j-1) through LDS to memory (8-byte pieces: lane
+    // (col, hf) holds dims 32 dt + 8 a + 4 hf .. +3 of row col in oacc[dt][4 a ..])
+    f32x16 sc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const i32x8 k0 = read_k8(kslot, kt, 0, rp, hf);
+      const i32x8 k1 = read_k8(kslot, kt, 1, rp, hf);
+      sc[kt] = mfma8(k0, bq0, f32x16{});
+      sc[kt] = mfma8(k1, bq1, sc[kt]);
+      // stage dim tile kt of the previous output
+      {
+        int cc = col;
+        asm volatile("" : "+v"(cc));
+        u32x2* const row = reinterpret_cast<u32x2*>(obuf + cc * 16);
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[kt][4 * a4], oacc[kt][4 * a4 + 1]);
+          w[1] = pack_bf16x2(oacc[kt][4 * a4 + 2], oacc[kt][4 * a4 + 3]);
+          row[2 * ((4 * kt + a4) ^ (cc & 15)) + hf] = w;
+        }
+      }
+    }
+    {
+      const __amdgpu_buffer_rsrc_t ro = srd(a.part_o + o_row0 * kD, o_nrow * kD * 2);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
+        // streaming store: the partials are read once, by the combine kernel
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_voff + i * 1024, 0, 2);
+      }
+      const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
+      const float o_lse =
+          o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                            srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                            srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+    }
+    if (trans) {
+      __syncthreads();        // every wave is done with this bucket's K
+      dma_block8<true>(kvs[ks_], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
+                       wave, lane);
+    }
+    // Q of the next tile into the staging buffer, whose read-back is complete
+    tq1.dma(obuf, a.q, a.hq, h1, g, lane);
+    // ---- row max of S(j)
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sc[kt][i] = (kt * 32 + 16 * hf + i <= kmax) ? sc[kt][i] : -__builtin_inff();
+    }
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
+    m = fmaxf(m, shfl_xor_f(m, 32));
+    const bool any = m > -__builtin_inff();
+    const float c = any ? m * sl2 : 0.f;
+    // ---- phase B: PV(j) and the weight sum (ones) on the MFMA pipe
+    f32x16 lacc = {};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      i32x8 phi, plo;
+      pack_p8(sc, ks, sl2, c, phi, plo);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const i32x8 va = read_v8(vslot, dt, ks, lane);
+        oacc[dt] = mfma8(va, phi, ks == 0 ? f32x16{} : oacc[dt], v_scale);
+        oacc[dt] = mfma8(va, plo, oacc[dt], v_scale);
+      }
+      lacc = mfma8(ones, phi, lacc);
+      lacc = mfma8(ones, plo, lacc);
+    }
+    // lacc: sum of the quantised, 2^8-scaled probabilities of the lane's row (every element)
+    o_lacc = lacc;
+    o_c = c;
+    o_any = any;
+    o_nrow = max(0, min(32, d0.n * G - wave * 32));
+    o_row0 = (size_t)d0.e0 * G + wave * 32;
+    if (d1.n == 0) break;
+    if (trans) {
+      const int k2 = fs_;
+      fs_ = vs_;
+      vs_ = ks_;
+      ks_ = k2;
+    }
+    opened = trans;
+    d0 = d1;
+    d1 = d2;
+    d2 = d3;
+    sq0 = sq1;
+    h0 = h1;
+    tq0 = tq1;
+  }
+  // output of the last tile (after the last, unused, Q load into the buffer)
+  wait_vm0();
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    u32x2* const row = reinterpret_cast<u32x2*>(obuf + col * 16);
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[dt][4 * a4], oacc[dt][4 * a4 + 1]);
+      w[1] = pack_bf16x2(oacc[dt][4 * a4 + 2], oacc[dt][4 * a4 + 3]);
+      row[2 * ((4 * dt + a4) ^ (col & 15)) + hf] = w;
+    }
+  }
+  const __amdgpu_buffer_rsrc_t ro = srd(a.part_o + o_row0 * kD, o_nrow * kD * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
+    __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_voff + i * 1024, 0, 2);
+  }
+  const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
+  const float o_lse =
+      o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                        srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                        srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+}
+
+template <int G>
+hipError_t launch_kv_f8_g(const KvTArgs& a, int n_wg, hipStream_t st) {
+  hipLaunchKernelGGL((attn_kv_f8_kernel<G>), dim3(n_wg), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
-template <bool FP8>
-hipError_t launch_kv_g(const KvArgs& a, int group, int n_wg, hipStream_t st) {
-  dim3 grid(n_wg), blk(512);
-  switch (group) {
-    case 1: hipLaunchKernelGGL((attn_kv_kernel<FP8, 1>), grid, blk, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((attn_kv_kernel<FP8, 2>), grid, blk, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((attn_kv_kernel<FP8, 4>), grid, blk, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((attn_kv_kernel<FP8, 8>), grid, blk, 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_kv_kernel<FP8, 16>), grid, blk, 0, st, a); break;
-  }
+template <int G>
+hipError_t launch_kv_tiled_g(const KvTArgs& a, int n_wg, hipStream_t st) {
+  hipLaunchKernelGGL((attn_kv_tiled_kernel<G>), dim3(n_wg), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
@@ -858,73 +975,51 @@ hipError_t launch_attn_kv(const msa_shape& s, const Geometry& g, const Layout& L
                           const void* q, const void* k, const void* v, const float* descale,
                           float scale, const int32_t* cu_q, const int32_t* cu_k, char* ws,
                           hipStream_t st) {
-  KvArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.descale = descale;
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.cu_q = cu_q;
-  a.cu_k = cu_k;
-  a.counters = reinterpret_cast<const int32_t*>(ws + L.counters);
-  a.offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
-  a.entry_q = reinterpret_cast<const int32_t*>(ws + L.entry_q);
-  a.entry_bucket = reinterpret_cast<const int32_t*>(ws + L.entry_bucket);
-  a.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
-  a.part_l = reinterpret_cast<float*>(ws + L.part_l);
-  a.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
-  a.dummy = reinterpret_cast<uint16_t*>(ws + L.dummy);
-  a.total_q = s.total_q;
-  a.total_k = s.total_k;
-  a.max_q = s.max_q;
-  a.max_k = s.max_k;
-  a.hq = s.hq;
-  a.hkv = s.hkv;
-  a.nb_max = (int)g.nb_max;
-  a.wr = (int)g.wr;
-  a.n_r = (int)g.n_r;
-  a.n_buckets = (int)g.n_buckets;
-  a.causal = s.causal;
   if (g.n_words == 0) return hipSuccess;
   const int n_wg = device_cu_count();   // one workgroup (eight waves) per CU
-  if (g.tiled) {
-    KvTArgs t;
-    t.q = q;
-    t.k = k;
-    t.v = v;
-    t.scale_log2 = a.scale_log2;
-    t.cu_q = cu_q;
-    t.cu_k = cu_k;
-    t.counters = a.counters;
-    t.entry_q = a.entry_q;
-    t.phase_base = reinterpret_cast<const int32_t*>(ws + L.phase_base);
-    t.recs = reinterpret_cast<const int2*>(ws + L.tiles);
-    t.part_lse = a.part_lse;
-    t.part_l = a.part_l;
-    t.part_o = a.part_o;
-    t.total_q = s.total_q;
-    t.total_k = s.total_k;
-    t.max_q = s.max_q;
-    t.max_k = s.max_k;
-    t.hq = s.hq;
-    t.hkv = s.hkv;
-    t.nb_max = (int)g.nb_max;
-    t.n_r = (int)g.n_r;
-    t.n_phase = (int)g.n_phase;
-    t.n_xcd = device_xcd_count();
-    t.n_share = n_wg / t.n_xcd;
-    t.causal = s.causal;
+  KvTArgs t;
+  t.q = q;
+  t.k = k;
+  t.v = v;
+  t.descale = descale;
+  t.scale_log2 = scale * 1.4426950408889634f;
+  t.cu_q = cu_q;
+  t.cu_k = cu_k;
+  t.counters = reinterpret_cast<const int32_t*>(ws + L.counters);
+  t.entry_q = reinterpret_cast<const int32_t*>(ws + L.entry_q);
+  t.phase_base = reinterpret_cast<const int32_t*>(ws + L.phase_base);
+  t.recs = reinterpret_cast<const int2*>(ws + L.tiles);
+  t.part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  t.part_l = reinterpret_cast<float*>(ws + L.part_l);
+  t.part_o = reinterpret_cast<uint16_t*>(ws + L.part_o);
+  t.total_q = s.total_q;
+  t.total_k = s.total_k;
+  t.max_q = s.max_q;
+  t.max_k = s.max_k;
+  t.hq = s.hq;
+  t.hkv = s.hkv;
+  t.nb_max = (int)g.nb_max;
+  t.n_r = (int)g.n_r;
+  t.n_phase = (int)g.n_phase;
+  t.n_xcd = device_xcd_count();
+  t.n_share = n_wg / t.n_xcd;
+  t.causal = s.causal;
+  if (s.dtype == MSA_FP8_E4M3) {
     switch (g.group) {
-      case 1: return launch_kv_tiled_g<1>(t, n_wg, st);
-      case 2: return launch_kv_tiled_g<2>(t, n_wg, st);
-      case 4: return launch_kv_tiled_g<4>(t, n_wg, st);
-      case 8: return launch_kv_tiled_g<8>(t, n_wg, st);
-      default: return launch_kv_tiled_g<16>(t, n_wg, st);
+      case 1: return launch_kv_f8_g<1>(t, n_wg, st);
+      case 2: return launch_kv_f8_g<2>(t, n_wg, st);
+      case 4: return launch_kv_f8_g<4>(t, n_wg, st);
+      case 8: return launch_kv_f8_g<8>(t, n_wg, st);
+      default: return launch_kv_f8_g<16>(t, n_wg, st);
     }
   }
-  a.n_wg = n_wg;
-  return s.dtype == MSA_FP8_E4M3 ? launch_kv_g<true>(a, g.group, n_wg, st)
-                                 : launch_kv_g<false>(a, g.group, n_wg, st);
+  switch (g.group) {
+    case 1: return launch_kv_tiled_g<1>(t, n_wg, st);
+    case 2: return launch_kv_tiled_g<2>(t, n_wg, st);
+    case 4: return launch_kv_tiled_g<4>(t, n_wg, st);
+    case 8: return launch_kv_tiled_g<8>(t, n_wg, st);
+    default: return launch_kv_tiled_g<16>(t, n_wg, st);
+  }
 }
 
 }  // namespace msa

@@ -79,7 +79,7 @@ msa_status check_mode(const msa_shape& s, msa_mode mode, msa_mode* out) {
     if (nb_max > 8192) return MSA_ERR_SHAPE;           // LDS bitmap tile of the plan
     const Geometry g = geometry(s, m);
     if (g.n_words + 1 > kInt32Max) return MSA_ERR_SHAPE;   // 32-bit scan
-    if (g.tiled && g.n_tiles_max > kInt32Max) return MSA_ERR_SHAPE;
+    if (g.n_tiles_max > kInt32Max) return MSA_ERR_SHAPE;
   }
   *out = m;
   return MSA_OK;
@@ -105,9 +105,8 @@ Geometry geometry(const msa_shape& s, msa_mode mode) {
     g.n_buckets = g.n_phase * g.nb_max;
     g.n_words = g.n_buckets * g.wr;
     g.e_max = (int64_t)s.total_q * s.hkv * s.topk;
-    g.tiled = s.dtype == MSA_BF16;
     // a bucket of c entries makes ceil(c / (256 / group)) tiles
-    g.n_tiles_max = g.tiled ? std::min(g.e_max, g.e_max / (256 / g.group) + g.n_buckets) + 1 : 0;
+    g.n_tiles_max = std::min(g.e_max, g.e_max / (256 / g.group) + g.n_buckets) + 1;
     g.n_scan_blocks = cdiv(g.n_words, kScanTile);
   } else {
     g.splits = s.list_q == 1 ? choose_splits(s) : 1;
@@ -134,8 +133,8 @@ Layout layout(const msa_shape& s, msa_mode mode) {
     L.entry_q = take((size_t)g.e_max * 4);
     L.entry_bucket = take((size_t)g.e_max * 4);
     L.cmap = take((size_t)s.total_q * s.hkv * s.topk * 4);
-    L.tile_off = take(g.tiled ? (size_t)g.n_buckets * 4 : 0);
-    L.phase_base = take(g.tiled ? (size_t)(g.n_phase + 1) * 8 : 0);
+    L.tile_off = take((size_t)g.n_buckets * 4);
+    L.phase_base = take((size_t)(g.n_phase + 1) * 8);
     L.tiles = take((size_t)g.n_tiles_max * 8);
   } else {
     L.slots = g.splits;
@@ -146,7 +145,6 @@ Layout layout(const msa_shape& s, msa_mode mode) {
   L.part_lse = take((size_t)g.e_max * g.group * 4);
   L.part_l = take((size_t)g.e_max * g.group * 4);
   L.part_o = take((size_t)g.e_max * g.group * s.d * 2);
-  L.dummy = take(mode == MSA_KV_OUTER ? 65536 : 0);
   L.total = off;
   return L;
 }

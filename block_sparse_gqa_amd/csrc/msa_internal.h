@@ -17,15 +17,23 @@ constexpr int kSplitIndexChunk = 32;
 inline int split_index_chunk(int64_t nb_max) { return nb_max <= 1024 ? 16 : kSplitIndexChunk; }
 // Queries per inverted-index bitmap word.
 constexpr int kWordQ = 64;
-// Queries per range of the entry order (s, group, range, block, query). The bf16 attention
-// kernel hands each (s, group, range) phase to one XCD, whose workgroups split the phase's
-// tiles; 512 queries of one group hold 2 MiB of Q rows, half an XCD's L2, so a query's Q rows
-// are fetched from memory once and re-read from L2 for each of its blocks. The fp8 kernel
-// walks one range per sequence, every workgroup taking an equal share of it.
+// Queries per range of the entry order (s, group, range, block, query). The attention
+// kernels hand each (s, group, range) phase to one XCD, whose workgroups split the phase's
+// tiles. bf16: 512 queries of one group hold 2 MiB of Q rows, half an XCD's L2, so a query's
+// Q rows are fetched from memory once and re-read from L2 for each of its blocks. fp8 rows
+// are half the bytes and its kernel is bound by issue rather than memory, so it takes longer
+// ranges, whose buckets hold more queries (fuller tiles, fewer K/V loads): up to 4096, as long
+// as the schedule keeps at least 128 phases (16 per XCD) to spread.
 constexpr int kRangeQBf16 = 512;
-constexpr int kRangeQFp8 = 1 << 24;
+constexpr int kRangeQFp8Max = 4096;
+constexpr int64_t kMinPhases = 128;
 inline int range_q(const msa_shape& s) {
-  return s.dtype == MSA_FP8_E4M3 ? kRangeQFp8 : kRangeQBf16;
+  if (s.dtype != MSA_FP8_E4M3) return kRangeQBf16;
+  int r = kRangeQFp8Max;
+  while (r > kRangeQBf16 &&
+         (int64_t)s.batch * s.hkv * ((s.max_q + (int64_t)r - 1) / r) < kMinPhases)
+    r /= 2;
+  return r;
 }
 // Elements per workgroup in the scan kernels.
 constexpr int kScanTile = 4096;
@@ -38,7 +46,6 @@ struct Geometry {
   int64_t n_buckets;     // batch * hkv * n_r * nb_max
   int64_t n_phase;       // batch * hkv * n_r: (sequence, group, range) phases
   int64_t n_tiles_max;   // bound on attention tiles (entries split per bucket into tiles)
-  bool tiled;            // the bf16 tiled attention kernel (tile records, XCD phases)
   int64_t n_words;       // n_buckets * w_max
   int64_t e_max;         // total_q * hkv * topk (upper bound on entries)
   int64_t n_scan_blocks; // ceil(n_words / kScanTile)
@@ -65,7 +72,6 @@ struct Layout {
   size_t part_lse;      // float  [e_max * group]
   size_t part_l;        // float  [e_max * group]: weight sums (partials are unnormalised)
   size_t part_o;        // bf16   [e_max * group * d]
-  size_t dummy;         // 64 KiB sink for the stores of padding rows (KV-outer)
   size_t total;
   int slots;            // combine slots per (query, group): topk or splits
 };

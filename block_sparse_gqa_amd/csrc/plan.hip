@@ -335,7 +335,7 @@ hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_scatter_kernel, grid, dim3(256), 0, st, a);
   e = hipGetLastError();
-  if (e != hipSuccess || !g.tiled) return e;
+  if (e != hipSuccess) return e;
   TileArgs t;
   t.offsets = offsets;
   t.tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);

@@ -121,6 +121,18 @@ LAYER_CASES = [
     ("fp8_group4", mi.custom(name="f4", n_q=(800,), hq=8, hkv=2, topk=5, dp=32, dtype="fp8"), 3),
     ("fp8_group1_ragged", mi.custom(name="f1", n_q=(600, 300), n_k=(600, 900), hq=2, hkv=2,
                                     topk=4, dp=32, dtype="fp8"), 4),
+    # G = 16 (one entry per tile row group of 16) over ragged causal sequences
+    ("group16_ragged", mi.custom(name="g16r", n_q=(700, 257), n_k=(1500, 257), hq=32, hkv=2,
+                                 topk=6, dp=64), 1),
+    # non-causal, three 512-query ranges with a ragged last one, G = 8
+    ("noncausal_g8_ranges", mi.custom(name="nc8", n_q=(1300,), n_k=(2000,), hq=16, hkv=2,
+                                      topk=6, dp=32, causal=False), 2),
+    # 32 fp8 sequences: the schedule keeps 128 (sequence, group, range) phases by taking
+    # 1024-query ranges, two of them in the long sequence, one (or an empty second) elsewhere
+    ("fp8_ranges_1024", mi.custom(name="f8mr", n_q=(2048,) + tuple(17 + 11 * i for i in range(31)),
+                                  n_k=(2048,) + tuple(17 + 11 * i + (300 if i % 3 == 0 else 0)
+                                                      for i in range(31)),
+                                  hq=8, hkv=2, topk=5, dp=32, dtype="fp8", lowrank=True), 5),
 ]
 
 
@@ -154,11 +166,13 @@ def test_index_then_layer_end_to_end():
     assert st["max_abs"] <= 2e-2 and st["max_dlse"] <= 1e-2
 
 
-def test_partials_match_oracle_partials():
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_partials_match_oracle_partials(dtype):
     """KV-outer partial outputs and LSEs, read through the documented workspace layout."""
-    _say("[partials]")
+    _say(f"[partials] {dtype}")
     case = mi.make_case(mi.custom(name="p", n_q=(512, 300), n_k=(512, 700), hq=8, hkv=2, topk=4,
-                                  dp=32), seed=5)
+                                  dp=32, dtype=dtype), seed=5)
+    tol_o, tol_l = TOL[dtype]
     dev = upload(case)
     out = msa_case.run(case, want_output=False)
     lists = torch.from_numpy(out.topk_idx).cuda()
@@ -183,7 +197,8 @@ def test_partials_match_oracle_partials():
     assert len(np.unique(ents)) == ents.size == n_ent
     rows = np.nonzero(valid)[0]
     assert np.array_equal(entry_q[ents], rows)
-    q, k, v = widen(case.q), widen(case.k), widen(case.v)
+    dq, dk, dv = case.descale
+    q, k, v = widen(case.q, dq), widen(case.k, dk), widen(case.v, dv)
     for si in range(2):
         q0, q1 = case.cu_q[si], case.cu_q[si + 1]
         k0, k1 = case.cu_k[si], case.cu_k[si + 1]
@@ -196,8 +211,8 @@ def test_partials_match_oracle_partials():
                     if e < 0:
                         continue
                     heads = slice(g * G, (g + 1) * G)
-                    assert np.max(np.abs(po[e] - o_s[i, heads, slot])) <= 2e-2
-                    assert np.max(np.abs(plse[e] - l_s[i, heads, slot])) <= 1e-2
+                    assert np.max(np.abs(po[e] - o_s[i, heads, slot])) <= tol_o
+                    assert np.max(np.abs(plse[e] - l_s[i, heads, slot])) <= tol_l
     # entries are sorted by (sequence, group, query range, block, query) and carry their bucket
     ebk = wsn[L.entry_bucket:L.entry_bucket + n_ent * 4].view(torch.int32).numpy()
     qr = 64 * L.words_per_bucket
