@@ -97,8 +97,11 @@ typedef struct {
   size_t entry_bucket; /* int32 [E]: bucket ((s * hkv + g) * n_ranges + r) * nb_max + b */
   size_t cmap;         /* int32 [total_q, hkv, slots]: partial index of each slot, -1 = none */
   size_t part_lse;     /* float [E, hq/hkv]: log-sum-exp of each partial */
-  size_t part_l;       /* float [E, hq/hkv]: sum of each partial's softmax weights (relative
-                          to its maximum); 1 where the partial output is already normalised */
+  size_t part_l;       /* float [E, hq/hkv]: sum of each partial's softmax weights, each
+                          weight taken relative to the partial's maximum and multiplied by a
+                          positive factor of the kernel's choosing that part_o carries too
+                          (bf16: 1; fp8: 2^8 / sigma, with the V descale = sigma * 2^k,
+                          sigma in [1, 2)); 1 where the partial output is already normalised */
   size_t part_o;       /* bf16 [E, hq/hkv, d]: partial output before normalisation, i.e. the
                           partial's attention output times part_l ("Kernel optimization
                           ...", section 2: unnormalised accumulators, normalised in the

@@ -196,6 +196,27 @@ def test_partial_memory_ratio_matches_the_pages():
     assert part_o_bytes - out_bytes * g["bf16_partials_over_bf16_output"] in range(0, 256)
 
 
+def test_query_range_rule():
+    """bf16 ranges hold 512 queries; fp8 ranges the longest of 4096 .. 512 queries that leaves
+    at least 128 (sequence, group, range) phases."""
+    def q_range(s):
+        lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
+        return 64 * lay.words_per_bucket, lay.n_ranges
+    fp8 = msa.MSA_FP8_E4M3
+    assert q_range(m3_shape()) == (512, 64)
+    long = dict(total_q=131072, total_k=131072, max_q=131072, max_k=131072)
+    assert q_range(m3_shape(dtype=fp8, **long)) == (4096, 32)
+    assert q_range(m3_shape(**long)) == (512, 256)
+    assert q_range(m3_shape(dtype=fp8)) == (1024, 32)            # 4 groups x 32 ranges
+    # 32 sequences of at most 2048 queries, 2 groups: 1024-query ranges (32 x 2 x 2 = 128)
+    many = msa.make_shape(batch=32, total_q=8000, total_k=9000, max_q=2048, max_k=2348, hq=8,
+                          hkv=2, topk=5, dp=32, dtype=fp8)
+    assert q_range(many) == (1024, 2)
+    small = msa.make_shape(batch=1, total_q=1024, total_k=1024, max_q=1024, max_k=1024, hq=32,
+                           hkv=2, topk=6, dp=64, dtype=fp8)
+    assert q_range(small) == (512, 2)
+
+
 def test_q_outer_workspace():
     s = decode_shape()
     lay = msa.msa_workspace_layout_of(s, msa.MSA_Q_OUTER)

@@ -281,6 +281,78 @@ def test_tile_lists_edge_cases(name, cfg, seed):
         assert st["max_abs"] <= tol_o and st["max_dlse"] <= tol_l and st["lse_inf_match"]
 
 
+def _mutate_per_query_lists(case, lists, rng):
+    """-1 padding, rows with no block at all, repeated blocks, out-of-range ids and blocks
+    past the query's local block (every key masked under causality)."""
+    out = lists.copy()
+    t_q, hkv, k = out.shape
+    rows = [(t, g) for t in range(t_q) for g in range(hkv)]
+    pick = lambda frac: [rows[i] for i in rng.choice(len(rows), max(1, int(len(rows) * frac)),
+                                                     replace=False)]
+    for t, g in pick(0.2):
+        out[t, g, -1] = -1
+    for t, g in pick(0.2):
+        out[t, g, 2] = out[t, g, 0]
+    for t, g in pick(0.1):
+        out[t, g, 1] = 10_000
+    seq = np.searchsorted(case.cu_q, np.arange(t_q), side="right") - 1
+    for t, g in pick(0.1):
+        s = seq[t]
+        n_q = case.cu_q[s + 1] - case.cu_q[s]
+        n_k = case.cu_k[s + 1] - case.cu_k[s]
+        loc = (n_k - n_q + t - case.cu_q[s]) // 128
+        if loc + 1 < -(-n_k // 128):
+            out[t, g, 3] = loc + 1
+    for t, g in pick(0.05):
+        out[t, g, :] = -1
+    return out
+
+
+def test_per_query_lists_edge_cases_and_empty_sequence():
+    """A batch with an empty sequence between two ragged ones: the index branch on it, then
+    both schedules on per-query lists with degenerate entries, against the oracle on the
+    same lists."""
+    _say("[per-query list edges]")
+    cfg = mi.custom(name="pq", n_q=(400, 0, 333), n_k=(400, 200, 900), hq=8, hkv=2, topk=5,
+                    dp=32)
+    case = mi.make_case(cfg, seed=7)
+    dev = upload(case)
+    got, _ = gpu_index(case, dev)
+    out, scores = _oracle_index_scores(case)
+    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _bound_fn(case))
+    assert not bad, f"uncertified list differences at {bad[:5]}"
+    lists = _mutate_per_query_lists(case, out.topk_idx, np.random.default_rng(7))
+    ref = msa_case.run(case, lists=lists)
+    assert np.any(np.isneginf(ref.lse))                     # rows with no visible key
+    for mode in (msa.MSA_KV_OUTER, msa.MSA_Q_OUTER):
+        o, lse = gpu_attention(case, dev, torch.from_numpy(lists).cuda(), mode)
+        st = err_stats(o, ref.o, lse, ref.lse)
+        _say(mode, st)
+        assert st["max_abs"] <= 2e-2 and st["max_dlse"] <= 1e-2 and st["lse_inf_match"]
+
+
+def test_zero_queries_leave_outputs_untouched():
+    """total_q = 0: every entry point succeeds and writes nothing."""
+    _say("[zero queries]")
+    case = mi.make_case(mi.custom(name="z", n_q=(0,), n_k=(256,), hq=4, hkv=2, topk=3, dp=32),
+                        seed=1)
+    dev = upload(case)
+    s = shape_of(case)
+    lists = torch.full((1, 2, 3), -7, dtype=torch.int32, device="cuda")
+    iws = torch.empty(max(msa.msa_index_workspace_size(s), 256), dtype=torch.uint8, device="cuda")
+    msa.msa_index_topk(s, dev.q_idx, dev.k_idx, dev.cu_q, dev.cu_k, lists, None, iws)
+    o = torch.full((1, 4, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((1, 4), 3.0, dtype=torch.float32, device="cuda")
+    for mode in (msa.MSA_KV_OUTER, msa.MSA_Q_OUTER):
+        ws = torch.zeros(max(msa.msa_workspace_size(s, mode), 256), dtype=torch.uint8,
+                         device="cuda")
+        msa.msa_sparse_attn_fwd(s, dev.q, dev.k, dev.v, dev.descale, case.softmax_scale, lists,
+                                dev.cu_q, dev.cu_k, mode, ws, o, lse)
+        msa.msa_combine(s, mode, ws, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(lists == -7) and torch.all(o == 3.0) and torch.all(lse == 3.0)
+
+
 def test_decode_q_outer_splits():
     _say("[decode]")
     cfg = mi.Config(name="dec", batch=6, n_q=(), n_k=(), hq=64, hkv=4, topk=16, dp=64,
