@@ -31,6 +31,7 @@ from synth import msa_inputs as mi    # noqa: E402
 
 PEAK_HBM = 8.0e12            # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15           # dense bf16 MFMA FLOP/s
+PEAK_FP8 = 5.0e15            # dense fp8 MFMA FLOP/s
 KERNEL_SOURCES = ("block_sparse_gqa_amd/csrc/attn_kv.hip", "block_sparse_gqa_amd/csrc/attn_tile.h",
                   "block_sparse_gqa_amd/csrc/msa_device.h")
 
@@ -45,6 +46,10 @@ WORKLOADS = {
                                    "top-16, fp8 e4m3 Q/K/V, bf16 proxies and partials"),
     "decode": ("decode", "MSA decode: 64 requests x 1 query, Nk uniform over multiples of 128 in "
                          "[16384, 131072], Hq=64, Hkv=4, top-16, bf16"),
+    # the same workloads with e4m3 proxies (low-precision index scoring)
+    "m3_fp8_long_i8": ("m3_fp8_long_i8", "long-context fp8 MSA prefill as m3_fp8_long, proxies "
+                                         "fp8 e4m3 with per-tensor scales"),
+    "decode_i8": ("decode_i8", "MSA decode as decode, proxies fp8 e4m3 with per-tensor scales"),
 }
 
 
@@ -89,8 +94,9 @@ def useful_pairs(cfg, cu_q, cu_k, lists_np: np.ndarray, list_q: int) -> tuple[in
 
 def index_work(cfg, cu_q, cu_k) -> tuple[float, float]:
     """(proxy FLOPs, proxy bytes) the index branch must do: 2*dp per (query, group, key) over
-    the keys of every visible block other than the local one; q_idx and those k_idx rows once,
-    plus the lists written."""
+    the keys of every visible block other than the local one; q_idx and those k_idx rows once
+    (eb bytes per element), plus the lists written."""
+    eb = 1.0 if cfg.idx_dtype == "fp8" else 2.0
     flops, kbytes = 0.0, 0.0
     for s in range(len(cu_q) - 1):
         nq = int(cu_q[s + 1] - cu_q[s])
@@ -106,19 +112,20 @@ def index_work(cfg, cu_q, cu_k) -> tuple[float, float]:
             keys = np.full(nq, float(nk - min(128, nk)))         # all but the local block
             kread = nk
         flops += 2.0 * cfg.dp * cfg.hkv * float(np.sum(keys))
-        kbytes += 2.0 * cfg.dp * cfg.hkv * kread
+        kbytes += eb * cfg.dp * cfg.hkv * kread
     tq = int(cu_q[-1])
-    return flops, kbytes + 2.0 * cfg.dp * cfg.hkv * tq + 4.0 * cfg.hkv * cfg.topk * tq
+    return flops, kbytes + eb * cfg.dp * cfg.hkv * tq + 4.0 * cfg.hkv * cfg.topk * tq
 
 
-def roof(ms, bound, amount):
-    """Roofline entry of one kernel: amount = bytes (hbm) or FLOPs (mfma) per call."""
+def roof(ms, bound, amount, peak_mfma=PEAK_BF16):
+    """Roofline entry of one kernel: amount = bytes (hbm) or FLOPs (mfma, against the peak of
+    the contraction's own dtype) per call."""
     t = ms * 1e-3
     if bound == "hbm":
         return {"ms": ms, "bound": "hbm", "achieved": amount / t / 1e9, "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": amount / t / PEAK_HBM, "algorithmic": amount}
-    return {"ms": ms, "bound": "mfma", "achieved": amount / t / 1e12, "peak": PEAK_BF16 / 1e12,
-            "unit": "TFLOP/s", "frac": amount / t / PEAK_BF16, "algorithmic": amount}
+    return {"ms": ms, "bound": "mfma", "achieved": amount / t / 1e12, "peak": peak_mfma / 1e12,
+            "unit": "TFLOP/s", "frac": amount / t / peak_mfma, "algorithmic": amount}
 
 
 class Timer:
@@ -227,6 +234,8 @@ def main():
     up = lambda t: None if t is None else t.contiguous().to(dev)
     q, k, v = up(case.q), up(case.k), up(case.v)
     q_idx, k_idx = up(case.q_idx), up(case.k_idx)
+    idx8 = cfg.idx_dtype == "fp8"
+    idx_descale = torch.tensor(case.idx_descale, dtype=torch.float32, device=dev) if idx8 else None
     cu_q = torch.from_numpy(case.cu_q).to(dev)
     cu_k = torch.from_numpy(case.cu_k).to(dev)
     descale = torch.tensor(case.descale, dtype=torch.float32, device=dev) if dtype else None
@@ -251,8 +260,11 @@ def main():
         rec = (lambda: evs[i].record()) if evs else (lambda: None)
         if evs:
             evs[0].record()
-        if given is None:
+        if given is None and idx8:
+            msa.msa_index_topk_fp8(shape, q_idx, k_idx, idx_descale, cu_q, cu_k, topk, None, iws)
+        elif given is None:
             msa.msa_index_topk(shape, q_idx, k_idx, cu_q, cu_k, topk, None, iws)
+        if given is None:
             if evs:
                 i += 1
                 evs[i].record()
@@ -342,8 +354,9 @@ def main():
     kr = {}
     if given is None:
         ifl, ib = index_work(cfg, case.cu_q, case.cu_k)
-        ridge = PEAK_BF16 / PEAK_HBM
-        kr["index"] = roof(kms["index"], "mfma", ifl) if ifl / ib > ridge else \
+        pk = PEAK_FP8 if cfg.idx_dtype == "fp8" else PEAK_BF16
+        ridge = pk / PEAK_HBM
+        kr["index"] = roof(kms["index"], "mfma", ifl, pk) if ifl / ib > ridge else \
             roof(kms["index"], "hbm", ib)
     if kv:
         e_max = case.total_q * cfg.hkv * cfg.topk

@@ -65,9 +65,10 @@ __device__ __forceinline__ bool beats(float sa, int ia, float sb, int ib) {
   return sa > sb || (sa == sb && ia < ib);
 }
 
+// `scale` turns raw proxy dot products into scores (fp8 proxies: the two descales).
 __device__ __forceinline__ void write_list(int32_t* out_idx, float* out_sc, int topk,
                                            bool has_local, int local, const float* sc,
-                                           const int* id) {
+                                           const int* id, float scale) {
   int base = 0;
   if (has_local) {
     out_idx[0] = local;
@@ -78,7 +79,7 @@ __device__ __forceinline__ void write_list(int32_t* out_idx, float* out_sc, int 
   for (int k = 0; k < kMaxTopK; ++k) {
     if (base + k < topk) {
       out_idx[base + k] = id[k];
-      if (out_sc) out_sc[base + k] = id[k] >= 0 ? sc[k] : kNegInf;
+      if (out_sc) out_sc[base + k] = id[k] >= 0 ? sc[k] * scale : kNegInf;
     }
   }
 }
@@ -92,18 +93,39 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 MFMA on OCP e4m3 operands (scales 2^0): lane l supplies row l % 32 of A (column
+// l % 32 of B) at contraction indices 32 (l / 32) .. +31; the result has the layout of the
+// bf16 32x32 MFMA.
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, f32x16{}, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
 // A workgroup scores one 256-query tile of one group against every block it can see,
 // heavy (late, causal) tiles first. (Splitting long tiles' key ranges over several
 // workgroups, with a merge of the partial lists, measured slower at 32K and 128K keys.)
-template <int DP>
+// FP8: e4m3 proxies ("Sparse Attention", Chapter 4: a scorer on low-precision index vectors),
+// one 8-bit MFMA per 32 x 32 score tile over the whole proxy dim (dp = 32 fills the upper
+// half of the 64-long contraction with zeros); scores are the raw dot products times the two
+// descales, applied where they are written (a positive factor does not change the order).
+template <int DP, bool FP8>
 __global__ __launch_bounds__(256) void index_tile_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score, int hkv, int topk,
-    int causal, int total_q, int total_k, int max_q, int max_k, int one_round) {
-  constexpr int CH = DP / 8;       // 16-byte chunks per proxy key row
-  constexpr int STEPS = DP / 16;   // MFMA k-steps over the proxy dim
+    const void* __restrict__ q_idx_, const void* __restrict__ k_idx_,
+    const float* __restrict__ descale_idx, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_score, int hkv, int topk, int causal, int total_q, int total_k,
+    int max_q, int max_k, int one_round) {
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per proxy element
+  constexpr int CH = DP * EB / 16; // 16-byte chunks per proxy key row
+  constexpr int STEPS = DP / 16;   // bf16 MFMA k-steps over the proxy dim
   constexpr int PER_T = 128 * CH / 256;   // direct-to-LDS loads per thread per block
+  const char* const q_idx = reinterpret_cast<const char*>(q_idx_);
+  const char* const k_idx = reinterpret_cast<const char*>(k_idx_);
   constexpr int NBUF = 4;          // ring of key blocks: three in flight while one is scored
   __shared__ u32x4 kl[NBUF][128 * CH];
 
@@ -134,16 +156,27 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   const int jbeg = 0, jend = tile_blocks(sq, tile, causal);
 
   bf16x8 bq[2][STEPS];
+  i32x8 bq8[2];
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     const int iq = q_wave + qh * 32 + col;
     const bool ok = iq < sq.nq;
-    const uint16_t* qrow = q_idx + ((size_t)(sq.q0 + (ok ? iq : 0)) * hkv + h) * DP;
+    const char* qrow = q_idx + ((size_t)(sq.q0 + (ok ? iq : 0)) * hkv + h) * DP * EB;
+    if constexpr (FP8) {
+      // bytes 32 hf .. 32 hf + 31 of the row (dp = 32: the lanes of half 1 hold zeros)
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (ok && (DP == 64 || hf == 0)) {
+        lo = *reinterpret_cast<const u32x4*>(qrow + 32 * hf);
+        hi = *reinterpret_cast<const u32x4*>(qrow + 32 * hf + 16);
+      }
+      bq8[qh] = cat8(lo, hi);
+    } else {
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4*>(qrow + 16 * st + 8 * hf);
-      bq[qh][st] = as_bf16x8(v);
+      for (int st = 0; st < STEPS; ++st) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = *reinterpret_cast<const u32x4*>(qrow + 32 * st + 16 * hf);
+        bq[qh][st] = as_bf16x8(v);
+      }
     }
   }
 
@@ -159,8 +192,8 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   // swizzle term (row / 2) % CH is the same for all of them.
   const unsigned row0 = (unsigned)tid / CH;
   const unsigned cc0 = ((unsigned)tid % CH) ^ ((row0 >> 1) & (CH - 1));
-  const size_t krow = (size_t)hkv * DP;                 // elements between consecutive keys
-  const uint16_t* const kh = k_idx + (size_t)h * DP + cc0 * 8;
+  const size_t krow = (size_t)hkv * DP * EB;            // bytes between consecutive keys
+  const char* const kh = k_idx + (size_t)h * DP * EB + cc0 * 16;
   auto dma_block = [&](int j) {
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
@@ -185,20 +218,35 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     const int buf = j % NBUF;
 
     f32x16 acc[2][4];
-#pragma unroll
-    for (int st = 0; st < STEPS; ++st) {
-      bf16x8 ka[4];
+    if constexpr (FP8) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const int row = kt * 32 + col;
-        const int cc = 2 * st + hf;
-        ka[kt] = as_bf16x8(kl[buf][row * CH + (cc ^ ((row >> 1) & (CH - 1)))]);
+        const int sw = (row >> 1) & (CH - 1);
+        const int c0 = DP == 64 ? 2 * hf : 0;
+        const u32x4 lo = kl[buf][row * CH + (c0 ^ sw)];
+        const u32x4 hi = kl[buf][row * CH + ((c0 + 1) ^ sw)];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const i32x8 ka = (DP == 64 || hf == 0) ? cat8(lo, hi) : cat8(z, z);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) acc[qh][kt] = mfma_f8(ka, bq8[qh]);
       }
+    } else {
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh)
+      for (int st = 0; st < STEPS; ++st) {
+        bf16x8 ka[4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          acc[qh][kt] = mfma32(ka[kt], bq[qh][st], st == 0 ? f32x16{} : acc[qh][kt]);
+        for (int kt = 0; kt < 4; ++kt) {
+          const int row = kt * 32 + col;
+          const int cc = 2 * st + hf;
+          ka[kt] = as_bf16x8(kl[buf][row * CH + (cc ^ ((row >> 1) & (CH - 1)))]);
+        }
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            acc[qh][kt] = mfma32(ka[kt], bq[qh][st], st == 0 ? f32x16{} : acc[qh][kt]);
+      }
     }
     float mq[2];
 #pragma unroll
@@ -223,8 +271,9 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
 
   if (qvalid) {
     const size_t o = ((size_t)(sq.q0 + il) * hkv + h) * topk;
+    const float scale = FP8 ? descale_idx[0] * descale_idx[1] : 1.f;
     write_list(topk_idx + o, topk_score ? topk_score + o : nullptr, topk, pos >= 0, c, tl.sc,
-               tl.id);
+               tl.id, scale);
   }
 }
 
@@ -235,14 +284,21 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
 // the groups' interleaved proxy-key rows of the same keys together, i.e. one contiguous span
 // of memory (the scan is bound by HBM bandwidth). Dot products on the VALUs; the chunk's list
 // of each group (merged in LDS over the waves sharing the group) goes to the workspace.
-template <int DP>
+template <int DP, bool FP8>
 __global__ __launch_bounds__(256) void index_split_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-    float* __restrict__ part_sc, int32_t* __restrict__ part_id, int hkv, int max_q,
-    int causal, int n_chunks, int chunk_blocks, int total_q, int total_k, int max_k) {
-  constexpr int LPK = DP / 8;      // lanes per key row (16 bytes each)
+    const void* __restrict__ q_idx_, const void* __restrict__ k_idx_,
+    const float* __restrict__ descale_idx, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, float* __restrict__ part_sc, int32_t* __restrict__ part_id,
+    int hkv, int max_q, int causal, int n_chunks, int chunk_blocks, int total_q, int total_k,
+    int max_k) {
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per proxy element
+  constexpr int VPL = 16 / EB;     // proxy elements per lane (16 bytes)
+  constexpr int LPK = DP / VPL;    // lanes per key row
   constexpr int KPI = 64 / LPK;    // keys per wave instruction
+  const char* const q_idx = reinterpret_cast<const char*>(q_idx_);
+  const char* const k_idx = reinterpret_cast<const char*>(k_idx_);
+  // partial scores leave the kernel scaled (fp8: the two descales); the merge compares them
+  const float scale = FP8 ? descale_idx[0] * descale_idx[1] : 1.f;
   __shared__ float lsc[4][kMaxTopK];
   __shared__ int lid[4][kMaxTopK];
 
@@ -261,17 +317,31 @@ __global__ __launch_bounds__(256) void index_split_kernel(
   const int kk = lane / LPK, dc = lane % LPK;
 
   // this wave's best blocks of group h over blocks j0 + sub, j0 + sub + wph, ...
+  // the 16 bytes of a lane as VPL floats (bf16, or e4m3 codes)
+  auto unpack = [](const u32x4& w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (FP8) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+        f[4 * i] = lo[0];
+        f[4 * i + 1] = lo[1];
+        f[4 * i + 2] = hi[0];
+        f[4 * i + 3] = hi[1];
+      } else {
+        f[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    }
+  };
   auto scan = [&](int h, int sub, TopList& tl) {
-    float qv[8];
+    float qv[VPL];
     {
       u32x4 w = {0u, 0u, 0u, 0u};
       if (qvalid)
-        w = *reinterpret_cast<const u32x4*>(q_idx + ((size_t)(sq.q0 + il) * hkv + h) * DP + dc * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qv[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-        qv[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-      }
+        w = *reinterpret_cast<const u32x4*>(q_idx + (((size_t)(sq.q0 + il) * hkv + h) * DP) * EB +
+                                            dc * 16);
+      unpack(w, qv);
     }
     tl.init();
     for (int j = j0 + sub; j < j1; j += wph) {
@@ -284,17 +354,17 @@ __global__ __launch_bounds__(256) void index_split_kernel(
         const int u = j * kBlock + it * KPI + kk;
         u32x4 w = {0u, 0u, 0u, 0u};
         if (u < sq.nk)
-          w = *reinterpret_cast<const u32x4*>(k_idx + ((size_t)(sq.k0 + u) * hkv + h) * DP + dc * 8);
+          w = *reinterpret_cast<const u32x4*>(k_idx + (((size_t)(sq.k0 + u) * hkv + h) * DP) * EB +
+                                              dc * 16);
         kvv[it] = w;
       }
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
+        float kv[VPL];
+        unpack(kvv[it], kv);
         float dot = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dot = fmaf(qv[2 * i], bf16_bits_to_f32(kvv[it][i] & 0xFFFFu), dot);
-          dot = fmaf(qv[2 * i + 1], bf16_bits_to_f32(kvv[it][i] >> 16), dot);
-        }
+        for (int i = 0; i < VPL; ++i) dot = fmaf(qv[i], kv[i], dot);
         dot = group_sum<LPK>(dot);
         const int u = j * kBlock + it * KPI + kk;
         if (u >= sq.nk) dot = kNegInf;
@@ -317,7 +387,7 @@ __global__ __launch_bounds__(256) void index_split_kernel(
         const size_t base = out_base(h);
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k) {
-          part_sc[base + k] = tl.sc[k];
+          part_sc[base + k] = tl.sc[k] * scale;
           part_id[base + k] = tl.id[k];
         }
       }
@@ -352,7 +422,7 @@ __global__ __launch_bounds__(256) void index_split_kernel(
     }
     const size_t base = out_base(h);
     if (id >= 0 && rank < kMaxTopK) {
-      part_sc[base + rank] = sc;
+      part_sc[base + rank] = sc * scale;
       part_id[base + rank] = id;
     }
     // slots past the number of real candidates are empty
@@ -442,8 +512,9 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
   }
   if (lane == 0) {
     const size_t o = ((size_t)(sq.q0 + il) * hkv + h) * topk;
+    // (the chunk lists' scores are already scaled)
     write_list(topk_idx + o, topk_score ? topk_score + o : nullptr, topk, has_local, c, out_sc,
-               out_id);
+               out_id, 1.f);
   }
 }
 
@@ -473,30 +544,54 @@ static hipError_t launch_index_merge(const msa_shape& s, const float* part_sc,
   return hipGetLastError();
 }
 
-hipError_t launch_index_tile(const msa_shape& s, const void* q_idx, const void* k_idx,
-                             const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
-                             float* topk_score, hipStream_t st) {
+template <int DP, bool FP8>
+static void launch_tile_t(const msa_shape& s, dim3 grid, const void* q_idx, const void* k_idx,
+                          const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
+                          int32_t* topk_idx, float* topk_score, int one_round, hipStream_t st) {
+  hipLaunchKernelGGL((index_tile_kernel<DP, FP8>), grid, dim3(256), 0, st, q_idx, k_idx,
+                     descale_idx, cu_q, cu_k, topk_idx, topk_score, s.hkv, s.topk, s.causal,
+                     s.total_q, s.total_k, s.max_q, s.max_k, one_round);
+}
+
+hipError_t launch_index_tile(const msa_shape& s, bool fp8, const void* q_idx, const void* k_idx,
+                             const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
+                             int32_t* topk_idx, float* topk_score, hipStream_t st) {
   const int tiles = (s.max_q + kIndexTileQ - 1) / kIndexTileQ;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, s.hkv, s.batch);
   const int one_round = (int64_t)tiles * s.hkv * s.batch <= 2 * (int64_t)device_cu_count();
-  if (s.dp == 64) {
-    hipLaunchKernelGGL(index_tile_kernel<64>, grid, dim3(256), 0, st,
-                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
-                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k, s.max_q,
-                       s.max_k, one_round);
+  if (fp8) {
+    if (s.dp == 64)
+      launch_tile_t<64, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
+                              topk_score, one_round, st);
+    else
+      launch_tile_t<32, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
+                              topk_score, one_round, st);
   } else {
-    hipLaunchKernelGGL(index_tile_kernel<32>, grid, dim3(256), 0, st,
-                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, topk_idx,
-                       topk_score, s.hkv, s.topk, s.causal, s.total_q, s.total_k, s.max_q,
-                       s.max_k, one_round);
+    if (s.dp == 64)
+      launch_tile_t<64, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
+                               topk_score, one_round, st);
+    else
+      launch_tile_t<32, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
+                               topk_score, one_round, st);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_index_split(const msa_shape& s, const void* q_idx, const void* k_idx,
-                              const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
-                              float* topk_score, void* ws, hipStream_t st) {
+template <int DP, bool FP8>
+static void launch_split_t(const msa_shape& s, dim3 grid, const void* q_idx, const void* k_idx,
+                           const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
+                           float* part_sc, int32_t* part_id, int n_chunks, int cb,
+                           hipStream_t st) {
+  hipLaunchKernelGGL((index_split_kernel<DP, FP8>), grid, dim3(256), 0, st, q_idx, k_idx,
+                     descale_idx, cu_q, cu_k, part_sc, part_id, s.hkv, s.max_q, s.causal,
+                     n_chunks, cb, s.total_q, s.total_k, s.max_k);
+}
+
+hipError_t launch_index_split(const msa_shape& s, bool fp8, const void* q_idx,
+                              const void* k_idx, const float* descale_idx, const int32_t* cu_q,
+                              const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
+                              void* ws, hipStream_t st) {
   if (s.max_q == 0) return hipSuccess;
   const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
   const int cb = split_index_chunk(nb_max);
@@ -506,16 +601,20 @@ hipError_t launch_index_split(const msa_shape& s, const void* q_idx, const void*
   int32_t* part_id = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + n * 4);
   if (n_chunks > 0) {
     dim3 grid(n_chunks, s.batch * s.max_q);
-    if (s.dp == 64) {
-      hipLaunchKernelGGL(index_split_kernel<64>, grid, dim3(256), 0, st,
-                         (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, part_sc,
-                         part_id, s.hkv, s.max_q, s.causal, n_chunks, cb, s.total_q,
-                         s.total_k, s.max_k);
+    if (fp8) {
+      if (s.dp == 64)
+        launch_split_t<64, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
+                                 part_id, n_chunks, cb, st);
+      else
+        launch_split_t<32, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
+                                 part_id, n_chunks, cb, st);
     } else {
-      hipLaunchKernelGGL(index_split_kernel<32>, grid, dim3(256), 0, st,
-                         (const uint16_t*)q_idx, (const uint16_t*)k_idx, cu_q, cu_k, part_sc,
-                         part_id, s.hkv, s.max_q, s.causal, n_chunks, cb, s.total_q,
-                         s.total_k, s.max_k);
+      if (s.dp == 64)
+        launch_split_t<64, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
+                                  part_id, n_chunks, cb, st);
+      else
+        launch_split_t<32, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
+                                  part_id, n_chunks, cb, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -258,10 +258,10 @@ msa_status msa_index_workspace_size(const msa_shape* shape, size_t* bytes) {
   return MSA_OK;
 }
 
-msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx,
-                          const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
-                          float* topk_score, void* workspace, size_t ws_bytes,
-                          hipStream_t stream) {
+static msa_status index_topk(const msa_shape* shape, bool fp8, const void* q_idx,
+                             const void* k_idx, const float* descale_idx, const int32_t* cu_q,
+                             const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
   msa_status st = check_shape(shape);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
@@ -270,6 +270,7 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
   if (!cu_q || !cu_k || !topk_idx) return MSA_ERR_NULL;
   if (s.total_q > 0 && !q_idx) return MSA_ERR_NULL;
   if (s.total_k > 0 && !k_idx) return MSA_ERR_NULL;
+  if (fp8 && !descale_idx) return MSA_ERR_NULL;
   hipError_t e;
   if (s.max_q <= kSplitIndexMaxQ) {
     // key chunks merged by one wave per (query, group): at most 512 per query
@@ -277,15 +278,33 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
     if ((int64_t)s.batch * s.max_q > 65535) return MSA_ERR_SHAPE;      // grid y of the split kernel
     const size_t need = index_workspace_bytes(s);
     if (!workspace || ws_bytes < need) return MSA_ERR_WORKSPACE;
-    e = launch_index_split(s, q_idx, k_idx, cu_q, cu_k, topk_idx, topk_score, workspace, stream);
+    e = launch_index_split(s, fp8, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score,
+                           workspace, stream);
   } else {
-    e = launch_index_tile(s, q_idx, k_idx, cu_q, cu_k, topk_idx, topk_score, stream);
+    e = launch_index_tile(s, fp8, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score,
+                          stream);
   }
   if (e != hipSuccess) {
     fail_launch(e);
     return MSA_ERR_LAUNCH;
   }
   return MSA_OK;
+}
+
+msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                          const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                          float* topk_score, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  return index_topk(shape, false, q_idx, k_idx, nullptr, cu_q, cu_k, topk_idx, topk_score,
+                    workspace, ws_bytes, stream);
+}
+
+msa_status msa_index_topk_fp8(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                              const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
+                              int32_t* topk_idx, float* topk_score, void* workspace,
+                              size_t ws_bytes, hipStream_t stream) {
+  return index_topk(shape, true, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score,
+                    workspace, ws_bytes, stream);
 }
 
 static msa_status prep(const msa_shape* shape, msa_mode mode, const void* workspace,

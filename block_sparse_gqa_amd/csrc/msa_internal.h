@@ -81,12 +81,14 @@ Layout layout(const msa_shape& s, msa_mode mode);
 size_t index_workspace_bytes(const msa_shape& s);
 
 // ----- launchers (return hipSuccess or the launch error)
-hipError_t launch_index_tile(const msa_shape& s, const void* q_idx, const void* k_idx,
-                             const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
-                             float* topk_score, hipStream_t st);
-hipError_t launch_index_split(const msa_shape& s, const void* q_idx, const void* k_idx,
-                              const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
-                              float* topk_score, void* ws, hipStream_t st);
+// fp8: e4m3 proxies with device descales descale_idx[0] (q_idx), [1] (k_idx)
+hipError_t launch_index_tile(const msa_shape& s, bool fp8, const void* q_idx, const void* k_idx,
+                             const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
+                             int32_t* topk_idx, float* topk_score, hipStream_t st);
+hipError_t launch_index_split(const msa_shape& s, bool fp8, const void* q_idx,
+                              const void* k_idx, const float* descale_idx, const int32_t* cu_q,
+                              const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
+                              void* ws, hipStream_t st);
 
 hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
                        const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k,

@@ -22,7 +22,8 @@ MSA_AUTO, MSA_KV_OUTER, MSA_Q_OUTER = 0, 1, 2
 
 SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace_size",
            "msa_resolve_mode", "msa_crossover", "msa_status_string", "msa_last_error",
-           "msa_index_topk", "msa_sparse_attn_fwd", "msa_plan", "msa_attn_main", "msa_combine")
+           "msa_index_topk", "msa_index_topk_fp8", "msa_sparse_attn_fwd", "msa_plan",
+           "msa_attn_main", "msa_combine")
 
 
 class Shape(ctypes.Structure):
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
             "msa_resolve_mode": [sp, i32, ctypes.POINTER(i32)],
             "msa_crossover": [sp, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)],
             "msa_index_topk": [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "msa_index_topk_fp8": [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_sparse_attn_fwd": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, i32, vp, sz,
                                     vp, vp, vp],
             "msa_plan": [sp, vp, vp, vp, vp, sz, vp],
@@ -156,6 +158,14 @@ def msa_index_topk(shape, q_idx, k_idx, cu_q, cu_k, topk_idx, topk_score=None, w
     _check(lib().msa_index_topk(ctypes.byref(shape), _p(q_idx), _p(k_idx), _p(cu_q), _p(cu_k),
                                 _p(topk_idx), _p(topk_score), _p(workspace), _nbytes(workspace),
                                 _stream(stream)), "msa_index_topk")
+
+
+def msa_index_topk_fp8(shape, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score=None,
+                       workspace=None, stream=None) -> None:
+    _check(lib().msa_index_topk_fp8(ctypes.byref(shape), _p(q_idx), _p(k_idx), _p(descale_idx),
+                                    _p(cu_q), _p(cu_k), _p(topk_idx), _p(topk_score),
+                                    _p(workspace), _nbytes(workspace), _stream(stream)),
+           "msa_index_topk_fp8")
 
 
 def msa_sparse_attn_fwd(shape, q, k, v, descale_qkv, softmax_scale, topk_idx, cu_q, cu_k, mode,

@@ -7,6 +7,7 @@
  * selected blocks. This library runs the three steps as separate calls:
  *
  *   msa_index_topk       index branch: max-pooled proxy scores + top-K, local block forced
+ *   msa_index_topk_fp8   the same on fp8 e4m3 proxies (8-bit MFMA scoring)
  *   msa_sparse_attn_fwd  main branch: KV-outer partials (or Q-outer output) over the lists
  *   msa_combine          log-sum-exp merge of the per-slot partials into O and LSE
  *
@@ -168,6 +169,20 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
                           const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
                           float* topk_score, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
+
+/* Low-precision index scoring ("Sparse Attention", Chapter 4: a scorer that compares
+ * quantised index vectors, token by token, and keeps each block's largest score; the pages
+ * use 4-bit inputs, this call OCP fp8 e4m3fn). The same selection, arguments, workspace and
+ * errors as msa_index_topk, except:
+ *  - q_idx and k_idx hold e4m3fn codes; descale_idx is a DEVICE float[2] with their positive
+ *    per-tensor descales (proxy value = code * descale), NULL: MSA_ERR_NULL.
+ *  - Each proxy dot product is the exact products of the codes summed in fp32 (an 8-bit MFMA
+ *    per 32 x 32 score tile for prefill); block scores, and topk_score, are max(q.k) times
+ *    descale_idx[0] * descale_idx[1]. */
+msa_status msa_index_topk_fp8(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                              const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
+                              int32_t* topk_idx, float* topk_score, void* workspace,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* Main branch ("Kernel optimization ...", summary and section 2; "Sparse Attention",
  * Chapters 1 and 5). Every query head attends, with its own softmax, to the union of the

@@ -54,8 +54,12 @@ def run(case: Case, rows: np.ndarray | None = None, lists: np.ndarray | None = N
     q = widen(case.q, dq)
     k = widen(case.k, dk)
     v = widen(case.v, dv)
-    qi = widen(case.q_idx) if case.q_idx is not None else None
-    ki = widen(case.k_idx) if case.k_idx is not None else None
+    # proxies: bf16, or e4m3 codes times their per-tensor descale ("Sparse Attention",
+    # Chapter 4: the low-precision scorer compares quantised index vectors; the selection rule
+    # is unchanged)
+    dqi, dki = case.idx_descale
+    qi = widen(case.q_idx, dqi) if case.q_idx is not None else None
+    ki = widen(case.k_idx, dki) if case.k_idx is not None else None
     out_rows, out_sel, out_s, out_o, out_l = [], [], [], [], []
     for s, q0, q1, k0, k1, loc in seq_rows(case, rows):
         if loc.size == 0:

@@ -118,7 +118,8 @@ class Config:
     topk: int = 16
     dp: int = 64
     causal: bool = True
-    dtype: str = "bf16"     # "bf16" or "fp8" for Q/K/V; proxies are always bf16
+    dtype: str = "bf16"     # "bf16" or "fp8" for Q/K/V
+    idx_dtype: str = "bf16"  # "bf16" or "fp8" (e4m3fn, per-tensor scale) for the proxies
     lowrank: bool = False   # rank-8 per-group bias giving block reuse
     list_q: int = 1         # 1: per-query selection by the index branch; 128: given per-tile lists
     list_pool: int = 0      # per-tile lists: blocks drawn from range(list_pool)
@@ -152,6 +153,11 @@ CONFIGS = {
     # decode: 64 requests x 1 query, key lengths uniform over multiples of 128 in [16K, 128K]
     "decode": Config(name="decode", batch=64, n_q=(), n_k=(), hq=64, hkv=4, topk=16, dp=64,
                      length_seed_draw=(64, 128, 1024)),
+    # the same two workloads with the proxies quantised to fp8 e4m3 (low-precision scoring)
+    "m3_fp8_long_i8": _cfg("m3_fp8_long_i8", 131072, 131072, hq=64, hkv=4, topk=16, dp=64,
+                           lowrank=True, dtype="fp8", idx_dtype="fp8"),
+    "decode_i8": Config(name="decode_i8", batch=64, n_q=(), n_k=(), hq=64, hkv=4, topk=16, dp=64,
+                        length_seed_draw=(64, 128, 1024), idx_dtype="fp8"),
 }
 
 
@@ -180,11 +186,12 @@ class Case:
     k: torch.Tensor             # [Tk, Hkv, D]
     v: torch.Tensor             # [Tk, Hkv, D]
     descale: tuple              # (dq, dk, dv); (1,1,1) for bf16
-    q_idx: Optional[torch.Tensor] = None   # [Tq, Hkv, dp] bf16
-    k_idx: Optional[torch.Tensor] = None   # [Tk, Hkv, dp] bf16
+    q_idx: Optional[torch.Tensor] = None   # [Tq, Hkv, dp] bf16 or float8_e4m3fn
+    k_idx: Optional[torch.Tensor] = None   # [Tk, Hkv, dp]
     lists: Optional[np.ndarray] = None     # [Tq/list_q, Hkv, K] int32 for given lists
     softmax_scale: float = 0.0
     meta: dict = field(default_factory=dict)
+    idx_descale: tuple = (1.0, 1.0)        # (descale of q_idx, of k_idx); (1, 1) for bf16
 
     @property
     def total_q(self) -> int:
@@ -284,6 +291,7 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
     if with_proxies is None:
         with_proxies = cfg.list_q == 1
     q_idx = k_idx = None
+    idx_descale = (1.0, 1.0)
     if with_proxies:
         if cfg.proxy == "grid":
             qi = grid_f32(_stream(seed, "q_idx"), (tq, hkv, dp))
@@ -296,7 +304,14 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
                 up = _lowrank_factors(ssp[0], hkv, dp)
                 _add_lowrank(qi, "q", cu_q, up, ssp[1], 1, cfg.block)
                 _add_lowrank(ki, "k", cu_k, up, ssp[2], 1, cfg.block)
-        q_idx, k_idx = to_bf16(qi), to_bf16(ki)
+        if cfg.idx_dtype == "fp8":
+            q_idx, dqi = to_fp8(qi)
+            k_idx, dki = to_fp8(ki)
+            idx_descale = (dqi, dki)
+        elif cfg.idx_dtype == "bf16":
+            q_idx, k_idx = to_bf16(qi), to_bf16(ki)
+        else:
+            raise ValueError(f"unknown idx_dtype {cfg.idx_dtype}")
 
     lists = None
     if cfg.list_q > 1:
@@ -304,7 +319,7 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
 
     return Case(cfg=cfg, seed=seed, cu_q=cu_q, cu_k=cu_k, q=qs, k=ks, v=vs, descale=descale,
                 q_idx=q_idx, k_idx=k_idx, lists=lists,
-                softmax_scale=1.0 / math.sqrt(d))
+                softmax_scale=1.0 / math.sqrt(d), idx_descale=idx_descale)
 
 
 def tile_lists(cfg: Config, cu_q: np.ndarray, seed: int) -> np.ndarray:

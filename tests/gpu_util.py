@@ -22,6 +22,7 @@ class Dev:
     cu_k: torch.Tensor
     lists: torch.Tensor | None
     descale: torch.Tensor | None
+    idx_descale: torch.Tensor | None = None   # fp8 proxies: device [descale q_idx, k_idx]
 
 
 def upload(case: Case, device="cuda") -> Dev:
@@ -31,9 +32,13 @@ def upload(case: Case, device="cuda") -> Dev:
     ds = None
     if case.cfg.dtype == "fp8":
         ds = torch.tensor(case.descale, dtype=torch.float32, device=device)
+    ids = None
+    if case.cfg.idx_dtype == "fp8":
+        ids = torch.tensor(case.idx_descale, dtype=torch.float32, device=device)
     return Dev(q=up(case.q), k=up(case.k), v=up(case.v), q_idx=up(case.q_idx),
                k_idx=up(case.k_idx), cu_q=torch.from_numpy(case.cu_q).to(device),
-               cu_k=torch.from_numpy(case.cu_k).to(device), lists=lists, descale=ds)
+               cu_k=torch.from_numpy(case.cu_k).to(device), lists=lists, descale=ds,
+               idx_descale=ids)
 
 
 def shape_of(case: Case, list_q=None) -> msa.Shape:
@@ -45,13 +50,29 @@ def shape_of(case: Case, list_q=None) -> msa.Shape:
                           list_q=c.list_q if list_q is None else list_q)
 
 
+def run_index(case: Case, dev: Dev, s, topk, score, ws) -> None:
+    """The index branch for the case's proxy type (bf16, or fp8 with its descales)."""
+    if case.cfg.idx_dtype == "fp8":
+        msa.msa_index_topk_fp8(s, dev.q_idx, dev.k_idx, dev.idx_descale, dev.cu_q, dev.cu_k,
+                               topk, score, ws)
+    else:
+        msa.msa_index_topk(s, dev.q_idx, dev.k_idx, dev.cu_q, dev.cu_k, topk, score, ws)
+
+
+def proxies(case: Case) -> tuple[np.ndarray, np.ndarray]:
+    """The proxies' exact values as float64 (fp8 codes times their descales)."""
+    from synth.msa_inputs import widen
+    dqi, dki = case.idx_descale
+    return widen(case.q_idx, dqi), widen(case.k_idx, dki)
+
+
 def gpu_index(case: Case, dev: Dev):
     s = shape_of(case)
     topk = torch.full((case.total_q, case.cfg.hkv, case.cfg.topk), -7, dtype=torch.int32,
                       device="cuda")
     score = torch.full(topk.shape, float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(msa.msa_index_workspace_size(s), 256), dtype=torch.uint8, device="cuda")
-    msa.msa_index_topk(s, dev.q_idx, dev.k_idx, dev.cu_q, dev.cu_k, topk, score, ws)
+    run_index(case, dev, s, topk, score, ws)
     torch.cuda.synchronize()
     return topk.cpu().numpy(), score.cpu().numpy()
 
@@ -75,11 +96,21 @@ def gpu_attention(case: Case, dev: Dev, lists: torch.Tensor, mode: int, list_q=N
     return out
 
 
-def near_tie_bound(qi: np.ndarray, ki: np.ndarray) -> float:
-    """Twice the fp32 summation error bound gamma_dp * sum |q_d k_d| (Higham), using
-    |q|_2 * max_u |k_u|_2 >= sum_d |q_d k_ud|, for one (query, group)."""
+# Error of one e4m3 proxy dot product on the 8-bit MFMA, relative to sum_d |q_d k_d|: the
+# products are summed in aligned groups of 8, each aligned to its largest product's exponent E
+# with the bits below 2^(E - 13) dropped (measured on the MI355X: of 448 + 63 x 2^-s, the 7
+# small terms sharing the large term's group vanish for s >= 6 and stay for s <= 5), so each
+# of the 7 other products of a group loses less than 2^-13 of the group's largest; the 8
+# group sums and the descale product add fp32 roundings.
+FP8_DOT_REL = 7 * 2.0 ** -13 + 10 * 2.0 ** -24
+
+
+def near_tie_bound(qi: np.ndarray, ki: np.ndarray, fp8: bool = False) -> float:
+    """Twice the error bound of one proxy dot product for one (query, group), as a multiple of
+    |q|_2 * max_u |k_u|_2 >= sum_d |q_d k_ud|: bf16 proxies, fp32 summation gamma_dp (Higham);
+    fp8 proxies, FP8_DOT_REL."""
     dp = qi.shape[-1]
-    gamma = dp * 2.0 ** -24 / (1 - dp * 2.0 ** -24)
+    gamma = FP8_DOT_REL if fp8 else dp * 2.0 ** -24 / (1 - dp * 2.0 ** -24)
     return 2 * gamma * float(np.linalg.norm(qi)) * float(np.max(np.linalg.norm(ki, axis=-1)))
 
 

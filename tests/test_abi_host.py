@@ -103,6 +103,8 @@ def test_bad_shapes_are_rejected_by_every_entry_point(L, name, kw, status):
     fake = ctypes.c_void_p(0x1000)
     assert L.msa_index_topk(ctypes.byref(s), fake, fake, fake, fake, fake, None, None, 0,
                             None) == status
+    assert L.msa_index_topk_fp8(ctypes.byref(s), fake, fake, fake, fake, fake, fake, None, None,
+                                0, None) == status
     assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
                                  msa.MSA_AUTO, fake, 1 << 40, fake, None, None) == status
     assert L.msa_combine(ctypes.byref(s), msa.MSA_AUTO, fake, 1 << 40, fake, None,
@@ -131,6 +133,11 @@ def test_null_device_pointers_and_small_workspace(L):
     s_dp = m3_shape(dp=48)
     assert L.msa_index_topk(ctypes.byref(s_dp), fake, fake, fake, fake, fake, None, None, 0,
                             None) == msa.MSA_ERR_SHAPE
+    # fp8 proxies: the descales are required
+    assert L.msa_index_topk_fp8(ctypes.byref(s), fake, fake, None, fake, fake, fake, None, None,
+                                0, None) == msa.MSA_ERR_NULL
+    assert L.msa_index_topk_fp8(ctypes.byref(s_dp), fake, fake, fake, fake, fake, fake, None,
+                                None, 0, None) == msa.MSA_ERR_SHAPE
     # main branch: workspace checks come first, then pointers
     assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
                                  msa.MSA_AUTO, fake, need - 1, fake, None,

@@ -13,9 +13,8 @@ import torch
 from block_sparse_gqa_amd import msa
 from oracle import msa_case
 from synth import msa_inputs as mi
-from synth.msa_inputs import widen
 
-from gpu_util import compare_lists, err_stats, near_tie_bound, shape_of, upload
+from gpu_util import compare_lists, err_stats, near_tie_bound, proxies, run_index, shape_of, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +34,7 @@ def bench_sequence(case, dev):
         lists = torch.full((case.total_q, c.hkv, c.topk), -7, dtype=torch.int32, device="cuda")
         iws = torch.empty(max(msa.msa_index_workspace_size(s), 256), dtype=torch.uint8,
                           device="cuda")
-        msa.msa_index_topk(s, dev.q_idx, dev.k_idx, dev.cu_q, dev.cu_k, lists, None, iws)
+        run_index(case, dev, s, lists, None, iws)
     else:
         lists = dev.lists
     ws = torch.empty(msa.msa_workspace_size(s, chosen), dtype=torch.uint8, device="cuda")
@@ -98,7 +97,7 @@ def compare(case, lists, rows, out, o_s, lse_s):
     if case.lists is None:
         check_list_properties(case, lists)
         seq_of = np.searchsorted(case.cu_q, rows, side="right") - 1
-        qi, ki = widen(case.q_idx), widen(case.k_idx)
+        qi, ki = proxies(case)
 
         seqs = np.unique(seq_of)          # the oracle keeps scores of sampled sequences only
 
@@ -111,7 +110,8 @@ def compare(case, lists, rows, out, o_s, lse_s):
 
         def bound(n, g):
             s = seq_of[n]
-            return near_tie_bound(qi[rows[n], g], ki[case.cu_k[s]:case.cu_k[s + 1], g])
+            return near_tie_bound(qi[rows[n], g], ki[case.cu_k[s]:case.cu_k[s + 1], g],
+                                  case.cfg.idx_dtype == "fp8")
 
         got = lists[rows]
         n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, bound)
@@ -135,6 +135,13 @@ def test_m3_prefill_32k():
 
 def test_fp8_prefill_128k():
     case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long", every=256)
+    assert chosen == msa.MSA_KV_OUTER
+    compare(case, lists, rows, out, o_s, lse_s)
+
+
+def test_fp8_proxies_prefill_128k():
+    """The 128K fp8 workload with its proxies quantised to e4m3 too (8-bit MFMA scoring)."""
+    case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long_i8", every=256)
     assert chosen == msa.MSA_KV_OUTER
     compare(case, lists, rows, out, o_s, lse_s)
 

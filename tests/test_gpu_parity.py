@@ -16,7 +16,7 @@ from synth import msa_inputs as mi
 from synth.msa_inputs import widen
 
 from gpu_util import (compare_lists, err_stats, gpu_attention, gpu_index, near_tie_bound,
-                      shape_of, upload)
+                      proxies, shape_of, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,12 +39,13 @@ def _oracle_index_scores(case):
 
 
 def _bound_fn(case):
-    qi, ki = widen(case.q_idx), widen(case.k_idx)
+    qi, ki = proxies(case)
     seq_of = np.searchsorted(case.cu_q, np.arange(case.total_q), side="right") - 1
 
     def bound(i, g):
         s = seq_of[i]
-        return near_tie_bound(qi[i, g], ki[case.cu_k[s]:case.cu_k[s + 1], g])
+        return near_tie_bound(qi[i, g], ki[case.cu_k[s]:case.cu_k[s + 1], g],
+                              case.cfg.idx_dtype == "fp8")
     return bound
 
 
@@ -97,6 +98,46 @@ def test_index_topk_gaussian_certified(cfgname):
     n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _bound_fn(case))
     _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
     assert not bad, f"uncertified list differences at {bad[:5]}"
+
+
+FP8_INDEX_CASES = [
+    # prefill tiles: dp = 64 with block reuse, ragged, causal
+    ("tile_dp64", dict(n_q=(1024, 300), n_k=(1024, 2000), hq=8, hkv=2, topk=8, dp=64,
+                       lowrank=True)),
+    # dp = 32 (zero-filled upper half of the 64-long contraction), non-causal
+    ("tile_dp32_noncausal", dict(n_q=(700,), n_k=(3000,), hq=4, hkv=2, topk=6, dp=32,
+                                 causal=False)),
+    # short-query (key-split) path
+    ("split_dp64", dict(n_q=(1, 3), n_k=(5000, 20000), hq=8, hkv=2, topk=16, dp=64)),
+    ("split_dp32_noncausal", dict(n_q=(4, 16), n_k=(3000, 7000), hq=8, hkv=4, topk=10, dp=32,
+                                  causal=False)),
+]
+
+
+@pytest.mark.parametrize("name,kw", FP8_INDEX_CASES, ids=[c[0] for c in FP8_INDEX_CASES])
+def test_index_topk_fp8_proxies_certified(name, kw):
+    """e4m3 proxies: lists equal the oracle's on the dequantised proxies up to certified
+    near-ties; reported scores are the oracle's block maxima within the fp32 summation bound."""
+    _say(f"[index fp8 proxies] {name}")
+    case = mi.make_case(mi.custom(name=name, idx_dtype="fp8", **kw), seed=2)
+    got, got_sc = gpu_index(case, upload(case))
+    out, scores = _oracle_index_scores(case)
+    bound = _bound_fn(case)
+    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, bound)
+    _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
+    assert not bad, f"uncertified list differences at {bad[:5]}"
+    n_checked = 0
+    for i in range(0, case.total_q, 7):
+        for g in range(case.cfg.hkv):
+            for k, b in enumerate(got[i, g]):
+                want = scores(i, g)[b] if b >= 0 else -np.inf
+                if not np.isfinite(want):
+                    assert got_sc[i, g, k] == want
+                    continue
+                tol = bound(i, g) / 2 + 2.0 ** -22 * abs(want)    # one dot product's bound
+                assert abs(got_sc[i, g, k] - want) <= tol, (i, g, k, got_sc[i, g, k], want)
+                n_checked += 1
+    assert n_checked > 0
 
 
 # ------------------------------------------------------------------ whole layer

@@ -91,3 +91,28 @@ def test_case_oracle_tile_lists():
             e = sdpa(qq, k[keys, h:h + 1], v[keys, h:h + 1], np.ones((128, keys.size), bool),
                      case.softmax_scale)
             np.testing.assert_allclose(out.o[t * 128:(t + 1) * 128, h:h + 1], e, atol=1e-12)
+
+
+def test_fp8_proxies_from_the_same_draws_and_scale_invariant():
+    """e4m3 proxies: codes within +-448 with descale amax / 448, drawn from the same numbers as
+    the bf16 proxies of the same seed; the oracle's selection on the dequantised proxies is
+    the selection on the codes alone (a positive factor keeps the order) and its block scores
+    are the codes' scores times the two descales."""
+    kw = dict(n_q=(300,), n_k=(700,), hq=4, hkv=2, topk=5, dp=32)
+    case = mi.make_case(mi.custom(name="p8", idx_dtype="fp8", **kw), seed=3)
+    bf = mi.make_case(mi.custom(name="p8", **kw), seed=3)
+    assert case.q_idx.dtype == torch.float8_e4m3fn and case.k_idx.dtype == torch.float8_e4m3fn
+    dqi, dki = case.idx_descale
+    for t8, t16, d in ((case.q_idx, bf.q_idx, dqi), (case.k_idx, bf.k_idx, dki)):
+        c = mi.widen(t8)
+        assert np.max(np.abs(c)) == 448.0                 # amax maps to the largest code
+        a8, a16 = c * d, mi.widen(t16)
+        # e4m3 keeps 3 fraction bits (subnormal step 2^-9 x descale), bf16 7
+        assert np.all(np.abs(a8 - a16) <= 2.0 ** -4 * np.abs(a16) + 2.0 ** -9 * d)
+    out = msa_case.run(case, want_output=False)
+    case.idx_descale = (1.0, 1.0)
+    out1 = msa_case.run(case, want_output=False)
+    assert np.array_equal(out.topk_idx, out1.topk_idx)
+    fin = np.isfinite(out1.scores[0])
+    assert np.array_equal(np.isfinite(out.scores[0]), fin)
+    np.testing.assert_allclose(out.scores[0][fin], out1.scores[0][fin] * dqi * dki, rtol=1e-12)
