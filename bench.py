@@ -46,6 +46,11 @@ WORKLOADS = {
                                    "top-16, fp8 e4m3 Q/K/V, bf16 proxies and partials"),
     "decode": ("decode", "MSA decode: 64 requests x 1 query, Nk uniform over multiples of 128 in "
                          "[16384, 131072], Hq=64, Hkv=4, top-16, bf16"),
+    # R1 / R4 selector -> per-tile attention ("Sparse Attention", Chapter 4 benchmark shape)
+    "sel_r1": ("sel_r1", "R1 selector + per-tile block-sparse fwd: B=2, 4096 queries, 16384 keys, "
+                         "non-causal, Hq=16, Hkv=1, 16 blocks per Q128 tile, bf16"),
+    "sel_r4": ("sel_r4", "R4 selector + per-tile block-sparse fwd: B=2, 4096 queries, 16384 keys, "
+                         "non-causal, Hq=16, Hkv=1, 16 blocks per Q128 tile, bf16"),
     # the same workloads with e4m3 proxies (low-precision index scoring)
     "m3_fp8_long_i8": ("m3_fp8_long_i8", "long-context fp8 MSA prefill as m3_fp8_long, proxies "
                                          "fp8 e4m3 with per-tensor scales"),
@@ -162,6 +167,21 @@ def cpu_baseline(case, budget_s: float) -> dict:
     rng = np.random.default_rng(0)
     blocks = rng.permutation(max(1, nqb))
     t0 = time.perf_counter()
+    what = "index branch"
+    if case.cfg.selector:
+        # the selector oracle over every tile (its time counted), then the lists it chose
+        from oracle import selectors
+        from synth.msa_inputs import widen
+        c = case.cfg
+        q, k = widen(case.q), widen(case.k)
+        case.lists = np.full(((len(case.cu_q) - 1) * nqb, c.hkv, c.topk), -1, dtype=np.int32)
+        for s in range(len(case.cu_q) - 1):
+            q0, q1, k0, k1 = case.cu_q[s], case.cu_q[s + 1], case.cu_k[s], case.cu_k[s + 1]
+            lst, _ = selectors.select_tiles(q[q0:q1], k[k0:k1], c.selector, 128,
+                                            c.hq // c.hkv, c.topk, c.causal)
+            case.lists[s * nqb:s * nqb + lst.shape[0]] = lst
+        del q, k
+        what = f"R{case.cfg.selector} selector over every tile"
     for b in blocks:
         rows = np.arange(b * 128, min(case.total_q, (b + 1) * 128))
         if case.cfg.length_seed_draw is not None:      # decode: one query per request
@@ -182,7 +202,7 @@ def cpu_baseline(case, budget_s: float) -> dict:
     return {"value": flops / max(t_used, 1e-9) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n_rows} query rows ({len(rows_done)} groups of whole 128-query blocks, "
-                      f"all heads) of the same workload, index branch + sparse attention, "
+                      f"all heads) of the same workload, {what} + sparse attention, "
                       f"fp64 NumPy, {t_used:.1f} s wall on {platform.processor() or 'host'}"}
 
 
@@ -240,10 +260,14 @@ def main():
     cu_k = torch.from_numpy(case.cu_k).to(dev)
     descale = torch.tensor(case.descale, dtype=torch.float32, device=dev) if dtype else None
     given = torch.from_numpy(case.lists).to(dev) if case.lists is not None else None
-    n_lists = case.total_q
+    sel = cfg.selector                         # per-tile lists from the R1 / R4 selector
+    n_lists = case.total_q if cfg.list_q == 1 else (len(case.cu_q) - 1) * -(-case.max_q // 128)
     topk = given if given is not None else torch.empty((n_lists, cfg.hkv, cfg.topk),
                                                       dtype=torch.int32, device=dev)
-    iws = torch.empty(max(msa.msa_index_workspace_size(shape) if given is None else 0, 256),
+    iws = torch.empty(max(msa.msa_index_workspace_size(shape)
+                          if given is None and not sel else 0, 256), dtype=torch.uint8,
+                      device=dev)
+    sws = torch.empty(msa.msa_select_workspace_size(shape, sel) if sel else 256,
                       dtype=torch.uint8, device=dev)
     ws = torch.empty(msa.msa_workspace_size(shape, chosen), dtype=torch.uint8, device=dev)
     o = torch.empty((case.total_q, cfg.hq, 128), dtype=torch.bfloat16, device=dev)
@@ -251,8 +275,8 @@ def main():
     scale = case.softmax_scale
 
     kv = chosen == msa.MSA_KV_OUTER
-    names = (["index"] if given is None else []) + (["plan", "attn_main"] if kv else ["attn_q"]) \
-        + ["combine"]
+    first = (["select"] if sel else ["index"]) if given is None else []
+    names = first + (["plan", "attn_main"] if kv else ["attn_q"]) + ["combine"]
     timer = Timer(names)
 
     def step(evs=None):
@@ -260,7 +284,9 @@ def main():
         rec = (lambda: evs[i].record()) if evs else (lambda: None)
         if evs:
             evs[0].record()
-        if given is None and idx8:
+        if given is None and sel:
+            msa.msa_select_tiles(shape, sel, q, k, cu_q, cu_k, topk, None, sws)
+        elif given is None and idx8:
             msa.msa_index_topk_fp8(shape, q_idx, k_idx, idx_descale, cu_q, cu_k, topk, None, iws)
         elif given is None:
             msa.msa_index_topk(shape, q_idx, k_idx, cu_q, cu_k, topk, None, iws)
@@ -352,7 +378,11 @@ def main():
                                "traffic": None, "algorithmic_bytes": qbytes}
     # every call of the step against its own roofline
     kr = {}
-    if given is None:
+    if given is None and sel:
+        # representatives read Q and K once; the lists are written
+        kr["select"] = roof(kms["select"], "hbm", (case.total_q * cfg.hq + case.total_k * cfg.hkv)
+                            * 128 * 2 + n_lists * cfg.hkv * cfg.topk * 4)
+    elif given is None:
         ifl, ib = index_work(cfg, case.cu_q, case.cu_k)
         pk = PEAK_FP8 if cfg.idx_dtype == "fp8" else PEAK_BF16
         ridge = pk / PEAK_HBM

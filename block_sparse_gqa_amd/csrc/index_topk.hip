@@ -35,36 +35,6 @@ __device__ __forceinline__ int tile_blocks(const Seq& sq, int tile, int causal) 
 }
 constexpr float kPosInf = __builtin_inff();
 
-// Running top list of (score, block) sorted by score descending; a new block goes after
-// equal scores. Fully unrolled so that the list lives in registers.
-struct TopList {
-  float sc[kMaxTopK];
-  int id[kMaxTopK];
-  __device__ __forceinline__ void init() {
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) { sc[k] = kNegInf; id[k] = -1; }
-  }
-  __device__ __forceinline__ void insert(float v, int j) {
-#pragma unroll
-    for (int k = kMaxTopK - 1; k >= 1; --k) {
-      const bool gp = v > sc[k - 1];
-      const bool gc = v > sc[k];
-      sc[k] = gp ? sc[k - 1] : (gc ? v : sc[k]);
-      id[k] = gp ? id[k - 1] : (gc ? j : id[k]);
-    }
-    const bool g0 = v > sc[0];
-    sc[0] = g0 ? v : sc[0];
-    id[0] = g0 ? j : id[0];
-  }
-};
-
-// (a beats b) in the order score desc, block asc; empty entries (-1) lose to everything.
-__device__ __forceinline__ bool beats(float sa, int ia, float sb, int ib) {
-  if (ia < 0) return false;
-  if (ib < 0) return true;
-  return sa > sb || (sa == sb && ia < ib);
-}
-
 // `scale` turns raw proxy dot products into scores (fp8 proxies: the two descales).
 __device__ __forceinline__ void write_list(int32_t* out_idx, float* out_sc, int topk,
                                            bool has_local, int local, const float* sc,

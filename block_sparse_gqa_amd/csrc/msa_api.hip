@@ -18,10 +18,6 @@ thread_local std::string g_last_error;
 
 constexpr int64_t kInt32Max = 2147483647LL;
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 msa_status check_shape(const msa_shape* s) {
   if (!s) return MSA_ERR_NULL;
   if (s->dtype != MSA_BF16 && s->dtype != MSA_FP8_E4M3) return MSA_ERR_DTYPE;
@@ -305,6 +301,38 @@ msa_status msa_index_topk_fp8(const msa_shape* shape, const void* q_idx, const v
                               size_t ws_bytes, hipStream_t stream) {
   return index_topk(shape, true, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score,
                     workspace, ws_bytes, stream);
+}
+
+msa_status msa_select_workspace_size(const msa_shape* shape, int reps, size_t* bytes) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  if (reps != 1 && reps != 4) return MSA_ERR_SHAPE;
+  *bytes = select_geometry(*shape, reps).total;
+  return MSA_OK;
+}
+
+msa_status msa_select_tiles(const msa_shape* shape, int reps, const void* q, const void* k,
+                            const int32_t* cu_q, const int32_t* cu_k, int32_t* lists,
+                            float* scores, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (s.dtype != MSA_BF16) return MSA_ERR_DTYPE;
+  if (s.list_q != kBlock || (reps != 1 && reps != 4)) return MSA_ERR_SHAPE;
+  const SelectGeometry sg = select_geometry(s, reps);
+  if (sg.n_chunks > 65535 || (int64_t)s.batch * sg.tiles_max > kInt32Max) return MSA_ERR_SHAPE;
+  if (!cu_q || !cu_k || !lists) return MSA_ERR_NULL;
+  if ((s.total_q > 0 && !q) || (s.total_k > 0 && !k)) return MSA_ERR_NULL;
+  if (!workspace || ws_bytes < sg.total) return MSA_ERR_WORKSPACE;
+  const hipError_t e = launch_select_tiles(s, reps, q, k, cu_q, cu_k, lists, scores,
+                                           static_cast<char*>(workspace), stream);
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
 }
 
 static msa_status prep(const msa_shape* shape, msa_mode mode, const void* workspace,

@@ -171,6 +171,37 @@ __device__ __forceinline__ Seq load_seq_clamped(const int32_t* cu_q, const int32
   return r;
 }
 
+// Running top list of (score, block) sorted by score descending; a new block goes after
+// equal scores, so blocks inserted in ascending order keep the lower index first among ties.
+// Fully unrolled so that the list lives in registers.
+struct TopList {
+  float sc[kMaxTopK];
+  int id[kMaxTopK];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) { sc[k] = -__builtin_inff(); id[k] = -1; }
+  }
+  __device__ __forceinline__ void insert(float v, int j) {
+#pragma unroll
+    for (int k = kMaxTopK - 1; k >= 1; --k) {
+      const bool gp = v > sc[k - 1];
+      const bool gc = v > sc[k];
+      sc[k] = gp ? sc[k - 1] : (gc ? v : sc[k]);
+      id[k] = gp ? id[k - 1] : (gc ? j : id[k]);
+    }
+    const bool g0 = v > sc[0];
+    sc[0] = g0 ? v : sc[0];
+    id[0] = g0 ? j : id[0];
+  }
+};
+
+// (a beats b) in the order score desc, block asc; empty entries (-1) lose to everything.
+__device__ __forceinline__ bool beats(float sa, int ia, float sb, int ib) {
+  if (ia < 0) return false;
+  if (ib < 0) return true;
+  return sa > sb || (sa == sb && ia < ib);
+}
+
 // floor(a / b) for b > 0 and any sign of a.
 __device__ __forceinline__ int floordiv(int a, int b) {
   return a >= 0 ? a / b : -((-a + b - 1) / b);

@@ -56,6 +56,9 @@ struct Geometry {
   int64_t index_chunks;  // split index kernel: key chunks per sequence
 };
 
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 // Offsets (bytes) of each region of the caller's workspace.
 struct Layout {
   size_t counters;      // int32[64]: [0] = number of entries
@@ -89,6 +92,19 @@ hipError_t launch_index_split(const msa_shape& s, bool fp8, const void* q_idx,
                               const void* k_idx, const float* descale_idx, const int32_t* cu_q,
                               const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
                               void* ws, hipStream_t st);
+
+// Per-Q-tile selectors R1 / R4: the workspace regions (query and key representatives, fp32;
+// block scores) and the block chunks of the scoring kernel.
+struct SelectGeometry {
+  int reps;
+  int chunk;             // blocks scored per workgroup
+  int64_t tiles_max, nb_max, n_chunks;
+  size_t off_qrep, off_krep, off_scores, total;
+};
+SelectGeometry select_geometry(const msa_shape& s, int reps);
+hipError_t launch_select_tiles(const msa_shape& s, int reps, const void* q, const void* k,
+                               const int32_t* cu_q, const int32_t* cu_k, int32_t* lists,
+                               float* scores, char* ws, hipStream_t st);
 
 hipError_t launch_plan(const msa_shape& s, const Geometry& g, const Layout& L,
                        const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k,

@@ -23,7 +23,7 @@ MSA_AUTO, MSA_KV_OUTER, MSA_Q_OUTER = 0, 1, 2
 SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace_size",
            "msa_resolve_mode", "msa_crossover", "msa_status_string", "msa_last_error",
            "msa_index_topk", "msa_index_topk_fp8", "msa_sparse_attn_fwd", "msa_plan",
-           "msa_attn_main", "msa_combine")
+           "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles")
 
 
 class Shape(ctypes.Structure):
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "msa_crossover": [sp, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)],
             "msa_index_topk": [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_index_topk_fp8": [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "msa_select_workspace_size": [sp, i32, ctypes.POINTER(sz)],
+            "msa_select_tiles": [sp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_sparse_attn_fwd": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, i32, vp, sz,
                                     vp, vp, vp],
             "msa_plan": [sp, vp, vp, vp, vp, sz, vp],
@@ -166,6 +168,20 @@ def msa_index_topk_fp8(shape, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, t
                                     _p(cu_q), _p(cu_k), _p(topk_idx), _p(topk_score),
                                     _p(workspace), _nbytes(workspace), _stream(stream)),
            "msa_index_topk_fp8")
+
+
+def msa_select_workspace_size(shape, reps) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().msa_select_workspace_size(ctypes.byref(shape), int(reps), ctypes.byref(n)),
+           "msa_select_workspace_size")
+    return n.value
+
+
+def msa_select_tiles(shape, reps, q, k, cu_q, cu_k, lists, scores=None, workspace=None,
+                     stream=None) -> None:
+    _check(lib().msa_select_tiles(ctypes.byref(shape), int(reps), _p(q), _p(k), _p(cu_q),
+                                  _p(cu_k), _p(lists), _p(scores), _p(workspace),
+                                  _nbytes(workspace), _stream(stream)), "msa_select_tiles")
 
 
 def msa_sparse_attn_fwd(shape, q, k, v, descale_qkv, softmax_scale, topk_idx, cu_q, cu_k, mode,

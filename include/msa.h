@@ -8,6 +8,7 @@
  *
  *   msa_index_topk       index branch: max-pooled proxy scores + top-K, local block forced
  *   msa_index_topk_fp8   the same on fp8 e4m3 proxies (8-bit MFMA scoring)
+ *   msa_select_tiles     per-Q-tile lists from block representatives (R1 / R4 selectors)
  *   msa_sparse_attn_fwd  main branch: KV-outer partials (or Q-outer output) over the lists
  *   msa_combine          log-sum-exp merge of the per-slot partials into O and LSE
  *
@@ -183,6 +184,27 @@ msa_status msa_index_topk_fp8(const msa_shape* shape, const void* q_idx, const v
                               const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
                               int32_t* topk_idx, float* topk_score, void* workspace,
                               size_t ws_bytes, hipStream_t stream);
+
+/* Per-Q-tile block selectors R1 and R4 ("Sparse Attention", Chapter 4: one or four
+ * representatives). Every 128-query tile of a sequence and every 128-key block is summarised,
+ * per head, by the mean of its token vectors (reps = 1) or by the means of its four
+ * consecutive 32-token groups (reps = 4); a ragged tile or block averages the tokens it has
+ * and an empty group takes part in no comparison. A block's score for a (tile, group) is the
+ * largest dot product between a query representative of any query head of the group and a
+ * key representative of the block (the raw values: no softmax scale). With causal = 1 a block
+ * is visible to a tile when its first key is not after the tile's last query position
+ * (bottom-right aligned); no block is forced. Writes the per-tile lists the per-Q-tile
+ * attention reads: lists [batch * ceil(max_q / 128), hkv, topk] int32, row
+ * s * ceil(max_q / 128) + t, the blocks by score descending then block ascending, -1 where
+ * fewer blocks are visible (and for rows past a sequence's tiles); scores (nullable) the same
+ * shape, fp32, -inf at -1 slots. Requires list_q == 128 and bf16 Q and K
+ * (MSA_ERR_DTYPE otherwise); q [total_q, hq, d], k [total_k, hkv, d]; reps in {1, 4}.
+ * workspace: msa_select_workspace_size() bytes (fp32 representatives and block scores). */
+msa_status msa_select_workspace_size(const msa_shape* shape, int reps, size_t* bytes);
+msa_status msa_select_tiles(const msa_shape* shape, int reps, const void* q, const void* k,
+                            const int32_t* cu_q, const int32_t* cu_k, int32_t* lists,
+                            float* scores, void* workspace, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* Main branch ("Kernel optimization ...", summary and section 2; "Sparse Attention",
  * Chapters 1 and 5). Every query head attends, with its own softmax, to the union of the

@@ -123,6 +123,7 @@ class Config:
     lowrank: bool = False   # rank-8 per-group bias giving block reuse
     list_q: int = 1         # 1: per-query selection by the index branch; 128: given per-tile lists
     list_pool: int = 0      # per-tile lists: blocks drawn from range(list_pool)
+    selector: int = 0       # per-tile lists chosen by the R1 (1) or R4 (4) selector, not drawn
     proxy: str = "normal"   # "normal" or "grid"
     length_seed_draw: Optional[tuple] = None  # decode: (R, lo_blocks, hi_blocks) drawn per seed
 
@@ -153,6 +154,12 @@ CONFIGS = {
     # decode: 64 requests x 1 query, key lengths uniform over multiples of 128 in [16K, 128K]
     "decode": Config(name="decode", batch=64, n_q=(), n_k=(), hq=64, hkv=4, topk=16, dp=64,
                      length_seed_draw=(64, 128, 1024)),
+    # selector -> per-tile attention ("Sparse Attention", Chapter 4 benchmark): B=2, 4096
+    # queries, 16K keys, 16 query heads on one KV head, 16 blocks per Q128 tile, non-causal
+    "sel_r1": _cfg("sel_r1", 4096, 16384, batch=2, hq=16, hkv=1, topk=16, causal=False,
+                   list_q=128, selector=1),
+    "sel_r4": _cfg("sel_r4", 4096, 16384, batch=2, hq=16, hkv=1, topk=16, causal=False,
+                   list_q=128, selector=4),
     # the same two workloads with the proxies quantised to fp8 e4m3 (low-precision scoring)
     "m3_fp8_long_i8": _cfg("m3_fp8_long_i8", 131072, 131072, hq=64, hkv=4, topk=16, dp=64,
                            lowrank=True, dtype="fp8", idx_dtype="fp8"),
@@ -314,7 +321,7 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
             raise ValueError(f"unknown idx_dtype {cfg.idx_dtype}")
 
     lists = None
-    if cfg.list_q > 1:
+    if cfg.list_q > 1 and cfg.selector == 0:
         lists = tile_lists(cfg, cu_q, seed)
 
     return Case(cfg=cfg, seed=seed, cu_q=cu_q, cu_k=cu_k, q=qs, k=ks, v=vs, descale=descale,

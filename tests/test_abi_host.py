@@ -105,6 +105,9 @@ def test_bad_shapes_are_rejected_by_every_entry_point(L, name, kw, status):
                             None) == status
     assert L.msa_index_topk_fp8(ctypes.byref(s), fake, fake, fake, fake, fake, fake, None, None,
                                 0, None) == status
+    assert L.msa_select_tiles(ctypes.byref(s), 4, fake, fake, fake, fake, fake, None, fake,
+                              1 << 40, None) == status
+    assert L.msa_select_workspace_size(ctypes.byref(s), 4, ctypes.byref(n)) == status
     assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
                                  msa.MSA_AUTO, fake, 1 << 40, fake, None, None) == status
     assert L.msa_combine(ctypes.byref(s), msa.MSA_AUTO, fake, 1 << 40, fake, None,
@@ -166,6 +169,30 @@ def test_null_device_pointers_and_small_workspace(L):
     # a mode outside the enum
     assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
                                  5, fake, need, fake, None, None) == msa.MSA_ERR_MODE
+
+
+def test_selector_argument_checks(L):
+    """Per-tile lists only, bf16 Q/K only, one or four representatives, pointers and
+    workspace checked before any launch."""
+    fake = ctypes.c_void_p(0x1000)
+    s = msa.make_shape(batch=2, total_q=8192, total_k=32768, max_q=4096, max_k=16384, hq=16,
+                       hkv=1, topk=16, causal=False, list_q=128)
+    need = msa.msa_select_workspace_size(s, 4)
+    # representatives (fp32) of 64 tiles x 16 heads and 256 blocks, 4 each, and the scores
+    assert need >= 64 * 16 * 4 * 128 * 4 + 256 * 4 * 128 * 4 + 64 * 128 * 4
+    assert msa.msa_select_workspace_size(s, 1) < need
+    sel = lambda shape, reps, ws=fake, nbytes=need, lists=fake, q=fake: L.msa_select_tiles(
+        ctypes.byref(shape), reps, q, fake, fake, fake, lists, None, ws, nbytes, None)
+    assert sel(s, 2) == msa.MSA_ERR_SHAPE
+    assert sel(msa.make_shape(batch=2, total_q=8192, total_k=32768, max_q=4096, max_k=16384,
+                              hq=16, hkv=1, topk=16, causal=False), 4) == msa.MSA_ERR_SHAPE
+    s8 = msa.make_shape(batch=2, total_q=8192, total_k=32768, max_q=4096, max_k=16384, hq=16,
+                        hkv=1, topk=16, causal=False, list_q=128, dtype=msa.MSA_FP8_E4M3)
+    assert sel(s8, 4) == msa.MSA_ERR_DTYPE
+    assert sel(s, 4, lists=None) == msa.MSA_ERR_NULL
+    assert sel(s, 4, q=None) == msa.MSA_ERR_NULL
+    assert sel(s, 4, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE
+    assert sel(s, 4, ws=None) == msa.MSA_ERR_WORKSPACE
 
 
 def test_python_binding_raises_on_error(L):
