@@ -213,15 +213,19 @@ __global__ __launch_bounds__(64) void select_topk_kernel(
   for (int k = 0; k < topk; ++k) {
     float ws = tl.sc[0];
     int wi = tl.id[0];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float os = shfl_xor_f(ws, off);
-      const int oi = shfl_xor_i(wi, off);
+    // wave arg-best: four levels on the DPP network, then lanes ^ 16 and ^ 32
+    auto take = [&](float os, int oi) {
       if (beats(os, oi, ws, wi)) {
         ws = os;
         wi = oi;
       }
-    }
+    };
+    take(dpp_f<kDppXor1>(ws), dpp_i<kDppXor1>(wi));
+    take(dpp_f<kDppXor2>(ws), dpp_i<kDppXor2>(wi));
+    take(dpp_f<kDppHalfMirror>(ws), dpp_i<kDppHalfMirror>(wi));
+    take(dpp_f<kDppMirror>(ws), dpp_i<kDppMirror>(wi));
+    take(shfl_xor_f(ws, 16), shfl_xor_i(wi, 16));
+    take(shfl_xor_f(ws, 32), shfl_xor_i(wi, 32));
     // the lane holding the winner drops it (each block sits in one lane's list)
     if (wi >= 0 && tl.id[0] == wi) {
 #pragma unroll
