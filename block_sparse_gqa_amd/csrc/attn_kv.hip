@@ -116,11 +116,11 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // ======================================================================================
 // bf16: tiles of XCD-local query ranges, K/V restaged asynchronously.
 //
-// The plan cuts the entries of every (sequence, group, 512-query range) phase into tiles of
+// The plan cuts the entries of every (sequence, group, query range) phase into tiles of
 // 256 / G entries of one bucket and writes one record per tile. Phase p belongs to XCD
 // p % n_xcd (workgroup i runs on XCD i % n_xcd), whose n_share workgroups split the phase's
-// tiles into contiguous shares; the Q rows of a phase (2 MiB for 16 heads) stay in that XCD's
-// L2 while every block of the range re-reads them.
+// tiles into contiguous shares; the Q rows of a phase (at most 4 MiB for 16 heads and 1024
+// queries) stay in that XCD's L2 while every block of the range re-reads them.
 //
 // K and V blocks go to LDS by direct loads into three rotating 32 KiB slots. When the next
 // tile starts a new bucket, its K block is loaded at the start of the current tile into the

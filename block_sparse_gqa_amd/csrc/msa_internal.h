@@ -19,18 +19,18 @@ inline int split_index_chunk(int64_t nb_max) { return nb_max <= 1024 ? 16 : kSpl
 constexpr int kWordQ = 64;
 // Queries per range of the entry order (s, group, range, block, query). The attention
 // kernels hand each (s, group, range) phase to one XCD, whose workgroups split the phase's
-// tiles. bf16: 512 queries of one group hold 2 MiB of Q rows, half an XCD's L2, so a query's
-// Q rows are fetched from memory once and re-read from L2 for each of its blocks. fp8 rows
-// are half the bytes and its kernel is bound by issue rather than memory, so it takes longer
-// ranges, whose buckets hold more queries (fuller tiles, fewer K/V loads): up to 4096, as long
-// as the schedule keeps at least 128 phases (16 per XCD) to spread.
-constexpr int kRangeQBf16 = 512;
+// tiles. Longer ranges hold more queries per bucket (fuller tiles, fewer K/V loads) but more
+// Q rows per phase: bf16 takes up to 1024 queries (16 heads x 256 B x 1024 = 4 MiB, one XCD's
+// L2: at the M3 shape 3.21 ms with 512, 3.10 with 1024, 3.11 with 2048), fp8, whose kernel is
+// bound by issue rather than memory, up to 4096; either as long as the schedule keeps at least
+// 128 phases (16 per XCD) to spread, and never below 512.
+constexpr int kRangeQMin = 512;
+constexpr int kRangeQBf16Max = 1024;
 constexpr int kRangeQFp8Max = 4096;
 constexpr int64_t kMinPhases = 128;
 inline int range_q(const msa_shape& s) {
-  if (s.dtype != MSA_FP8_E4M3) return kRangeQBf16;
-  int r = kRangeQFp8Max;
-  while (r > kRangeQBf16 &&
+  int r = s.dtype == MSA_FP8_E4M3 ? kRangeQFp8Max : kRangeQBf16Max;
+  while (r > kRangeQMin &&
          (int64_t)s.batch * s.hkv * ((s.max_q + (int64_t)r - 1) / r) < kMinPhases)
     r /= 2;
   return r;

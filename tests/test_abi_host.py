@@ -231,16 +231,17 @@ def test_partial_memory_ratio_matches_the_pages():
 
 
 def test_query_range_rule():
-    """bf16 ranges hold 512 queries; fp8 ranges the longest of 4096 .. 512 queries that leaves
-    at least 128 (sequence, group, range) phases."""
+    """Ranges hold the longest of 1024 (bf16) or 4096 (fp8) .. 512 queries that leaves at least
+    128 (sequence, group, range) phases."""
     def q_range(s):
         lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
         return 64 * lay.words_per_bucket, lay.n_ranges
     fp8 = msa.MSA_FP8_E4M3
-    assert q_range(m3_shape()) == (512, 64)
+    assert q_range(m3_shape()) == (1024, 32)                     # 4 groups x 32 ranges
     long = dict(total_q=131072, total_k=131072, max_q=131072, max_k=131072)
     assert q_range(m3_shape(dtype=fp8, **long)) == (4096, 32)
-    assert q_range(m3_shape(**long)) == (512, 256)
+    assert q_range(m3_shape(**long)) == (1024, 128)
+    assert q_range(m3_shape(total_q=4096, total_k=4096, max_q=4096, max_k=4096)) == (512, 8)
     assert q_range(m3_shape(dtype=fp8)) == (1024, 32)            # 4 groups x 32 ranges
     # 32 sequences of at most 2048 queries, 2 groups: 1024-query ranges (32 x 2 x 2 = 128)
     many = msa.make_shape(batch=32, total_q=8000, total_k=9000, max_q=2048, max_k=2348, hq=8,
