@@ -335,6 +335,38 @@ msa_status msa_select_tiles(const msa_shape* shape, int reps, const void* q, con
   return MSA_OK;
 }
 
+msa_status msa_bwd_workspace_size(const msa_shape* shape, size_t* bytes) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  if (shape->dtype != MSA_BF16) return MSA_ERR_DTYPE;
+  *bytes = bwd_workspace_bytes(*shape);
+  return MSA_OK;
+}
+
+msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k,
+                               const void* v, const void* o, const float* lse, const void* dout,
+                               float softmax_scale, const int32_t* topk_idx,
+                               const int32_t* cu_q, const int32_t* cu_k, void* workspace,
+                               size_t ws_bytes, float* dq, float* dk, float* dv,
+                               hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (s.dtype != MSA_BF16) return MSA_ERR_DTYPE;
+  if (!topk_idx || !cu_q || !cu_k) return MSA_ERR_NULL;
+  if (s.total_q > 0 && (!q || !o || !lse || !dout || !dq)) return MSA_ERR_NULL;
+  if (s.total_k > 0 && (!k || !v || !dk || !dv)) return MSA_ERR_NULL;
+  if (!workspace || ws_bytes < bwd_workspace_bytes(s)) return MSA_ERR_WORKSPACE;
+  const hipError_t e = launch_bwd(s, q, k, v, o, lse, dout, softmax_scale, topk_idx, cu_q, cu_k,
+                                  static_cast<char*>(workspace), dq, dk, dv, stream);
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
 static msa_status prep(const msa_shape* shape, msa_mode mode, const void* workspace,
                        size_t ws_bytes, msa_mode* m, Geometry* g, Layout* L) {
   msa_status st = check_shape(shape);

@@ -119,6 +119,12 @@ hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
                          const int32_t* cu_k, char* ws, void* o, float* lse, hipStream_t st);
 hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L,
                           const char* ws, void* o, float* lse, hipStream_t st);
+// Main-branch backward: workspace = the KV-outer plan, then fp32 dQ partials [E, group, d].
+size_t bwd_workspace_bytes(const msa_shape& s);
+hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, float scale,
+                      const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k, char* ws,
+                      float* dq, float* dk, float* dv, hipStream_t st);
 
 int device_cu_count();
 int device_xcd_count();

@@ -23,7 +23,8 @@ MSA_AUTO, MSA_KV_OUTER, MSA_Q_OUTER = 0, 1, 2
 SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace_size",
            "msa_resolve_mode", "msa_crossover", "msa_status_string", "msa_last_error",
            "msa_index_topk", "msa_index_topk_fp8", "msa_sparse_attn_fwd", "msa_plan",
-           "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles")
+           "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles",
+           "msa_bwd_workspace_size", "msa_sparse_attn_bwd")
 
 
 class Shape(ctypes.Structure):
@@ -75,6 +76,9 @@ def lib() -> ctypes.CDLL:
             "msa_plan": [sp, vp, vp, vp, vp, sz, vp],
             "msa_attn_main": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp],
             "msa_combine": [sp, i32, vp, sz, vp, vp, vp],
+            "msa_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
+            "msa_sparse_attn_bwd": [sp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                    sz, vp, vp, vp, vp],
         }.items():
             f = getattr(L, name)
             f.restype = i32
@@ -207,3 +211,18 @@ def msa_attn_main(shape, q, k, v, descale_qkv, softmax_scale, cu_q, cu_k, worksp
 def msa_combine(shape, mode, workspace, o, lse, stream=None) -> None:
     _check(lib().msa_combine(ctypes.byref(shape), mode, _p(workspace), _nbytes(workspace), _p(o),
                              _p(lse), _stream(stream)), "msa_combine")
+
+
+def msa_bwd_workspace_size(shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().msa_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
+           "msa_bwd_workspace_size")
+    return n.value
+
+
+def msa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, softmax_scale, topk_idx, cu_q, cu_k,
+                        workspace, dq, dk, dv, stream=None) -> None:
+    _check(lib().msa_sparse_attn_bwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(o), _p(lse),
+                                     _p(dout), float(softmax_scale), _p(topk_idx), _p(cu_q),
+                                     _p(cu_k), _p(workspace), _nbytes(workspace), _p(dq), _p(dk),
+                                     _p(dv), _stream(stream)), "msa_sparse_attn_bwd")

@@ -11,6 +11,7 @@
  *   msa_select_tiles     per-Q-tile lists from block representatives (R1 / R4 selectors)
  *   msa_sparse_attn_fwd  main branch: KV-outer partials (or Q-outer output) over the lists
  *   msa_combine          log-sum-exp merge of the per-slot partials into O and LSE
+ *   msa_sparse_attn_bwd  main-branch backward: dQ, dK, dV over the selected blocks
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers allocated and owned by the caller; the library never
@@ -247,6 +248,29 @@ msa_status msa_attn_main(const msa_shape* shape, const void* q, const void* k, c
  * schedule already wrote O. */
 msa_status msa_combine(const msa_shape* shape, msa_mode mode, const void* workspace,
                        size_t ws_bytes, void* o, float* lse, hipStream_t stream);
+
+/* Main-branch backward ("Flash-MSA: accelerating million-token training": the selected block
+ * ids and the main branch's LSE are kept for the backward; the gradients are those of the
+ * exact attention over each query's union of selected keys, as in msa_sparse_attn_fwd; the
+ * lists themselves are not differentiated). With P = exp(softmax_scale q.k - LSE) over the
+ * visible keys and D = sum_d dO O per (query, head):
+ *   dV_u = sum P dO,  dS = P (dO.v_u - D),  dQ = softmax_scale sum_u dS k_u,
+ *   dK_u = softmax_scale sum dS q  (sums over the query heads of u's group that see u).
+ * bf16 only (DTYPE otherwise). In: q, o, dout bf16 [total_q, hq, d]; k, v bf16
+ * [total_k, hkv, d]; lse fp32 [total_q, hq] as written by msa_combine (natural log); lists,
+ * cu_q, cu_k as for msa_sparse_attn_fwd. Out (fp32, written, not accumulated): dq
+ * [total_q, hq, d]; dk, dv [total_k, hkv, d]. Every row of dq is written (zero for rows with
+ * no visible key or in no sequence); dk and dv rows of keys in a sequence are written (zero
+ * for keys no query sees), other rows are not touched. Deterministic: no atomics. Workspace:
+ * msa_bwd_workspace_size bytes (the KV-outer plan plus fp32 dQ partials of every
+ * (query-group, block) entry: E x hq/hkv x d x 4 bytes). */
+msa_status msa_bwd_workspace_size(const msa_shape* shape, size_t* bytes);
+msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k,
+                               const void* v, const void* o, const float* lse, const void* dout,
+                               float softmax_scale, const int32_t* topk_idx,
+                               const int32_t* cu_q, const int32_t* cu_k, void* workspace,
+                               size_t ws_bytes, float* dq, float* dk, float* dv,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

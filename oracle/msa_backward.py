@@ -58,3 +58,34 @@ def sparse_attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: 
             np.add.at(dk[:, g], keys, scale * (ds.T @ q[i, heads]))
             np.add.at(dv[:, g], keys, p.T @ do[i, heads])
     return dq, dk, dv, o, lse
+
+
+def run_case(case, dout, lists: np.ndarray | None = None):
+    """The backward of a whole seeded case: per sequence, on the lists the oracle's own index
+    branch selects (or the case's per-tile lists, or ``lists`` [Tq, Hkv, K] when given).
+    Returns (dQ [Tq, Hq, D], dK, dV [Tk, Hkv, D], O, LSE, per-query lists [Tq, Hkv, K])."""
+    from oracle import msa_case
+    from synth.msa_inputs import widen
+    cfg = case.cfg
+    dsq, dsk, dsv = case.descale
+    q, k, v = widen(case.q, dsq), widen(case.k, dsk), widen(case.v, dsv)
+    g_out = widen(dout)
+    if lists is None:
+        lists = np.full((case.total_q, cfg.hkv, cfg.topk), -1, dtype=np.int32)
+        sel = msa_case.run(case, want_output=False)
+        if sel.rows is not None:
+            lists[sel.rows] = sel.topk_idx
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    o = np.zeros_like(q)
+    lse = np.full((case.total_q, cfg.hq), -np.inf)
+    for s in range(len(case.cu_q) - 1):
+        q0, q1 = int(case.cu_q[s]), int(case.cu_q[s + 1])
+        k0, k1 = int(case.cu_k[s]), int(case.cu_k[s + 1])
+        if q1 == q0:
+            continue
+        r = sparse_attention_backward(q[q0:q1], k[k0:k1], v[k0:k1], lists[q0:q1], g_out[q0:q1],
+                                      case.softmax_scale, cfg.block, cfg.causal)
+        dq[q0:q1], dk[k0:k1], dv[k0:k1], o[q0:q1], lse[q0:q1] = r
+    return dq, dk, dv, o, lse, lists

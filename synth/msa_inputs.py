@@ -31,7 +31,7 @@ import torch
 # Child index of each named stream under SeedSequence(seed).
 _STREAMS = {
     "q": 0, "k": 1, "v": 2, "q_idx": 3, "k_idx": 4,
-    "bias_proxy": 5, "bias_main": 6, "lists": 7, "lengths": 8,
+    "bias_proxy": 5, "bias_main": 6, "lists": 7, "lengths": 8, "dout": 9,
 }
 _CHUNK = 1 << 22          # elements per independently seeded chunk
 FP8_MAX = 448.0           # largest finite OCP e4m3fn magnitude
@@ -345,3 +345,10 @@ def tile_lists(cfg: Config, cu_q: np.ndarray, seed: int) -> np.ndarray:
                 out[s * tiles_max + t, h] = np.sort(rng.choice(cfg.list_pool, cfg.topk,
                                                                replace=False))
     return out
+
+
+def grad_output(case: Case, seed: Optional[int] = None) -> torch.Tensor:
+    """Seeded upstream gradient dO for the backward: N(0, 1) bf16 [Tq, Hq, D]."""
+    cfg = case.cfg
+    ss = _stream(case.seed if seed is None else seed, "dout")
+    return to_bf16(normal_f32(ss, (case.total_q, cfg.hq, cfg.d)))

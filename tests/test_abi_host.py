@@ -295,3 +295,30 @@ def test_crossover_is_monotone_in_cache_bandwidth():
     s8 = m3_shape(dtype=msa.MSA_FP8_E4M3)
     # fp8 data halves the K/V bytes Q-outer re-reads: the crossover moves down
     assert msa.msa_crossover(s8, 8.0, 16.0) < xs[1]
+
+
+def test_backward_argument_checks(L):
+    """bf16 only; every pointer and the workspace checked before any launch; the workspace
+    holds the KV-outer plan plus fp32 dQ partials of every (query-group, block) entry."""
+    fake = ctypes.c_void_p(0x1000)
+    s = m3_shape()
+    need = msa.msa_bwd_workspace_size(s)
+    fwd = msa.msa_workspace_size(s, msa.MSA_KV_OUTER)
+    lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
+    e_max = s.total_q * s.hkv * s.topk
+    assert need - fwd - e_max * (s.hq // s.hkv) * 128 * 4 in range(0, 256)
+    assert lay.part_lse + s.total_q * s.hq * 4 <= lay.part_l     # the D rows fit the LSE region
+
+    def bwd(shape, ws=fake, nbytes=need, q=fake, dout=fake, dk=fake, lists=fake):
+        return L.msa_sparse_attn_bwd(ctypes.byref(shape), q, fake, fake, fake, fake, dout, 0.1,
+                                     lists, fake, fake, ws, nbytes, fake, dk, fake, None)
+    assert bwd(m3_shape(dtype=msa.MSA_FP8_E4M3)) == msa.MSA_ERR_DTYPE
+    assert bwd(s, q=None) == msa.MSA_ERR_NULL
+    assert bwd(s, dout=None) == msa.MSA_ERR_NULL
+    assert bwd(s, dk=None) == msa.MSA_ERR_NULL
+    assert bwd(s, lists=None) == msa.MSA_ERR_NULL
+    assert bwd(s, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE
+    assert bwd(s, ws=None) == msa.MSA_ERR_WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert L.msa_bwd_workspace_size(ctypes.byref(m3_shape(dtype=msa.MSA_FP8_E4M3)),
+                                    ctypes.byref(n)) == msa.MSA_ERR_DTYPE
