@@ -217,6 +217,98 @@ def load_traffic(workload: str, launches_bytes_alg: float):
     return t.get("traffic_bytes_per_launch")
 
 
+def bench_backward(args, case, shape, desc, t) -> None:
+    """Main-branch backward: one step = msa_sparse_attn_bwd (inverted index, D = rowsum(dO O),
+    the KV-stationary dK / dV / dQ-partial kernel, the dQ sum) on the forward's lists, O and
+    LSE. value = useful FLOPs (10 D per unmasked selected (query, head, key) triple: S, dP, dV,
+    dK, dQ) / time."""
+    q, k, v, o, lse, topk, cu_q, cu_k = t
+    cfg = case.cfg
+    if cfg.dtype != "bf16":
+        print("the backward runs on bf16 workloads only", file=sys.stderr)
+        sys.exit(2)
+    dout = mi.grad_output(case).to("cuda")
+    bws = torch.empty(msa.msa_bwd_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    dq = torch.empty((case.total_q, cfg.hq, 128), dtype=torch.float32, device="cuda")
+    dk = torch.empty((case.total_k, cfg.hkv, 128), dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+
+    def bwd():
+        msa.msa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, case.softmax_scale, topk, cu_q,
+                                cu_k, bws, dq, dk, dv)
+    for _ in range(args.warmup):
+        bwd()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(args.steps):
+        bwd()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = sum(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)) / args.steps
+    pairs, nsb = useful_pairs(cfg, case.cu_q, case.cu_k, topk.cpu().numpy(), cfg.list_q)
+    flops = 10.0 * 128 * pairs
+    res = {
+        "metric": "main-branch backward TFLOP/s (useful pairs); ms per backward call",
+        "value": flops / (ms_per_step * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded NumPy draws, see DESIGN.md input recipe)",
+        "config": {"workload": args.workload + "_backward", "description": desc,
+                   "global_batch": len(case.cu_q) - 1, "seq_len": case.max_q, "hq": cfg.hq,
+                   "hkv": cfg.hkv, "d": 128, "block": 128, "topk": cfg.topk,
+                   "causal": cfg.causal, "parallelism": "single GPU"},
+        "call_ms_events": ev_ms,
+        "useful_gflop": flops / 1e9, "nsb": nsb,
+        "roofline": {"bound": "mfma", "kernel": "msa_sparse_attn_bwd (all its kernels)",
+                     "achieved": flops / (ev_ms * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12,
+                     "unit": "TFLOP/s", "frac": flops / (ev_ms * 1e-3) / PEAK_BF16,
+                     "traffic": None},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_backward(case, topk.cpu().numpy(), dout,
+                                                    args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_backward(case, lists: np.ndarray, dout, budget_s: float) -> dict:
+    """The backward oracle, untuned, on growing suffixes of the first sequence (a suffix keeps
+    the queries' positions), scaled to useful TFLOP/s."""
+    from oracle.msa_backward import sparse_attention_backward
+    from synth.msa_inputs import widen
+    cfg = case.cfg
+    q0, q1 = int(case.cu_q[0]), int(case.cu_q[1])
+    k0, k1 = int(case.cu_k[0]), int(case.cu_k[1])
+    k, v = widen(case.k[k0:k1]), widen(case.v[k0:k1])
+    n, t_used, flops = 0, 0.0, 0.0
+    t0 = time.perf_counter()
+    while n < q1 - q0 and t_used < budget_s:
+        m = min(128, q1 - q0 - n)
+        a, b = q1 - n - m, q1 - n
+        part = lists[a:q1].copy()
+        part[m:] = -1                          # rows already done take no keys
+        sparse_attention_backward(widen(case.q[a:q1]), k, v, part, widen(dout[a:q1].cpu()),
+                                  case.softmax_scale, cfg.block, cfg.causal)
+        sub = np.full_like(lists, -1)
+        sub[a:b] = lists[a:b]
+        p, _ = useful_pairs(cfg, case.cu_q, case.cu_k, sub, 1)
+        flops += 10.0 * 128 * p
+        n += m
+        t_used = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    return {"value": flops / max(t_used, 1e-9) / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the last {n} queries of sequence 0 (all heads), backward oracle, fp64 "
+                      f"NumPy, {t_used:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +319,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the main-branch backward (msa_sparse_attn_bwd) instead")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also time a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -311,6 +405,10 @@ def main():
             i += 1
             evs[i].record()
 
+    if args.backward:
+        step()                                 # lists, O and LSE of the forward
+        bench_backward(args, case, shape, desc, (q, k, v, o, lse, topk, cu_q, cu_k))
+        return
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -74,30 +74,65 @@ struct BwdArgs {
   const int32_t* cu_k;
   const int32_t* offsets;
   const int32_t* entry_q;
+  const int32_t* chunk_base;   // [n_cols + 1]: first chunk of each (sequence, group, block)
+  const int32_t* col_of;       // [chunks]: the column of each chunk
   float* dq_part;
+  float* dkv_part;             // [chunks][2][kBlock][kD]: dK, dV of chunks of split columns
   float* dk;
   float* dv;
   float scale, scale_log2;
-  int total_q, total_k, max_q, max_k, hq, hkv, nb_max, wr, n_r, causal;
+  int total_q, total_k, max_q, max_k, hq, hkv, nb_max, wr, n_r, causal, chunk_e;
 };
+
+// Entries of column (s, g, b) over all query ranges: bucket (s, g, r, b) holds
+// offsets[bk wr] .. offsets[(bk + 1) wr].
+__device__ __forceinline__ size_t bucket_at(const BwdArgs& a, int s, int g, int r, int b) {
+  return (((size_t)s * a.hkv + g) * a.n_r + r) * a.nb_max + b;
+}
+
+// Walk over the tiles of one chunk: the chunk's entries [lo, hi) of the column, numbered
+// across the query ranges in order, cut per range segment into tiles of TE entries.
+struct TileIt {
+  int r, base, et, e1;
+};
+
+__device__ __forceinline__ bool next_segment(const BwdArgs& a, int s, int g, int b, int lo,
+                                             int hi, TileIt& it) {
+  while (it.r < a.n_r && it.base < hi) {
+    const size_t bk = bucket_at(a, s, g, it.r, b);
+    const int f0 = a.offsets[bk * a.wr], f1 = a.offsets[(bk + 1) * a.wr];
+    const int e0 = f0 + max(lo - it.base, 0), e1 = f0 + min(hi - it.base, f1 - f0);
+    it.base += f1 - f0;
+    ++it.r;
+    if (e0 < e1) {
+      it.et = e0;
+      it.e1 = e1;
+      return true;
+    }
+  }
+  return false;
+}
 
 template <int G>
 __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
   constexpr int TE = 32 / G;                 // entries per tile of 32 rows
   __shared__ uint16_t kb[kBlock * kD];       // K_b, V_b, row-major
   __shared__ uint16_t vb[kBlock * kD];
-  __shared__ uint16_t qt[32 * kD];           // the tile's Q and dO rows
-  __shared__ uint16_t dot[32 * kD];
+  __shared__ uint16_t qt[2][32 * kD];        // the tile's Q and dO rows, double-buffered
+  __shared__ uint16_t dot[2][32 * kD];
   __shared__ uint16_t pbuf[4][32 * 32];      // per wave: P and dS of its keys, [row][key]
   __shared__ uint16_t sbuf[4][32 * 32];
-  __shared__ float red[4][32][64];           // dQ of the four waves, half the dims at a time
 
-  const int b = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
+  const int cl = a.col_of[chunk];            // -1: past the last chunk
+  if (cl < 0) return;
+  const int b = cl % a.nb_max, g = (cl / a.nb_max) % a.hkv, s = cl / (a.nb_max * a.hkv);
+  const int j = chunk - a.chunk_base[cl];
+  const bool split = a.chunk_base[cl + 1] - a.chunk_base[cl] > 1;
+  const int lo = j * a.chunk_e, hi = lo + a.chunk_e;   // the chunk's entries of the column
   const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
-  const int nb = (sq.nk + kBlock - 1) / kBlock;
-  if (b >= nb) return;
   const int u0 = b * kBlock;
 
   // K_b and V_b (rows past the sequence repeat its last key; their weights are masked)
@@ -116,122 +151,166 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
   }
   const int key0 = 32 * wave;                // this wave's keys within the block
 
-  for (int r = 0; r < a.n_r; ++r) {
-    const size_t bk = (((size_t)s * a.hkv + g) * a.n_r + r) * a.nb_max + b;
-    const int e0 = a.offsets[bk * a.wr], e1 = a.offsets[(bk + 1) * a.wr];
-    for (int et = e0; et < e1; et += TE) {
-      __syncthreads();                       // K/V staged; previous tile's buffers free
-      // Q and dO rows of the tile: row n = entry et + n / G, head g G + n % G
-      for (int i = tid; i < 32 * kD / 8; i += 256) {
-        const int n = i / (kD / 8), c = i % (kD / 8);
-        const int e = et + n / G;
-        u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u};
-        if (e < e1) {
-          const size_t row = (size_t)a.entry_q[e] * a.hq + g * G + n % G;
-          qv = *reinterpret_cast<const u32x4*>(a.q + row * kD + 8 * c);
-          dv4 = *reinterpret_cast<const u32x4*>(a.dout + row * kD + 8 * c);
-        }
-        *reinterpret_cast<u32x4*>(qt + n * kD + 8 * c) = qv;
-        *reinterpret_cast<u32x4*>(dot + n * kD + 8 * c) = dv4;
-      }
-      // this lane's row (column n = col of S^T): its query, LSE and D
-      const int e_row = et + col / G;
-      const bool row_ok = e_row < e1;
-      int t = 0;
-      float lse2 = 0.f, dsum = 0.f;
-      if (row_ok) {
-        t = a.entry_q[e_row];
-        const size_t hrow = (size_t)t * a.hq + g * G + col % G;
-        lse2 = a.lse[hrow] * 1.4426950408889634f;
-        dsum = a.dsum[hrow];
-      }
-      const int pos = sq.nk - sq.nq + (t - sq.q0);
-      __syncthreads();
-
-      // S^T and dP^T for the wave's 32 keys x the tile's 32 rows
-      f32x16 st = {}, dpt = {};
+  // Staging rows of this thread: n = tid / 16 + 16 k (k = 0, 1), 16-byte column tid % 16.
+  // Compute row of this lane: n = col. Loads of a tile: entry rows first, then Q, dO, LSE, D.
+  const int c16 = tid % 16;
+  auto load_rows = [&](int et, int e1, int eq[2], int& eqc) {
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        const bf16x8 ka = read_rows(kb, kD, key0, 16 * ks, lane);
-        const bf16x8 va = read_rows(vb, kD, key0, 16 * ks, lane);
-        const bf16x8 qb = read_rows(qt, kD, 0, 16 * ks, lane);
-        const bf16x8 ob = read_rows(dot, kD, 0, 16 * ks, lane);
-        st = mfma32(ka, qb, st);
-        dpt = mfma32(va, ob, dpt);
-      }
-      // P = exp(tau S - LSE) on visible keys; dS = P (dP - D); both to the wave's buffers as
-      // [row][key] (lane (row col, half hf) holds keys 8 (r / 4) + 4 hf + r % 4 in st[r])
-      uint16_t* const pb = pbuf[wave];
-      uint16_t* const sb = sbuf[wave];
+    for (int k = 0; k < 2; ++k) {
+      const int e = et + (tid / 16 + 16 * k) / G;
+      eq[k] = e < e1 ? a.entry_q[e] : -1;
+    }
+    const int e = et + col / G;
+    eqc = e < e1 ? a.entry_q[e] : -1;
+  };
+  auto load_data = [&](const int eq[2], int eqc, u32x4 qv[2], u32x4 ov[2], float& lse2,
+                       float& dsum) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float p[4], d[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 8 * q4 + 4 * hf + i;
-          const int u = u0 + key0 + m;
-          const bool vis = row_ok && u < sq.nk && !(a.causal && u > pos) &&
-                           lse2 > -__builtin_inff();
-          p[i] = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
-          d[i] = p[i] * (dpt[4 * q4 + i] - dsum);
-        }
-        u32x2 pw, sw;
-        pw[0] = pack_bf16x2(p[0], p[1]);
-        pw[1] = pack_bf16x2(p[2], p[3]);
-        sw[0] = pack_bf16x2(d[0], d[1]);
-        sw[1] = pack_bf16x2(d[2], d[3]);
-        *reinterpret_cast<u32x2*>(pb + col * 32 + 8 * q4 + 4 * hf) = pw;
-        *reinterpret_cast<u32x2*>(sb + col * 32 + 8 * q4 + 4 * hf) = sw;
-      }
-      __syncthreads();                       // P, dS of every wave written
-
-      // dV += P^T dO, dK += dS^T Q: contraction over the tile's 32 rows (2 steps of 16)
-#pragma unroll
-      for (int kr = 0; kr < 2; ++kr) {
-        const bf16x8 pa = read_tr(pb, 32, 16 * kr, 0, lane);   // P^T[key][rows]
-        const bf16x8 sa = read_tr(sb, 32, 16 * kr, 0, lane);   // dS^T[key][rows]
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 ob = read_tr(dot, kD, 16 * kr, 32 * dt, lane);   // dO[rows][dims]
-          const bf16x8 qb = read_tr(qt, kD, 16 * kr, 32 * dt, lane);    // Q[rows][dims]
-          dv_acc[dt] = mfma32(pa, ob, dv_acc[dt]);
-          dk_acc[dt] = mfma32(sa, qb, dk_acc[dt]);
-        }
-      }
-      // dQ of the tile's rows from this wave's keys: dS[rows][keys] K[keys][dims]
-      f32x16 dq[4] = {};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 sa = read_rows(sb, 32, 0, 16 * kk, lane);            // dS[row][keys]
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 kbf = read_tr(kb, kD, key0 + 16 * kk, 32 * dt, lane);  // K[keys][dims]
-          dq[dt] = mfma32(sa, kbf, dq[dt]);
-        }
-      }
-      // sum over the four waves and write the entries' partials, half the dims at a time
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            red[wave][8 * (rr / 4) + 4 * hf + rr % 4][32 * d2 + col] = dq[2 * half + d2][rr];
-        __syncthreads();
-        for (int i = tid; i < 32 * 64; i += 256) {
-          const int n = i / 64, dd = i % 64;
-          const int e = et + n / G;
-          if (e < e1) {
-            const float v4 = (red[0][n][dd] + red[1][n][dd]) + (red[2][n][dd] + red[3][n][dd]);
-            a.dq_part[((size_t)e * G + n % G) * kD + 64 * half + dd] = v4 * a.scale;
-          }
-        }
-        __syncthreads();
+    for (int k = 0; k < 2; ++k) {
+      const int n = tid / 16 + 16 * k;
+      qv[k] = u32x4{0u, 0u, 0u, 0u};
+      ov[k] = u32x4{0u, 0u, 0u, 0u};
+      if (eq[k] >= 0) {
+        const size_t row = (size_t)eq[k] * a.hq + g * G + n % G;
+        qv[k] = *reinterpret_cast<const u32x4*>(a.q + row * kD + 8 * c16);
+        ov[k] = *reinterpret_cast<const u32x4*>(a.dout + row * kD + 8 * c16);
       }
     }
+    lse2 = 0.f;
+    dsum = 0.f;
+    if (eqc >= 0) {
+      const size_t hrow = (size_t)eqc * a.hq + g * G + col % G;
+      lse2 = a.lse[hrow] * 1.4426950408889634f;
+      dsum = a.dsum[hrow];
+    }
+  };
+  auto store_slot = [&](int slot, const u32x4 qv[2], const u32x4 ov[2]) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int n = tid / 16 + 16 * k;
+      *reinterpret_cast<u32x4*>(qt[slot] + n * kD + 8 * c16) = qv[k];
+      *reinterpret_cast<u32x4*>(dot[slot] + n * kD + 8 * c16) = ov[k];
+    }
+  };
+
+  TileIt it{0, 0, 0, 0};
+  bool have = next_segment(a, s, g, b, lo, hi, it);
+  int cur_et = it.et, cur_e1 = it.e1;
+  int eq[2] = {-1, -1}, eqc = -1;
+  u32x4 qv[2], ov[2];
+  float lse2 = 0.f, dsum = 0.f;
+  if (have) {
+    load_rows(cur_et, cur_e1, eq, eqc);
+    load_data(eq, eqc, qv, ov, lse2, dsum);
+    store_slot(0, qv, ov);
   }
-  // dK, dV rows of the wave's keys (D layout: lane l, reg r -> key 8 (r / 4) + 4 (l / 32) +
-  // r % 4, dim 32 dt + l % 32)
+  int cur_t = eqc;
+  // the following tile
+  it.et += TE;
+  bool have_next = have && (it.et < it.e1 || next_segment(a, s, g, b, lo, hi, it));
+  int slot = 0;
+
+  while (have) {
+    __syncthreads();                         // slot written; last tile's P / dS reads done
+    const int nx_et = it.et, nx_e1 = it.e1;
+    int nq[2] = {-1, -1}, nqc = -1;
+    if (have_next) load_rows(nx_et, nx_e1, nq, nqc);
+
+    const bool row_ok = cur_t >= 0;
+    const int pos = sq.nk - sq.nq + (cur_t - sq.q0);
+    const uint16_t* const qs = qt[slot];
+    const uint16_t* const os = dot[slot];
+    // S^T and dP^T for the wave's 32 keys x the tile's 32 rows
+    f32x16 st = {}, dpt = {};
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      const bf16x8 ka = read_rows(kb, kD, key0, 16 * ks, lane);
+      const bf16x8 va = read_rows(vb, kD, key0, 16 * ks, lane);
+      const bf16x8 qb = read_rows(qs, kD, 0, 16 * ks, lane);
+      const bf16x8 ob = read_rows(os, kD, 0, 16 * ks, lane);
+      st = mfma32(ka, qb, st);
+      dpt = mfma32(va, ob, dpt);
+    }
+    // P = exp(tau S - LSE) on visible keys; dS = P (dP - D); both to the wave's buffers as
+    // [row][key] (lane (row col, half hf) holds keys 8 (r / 4) + 4 hf + r % 4 in st[r])
+    uint16_t* const pb = pbuf[wave];
+    uint16_t* const sb = sbuf[wave];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float p[4], d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 8 * q4 + 4 * hf + i;
+        const int u = u0 + key0 + m;
+        const bool vis = row_ok && u < sq.nk && !(a.causal && u > pos) &&
+                         lse2 > -__builtin_inff();
+        p[i] = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
+        d[i] = p[i] * (dpt[4 * q4 + i] - dsum);
+      }
+      u32x2 pw, sw;
+      pw[0] = pack_bf16x2(p[0], p[1]);
+      pw[1] = pack_bf16x2(p[2], p[3]);
+      sw[0] = pack_bf16x2(d[0], d[1]);
+      sw[1] = pack_bf16x2(d[2], d[3]);
+      *reinterpret_cast<u32x2*>(pb + col * 32 + 8 * q4 + 4 * hf) = pw;
+      *reinterpret_cast<u32x2*>(sb + col * 32 + 8 * q4 + 4 * hf) = sw;
+    }
+    // the following tile's data, in flight during the products below
+    if (have_next) load_data(nq, nqc, qv, ov, lse2, dsum);
+    __syncthreads();                         // P, dS of every wave written
+
+    // dV += P^T dO, dK += dS^T Q: contraction over the tile's 32 rows (2 steps of 16)
+#pragma unroll
+    for (int kr = 0; kr < 2; ++kr) {
+      const bf16x8 pa = read_tr(pb, 32, 16 * kr, 0, lane);   // P^T[key][rows]
+      const bf16x8 sa = read_tr(sb, 32, 16 * kr, 0, lane);   // dS^T[key][rows]
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 ob = read_tr(os, kD, 16 * kr, 32 * dt, lane);   // dO[rows][dims]
+        const bf16x8 qb = read_tr(qs, kD, 16 * kr, 32 * dt, lane);   // Q[rows][dims]
+        dv_acc[dt] = mfma32(pa, ob, dv_acc[dt]);
+        dk_acc[dt] = mfma32(sa, qb, dk_acc[dt]);
+      }
+    }
+    // dQ of the tile's rows, dims 32 wave .. +31, over all 128 keys: dS[rows][keys] K[keys][dims]
+    f32x16 dq = {};
+#pragma unroll
+    for (int kk = 0; kk < kBlock / 16; ++kk) {
+      const bf16x8 sa = read_rows(sbuf[kk >> 1], 32, 0, 16 * (kk & 1), lane);
+      const bf16x8 kbf = read_tr(kb, kD, 16 * kk, 32 * wave, lane);
+      dq = mfma32(sa, kbf, dq);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int n = 8 * (rr / 4) + 4 * hf + rr % 4;
+      const int e = cur_et + n / G;
+      if (e < cur_e1)
+        a.dq_part[((size_t)e * G + n % G) * kD + 32 * wave + col] = dq[rr] * a.scale;
+    }
+    if (have_next) store_slot(slot ^ 1, qv, ov);
+    slot ^= 1;
+    have = have_next;
+    cur_et = nx_et;
+    cur_e1 = nx_e1;
+    cur_t = nqc;
+    if (have) {
+      it.et += TE;
+      have_next = it.et < it.e1 || next_segment(a, s, g, b, lo, hi, it);
+    }
+  }
+  if (split) {                              // partials, summed per column in chunk order
+    float* const pk = a.dkv_part + (size_t)chunk * 2 * kBlock * kD;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int m = key0 + 8 * (rr / 4) + 4 * hf + rr % 4;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        pk[m * kD + 32 * dt + col] = dk_acc[dt][rr] * a.scale;
+        pk[(kBlock + m) * kD + 32 * dt + col] = dv_acc[dt][rr];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
     const int u = u0 + key0 + 8 * (rr / 4) + 4 * hf + rr % 4;
@@ -243,6 +322,77 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
         a.dv[row + 32 * dt + col] = dv_acc[dt][rr];
       }
     }
+  }
+}
+
+// Chunks of every column (s, g, b): ceil(entries / chunk_e), at least one for a block that
+// lies in its sequence (its dK, dV rows are written even when no query chose it), none past
+// it. One workgroup scans the columns in order: chunk_base, the chunk -> column map, and -1
+// for the unused tail of the map (the grid is sized for the bound).
+__global__ __launch_bounds__(256) void bwd_chunks_kernel(BwdArgs a, int32_t* chunk_base,
+                                                         int32_t* col_of, int n_cols,
+                                                         int chunks_max) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int run = 0;
+  for (int c0 = 0; c0 < n_cols; c0 += 256) {
+    const int c = c0 + tid;
+    int n = 0;
+    if (c < n_cols) {
+      const int b = c % a.nb_max, g = (c / a.nb_max) % a.hkv, s = c / (a.nb_max * a.hkv);
+      const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q,
+                                      a.max_k);
+      if (b * kBlock < sq.nk) {
+        int e = 0;
+        for (int r = 0; r < a.n_r; ++r) {
+          const size_t bk = bucket_at(a, s, g, r, b);
+          e += a.offsets[(bk + 1) * a.wr] - a.offsets[bk * a.wr];
+        }
+        n = max(1, (e + a.chunk_e - 1) / a.chunk_e);
+      }
+    }
+    int x = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int pre = run, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      pre += (w < wave) ? wsum[w] : 0;
+      tot += wsum[w];
+    }
+    __syncthreads();
+    pre += x - n;
+    if (c < n_cols) {
+      chunk_base[c] = pre;
+      for (int i = 0; i < n && pre + i < chunks_max; ++i) col_of[pre + i] = c;
+    }
+    run += tot;
+  }
+  if (tid == 0) chunk_base[n_cols] = run;
+  for (int i = run + tid; i < chunks_max; i += 256) col_of[i] = -1;
+}
+
+// dK, dV of split columns: the chunks' partials added in chunk order (deterministic).
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a) {
+  const int cl = blockIdx.x, tid = threadIdx.x;
+  const int c0 = a.chunk_base[cl], c1 = a.chunk_base[cl + 1];
+  if (c1 - c0 < 2) return;
+  const int b = cl % a.nb_max, g = (cl / a.nb_max) % a.hkv, s = cl / (a.nb_max * a.hkv);
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  for (int i = tid; i < 2 * kBlock * kD / 4; i += 256) {
+    const int m = (i / (kD / 4)) % kBlock, which = i / (kBlock * kD / 4);
+    const int u = b * kBlock + m;
+    if (u >= sq.nk) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = c0; c < c1; ++c)
+      acc += reinterpret_cast<const f32x4*>(a.dkv_part + (size_t)c * 2 * kBlock * kD)[i];
+    float* const dst = which ? a.dv : a.dk;
+    reinterpret_cast<f32x4*>(dst + ((size_t)(sq.k0 + u) * a.hkv + g) * kD)[i % (kD / 4)] = acc;
   }
 }
 
@@ -275,18 +425,46 @@ __global__ __launch_bounds__(256) void bwd_clear_kernel(int32_t* __restrict__ p,
 }
 
 template <int G>
-hipError_t launch_kv_g(const msa_shape& s, const Geometry& g, const BwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_kv_kernel<G>), dim3((unsigned)g.nb_max, s.hkv, s.batch), dim3(256), 0,
-                     st, a);
+hipError_t launch_kv_g(const BwdArgs& a, int64_t chunks_max, hipStream_t st) {
+  hipLaunchKernelGGL((bwd_kv_kernel<G>), dim3((unsigned)chunks_max), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// Rows (query heads) per chunk of a column; a chunk is 128 tiles of 32 rows.
+constexpr int kChunkRows = 4096;
+
+struct BwdGeometry {
+  int64_t n_cols, chunks_max;
+  size_t off_dq, off_base, off_col, off_kv, total;
+};
+
+BwdGeometry bwd_geometry(const msa_shape& s) {
+  const Geometry g = geometry(s, MSA_KV_OUTER);
+  const Layout L = layout(s, MSA_KV_OUTER);
+  BwdGeometry b;
+  b.n_cols = (int64_t)s.batch * s.hkv * g.nb_max;
+  b.chunks_max = g.e_max / (kChunkRows / g.group) + b.n_cols;
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  b.off_dq = take((size_t)g.e_max * g.group * kD * 4);
+  b.off_base = take((size_t)(b.n_cols + 1) * 4);
+  b.off_col = take((size_t)b.chunks_max * 4);
+  b.off_kv = take((size_t)b.chunks_max * 2 * kBlock * kD * 4);
+  b.total = off;
+  return b;
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(const msa_shape& s) {
-  const Layout L = layout(s, MSA_KV_OUTER);
-  const Geometry g = geometry(s, MSA_KV_OUTER);
-  return L.total + align256((size_t)g.e_max * g.group * kD * 4);
+size_t bwd_workspace_bytes(const msa_shape& s) { return bwd_geometry(s).total; }
+
+bool bwd_fits(const msa_shape& s) {
+  const BwdGeometry b = bwd_geometry(s);
+  return b.chunks_max < (1LL << 31) && b.n_cols + 1 < (1LL << 31);
 }
 
 hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const void* v,
@@ -321,7 +499,12 @@ hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const vo
   a.cu_k = cu_k;
   a.offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
   a.entry_q = reinterpret_cast<const int32_t*>(ws + L.entry_q);
-  a.dq_part = reinterpret_cast<float*>(ws + L.total);
+  const BwdGeometry bg = bwd_geometry(s);
+  a.dq_part = reinterpret_cast<float*>(ws + bg.off_dq);
+  a.chunk_base = reinterpret_cast<const int32_t*>(ws + bg.off_base);
+  a.col_of = reinterpret_cast<const int32_t*>(ws + bg.off_col);
+  a.dkv_part = reinterpret_cast<float*>(ws + bg.off_kv);
+  a.chunk_e = kChunkRows / g.group;
   a.dk = dk;
   a.dv = dv;
   a.scale = scale;
@@ -336,14 +519,21 @@ hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const vo
   a.wr = (int)g.wr;
   a.n_r = (int)g.n_r;
   a.causal = s.causal;
-  if (g.nb_max > 0) {
+  if (bg.n_cols > 0) {
+    hipLaunchKernelGGL(bwd_chunks_kernel, dim3(1), dim3(256), 0, st, a,
+                       reinterpret_cast<int32_t*>(ws + bg.off_base),
+                       reinterpret_cast<int32_t*>(ws + bg.off_col), (int)bg.n_cols,
+                       (int)bg.chunks_max);
     switch (g.group) {
-      case 1: e = launch_kv_g<1>(s, g, a, st); break;
-      case 2: e = launch_kv_g<2>(s, g, a, st); break;
-      case 4: e = launch_kv_g<4>(s, g, a, st); break;
-      case 8: e = launch_kv_g<8>(s, g, a, st); break;
-      default: e = launch_kv_g<16>(s, g, a, st); break;
+      case 1: e = launch_kv_g<1>(a, bg.chunks_max, st); break;
+      case 2: e = launch_kv_g<2>(a, bg.chunks_max, st); break;
+      case 4: e = launch_kv_g<4>(a, bg.chunks_max, st); break;
+      case 8: e = launch_kv_g<8>(a, bg.chunks_max, st); break;
+      default: e = launch_kv_g<16>(a, bg.chunks_max, st); break;
     }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)bg.n_cols), dim3(256), 0, st, a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t n = (int64_t)rows * 32;

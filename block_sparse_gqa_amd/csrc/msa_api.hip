@@ -340,6 +340,7 @@ msa_status msa_bwd_workspace_size(const msa_shape* shape, size_t* bytes) {
   if (st != MSA_OK) return st;
   if (!bytes) return MSA_ERR_NULL;
   if (shape->dtype != MSA_BF16) return MSA_ERR_DTYPE;
+  if (!bwd_fits(*shape)) return MSA_ERR_SHAPE;
   *bytes = bwd_workspace_bytes(*shape);
   return MSA_OK;
 }
@@ -354,6 +355,7 @@ msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
   if (s.dtype != MSA_BF16) return MSA_ERR_DTYPE;
+  if (!bwd_fits(s)) return MSA_ERR_SHAPE;
   if (!topk_idx || !cu_q || !cu_k) return MSA_ERR_NULL;
   if (s.total_q > 0 && (!q || !o || !lse || !dout || !dq)) return MSA_ERR_NULL;
   if (s.total_k > 0 && (!k || !v || !dk || !dv)) return MSA_ERR_NULL;

@@ -121,6 +121,7 @@ hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L
                           const char* ws, void* o, float* lse, hipStream_t st);
 // Main-branch backward: workspace = the KV-outer plan, then fp32 dQ partials [E, group, d].
 size_t bwd_workspace_bytes(const msa_shape& s);
+bool bwd_fits(const msa_shape& s);   // chunk and column counts within 32-bit indexing
 hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, float scale,
                       const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k, char* ws,

@@ -34,6 +34,10 @@ CASES = [
     # G = 2 and G = 8
     ("g2", dict(n_q=(520,), n_k=(1300,), hq=4, hkv=2, topk=3)),
     ("g8_decode", dict(n_q=(1, 2, 3), n_k=(4096 + 77, 256, 130), hq=16, hkv=2, topk=8)),
+    # every query selects every block: columns of 4500 entries split into two chunks of 4096
+    # rows whose dK / dV partials are summed (G = 1), and many chunks per column at G = 16
+    ("g1_split_columns", dict(n_q=(4500,), n_k=(600,), hq=1, hkv=1, topk=5, causal=False)),
+    ("g16_split_columns", dict(n_q=(1100,), n_k=(512,), hq=16, hkv=1, topk=4, causal=False)),
     # per-Q-tile lists (list_q = 128) drawn by the case
     ("g8_tile_lists", dict(n_q=(384, 200), n_k=(1024, 640), hq=8, hkv=1, topk=4, list_q=128,
                            list_pool=8)),
