@@ -48,6 +48,31 @@ __device__ __forceinline__ bf16x8 read_rows(const uint16_t* buf, int rs, int r0,
                                                    8 * (lane >> 5)));
 }
 
+// 128-wide bf16 tiles in LDS are stored with their 16-byte chunks XOR-swizzled by the row
+// (chunk c of row r at c ^ (r % 16)), so that the 32 rows one fragment read touches, and the
+// 4 rows of each transpose load, fall in different banks.
+__device__ __forceinline__ int sw(int row, int col) {
+  return row * kD + ((((col >> 3) ^ row) & 15) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ bf16x8 read_rows_sw(const uint16_t* buf, int r0, int c0, int lane) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + sw(r0 + (lane & 31),
+                                                            c0 + 8 * (lane >> 5))));
+}
+
+__device__ __forceinline__ bf16x8 read_tr_sw(const uint16_t* buf, int r0, int c0, int lane) {
+  const int i = lane & 15, grp = (lane >> 4) & 1, kb = lane >> 5;
+  const int col = c0 + 16 * grp + 4 * (i & 3);
+  s4 r[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int row = r0 + 8 * kb + 4 * h2 + (i >> 2);
+    r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4*)(buf + sw(row, col)));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // D[t, h] = sum_d dO[t, h, d] O[t, h, d] (fp32), one wave per row of 128.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
@@ -139,8 +164,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
   for (int i = tid; i < kBlock * kD / 8; i += 256) {
     const int row = i / (kD / 8), c = i % (kD / 8);
     const size_t src = ((size_t)(sq.k0 + min(u0 + row, sq.nk - 1)) * a.hkv + g) * kD + 8 * c;
-    *reinterpret_cast<u32x4*>(kb + row * kD + 8 * c) = *reinterpret_cast<const u32x4*>(a.k + src);
-    *reinterpret_cast<u32x4*>(vb + row * kD + 8 * c) = *reinterpret_cast<const u32x4*>(a.v + src);
+    *reinterpret_cast<u32x4*>(kb + sw(row, 8 * c)) = *reinterpret_cast<const u32x4*>(a.k + src);
+    *reinterpret_cast<u32x4*>(vb + sw(row, 8 * c)) = *reinterpret_cast<const u32x4*>(a.v + src);
   }
 
   f32x16 dk_acc[4], dv_acc[4];
@@ -188,8 +213,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int n = tid / 16 + 16 * k;
-      *reinterpret_cast<u32x4*>(qt[slot] + n * kD + 8 * c16) = qv[k];
-      *reinterpret_cast<u32x4*>(dot[slot] + n * kD + 8 * c16) = ov[k];
+      *reinterpret_cast<u32x4*>(qt[slot] + sw(n, 8 * c16)) = qv[k];
+      *reinterpret_cast<u32x4*>(dot[slot] + sw(n, 8 * c16)) = ov[k];
     }
   };
 
@@ -224,10 +249,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
-      const bf16x8 ka = read_rows(kb, kD, key0, 16 * ks, lane);
-      const bf16x8 va = read_rows(vb, kD, key0, 16 * ks, lane);
-      const bf16x8 qb = read_rows(qs, kD, 0, 16 * ks, lane);
-      const bf16x8 ob = read_rows(os, kD, 0, 16 * ks, lane);
+      const bf16x8 ka = read_rows_sw(kb, key0, 16 * ks, lane);
+      const bf16x8 va = read_rows_sw(vb, key0, 16 * ks, lane);
+      const bf16x8 qb = read_rows_sw(qs, 0, 16 * ks, lane);
+      const bf16x8 ob = read_rows_sw(os, 0, 16 * ks, lane);
       st = mfma32(ka, qb, st);
       dpt = mfma32(va, ob, dpt);
     }
@@ -266,8 +291,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
       const bf16x8 sa = read_tr(sb, 32, 16 * kr, 0, lane);   // dS^T[key][rows]
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 ob = read_tr(os, kD, 16 * kr, 32 * dt, lane);   // dO[rows][dims]
-        const bf16x8 qb = read_tr(qs, kD, 16 * kr, 32 * dt, lane);   // Q[rows][dims]
+        const bf16x8 ob = read_tr_sw(os, 16 * kr, 32 * dt, lane);   // dO[rows][dims]
+        const bf16x8 qb = read_tr_sw(qs, 16 * kr, 32 * dt, lane);   // Q[rows][dims]
         dv_acc[dt] = mfma32(pa, ob, dv_acc[dt]);
         dk_acc[dt] = mfma32(sa, qb, dk_acc[dt]);
       }
@@ -277,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < kBlock / 16; ++kk) {
       const bf16x8 sa = read_rows(sbuf[kk >> 1], 32, 0, 16 * (kk & 1), lane);
-      const bf16x8 kbf = read_tr(kb, kD, 16 * kk, 32 * wave, lane);
+      const bf16x8 kbf = read_tr_sw(kb, 16 * kk, 32 * wave, lane);
       dq = mfma32(sa, kbf, dq);
     }
 #pragma unroll
