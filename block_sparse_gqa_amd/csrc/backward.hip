@@ -101,7 +101,7 @@ struct BwdArgs {
   const int32_t* entry_q;
   const int32_t* chunk_base;   // [n_cols + 1]: first chunk of each (sequence, group, block)
   const int32_t* col_of;       // [chunks]: the column of each chunk
-  float* dq_part;
+  uint16_t* dq_part;           // [E][G][kD] bf16: each entry's dQ contribution
   float* dkv_part;             // [chunks][2][kBlock][kD]: dK, dV of chunks of split columns
   float* dk;
   float* dv;
@@ -218,6 +218,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     }
   };
 
+  __syncthreads();                           // K_b, V_b staged
+  // the wave's K and V rows as A operands of S^T and dP^T, kept for the whole chunk
+  bf16x8 kf[kD / 16], vf[kD / 16];
+#pragma unroll
+  for (int ks = 0; ks < kD / 16; ++ks) {
+    kf[ks] = read_rows_sw(kb, key0, 16 * ks, lane);
+    vf[ks] = read_rows_sw(vb, key0, 16 * ks, lane);
+  }
+
   TileIt it{0, 0, 0, 0};
   bool have = next_segment(a, s, g, b, lo, hi, it);
   int cur_et = it.et, cur_e1 = it.e1;
@@ -249,12 +258,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
-      const bf16x8 ka = read_rows_sw(kb, key0, 16 * ks, lane);
-      const bf16x8 va = read_rows_sw(vb, key0, 16 * ks, lane);
       const bf16x8 qb = read_rows_sw(qs, 0, 16 * ks, lane);
       const bf16x8 ob = read_rows_sw(os, 0, 16 * ks, lane);
-      st = mfma32(ka, qb, st);
-      dpt = mfma32(va, ob, dpt);
+      st = mfma32(kf[ks], qb, st);
+      dpt = mfma32(vf[ks], ob, dpt);
     }
     // P = exp(tau S - LSE) on visible keys; dS = P (dP - D); both to the wave's buffers as
     // [row][key] (lane (row col, half hf) holds keys 8 (r / 4) + 4 hf + r % 4 in st[r])
@@ -298,19 +305,24 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
       }
     }
     // dQ of the tile's rows, dims 32 wave .. +31, over all 128 keys: dS[rows][keys] K[keys][dims]
-    f32x16 dq = {};
+    f32x16 dq0 = {}, dq1 = {};
 #pragma unroll
-    for (int kk = 0; kk < kBlock / 16; ++kk) {
-      const bf16x8 sa = read_rows(sbuf[kk >> 1], 32, 0, 16 * (kk & 1), lane);
-      const bf16x8 kbf = read_tr_sw(kb, 16 * kk, 32 * wave, lane);
-      dq = mfma32(sa, kbf, dq);
+    for (int kk = 0; kk < kBlock / 16; kk += 2) {
+      const bf16x8 s0 = read_rows(sbuf[kk >> 1], 32, 0, 0, lane);
+      const bf16x8 k0 = read_tr_sw(kb, 16 * kk, 32 * wave, lane);
+      const bf16x8 s1 = read_rows(sbuf[kk >> 1], 32, 0, 16, lane);
+      const bf16x8 k1 = read_tr_sw(kb, 16 * kk + 16, 32 * wave, lane);
+      dq0 = mfma32(s0, k0, dq0);
+      dq1 = mfma32(s1, k1, dq1);
     }
+    const f32x16 dq = dq0 + dq1;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const int n = 8 * (rr / 4) + 4 * hf + rr % 4;
       const int e = cur_et + n / G;
       if (e < cur_e1)
-        a.dq_part[((size_t)e * G + n % G) * kD + 32 * wave + col] = dq[rr] * a.scale;
+        a.dq_part[((size_t)e * G + n % G) * kD + 32 * wave + col] =
+            (uint16_t)f32_to_bf16_bits(dq[rr] * a.scale);
     }
     if (have_next) store_slot(slot ^ 1, qv, ov);
     slot ^= 1;
@@ -424,7 +436,7 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a) {
 // dQ[t, h] = sum over the (query, group)'s entries of their partials (the combine map), one
 // thread per 4 dims of a (query, head) row.
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ cmap,
-                                                     const float* __restrict__ dq_part,
+                                                     const uint16_t* __restrict__ dq_part,
                                                      float* __restrict__ dq, int64_t n, int hq,
                                                      int group, int topk) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -438,7 +450,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__
   for (int k = 0; k < topk; ++k) {
     const int e = cm[k];
     if (e < 0) continue;
-    acc += *reinterpret_cast<const f32x4*>(dq_part + ((size_t)e * group + gi) * kD + 4 * c);
+    const u32x2 w = *reinterpret_cast<const u32x2*>(dq_part + ((size_t)e * group + gi) * kD + 4 * c);
+    acc[0] += bf16_bits_to_f32(w[0] & 0xFFFFu);
+    acc[1] += bf16_bits_to_f32(w[0] >> 16);
+    acc[2] += bf16_bits_to_f32(w[1] & 0xFFFFu);
+    acc[3] += bf16_bits_to_f32(w[1] >> 16);
   }
   *reinterpret_cast<f32x4*>(dq + row * kD + 4 * c) = acc;
 }
@@ -475,7 +491,7 @@ BwdGeometry bwd_geometry(const msa_shape& s) {
     off += align256(bytes);
     return at;
   };
-  b.off_dq = take((size_t)g.e_max * g.group * kD * 4);
+  b.off_dq = take((size_t)g.e_max * g.group * kD * 2);
   b.off_base = take((size_t)(b.n_cols + 1) * 4);
   b.off_col = take((size_t)b.chunks_max * 4);
   b.off_kv = take((size_t)b.chunks_max * 2 * kBlock * kD * 4);
@@ -525,7 +541,7 @@ hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const vo
   a.offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
   a.entry_q = reinterpret_cast<const int32_t*>(ws + L.entry_q);
   const BwdGeometry bg = bwd_geometry(s);
-  a.dq_part = reinterpret_cast<float*>(ws + bg.off_dq);
+  a.dq_part = reinterpret_cast<uint16_t*>(ws + bg.off_dq);
   a.chunk_base = reinterpret_cast<const int32_t*>(ws + bg.off_base);
   a.col_of = reinterpret_cast<const int32_t*>(ws + bg.off_col);
   a.dkv_part = reinterpret_cast<float*>(ws + bg.off_kv);

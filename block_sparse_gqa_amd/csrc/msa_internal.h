@@ -119,7 +119,8 @@ hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
                          const int32_t* cu_k, char* ws, void* o, float* lse, hipStream_t st);
 hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L,
                           const char* ws, void* o, float* lse, hipStream_t st);
-// Main-branch backward: workspace = the KV-outer plan, then fp32 dQ partials [E, group, d].
+// Main-branch backward: workspace = the KV-outer plan, bf16 dQ partials [E, group, d], the
+// chunk map and fp32 dK / dV partials of chunks of split columns.
 size_t bwd_workspace_bytes(const msa_shape& s);
 bool bwd_fits(const msa_shape& s);   // chunk and column counts within 32-bit indexing
 hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const void* v,

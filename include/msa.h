@@ -262,8 +262,8 @@ msa_status msa_combine(const msa_shape* shape, msa_mode mode, const void* worksp
  * [total_q, hq, d]; dk, dv [total_k, hkv, d]. Every row of dq is written (zero for rows with
  * no visible key or in no sequence); dk and dv rows of keys in a sequence are written (zero
  * for keys no query sees), other rows are not touched. Deterministic: no atomics. Workspace:
- * msa_bwd_workspace_size bytes (the KV-outer plan plus fp32 dQ partials of every
- * (query-group, block) entry: E x hq/hkv x d x 4 bytes). */
+ * msa_bwd_workspace_size bytes (the KV-outer plan plus bf16 dQ partials of every
+ * (query-group, block) entry: E x hq/hkv x d x 2 bytes). */
 msa_status msa_bwd_workspace_size(const msa_shape* shape, size_t* bytes);
 msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k,
                                const void* v, const void* o, const float* lse, const void* dout,

@@ -306,10 +306,10 @@ def test_backward_argument_checks(L):
     fwd = msa.msa_workspace_size(s, msa.MSA_KV_OUTER)
     lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
     e_max = s.total_q * s.hkv * s.topk
-    # plan, fp32 dQ partials, and per chunk of 4096 rows (at most E / 256 + 4 x 256 chunks at
+    # plan, bf16 dQ partials, and per chunk of 4096 rows (at most E / 256 + 4 x 256 chunks at
     # G = 16) its column and a 128 KiB dK / dV partial
     chunks = e_max // 256 + 4 * 256
-    extra = need - fwd - e_max * (s.hq // s.hkv) * 128 * 4
+    extra = need - fwd - e_max * (s.hq // s.hkv) * 128 * 2
     assert extra - ((4 * 256 + 1) * 4 + chunks * 4 + chunks * 2 * 128 * 128 * 4) in range(0, 1024)
     assert lay.part_lse + s.total_q * s.hq * 4 <= lay.part_l     # the D rows fit the LSE region
 
