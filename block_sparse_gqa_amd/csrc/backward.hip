@@ -73,19 +73,22 @@ __device__ __forceinline__ bf16x8 read_tr_sw(const uint16_t* buf, int r0, int c0
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// D[t, h] = sum_d dO[t, h, d] O[t, h, d] (fp32), one wave per row of 128.
+// D[t, h] = sum_d dO[t, h, d] O[t, h, d] (fp32): 16 lanes per row of 128, 16-byte loads.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
                                                        float* __restrict__ dsum, int rows) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
   if (row >= rows) return;
-  const uint32_t a = reinterpret_cast<const uint32_t*>(o + (size_t)row * kD)[lane];
-  const uint32_t b = reinterpret_cast<const uint32_t*>(dout + (size_t)row * kD)[lane];
-  float v = bf16_bits_to_f32(a & 0xFFFFu) * bf16_bits_to_f32(b & 0xFFFFu) +
-            bf16_bits_to_f32(a >> 16) * bf16_bits_to_f32(b >> 16);
+  const u32x4 x = *reinterpret_cast<const u32x4*>(o + (size_t)row * kD + 8 * c);
+  const u32x4 y = *reinterpret_cast<const u32x4*>(dout + (size_t)row * kD + 8 * c);
+  float v = 0.f;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += shfl_xor_f(v, off);
-  if (lane == 0) dsum[row] = v;
+  for (int i = 0; i < 4; ++i)
+    v += bf16_bits_to_f32(x[i] & 0xFFFFu) * bf16_bits_to_f32(y[i] & 0xFFFFu) +
+         bf16_bits_to_f32(x[i] >> 16) * bf16_bits_to_f32(y[i] >> 16);
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) v += shfl_xor_f(v, off);
+  if (c == 0) dsum[row] = v;
 }
 
 struct BwdArgs {
@@ -414,18 +417,22 @@ __global__ __launch_bounds__(256) void bwd_chunks_kernel(BwdArgs a, int32_t* chu
   for (int i = run + tid; i < chunks_max; i += 256) col_of[i] = -1;
 }
 
-// dK, dV of split columns: the chunks' partials added in chunk order (deterministic).
+// dK, dV of split columns: the chunks' partials added in chunk order (deterministic). Eight
+// workgroups per column, each over 1 / 8 of its 2 x 128 x 128 values.
+constexpr int kReduceParts = 8;
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a) {
   const int cl = blockIdx.x, tid = threadIdx.x;
+  constexpr int kPer = 2 * kBlock * kD / 4 / kReduceParts;   // float4 values per workgroup
   const int c0 = a.chunk_base[cl], c1 = a.chunk_base[cl + 1];
   if (c1 - c0 < 2) return;
   const int b = cl % a.nb_max, g = (cl / a.nb_max) % a.hkv, s = cl / (a.nb_max * a.hkv);
   const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
-  for (int i = tid; i < 2 * kBlock * kD / 4; i += 256) {
+  for (int i = blockIdx.y * kPer + tid; i < (blockIdx.y + 1) * kPer; i += 256) {
     const int m = (i / (kD / 4)) % kBlock, which = i / (kBlock * kD / 4);
     const int u = b * kBlock + m;
     if (u >= sq.nk) continue;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int c = c0; c < c1; ++c)
       acc += reinterpret_cast<const f32x4*>(a.dkv_part + (size_t)c * 2 * kBlock * kD)[i];
     float* const dst = which ? a.dv : a.dk;
@@ -524,7 +531,7 @@ hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const vo
   float* const dsum = reinterpret_cast<float*>(ws + L.part_lse);   // [total_q, hq]
   const int rows = s.total_q * s.hq;
   if (rows > 0) {
-    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
                        (const uint16_t*)o, (const uint16_t*)dout, dsum, rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -573,7 +580,8 @@ hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const vo
       default: e = launch_kv_g<16>(a, bg.chunks_max, st); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)bg.n_cols), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)bg.n_cols, kReduceParts), dim3(256), 0,
+                       st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
