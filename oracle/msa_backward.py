@@ -89,3 +89,29 @@ def run_case(case, dout, lists: np.ndarray | None = None):
                                       case.softmax_scale, cfg.block, cfg.causal)
         dq[q0:q1], dk[k0:k1], dv[k0:k1], o[q0:q1], lse[q0:q1] = r
     return dq, dk, dv, o, lse, lists
+
+
+def query_rows_gradient(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_rows: np.ndarray,
+                        do_rows: np.ndarray, rows: np.ndarray, scale: float, block: int,
+                        causal: bool) -> np.ndarray:
+    """dQ of the given query ``rows`` of one sequence only (each row's dQ depends on its own
+    list, O and LSE alone): q [N, Hq, D], k / v [Nk, Hkv, D], sel_rows [R, Hkv, K], do_rows
+    [R, Hq, D]; the same formulas as sparse_attention_backward. Returns [R, Hq, D]."""
+    n_q, hq, _ = q.shape
+    n_k, hkv, _ = k.shape
+    grp = hq // hkv
+    pos = query_positions(n_q, n_k)
+    out = np.zeros((rows.size, hq, q.shape[2]))
+    for r, i in enumerate(rows):
+        for g in range(hkv):
+            keys = _key_set(sel_rows[r, g], n_k, block, int(pos[i]), causal)
+            if keys.size == 0:
+                continue
+            heads = slice(g * grp, (g + 1) * grp)
+            kk, vv = k[keys, g], v[keys, g]
+            oi, li = attend(q[i, heads], kk, vv, scale)
+            p = np.exp(scale * (q[i, heads] @ kk.T) - li[:, None])
+            ds = p * (do_rows[r, heads] @ vv.T - np.sum(do_rows[r, heads] * oi, axis=1,
+                                                         keepdims=True))
+            out[r, heads] = scale * (ds @ kk)
+    return out

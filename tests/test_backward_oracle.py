@@ -101,3 +101,20 @@ def test_backward_finite_differences():
         minus = dict(args); minus[which] = args[which] - eps * e
         fd = (loss(plus["q"], plus["k"], plus["v"]) - loss(minus["q"], minus["k"], minus["v"])) / (2 * eps)
         assert abs(fd - float(np.sum(grad * e))) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_row_gradient_matches_the_whole_sequence_backward():
+    """dQ of sampled rows alone (used at full size) equals the whole-sequence backward's."""
+    from oracle import msa_case
+    from oracle.msa_backward import query_rows_gradient, sparse_attention_backward
+    from synth import msa_inputs as mi
+    from synth.msa_inputs import widen
+    cfg = mi.custom("rows", n_q=(300,), n_k=(700,), hq=8, hkv=2, topk=4)
+    case = mi.make_case(cfg, seed=3)
+    do = widen(mi.grad_output(case))
+    q, k, v = widen(case.q), widen(case.k), widen(case.v)
+    lists = msa_case.run(case, want_output=False).topk_idx
+    dq = sparse_attention_backward(q, k, v, lists, do, case.softmax_scale, 128, True)[0]
+    rows = np.array([0, 5, 150, 299])
+    got = query_rows_gradient(q, k, v, lists[rows], do[rows], rows, case.softmax_scale, 128, True)
+    assert np.array_equal(got, dq[rows])
