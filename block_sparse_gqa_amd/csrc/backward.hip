@@ -472,6 +472,286 @@ __global__ __launch_bounds__(256) void bwd_clear_kernel(int32_t* __restrict__ p,
   if (i < n) p[i] = -1;
 }
 
+// ---------------------------------------------------------------------------------------
+// Proxy (index-branch) backward. Per (query, group) over the same selected keys as the main
+// branch: T = the main weights averaged over the group's G heads (recomputed from Q, K and
+// the main LSE; held fixed), Pp = exp(tau_p z - LSEp) with z = q_idx . k_idx, and the
+// gradients of sum KL(T || Pp): dz = tau_p (Pp - T), dq_idx = dz k_idx, dk_idx = dz^T q_idx.
+// The proxy LSE is recomputed over the sparse keys first (one wave per (query, group)).
+
+struct ProxyArgs {
+  BwdArgs b;                   // main-branch fields: Q, K, main LSE, plan, chunks
+  const uint16_t* q_idx;
+  const uint16_t* k_idx;
+  const float* lsep;           // [total_q, hkv] proxy LSE (natural log)
+  float* dqi_part;             // [E][dp]: each entry's dq_idx contribution
+  float* dki_part;             // [chunks][kBlock][dp]: dk_idx of chunks of split columns
+  float* dk_idx;
+  float pscale, pscale_log2;
+};
+
+template <int DP>
+__global__ __launch_bounds__(256) void proxy_lse_kernel(ProxyArgs pa, const int32_t* lists,
+                                                        float* lsep, int topk, int list_q,
+                                                        int tiles_max, int batch) {
+  const BwdArgs& a = pa.b;
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = gw / a.hkv, g = gw % a.hkv;
+  if (t >= a.total_q) return;
+  // the sequence holding row t (cu_q non-decreasing)
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_q[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  const int il = t - sq.q0;
+  float m = -__builtin_inff(), l = 0.f;
+  if (il >= 0 && il < sq.nq) {
+    float qv[DP];
+#pragma unroll
+    for (int c = 0; c < DP / 8; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(pa.q_idx + ((size_t)t * a.hkv + g) * DP + 8 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qv[8 * c + 2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+        qv[8 * c + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    }
+    const int64_t row = list_q == 1 ? (int64_t)t : (int64_t)s * tiles_max + il / list_q;
+    const int32_t* L = lists + (row * a.hkv + g) * topk;
+    const int nb = (sq.nk + kBlock - 1) / kBlock;
+    const int pos = sq.nk - sq.nq + il;
+    for (int k = 0; k < topk; ++k) {
+      const int b = L[k];
+      bool ok = b >= 0 && b < nb && !(a.causal && b * kBlock > pos);
+      for (int p = 0; p < k && ok; ++p) ok = L[p] != b;
+      if (!ok) continue;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int u = b * kBlock + lane + 64 * jj;
+        if (u >= sq.nk || (a.causal && u > pos)) continue;
+        const uint16_t* kr = pa.k_idx + ((size_t)(sq.k0 + u) * a.hkv + g) * DP;
+        float z = 0.f;
+#pragma unroll
+        for (int c = 0; c < DP / 8; ++c) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 8 * c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            z = fmaf(qv[8 * c + 2 * i], bf16_bits_to_f32(w[i] & 0xFFFFu), z);
+            z = fmaf(qv[8 * c + 2 * i + 1], bf16_bits_to_f32(w[i] >> 16), z);
+          }
+        }
+        const float zs = z * pa.pscale_log2;
+        const float mn = fmaxf(m, zs);
+        l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(zs - mn);
+        m = mn;
+      }
+    }
+  }
+  // wave reduction of (max, sum)
+  float mw = m;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) mw = fmaxf(mw, shfl_xor_f(mw, off));
+  float lw = mw == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f(m - mw);
+  if (m == -__builtin_inff()) lw = 0.f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) lw += shfl_xor_f(lw, off);
+  if (lane == 0)
+    lsep[(size_t)t * a.hkv + g] =
+        mw == -__builtin_inff() ? -__builtin_inff() : (mw + log2f(lw)) * 0.6931471805599453f;
+}
+
+template <int G, int DP>
+__global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
+  const BwdArgs& a = pa.b;
+  constexpr int TE = 32 / G;
+  __shared__ uint16_t kb[kBlock * kD];       // K_b (swizzled)
+  __shared__ uint16_t kib[kBlock * DP];      // k_idx of the block, row-major
+  __shared__ uint16_t qt[32 * kD];           // the tile's Q rows (swizzled)
+  __shared__ uint16_t qit[32 * DP];          // row n: q_idx of the entry of row n
+  __shared__ uint16_t zbuf[4][32 * 32];      // per wave: dz / G of its keys, [row][key]
+
+  const int chunk = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int cl = a.col_of[chunk];
+  if (cl < 0) return;
+  const int b = cl % a.nb_max, g = (cl / a.nb_max) % a.hkv, s = cl / (a.nb_max * a.hkv);
+  const int j = chunk - a.chunk_base[cl];
+  const bool split = a.chunk_base[cl + 1] - a.chunk_base[cl] > 1;
+  const int lo = j * a.chunk_e, hi = lo + a.chunk_e;
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  const int u0 = b * kBlock;
+
+  for (int i = tid; i < kBlock * kD / 8; i += 256) {
+    const int row = i / (kD / 8), c = i % (kD / 8);
+    const size_t src = ((size_t)(sq.k0 + min(u0 + row, sq.nk - 1)) * a.hkv + g) * kD + 8 * c;
+    *reinterpret_cast<u32x4*>(kb + sw(row, 8 * c)) = *reinterpret_cast<const u32x4*>(a.k + src);
+  }
+  for (int i = tid; i < kBlock * DP / 8; i += 256) {
+    const int row = i / (DP / 8), c = i % (DP / 8);
+    const size_t src = ((size_t)(sq.k0 + min(u0 + row, sq.nk - 1)) * a.hkv + g) * DP + 8 * c;
+    *reinterpret_cast<u32x4*>(kib + row * DP + 8 * c) =
+        *reinterpret_cast<const u32x4*>(pa.k_idx + src);
+  }
+  __syncthreads();
+  const int key0 = 32 * wave;
+  bf16x8 kf[kD / 16], kif[DP / 16];
+#pragma unroll
+  for (int ks = 0; ks < kD / 16; ++ks) kf[ks] = read_rows_sw(kb, key0, 16 * ks, lane);
+#pragma unroll
+  for (int ks = 0; ks < DP / 16; ++ks) kif[ks] = read_rows(kib, DP, key0, 16 * ks, lane);
+  f32x16 acc[DP / 32];
+#pragma unroll
+  for (int dt = 0; dt < DP / 32; ++dt) acc[dt] = f32x16{};
+
+  TileIt it{0, 0, 0, 0};
+  bool have = next_segment(a, s, g, b, lo, hi, it);
+  while (have) {
+    const int et = it.et, e1 = it.e1;
+    __syncthreads();                         // last tile's reads done
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int n = tid / 16 + 16 * k, c = tid % 16;
+      const int e = et + n / G;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (e < e1)
+        v = *reinterpret_cast<const u32x4*>(
+            a.q + ((size_t)a.entry_q[e] * a.hq + g * G + n % G) * kD + 8 * c);
+      *reinterpret_cast<u32x4*>(qt + sw(n, 8 * c)) = v;
+    }
+    if (tid < 32 * DP / 8) {
+      const int n = tid / (DP / 8), c = tid % (DP / 8);
+      const int e = et + n / G;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (e < e1)
+        v = *reinterpret_cast<const u32x4*>(pa.q_idx + ((size_t)a.entry_q[e] * a.hkv + g) * DP +
+                                            8 * c);
+      *reinterpret_cast<u32x4*>(qit + n * DP + 8 * c) = v;
+    }
+    const int e_row = et + col / G;
+    const bool row_ok = e_row < e1;
+    int t = 0;
+    float lse2 = -__builtin_inff(), lsep2 = -__builtin_inff();
+    if (row_ok) {
+      t = a.entry_q[e_row];
+      lse2 = a.lse[(size_t)t * a.hq + g * G + col % G] * 1.4426950408889634f;
+      lsep2 = pa.lsep[(size_t)t * a.hkv + g] * 1.4426950408889634f;
+    }
+    const int pos = sq.nk - sq.nq + (t - sq.q0);
+    __syncthreads();
+
+    f32x16 st = {}, zt = {};
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks)
+      st = mfma32(kf[ks], read_rows_sw(qt, 0, 16 * ks, lane), st);
+#pragma unroll
+    for (int ks = 0; ks < DP / 16; ++ks)
+      zt = mfma32(kif[ks], read_rows(qit, DP, 0, 16 * ks, lane), zt);
+    uint16_t* const zb = zbuf[wave];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      float d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 8 * q4 + 4 * hf + i;
+        const int u = u0 + key0 + m;
+        const bool vis = row_ok && u < sq.nk && !(a.causal && u > pos) &&
+                         lse2 > -__builtin_inff() && lsep2 > -__builtin_inff();
+        float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
+#pragma unroll
+        for (int o = 1; o < G; o <<= 1) p += shfl_xor_f(p, o);   // sum over the entry's heads
+        const float pp =
+            vis ? __builtin_amdgcn_exp2f(fmaf(zt[4 * q4 + i], pa.pscale_log2, -lsep2)) : 0.f;
+        d[i] = pa.pscale * (pp - p * (1.f / G)) * (1.f / G);
+      }
+      u32x2 w;
+      w[0] = pack_bf16x2(d[0], d[1]);
+      w[1] = pack_bf16x2(d[2], d[3]);
+      *reinterpret_cast<u32x2*>(zb + col * 32 + 8 * q4 + 4 * hf) = w;
+    }
+    __syncthreads();
+    // dk_idx += (dz / G)^T q_idx over the tile's 32 rows (each entry counted G times)
+#pragma unroll
+    for (int kr = 0; kr < 2; ++kr) {
+      const bf16x8 za = read_tr(zb, 32, 16 * kr, 0, lane);
+#pragma unroll
+      for (int dt = 0; dt < DP / 32; ++dt)
+        acc[dt] = mfma32(za, read_tr(qit, DP, 16 * kr, 32 * dt, lane), acc[dt]);
+    }
+    // dq_idx of the tile's entries, dims 32 wave .. +31, over all 128 keys
+    if (wave < DP / 32) {
+      f32x16 dq = {};
+#pragma unroll
+      for (int kk = 0; kk < kBlock / 16; ++kk)
+        dq = mfma32(read_rows(zbuf[kk >> 1], 32, 0, 16 * (kk & 1), lane),
+                    read_tr(kib, DP, 16 * kk, 32 * wave, lane), dq);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int n = 8 * (rr / 4) + 4 * hf + rr % 4;
+        const int e = et + n / G;
+        if (n % G == 0 && e < e1) pa.dqi_part[(size_t)e * DP + 32 * wave + col] = dq[rr] * G;
+      }
+    }
+    it.et += TE;
+    have = it.et < it.e1 || next_segment(a, s, g, b, lo, hi, it);
+  }
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int m = key0 + 8 * (rr / 4) + 4 * hf + rr % 4;
+    const int u = u0 + m;
+#pragma unroll
+    for (int dt = 0; dt < DP / 32; ++dt) {
+      if (split)
+        pa.dki_part[((size_t)chunk * kBlock + m) * DP + 32 * dt + col] = acc[dt][rr];
+      else if (u < sq.nk)
+        pa.dk_idx[((size_t)(sq.k0 + u) * a.hkv + g) * DP + 32 * dt + col] = acc[dt][rr];
+    }
+  }
+}
+
+// dk_idx of split columns: chunk partials added in chunk order.
+template <int DP>
+__global__ __launch_bounds__(256) void proxy_dk_reduce_kernel(ProxyArgs pa) {
+  const BwdArgs& a = pa.b;
+  const int cl = blockIdx.x, tid = threadIdx.x;
+  const int c0 = a.chunk_base[cl], c1 = a.chunk_base[cl + 1];
+  if (c1 - c0 < 2) return;
+  const int b = cl % a.nb_max, g = (cl / a.nb_max) % a.hkv, s = cl / (a.nb_max * a.hkv);
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  for (int i = tid; i < kBlock * DP / 4; i += 256) {
+    const int m = i / (DP / 4), u = b * kBlock + m;
+    if (u >= sq.nk) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int c = c0; c < c1; ++c)
+      acc += reinterpret_cast<const f32x4*>(pa.dki_part + (size_t)c * kBlock * DP)[i];
+    reinterpret_cast<f32x4*>(pa.dk_idx + ((size_t)(sq.k0 + u) * a.hkv + g) * DP)[i % (DP / 4)] =
+        acc;
+  }
+}
+
+// dq_idx[t, g] = sum over the (query, group)'s entries of their partials.
+__global__ __launch_bounds__(256) void proxy_dq_kernel(const int32_t* __restrict__ cmap,
+                                                       const float* __restrict__ part,
+                                                       float* __restrict__ dq, int64_t n,
+                                                       int dp, int topk) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int c = (int)(i % (dp / 4));
+  const int64_t row = i / (dp / 4);          // query row * hkv + group
+  const int32_t* cm = cmap + row * topk;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < topk; ++k) {
+    const int e = cm[k];
+    if (e >= 0) acc += *reinterpret_cast<const f32x4*>(part + (size_t)e * dp + 4 * c);
+  }
+  *reinterpret_cast<f32x4*>(dq + row * dp + 4 * c) = acc;
+}
+
 template <int G>
 hipError_t launch_kv_g(const BwdArgs& a, int64_t chunks_max, hipStream_t st) {
   hipLaunchKernelGGL((bwd_kv_kernel<G>), dim3((unsigned)chunks_max), dim3(256), 0, st, a);
@@ -506,12 +786,143 @@ BwdGeometry bwd_geometry(const msa_shape& s) {
   return b;
 }
 
+struct ProxyGeometry {
+  int64_t n_cols, chunks_max;
+  size_t off_dqi, off_base, off_col, off_dki, off_lsep, total;
+};
+
+ProxyGeometry proxy_geometry(const msa_shape& s) {
+  const Geometry g = geometry(s, MSA_KV_OUTER);
+  const Layout L = layout(s, MSA_KV_OUTER);
+  ProxyGeometry b;
+  b.n_cols = (int64_t)s.batch * s.hkv * g.nb_max;
+  b.chunks_max = g.e_max / (kChunkRows / g.group) + b.n_cols;
+  size_t off = L.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  b.off_dqi = take((size_t)g.e_max * s.dp * 4);
+  b.off_base = take((size_t)(b.n_cols + 1) * 4);
+  b.off_col = take((size_t)b.chunks_max * 4);
+  b.off_dki = take((size_t)b.chunks_max * kBlock * s.dp * 4);
+  b.off_lsep = take((size_t)s.total_q * s.hkv * 4);
+  b.total = off;
+  return b;
+}
+
+template <int G, int DP>
+hipError_t launch_proxy_g(const ProxyArgs& pa, int64_t chunks_max, hipStream_t st) {
+  hipLaunchKernelGGL((proxy_bwd_kernel<G, DP>), dim3((unsigned)chunks_max), dim3(256), 0, st, pa);
+  return hipGetLastError();
+}
+
+template <int DP>
+hipError_t launch_proxy_dp(const ProxyArgs& pa, int group, int64_t chunks_max, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_proxy_g<1, DP>(pa, chunks_max, st);
+    case 2: return launch_proxy_g<2, DP>(pa, chunks_max, st);
+    case 4: return launch_proxy_g<4, DP>(pa, chunks_max, st);
+    case 8: return launch_proxy_g<8, DP>(pa, chunks_max, st);
+    default: return launch_proxy_g<16, DP>(pa, chunks_max, st);
+  }
+}
+
 }  // namespace
+
+size_t proxy_bwd_workspace_bytes(const msa_shape& s) { return proxy_geometry(s).total; }
+
+hipError_t launch_proxy_bwd(const msa_shape& s, const void* q, const void* k, const void* q_idx,
+                            const void* k_idx, const float* lse, float scale, float proxy_scale,
+                            const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k,
+                            char* ws, float* dq_idx, float* dk_idx, float* lse_proxy,
+                            hipStream_t st) {
+  const Geometry g = geometry(s, MSA_KV_OUTER);
+  const Layout L = layout(s, MSA_KV_OUTER);
+  const ProxyGeometry pg = proxy_geometry(s);
+  if (s.total_k == 0 && s.total_q == 0) return hipSuccess;
+  const int64_t n_map = (int64_t)s.total_q * s.hkv * s.topk;
+  if (n_map > 0)
+    hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)((n_map + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<int32_t*>(ws + L.cmap), n_map);
+  hipError_t e = launch_plan(s, g, L, lists, cu_q, cu_k, ws, st);
+  if (e != hipSuccess) return e;
+  ProxyArgs pa{};
+  BwdArgs& a = pa.b;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.lse = lse;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.offsets = reinterpret_cast<const int32_t*>(ws + L.offsets);
+  a.entry_q = reinterpret_cast<const int32_t*>(ws + L.entry_q);
+  a.chunk_base = reinterpret_cast<const int32_t*>(ws + pg.off_base);
+  a.col_of = reinterpret_cast<const int32_t*>(ws + pg.off_col);
+  a.chunk_e = kChunkRows / g.group;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.total_q = s.total_q;
+  a.total_k = s.total_k;
+  a.max_q = s.max_q;
+  a.max_k = s.max_k;
+  a.hq = s.hq;
+  a.hkv = s.hkv;
+  a.nb_max = (int)g.nb_max;
+  a.wr = (int)g.wr;
+  a.n_r = (int)g.n_r;
+  a.causal = s.causal;
+  pa.q_idx = (const uint16_t*)q_idx;
+  pa.k_idx = (const uint16_t*)k_idx;
+  float* const lsep = lse_proxy ? lse_proxy : reinterpret_cast<float*>(ws + pg.off_lsep);
+  pa.lsep = lsep;
+  pa.dqi_part = reinterpret_cast<float*>(ws + pg.off_dqi);
+  pa.dki_part = reinterpret_cast<float*>(ws + pg.off_dki);
+  pa.dk_idx = dk_idx;
+  pa.pscale = proxy_scale;
+  pa.pscale_log2 = proxy_scale * 1.4426950408889634f;
+  const int64_t waves = (int64_t)s.total_q * s.hkv;
+  if (waves > 0) {
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (s.dp == 32)
+      hipLaunchKernelGGL(proxy_lse_kernel<32>, grid, dim3(256), 0, st, pa, lists, lsep, s.topk,
+                         s.list_q, (int)g.tiles_max, s.batch);
+    else
+      hipLaunchKernelGGL(proxy_lse_kernel<64>, grid, dim3(256), 0, st, pa, lists, lsep, s.topk,
+                         s.list_q, (int)g.tiles_max, s.batch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pg.n_cols > 0) {
+    hipLaunchKernelGGL(bwd_chunks_kernel, dim3(1), dim3(256), 0, st, a,
+                       reinterpret_cast<int32_t*>(ws + pg.off_base),
+                       reinterpret_cast<int32_t*>(ws + pg.off_col), (int)pg.n_cols,
+                       (int)pg.chunks_max);
+    e = s.dp == 32 ? launch_proxy_dp<32>(pa, g.group, pg.chunks_max, st)
+                   : launch_proxy_dp<64>(pa, g.group, pg.chunks_max, st);
+    if (e != hipSuccess) return e;
+    if (s.dp == 32)
+      hipLaunchKernelGGL(proxy_dk_reduce_kernel<32>, dim3((unsigned)pg.n_cols), dim3(256), 0, st,
+                         pa);
+    else
+      hipLaunchKernelGGL(proxy_dk_reduce_kernel<64>, dim3((unsigned)pg.n_cols), dim3(256), 0, st,
+                         pa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n = (int64_t)s.total_q * s.hkv * (s.dp / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(proxy_dq_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const int32_t*>(ws + L.cmap), pa.dqi_part, dq_idx, n, s.dp,
+                     s.topk);
+  return hipGetLastError();
+}
 
 size_t bwd_workspace_bytes(const msa_shape& s) { return bwd_geometry(s).total; }
 
 bool bwd_fits(const msa_shape& s) {
   const BwdGeometry b = bwd_geometry(s);
+  if (proxy_geometry(s).chunks_max != b.chunks_max) return false;
   return b.chunks_max < (1LL << 31) && b.n_cols + 1 < (1LL << 31);
 }
 

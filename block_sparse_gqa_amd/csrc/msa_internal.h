@@ -122,7 +122,15 @@ hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L
 // Main-branch backward: workspace = the KV-outer plan, bf16 dQ partials [E, group, d], the
 // chunk map and fp32 dK / dV partials of chunks of split columns.
 size_t bwd_workspace_bytes(const msa_shape& s);
-bool bwd_fits(const msa_shape& s);   // chunk and column counts within 32-bit indexing
+bool bwd_fits(const msa_shape& s);
+// Proxy backward: workspace = the KV-outer plan, fp32 dq_idx partials [E, dp], the chunk map,
+// fp32 dk_idx partials of chunks of split columns and the proxy LSE [total_q, hkv].
+size_t proxy_bwd_workspace_bytes(const msa_shape& s);
+hipError_t launch_proxy_bwd(const msa_shape& s, const void* q, const void* k, const void* q_idx,
+                            const void* k_idx, const float* lse, float scale, float proxy_scale,
+                            const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k,
+                            char* ws, float* dq_idx, float* dk_idx, float* lse_proxy,
+                            hipStream_t st);   // chunk and column counts within 32-bit indexing
 hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, float scale,
                       const int32_t* lists, const int32_t* cu_q, const int32_t* cu_k, char* ws,

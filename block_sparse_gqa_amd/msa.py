@@ -24,7 +24,8 @@ SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace
            "msa_resolve_mode", "msa_crossover", "msa_status_string", "msa_last_error",
            "msa_index_topk", "msa_index_topk_fp8", "msa_sparse_attn_fwd", "msa_plan",
            "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles",
-           "msa_bwd_workspace_size", "msa_sparse_attn_bwd")
+           "msa_bwd_workspace_size", "msa_sparse_attn_bwd", "msa_proxy_bwd_workspace_size",
+           "msa_proxy_attn_bwd")
 
 
 class Shape(ctypes.Structure):
@@ -77,6 +78,9 @@ def lib() -> ctypes.CDLL:
             "msa_attn_main": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp],
             "msa_combine": [sp, i32, vp, sz, vp, vp, vp],
             "msa_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
+            "msa_proxy_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
+            "msa_proxy_attn_bwd": [sp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp,
+                                   vp, vp, vp, sz, vp, vp, vp, vp],
             "msa_sparse_attn_bwd": [sp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                     sz, vp, vp, vp, vp],
         }.items():
@@ -226,3 +230,19 @@ def msa_sparse_attn_bwd(shape, q, k, v, o, lse, dout, softmax_scale, topk_idx, c
                                      _p(dout), float(softmax_scale), _p(topk_idx), _p(cu_q),
                                      _p(cu_k), _p(workspace), _nbytes(workspace), _p(dq), _p(dk),
                                      _p(dv), _stream(stream)), "msa_sparse_attn_bwd")
+
+
+def msa_proxy_bwd_workspace_size(shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().msa_proxy_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
+           "msa_proxy_bwd_workspace_size")
+    return n.value
+
+
+def msa_proxy_attn_bwd(shape, q, k, q_idx, k_idx, lse, softmax_scale, proxy_scale, topk_idx,
+                       cu_q, cu_k, workspace, dq_idx, dk_idx, lse_proxy=None, stream=None) -> None:
+    _check(lib().msa_proxy_attn_bwd(ctypes.byref(shape), _p(q), _p(k), _p(q_idx), _p(k_idx),
+                                    _p(lse), float(softmax_scale), float(proxy_scale),
+                                    _p(topk_idx), _p(cu_q), _p(cu_k), _p(workspace),
+                                    _nbytes(workspace), _p(dq_idx), _p(dk_idx), _p(lse_proxy),
+                                    _stream(stream)), "msa_proxy_attn_bwd")

@@ -12,6 +12,7 @@
  *   msa_sparse_attn_fwd  main branch: KV-outer partials (or Q-outer output) over the lists
  *   msa_combine          log-sum-exp merge of the per-slot partials into O and LSE
  *   msa_sparse_attn_bwd  main-branch backward: dQ, dK, dV over the selected blocks
+ *   msa_proxy_attn_bwd   proxy backward: gradients of the proxies toward the main weights
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers allocated and owned by the caller; the library never
@@ -271,6 +272,27 @@ msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void
                                const int32_t* cu_q, const int32_t* cu_k, void* workspace,
                                size_t ws_bytes, float* dq, float* dk, float* dv,
                                hipStream_t stream);
+
+/* Proxy (index-branch) backward ("Flash-MSA: accelerating million-token training": the proxy
+ * gradients need the proxy and the main attention probabilities together, and the proxy LSE
+ * is recomputed over the sparse keys in the backward; the objective itself is not printed on
+ * the pages, and this library takes the following one). Per query row and KV group, over the
+ * same selected keys as msa_sparse_attn_fwd: T = the main weights exp(softmax_scale q.k - LSE)
+ * averaged over the group's heads (held fixed), Pp = softmax(proxy_scale q_idx.k_idx), and the
+ * gradients of sum KL(T || Pp): dz = proxy_scale (Pp - T), dq_idx = sum_u dz k_idx_u,
+ * dk_idx_u = sum dz q_idx. bf16 only, dp in {32, 64}. In: q bf16 [total_q, hq, d], k bf16
+ * [total_k, hkv, d], q_idx / k_idx bf16 proxies, lse fp32 [total_q, hq] (the forward's); lists
+ * as for msa_sparse_attn_fwd. Out (fp32, written): dq_idx [total_q, hkv, dp] (every row),
+ * dk_idx [total_k, hkv, dp] (rows of keys in a sequence); lse_proxy fp32 [total_q, hkv] when
+ * not NULL (natural log, -inf for a row with no visible key). Deterministic. Workspace:
+ * msa_proxy_bwd_workspace_size bytes. */
+msa_status msa_proxy_bwd_workspace_size(const msa_shape* shape, size_t* bytes);
+msa_status msa_proxy_attn_bwd(const msa_shape* shape, const void* q, const void* k,
+                              const void* q_idx, const void* k_idx, const float* lse,
+                              float softmax_scale, float proxy_scale, const int32_t* topk_idx,
+                              const int32_t* cu_q, const int32_t* cu_k, void* workspace,
+                              size_t ws_bytes, float* dq_idx, float* dk_idx, float* lse_proxy,
+                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

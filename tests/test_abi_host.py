@@ -326,3 +326,22 @@ def test_backward_argument_checks(L):
     n = ctypes.c_size_t(0)
     assert L.msa_bwd_workspace_size(ctypes.byref(m3_shape(dtype=msa.MSA_FP8_E4M3)),
                                     ctypes.byref(n)) == msa.MSA_ERR_DTYPE
+
+
+def test_proxy_backward_argument_checks(L):
+    """bf16, dp 32 or 64; pointers and workspace checked before any launch."""
+    fake = ctypes.c_void_p(0x1000)
+    s = m3_shape()
+    need = msa.msa_proxy_bwd_workspace_size(s)
+    e_max = s.total_q * s.hkv * s.topk
+    # at least the plan, the fp32 dq_idx partials and the proxy LSE
+    assert need >= msa.msa_workspace_size(s, msa.MSA_KV_OUTER) + e_max * 64 * 4 + s.total_q * 4 * 4
+
+    def pb(shape, ws=fake, nbytes=need, qi=fake, dki=fake):
+        return L.msa_proxy_attn_bwd(ctypes.byref(shape), fake, fake, qi, fake, fake, 0.1, 0.125,
+                                    fake, fake, fake, ws, nbytes, fake, dki, None, None)
+    assert pb(m3_shape(dtype=msa.MSA_FP8_E4M3)) == msa.MSA_ERR_DTYPE
+    assert pb(s, qi=None) == msa.MSA_ERR_NULL
+    assert pb(s, dki=None) == msa.MSA_ERR_NULL
+    assert pb(s, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE
+    assert pb(s, ws=None) == msa.MSA_ERR_WORKSPACE

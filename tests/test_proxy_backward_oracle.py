@@ -43,7 +43,7 @@ def _dense_kl(q, k, qi, ki, sel, scale, pscale, causal):
     kl = torch.where(m & (t > 0), t * (torch.log(t.clamp_min(1e-300)) - logp),
                      torch.zeros_like(t)).sum()
     kl.backward()
-    return tqi.grad.numpy(), tki.grad.numpy(), float(kl)
+    return tqi.grad.numpy(), tki.grad.numpy(), float(kl.detach())
 
 
 @pytest.mark.parametrize("causal", [True, False])
