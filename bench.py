@@ -222,7 +222,7 @@ def bench_backward(args, case, shape, desc, t) -> None:
     the KV-stationary dK / dV / dQ-partial kernel, the dQ sum) on the forward's lists, O and
     LSE. value = useful FLOPs (10 D per unmasked selected (query, head, key) triple: S, dP, dV,
     dK, dQ) / time."""
-    q, k, v, o, lse, topk, cu_q, cu_k = t
+    q, k, v, o, lse, topk, cu_q, cu_k, q_idx, k_idx = t
     cfg = case.cfg
     if cfg.dtype != "bf16":
         print("the backward runs on bf16 workloads only", file=sys.stderr)
@@ -268,6 +268,48 @@ def bench_backward(args, case, shape, desc, t) -> None:
                      "unit": "TFLOP/s", "frac": flops / (ev_ms * 1e-3) / PEAK_BF16,
                      "traffic": None},
     }
+    if q_idx is not None and cfg.idx_dtype == "bf16":
+        # the proxy backward of the same step (gradients of the proxies toward the main weights)
+        pws = torch.empty(msa.msa_proxy_bwd_workspace_size(shape), dtype=torch.uint8,
+                          device="cuda")
+        dqi = torch.empty((case.total_q, cfg.hkv, cfg.dp), dtype=torch.float32, device="cuda")
+        dki = torch.empty((case.total_k, cfg.hkv, cfg.dp), dtype=torch.float32, device="cuda")
+
+        def pbwd():
+            msa.msa_proxy_attn_bwd(shape, q, k, q_idx, k_idx, lse, case.softmax_scale,
+                                   1.0 / math.sqrt(cfg.dp), topk, cu_q, cu_k, pws, dqi, dki)
+        for _ in range(args.warmup):
+            pbwd()
+        torch.cuda.synchronize()
+        pev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        pev[0].record()
+        for i in range(args.steps):
+            pbwd()
+            pev[i + 1].record()
+        torch.cuda.synchronize()
+        res["proxy_backward_ms"] = sum(pev[i].elapsed_time(pev[i + 1])
+                                       for i in range(args.steps)) / args.steps
+        del pws
+        # both backward passes in one call (msa_train_bwd)
+        tws = torch.empty(msa.msa_train_bwd_workspace_size(shape), dtype=torch.uint8,
+                          device="cuda")
+
+        def tbwd():
+            msa.msa_train_bwd(shape, q, k, v, o, lse, dout, case.softmax_scale, q_idx, k_idx,
+                              1.0 / math.sqrt(cfg.dp), topk, cu_q, cu_k, tws, dq, dk, dv, dqi,
+                              dki)
+        for _ in range(args.warmup):
+            tbwd()
+        torch.cuda.synchronize()
+        tev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        tev[0].record()
+        for i in range(args.steps):
+            tbwd()
+            tev[i + 1].record()
+        torch.cuda.synchronize()
+        res["train_backward_ms"] = sum(tev[i].elapsed_time(tev[i + 1])
+                                       for i in range(args.steps)) / args.steps
+        del tws
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline_backward(case, topk.cpu().numpy(), dout,
                                                     args.cpu_budget)
@@ -407,7 +449,7 @@ def main():
 
     if args.backward:
         step()                                 # lists, O and LSE of the forward
-        bench_backward(args, case, shape, desc, (q, k, v, o, lse, topk, cu_q, cu_k))
+        bench_backward(args, case, shape, desc, (q, k, v, o, lse, topk, cu_q, cu_k, q_idx, k_idx))
         return
     for _ in range(args.warmup):
         step()

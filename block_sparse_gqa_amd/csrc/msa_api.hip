@@ -369,6 +369,46 @@ msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void
   return MSA_OK;
 }
 
+msa_status msa_train_bwd_workspace_size(const msa_shape* shape, size_t* bytes) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  if (!bytes) return MSA_ERR_NULL;
+  if (shape->dtype != MSA_BF16) return MSA_ERR_DTYPE;
+  if (!bwd_fits(*shape) || (shape->dp != 32 && shape->dp != 64)) return MSA_ERR_SHAPE;
+  *bytes = std::max(bwd_workspace_bytes(*shape), proxy_bwd_workspace_bytes(*shape));
+  return MSA_OK;
+}
+
+msa_status msa_train_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout, float softmax_scale,
+                         const void* q_idx, const void* k_idx, float proxy_scale,
+                         const int32_t* topk_idx, const int32_t* cu_q, const int32_t* cu_k,
+                         void* workspace, size_t ws_bytes, float* dq, float* dk, float* dv,
+                         float* dq_idx, float* dk_idx, float* lse_proxy, hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  const msa_shape& s = *shape;
+  if (s.dtype != MSA_BF16) return MSA_ERR_DTYPE;
+  if (!bwd_fits(s) || (s.dp != 32 && s.dp != 64)) return MSA_ERR_SHAPE;
+  if (!topk_idx || !cu_q || !cu_k) return MSA_ERR_NULL;
+  if (s.total_q > 0 && (!q || !o || !lse || !dout || !dq || !q_idx || !dq_idx))
+    return MSA_ERR_NULL;
+  if (s.total_k > 0 && (!k || !v || !dk || !dv || !k_idx || !dk_idx)) return MSA_ERR_NULL;
+  if (!workspace || ws_bytes < std::max(bwd_workspace_bytes(s), proxy_bwd_workspace_bytes(s)))
+    return MSA_ERR_WORKSPACE;
+  // the two passes one after the other on the caller's stream, sharing the workspace
+  hipError_t e = launch_bwd(s, q, k, v, o, lse, dout, softmax_scale, topk_idx, cu_q, cu_k,
+                            static_cast<char*>(workspace), dq, dk, dv, stream);
+  if (e == hipSuccess)
+    e = launch_proxy_bwd(s, q, k, q_idx, k_idx, lse, softmax_scale, proxy_scale, topk_idx, cu_q,
+                         cu_k, static_cast<char*>(workspace), dq_idx, dk_idx, lse_proxy, stream);
+  if (e != hipSuccess) {
+    fail_launch(e);
+    return MSA_ERR_LAUNCH;
+  }
+  return MSA_OK;
+}
+
 msa_status msa_proxy_bwd_workspace_size(const msa_shape* shape, size_t* bytes) {
   msa_status st = check_shape(shape);
   if (st != MSA_OK) return st;

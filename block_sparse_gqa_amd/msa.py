@@ -25,7 +25,7 @@ SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace
            "msa_index_topk", "msa_index_topk_fp8", "msa_sparse_attn_fwd", "msa_plan",
            "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles",
            "msa_bwd_workspace_size", "msa_sparse_attn_bwd", "msa_proxy_bwd_workspace_size",
-           "msa_proxy_attn_bwd")
+           "msa_proxy_attn_bwd", "msa_train_bwd_workspace_size", "msa_train_bwd")
 
 
 class Shape(ctypes.Structure):
@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
             "msa_combine": [sp, i32, vp, sz, vp, vp, vp],
             "msa_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
             "msa_proxy_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
+            "msa_train_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
+            "msa_train_bwd": [sp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, ctypes.c_float,
+                              vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp],
             "msa_proxy_attn_bwd": [sp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp,
                                    vp, vp, vp, sz, vp, vp, vp, vp],
             "msa_sparse_attn_bwd": [sp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp,
@@ -246,3 +249,21 @@ def msa_proxy_attn_bwd(shape, q, k, q_idx, k_idx, lse, softmax_scale, proxy_scal
                                     _p(topk_idx), _p(cu_q), _p(cu_k), _p(workspace),
                                     _nbytes(workspace), _p(dq_idx), _p(dk_idx), _p(lse_proxy),
                                     _stream(stream)), "msa_proxy_attn_bwd")
+
+
+def msa_train_bwd_workspace_size(shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().msa_train_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
+           "msa_train_bwd_workspace_size")
+    return n.value
+
+
+def msa_train_bwd(shape, q, k, v, o, lse, dout, softmax_scale, q_idx, k_idx, proxy_scale,
+                  topk_idx, cu_q, cu_k, workspace, dq, dk, dv, dq_idx, dk_idx, lse_proxy=None,
+                  stream=None) -> None:
+    _check(lib().msa_train_bwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(o), _p(lse),
+                               _p(dout), float(softmax_scale), _p(q_idx), _p(k_idx),
+                               float(proxy_scale), _p(topk_idx), _p(cu_q), _p(cu_k),
+                               _p(workspace), _nbytes(workspace), _p(dq), _p(dk), _p(dv),
+                               _p(dq_idx), _p(dk_idx), _p(lse_proxy), _stream(stream)),
+           "msa_train_bwd")

@@ -13,6 +13,7 @@
  *   msa_combine          log-sum-exp merge of the per-slot partials into O and LSE
  *   msa_sparse_attn_bwd  main-branch backward: dQ, dK, dV over the selected blocks
  *   msa_proxy_attn_bwd   proxy backward: gradients of the proxies toward the main weights
+ *   msa_train_bwd        both backward passes in one call
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers allocated and owned by the caller; the library never
@@ -293,6 +294,19 @@ msa_status msa_proxy_attn_bwd(const msa_shape* shape, const void* q, const void*
                               const int32_t* cu_q, const int32_t* cu_k, void* workspace,
                               size_t ws_bytes, float* dq_idx, float* dk_idx, float* lse_proxy,
                               hipStream_t stream);
+
+/* The whole backward of a training step in one call ("Flash-MSA ...": main and proxy
+ * gradients): msa_sparse_attn_bwd then msa_proxy_attn_bwd on the same arguments, enqueued on
+ * `stream` one after the other and sharing one workspace of msa_train_bwd_workspace_size
+ * bytes (the larger of the two). Same inputs, outputs, errors and conventions as those two
+ * calls, and bitwise the same results. */
+msa_status msa_train_bwd_workspace_size(const msa_shape* shape, size_t* bytes);
+msa_status msa_train_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                         const void* o, const float* lse, const void* dout, float softmax_scale,
+                         const void* q_idx, const void* k_idx, float proxy_scale,
+                         const int32_t* topk_idx, const int32_t* cu_q, const int32_t* cu_k,
+                         void* workspace, size_t ws_bytes, float* dq, float* dk, float* dv,
+                         float* dq_idx, float* dk_idx, float* lse_proxy, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -80,3 +80,24 @@ def test_proxy_backward_matches_oracle(name, kw):
     assert np.all(np.isneginf(lp[~fin])) and np.abs(lp[fin] - lsep_r[fin]).max() <= 1e-3
     _check("dq_idx", dqi.cpu().numpy(), dqi_r)
     _check("dk_idx", dki.cpu().numpy(), dki_r)
+
+    # both passes in one call: main gradients bitwise those of the main-only call, proxy
+    # gradients at the same bar
+    dout = mi.grad_output(case).cuda()
+    main = [torch.full((case.total_q, cfg.hq, 128), float("nan"), device="cuda"),
+            torch.full((case.total_k, cfg.hkv, 128), float("nan"), device="cuda"),
+            torch.full((case.total_k, cfg.hkv, 128), float("nan"), device="cuda")]
+    bws = torch.empty(msa.msa_bwd_workspace_size(s), dtype=torch.uint8, device="cuda")
+    msa.msa_sparse_attn_bwd(s, dev.q, dev.k, dev.v, o, lse, dout, case.softmax_scale, lists_dev,
+                            dev.cu_q, dev.cu_k, bws, *main)
+    both = [torch.full_like(t, float("nan")) for t in main]
+    tws = torch.empty(msa.msa_train_bwd_workspace_size(s), dtype=torch.uint8, device="cuda")
+    tws.fill_(0x3C)
+    dqi2, dki2 = torch.full_like(dqi, float("nan")), torch.full_like(dki, float("nan"))
+    msa.msa_train_bwd(s, dev.q, dev.k, dev.v, o, lse, dout, case.softmax_scale, dev.q_idx,
+                      dev.k_idx, pscale, lists_dev, dev.cu_q, dev.cu_k, tws, *both, dqi2, dki2)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(main, both):
+        assert torch.equal(a_, b_)
+    _check("dq_idx (train call)", dqi2.cpu().numpy(), dqi_r)
+    _check("dk_idx (train call)", dki2.cpu().numpy(), dki_r)
