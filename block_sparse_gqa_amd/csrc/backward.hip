@@ -570,8 +570,8 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
   constexpr int TE = 32 / G;
   __shared__ uint16_t kb[kBlock * kD];       // K_b (swizzled)
   __shared__ uint16_t kib[kBlock * DP];      // k_idx of the block, row-major
-  __shared__ uint16_t qt[32 * kD];           // the tile's Q rows (swizzled)
-  __shared__ uint16_t qit[32 * DP];          // row n: q_idx of the entry of row n
+  __shared__ uint16_t qt[2][32 * kD];        // the tile's Q rows (swizzled), double-buffered
+  __shared__ uint16_t qit[2][32 * DP];       // row n: q_idx of the entry of row n
   __shared__ uint16_t zbuf[4][32 * 32];      // per wave: dz / G of its keys, [row][key]
 
   const int chunk = blockIdx.x;
@@ -608,49 +608,78 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
 #pragma unroll
   for (int dt = 0; dt < DP / 32; ++dt) acc[dt] = f32x16{};
 
-  TileIt it{0, 0, 0, 0};
-  bool have = next_segment(a, s, g, b, lo, hi, it);
-  while (have) {
-    const int et = it.et, e1 = it.e1;
-    __syncthreads();                         // last tile's reads done
+  // a tile's loads: entry rows (Q staging rows tid / 16 + 16 k, proxy row tid / (DP / 8), the
+  // lane's compute row col), then Q, q_idx, the main LSE and the proxy LSE
+  auto load_rows = [&](int et, int e1, int eq[2], int& eqi, int& eqc) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int n = tid / 16 + 16 * k, c = tid % 16;
-      const int e = et + n / G;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (e < e1)
-        v = *reinterpret_cast<const u32x4*>(
-            a.q + ((size_t)a.entry_q[e] * a.hq + g * G + n % G) * kD + 8 * c);
-      *reinterpret_cast<u32x4*>(qt + sw(n, 8 * c)) = v;
+      const int e = et + (tid / 16 + 16 * k) / G;
+      eq[k] = e < e1 ? a.entry_q[e] : -1;
     }
-    if (tid < 32 * DP / 8) {
-      const int n = tid / (DP / 8), c = tid % (DP / 8);
-      const int e = et + n / G;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (e < e1)
-        v = *reinterpret_cast<const u32x4*>(pa.q_idx + ((size_t)a.entry_q[e] * a.hkv + g) * DP +
-                                            8 * c);
-      *reinterpret_cast<u32x4*>(qit + n * DP + 8 * c) = v;
+    const int ei = et + (tid / (DP / 8)) / G;
+    eqi = (tid < 4 * DP && ei < e1) ? a.entry_q[ei] : -1;
+    const int e = et + col / G;
+    eqc = e < e1 ? a.entry_q[e] : -1;
+  };
+  auto load_data = [&](const int eq[2], int eqi, int eqc, u32x4 qv[2], u32x4& pv, float& lse2,
+                       float& lsep2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int n = tid / 16 + 16 * k;
+      qv[k] = u32x4{0u, 0u, 0u, 0u};
+      if (eq[k] >= 0)
+        qv[k] = *reinterpret_cast<const u32x4*>(
+            a.q + ((size_t)eq[k] * a.hq + g * G + n % G) * kD + 8 * (tid % 16));
     }
-    const int e_row = et + col / G;
-    const bool row_ok = e_row < e1;
-    int t = 0;
-    float lse2 = -__builtin_inff(), lsep2 = -__builtin_inff();
-    if (row_ok) {
-      t = a.entry_q[e_row];
-      lse2 = a.lse[(size_t)t * a.hq + g * G + col % G] * 1.4426950408889634f;
-      lsep2 = pa.lsep[(size_t)t * a.hkv + g] * 1.4426950408889634f;
+    pv = u32x4{0u, 0u, 0u, 0u};
+    if (eqi >= 0)
+      pv = *reinterpret_cast<const u32x4*>(pa.q_idx + ((size_t)eqi * a.hkv + g) * DP +
+                                           8 * (tid % (DP / 8)));
+    lse2 = -__builtin_inff();
+    lsep2 = -__builtin_inff();
+    if (eqc >= 0) {
+      lse2 = a.lse[(size_t)eqc * a.hq + g * G + col % G] * 1.4426950408889634f;
+      lsep2 = pa.lsep[(size_t)eqc * a.hkv + g] * 1.4426950408889634f;
     }
-    const int pos = sq.nk - sq.nq + (t - sq.q0);
-    __syncthreads();
+  };
+  auto store_slot = [&](int slot, const u32x4 qv[2], const u32x4& pv) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      *reinterpret_cast<u32x4*>(qt[slot] + sw(tid / 16 + 16 * k, 8 * (tid % 16))) = qv[k];
+    if (tid < 4 * DP)
+      *reinterpret_cast<u32x4*>(qit[slot] + (tid / (DP / 8)) * DP + 8 * (tid % (DP / 8))) = pv;
+  };
+
+  TileIt it{0, 0, 0, 0};
+  bool have = next_segment(a, s, g, b, lo, hi, it);
+  int cur_et = it.et, cur_e1 = it.e1;
+  int eq[2] = {-1, -1}, eqi = -1, eqc = -1;
+  u32x4 qv[2], pv;
+  float lse2 = 0.f, lsep2 = 0.f;
+  if (have) {
+    load_rows(cur_et, cur_e1, eq, eqi, eqc);
+    load_data(eq, eqi, eqc, qv, pv, lse2, lsep2);
+    store_slot(0, qv, pv);
+  }
+  int cur_t = eqc;
+  it.et += TE;
+  bool have_next = have && (it.et < it.e1 || next_segment(a, s, g, b, lo, hi, it));
+  int slot = 0;
+  while (have) {
+    __syncthreads();                         // slot written; last tile's reads done
+    const int nx_et = it.et, nx_e1 = it.e1;
+    int nq[2] = {-1, -1}, nqi = -1, nqc = -1;
+    if (have_next) load_rows(nx_et, nx_e1, nq, nqi, nqc);
+    const bool row_ok = cur_t >= 0;
+    const int pos = sq.nk - sq.nq + (cur_t - sq.q0);
 
     f32x16 st = {}, zt = {};
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks)
-      st = mfma32(kf[ks], read_rows_sw(qt, 0, 16 * ks, lane), st);
+      st = mfma32(kf[ks], read_rows_sw(qt[slot], 0, 16 * ks, lane), st);
 #pragma unroll
     for (int ks = 0; ks < DP / 16; ++ks)
-      zt = mfma32(kif[ks], read_rows(qit, DP, 0, 16 * ks, lane), zt);
+      zt = mfma32(kif[ks], read_rows(qit[slot], DP, 0, 16 * ks, lane), zt);
     uint16_t* const zb = zbuf[wave];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
@@ -673,14 +702,15 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
       w[1] = pack_bf16x2(d[2], d[3]);
       *reinterpret_cast<u32x2*>(zb + col * 32 + 8 * q4 + 4 * hf) = w;
     }
-    __syncthreads();
+    if (have_next) load_data(nq, nqi, nqc, qv, pv, lse2, lsep2);
+    __syncthreads();                         // dz of every wave written
     // dk_idx += (dz / G)^T q_idx over the tile's 32 rows (each entry counted G times)
 #pragma unroll
     for (int kr = 0; kr < 2; ++kr) {
       const bf16x8 za = read_tr(zb, 32, 16 * kr, 0, lane);
 #pragma unroll
       for (int dt = 0; dt < DP / 32; ++dt)
-        acc[dt] = mfma32(za, read_tr(qit, DP, 16 * kr, 32 * dt, lane), acc[dt]);
+        acc[dt] = mfma32(za, read_tr(qit[slot], DP, 16 * kr, 32 * dt, lane), acc[dt]);
     }
     // dq_idx of the tile's entries, dims 32 wave .. +31, over all 128 keys
     if (wave < DP / 32) {
@@ -692,12 +722,20 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int n = 8 * (rr / 4) + 4 * hf + rr % 4;
-        const int e = et + n / G;
-        if (n % G == 0 && e < e1) pa.dqi_part[(size_t)e * DP + 32 * wave + col] = dq[rr] * G;
+        const int e = cur_et + n / G;
+        if (n % G == 0 && e < cur_e1) pa.dqi_part[(size_t)e * DP + 32 * wave + col] = dq[rr] * G;
       }
     }
-    it.et += TE;
-    have = it.et < it.e1 || next_segment(a, s, g, b, lo, hi, it);
+    if (have_next) store_slot(slot ^ 1, qv, pv);
+    slot ^= 1;
+    have = have_next;
+    cur_et = nx_et;
+    cur_e1 = nx_e1;
+    cur_t = nqc;
+    if (have) {
+      it.et += TE;
+      have_next = it.et < it.e1 || next_segment(a, s, g, b, lo, hi, it);
+    }
   }
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
