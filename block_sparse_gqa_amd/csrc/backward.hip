@@ -691,8 +691,7 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
         const bool vis = row_ok && u < sq.nk && !(a.causal && u > pos) &&
                          lse2 > -__builtin_inff() && lsep2 > -__builtin_inff();
         float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
-#pragma unroll
-        for (int o = 1; o < G; o <<= 1) p += shfl_xor_f(p, o);   // sum over the entry's heads
+        p = group_sum<G>(p);                 // sum over the entry's heads (DPP network)
         const float pp =
             vis ? __builtin_amdgcn_exp2f(fmaf(zt[4 * q4 + i], pa.pscale_log2, -lsep2)) : 0.f;
         d[i] = pa.pscale * (pp - p * (1.f / G)) * (1.f / G);
