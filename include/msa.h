@@ -80,7 +80,8 @@ typedef struct {
   int32_t block;    /* KV block size: 128 */
   int32_t topk;     /* selected blocks per list: 1..16 */
   int32_t causal;   /* 1: key u visible to a query at position pos iff u <= pos */
-  int32_t dtype;    /* msa_dtype of Q/K/V; proxies are always bf16 */
+  int32_t dtype;    /* msa_dtype of Q/K/V. Proxies are bf16 for msa_index_topk and e4m3fn
+                       (with their own descales) for msa_index_topk_fp8 */
   int32_t list_q;   /* 1: per-query lists topk_idx [total_q, hkv, topk];
                        128: per-Q-tile lists [batch * ceil(max_q/128), hkv, topk], row
                        s * ceil(max_q/128) + t holds the list of queries [128t, 128t+128)
@@ -217,9 +218,11 @@ msa_status msa_select_tiles(const msa_shape* shape, int reps, const void* q, con
  * [0, ceil(Nk/block)), repeated entries, and (causal) blocks wholly after the query are
  * ignored.
  * KV_OUTER: builds the block -> query inverted index in the workspace, then one kernel loads
- * each selected block once and writes, for every (query-group, block) entry, the normalised
- * partial output (bf16) and its LSE (fp32) contiguously in entry order; msa_combine must
- * follow on the same stream. `o` and `lse` are not touched.
+ * each selected block once and writes, for every (query-group, block) entry, contiguously
+ * in entry order: the UNNORMALISED partial output (bf16, part_o: the block's attention output
+ * times its weight sum), the weight sum (fp32, part_l) and the partial's LSE (fp32,
+ * part_lse); see msa_workspace_layout. msa_combine, which must follow on the same stream,
+ * divides by part_l and merges by LSE. `o` and `lse` are not touched.
  * Q_OUTER: writes O (same dtype as the result of msa_combine: bf16 [total_q, hq, d]) and LSE
  * (fp32 [total_q, hq]) directly, or - when the schedule splits long lists - partials that
  * msa_combine merges. Calling msa_combine after Q_OUTER is always valid.

@@ -115,3 +115,36 @@ def query_rows_gradient(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel_rows: n
                                                          keepdims=True))
             out[r, heads] = scale * (ds @ kk)
     return out
+
+
+def key_block_gradient(q: np.ndarray, k: np.ndarray, v: np.ndarray, sel: np.ndarray,
+                       do: np.ndarray, g: int, b: int, scale: float, block: int, causal: bool
+                       ) -> tuple[np.ndarray, np.ndarray]:
+    """dK and dV of the keys of block ``b`` of group ``g`` only (one (group, block) column):
+    the sum, over the queries whose list for g holds b, of their terms in the formulas of
+    sparse_attention_backward, each query's P and D taken over its own whole key set.
+    q [N, Hq, D], k / v [Nk, Hkv, D], sel [N, Hkv, K], do [N, Hq, D] (fp64).
+    Returns (dK, dV), each [n_b, D] for the keys block*b .. min(block*(b+1), Nk) - 1."""
+    n_q, hq, d = q.shape
+    n_k, hkv, _ = k.shape
+    grp = hq // hkv
+    pos = query_positions(n_q, n_k)
+    lo, hi = block * b, min(block * (b + 1), n_k)
+    dk = np.zeros((max(hi - lo, 0), d))
+    dv = np.zeros((max(hi - lo, 0), d))
+    heads = slice(g * grp, (g + 1) * grp)
+    for i in range(n_q):
+        if not np.any(sel[i, g] == b):
+            continue
+        keys = _key_set(sel[i, g], n_k, block, int(pos[i]), causal)
+        mine = (keys >= lo) & (keys < hi)
+        if not mine.any():
+            continue
+        kk, vv = k[keys, g], v[keys, g]
+        oi, li = attend(q[i, heads], kk, vv, scale)
+        p = np.exp(scale * (q[i, heads] @ kk.T) - li[:, None])          # [G, S]
+        ds = p * (do[i, heads] @ vv.T - np.sum(do[i, heads] * oi, axis=1, keepdims=True))
+        at = keys[mine] - lo
+        dk[at] += scale * (ds[:, mine].T @ q[i, heads])
+        dv[at] += p[:, mine].T @ do[i, heads]
+    return dk, dv

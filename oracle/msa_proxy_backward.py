@@ -15,6 +15,11 @@ and KV group g, over the same key set S(i, g) the main branch attends to,
     loss   = sum_(i, g) KL(T_i || Pp_i) = sum T log(T / Pp)
     dz_iu  = tau_p (Pp_iu - T_iu)
     dq_idx_i = sum_u dz_iu k_idx_u,   dk_idx_u = sum_i dz_iu q_idx_i.
+
+Parity unpinned against the pages: they fix neither this objective nor any gradient value.
+The pins (autograd of the same objective written densely, finite differences, the case
+where the two distributions are equal) tie this code to the objective above, which is a
+reading, not the pages' statement.
 """
 from __future__ import annotations
 
@@ -82,3 +87,57 @@ def run_case(case, lists: np.ndarray, proxy_scale: float):
         dq[q0:q1], dk[k0:k1], lsep[q0:q1] = a, b, lp
         loss += l
     return dq, dk, loss, lsep
+
+
+def _row_terms(q, k, q_idx, k_idx, keys, i, g, grp, scale, proxy_scale):
+    """One (query, group): (dz over its key set, proxy LSE), as in proxy_backward."""
+    heads = slice(g * grp, (g + 1) * grp)
+    kk = k[keys, g]
+    _, li = attend(q[i, heads], kk, kk, scale)
+    t = np.mean(np.exp(scale * (q[i, heads] @ kk.T) - li[:, None]), axis=0)
+    z = proxy_scale * (k_idx[keys, g] @ q_idx[i, g])
+    m = np.max(z)
+    lp = m + np.log(np.sum(np.exp(z - m)))
+    return proxy_scale * (np.exp(z - lp) - t), lp
+
+
+def proxy_rows_gradient(q, k, q_idx, k_idx, sel_rows, rows, scale, proxy_scale, block, causal):
+    """dq_idx and the proxy LSE of the given query ``rows`` of one sequence only (a row's
+    terms depend on its own list alone); sel_rows [R, Hkv, K]. The same formulas as
+    proxy_backward. Returns (dq_idx [R, Hkv, dp], LSEp [R, Hkv])."""
+    n_q, hq, _ = q.shape
+    n_k, hkv, _ = k.shape
+    grp = hq // hkv
+    pos = query_positions(n_q, n_k)
+    dqi = np.zeros((rows.size, hkv, q_idx.shape[2]))
+    lsep = np.full((rows.size, hkv), -np.inf)
+    for r, i in enumerate(rows):
+        for g in range(hkv):
+            keys = _key_set(sel_rows[r, g], n_k, block, int(pos[i]), causal)
+            if keys.size == 0:
+                continue
+            dz, lsep[r, g] = _row_terms(q, k, q_idx, k_idx, keys, i, g, grp, scale, proxy_scale)
+            dqi[r, g] = dz @ k_idx[keys, g]
+    return dqi, lsep
+
+
+def proxy_key_block_gradient(q, k, q_idx, k_idx, sel, g, b, scale, proxy_scale, block, causal):
+    """dk_idx of the keys of block ``b`` of group ``g`` only: the sum over the queries whose
+    list for g holds b of dz_iu q_idx_i, each query's dz over its own whole key set.
+    Returns [n_b, dp] for the keys block*b .. min(block*(b+1), Nk) - 1."""
+    n_q, hq, _ = q.shape
+    n_k, hkv, _ = k.shape
+    grp = hq // hkv
+    pos = query_positions(n_q, n_k)
+    lo, hi = block * b, min(block * (b + 1), n_k)
+    dki = np.zeros((max(hi - lo, 0), q_idx.shape[2]))
+    for i in range(n_q):
+        if not np.any(sel[i, g] == b):
+            continue
+        keys = _key_set(sel[i, g], n_k, block, int(pos[i]), causal)
+        mine = (keys >= lo) & (keys < hi)
+        if not mine.any():
+            continue
+        dz, _ = _row_terms(q, k, q_idx, k_idx, keys, i, g, grp, scale, proxy_scale)
+        dki[keys[mine] - lo] += np.outer(dz[mine], q_idx[i, g])
+    return dki

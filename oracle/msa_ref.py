@@ -53,15 +53,6 @@ def n_blocks(n_k: int, block: int) -> int:
     return -(-n_k // block)
 
 
-def visible_block_mask(pos: np.ndarray, n_k: int, block: int, causal: bool) -> np.ndarray:
-    """[N, nb] bool: block j holds at least one key the query may attend to."""
-    nb = n_blocks(n_k, block)
-    j = np.arange(nb, dtype=np.int64)
-    if causal:
-        return (j[None, :] * block) <= pos[:, None]
-    return np.ones((pos.shape[0], nb), dtype=bool)
-
-
 # --------------------------------------------------------------------------- index branch
 
 def proxy_block_scores(q_idx: np.ndarray, k_idx: np.ndarray, block: int, causal: bool,
@@ -224,14 +215,3 @@ def combine(o_slot: np.ndarray, lse_slot: np.ndarray) -> tuple[np.ndarray, np.nd
     wn = np.where(empty, 0.0, w / np.where(empty, 1.0, tot))
     o = np.einsum("...k,...kd->...d", wn, o_slot)
     return o, lse[..., 0]
-
-
-# --------------------------------------------------------------------------- whole layer
-
-def forward_sequence(q, k, v, q_idx, k_idx, *, block: int, topk: int, scale: float,
-                     causal: bool, rows=None):
-    """Index branch then main branch for one sequence (fp64 arrays). Returns
-    (topk_idx [N, Hkv, K], O [n, Hq, D], LSE [n, Hq], proxy scores [N, Hkv, nb])."""
-    sel, s = index_topk(q_idx, k_idx, block, topk, causal)
-    o, lse = sparse_attention(q, k, v, sel, scale, block, causal, rows=rows)
-    return sel, o, lse, s

@@ -311,7 +311,11 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
                 up = _lowrank_factors(ssp[0], hkv, dp)
                 _add_lowrank(qi, "q", cu_q, up, ssp[1], 1, cfg.block)
                 _add_lowrank(ki, "k", cu_k, up, ssp[2], 1, cfg.block)
-        if cfg.idx_dtype == "fp8":
+        if cfg.idx_dtype == "fp8" and cfg.proxy == "grid":
+            # every grid value {-16..16}/4 is an e4m3 code: stored as is, descale 1
+            q_idx = torch.from_numpy(qi).to(torch.float8_e4m3fn)
+            k_idx = torch.from_numpy(ki).to(torch.float8_e4m3fn)
+        elif cfg.idx_dtype == "fp8":
             q_idx, dqi = to_fp8(qi)
             k_idx, dki = to_fp8(ki)
             idx_descale = (dqi, dki)

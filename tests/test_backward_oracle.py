@@ -118,3 +118,26 @@ def test_row_gradient_matches_the_whole_sequence_backward():
     rows = np.array([0, 5, 150, 299])
     got = query_rows_gradient(q, k, v, lists[rows], do[rows], rows, case.softmax_scale, 128, True)
     assert np.array_equal(got, dq[rows])
+
+
+def test_key_block_gradient_matches_the_whole_sequence_backward():
+    """dK, dV of one (group, block) column alone (used at full size) equal the whole-sequence
+    backward's rows for those keys: every column of a ragged causal case, G = 4."""
+    from oracle import msa_case
+    from oracle.msa_backward import key_block_gradient, sparse_attention_backward
+    from synth import msa_inputs as mi
+    from synth.msa_inputs import widen
+    cfg = mi.custom("cols", n_q=(300,), n_k=(700,), hq=8, hkv=2, topk=3)
+    case = mi.make_case(cfg, seed=5)
+    do = widen(mi.grad_output(case))
+    q, k, v = widen(case.q), widen(case.k), widen(case.v)
+    lists = msa_case.run(case, want_output=False).topk_idx
+    _, dk, dv, _, _ = sparse_attention_backward(q, k, v, lists, do, case.softmax_scale, 128, True)
+    for g in range(2):
+        for b in range(6):
+            gk, gv = key_block_gradient(q, k, v, lists, do, g, b, case.softmax_scale, 128, True)
+            lo, hi = 128 * b, min(128 * b + 128, 700)
+            np.testing.assert_allclose(gk, dk[lo:hi, g], rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(gv, dv[lo:hi, g], rtol=1e-12, atol=1e-14)
+    # the compared values are far from zero, so the comparison is not vacuous
+    assert np.abs(dv[:128, 0]).max() > 1e-3

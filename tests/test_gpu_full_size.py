@@ -2,7 +2,8 @@
 
 The oracle cannot score every query of a 32K- or 128K-token layer in test time, so each
 workload is checked on a seeded systematic sample of whole 128-query blocks (lists bit-exact
-up to certified near-ties; outputs at the bf16 / fp8 bars on rows whose lists agree), and on
+up to certified near-ties, capped in number; outputs at the bf16 / fp8 bars against the
+oracle's attention over the lists the GPU used, on every sampled row), and on
 properties that hold for every row at any size: the local block fills slot 0, a row holds
 min(topK, c + 1) distinct visible blocks followed by -1 padding, and every output is finite.
 """
@@ -14,7 +15,8 @@ from block_sparse_gqa_amd import msa
 from oracle import msa_case
 from synth import msa_inputs as mi
 
-from gpu_util import compare_lists, err_stats, near_tie_bound, proxies, run_index, shape_of, upload
+from gpu_util import (compare_lists, err_stats, proxies, proxy_score_errors, run_index,
+                      shape_of, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,7 +95,10 @@ def run_workload(cfgname, every, seed=0, max_rows=None):
 
 
 def compare(case, lists, rows, out, o_s, lse_s):
+    """Sampled rows: lists bit-exact or certified near-ties (capped in number); outputs
+    against the oracle's attention over the lists the GPU used, on every sampled row."""
     c = case.cfg
+    ref_o, ref_lse = out.o, out.lse
     if case.lists is None:
         check_list_properties(case, lists)
         seq_of = np.searchsorted(case.cu_q, rows, side="right") - 1
@@ -108,22 +113,26 @@ def compare(case, lists, rows, out, o_s, lse_s):
             first = np.searchsorted(seq_of, s)
             return sc[n - first, g]
 
-        def bound(n, g):
+        def err(n, g):
             s = seq_of[n]
-            return near_tie_bound(qi[rows[n], g], ki[case.cu_k[s]:case.cu_k[s + 1], g],
-                                  case.cfg.idx_dtype == "fp8")
+            k0, k1 = case.cu_k[s], case.cu_k[s + 1]
+            pos = (k1 - k0) - (case.cu_q[s + 1] - case.cu_q[s]) + (rows[n] - case.cu_q[s])
+            return proxy_score_errors(qi[rows[n], g], ki[k0:k1, g],
+                                      int(pos) if c.causal else None, c.idx_dtype == "fp8")
 
         got = lists[rows]
-        n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, bound)
-        _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
+        n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, err)
+        _say(f"rows differing {n_diff}, certified near-ties {n_tie} of {got.shape[0] * c.hkv}")
         assert not bad, f"uncertified list differences at {bad[:5]}"
-        same = np.all(got == out.topk_idx, axis=(1, 2))
-        assert same.mean() > 0.99
-    else:
-        same = np.ones(rows.size, dtype=bool)
+        diff = np.nonzero(np.any(got != out.topk_idx, axis=(1, 2)))[0]
+        if diff.size:
+            # rows with a certified swap: the oracle's attention over the GPU's lists
+            alt = msa_case.run(case, rows=rows[diff], lists=lists)
+            ref_o, ref_lse = ref_o.copy(), ref_lse.copy()
+            ref_o[diff], ref_lse[diff] = alt.o, alt.lse
     tol_o, tol_l = TOL[c.dtype]
-    st = err_stats(o_s[same], out.o[same], lse_s[same], out.lse[same])
-    _say(st, "rows compared", int(same.sum()))
+    st = err_stats(o_s, ref_o, lse_s, ref_lse)
+    _say(st, "rows compared", rows.size)
     assert st["max_abs"] <= tol_o and st["max_dlse"] <= tol_l and st["lse_inf_match"]
 
 
@@ -134,14 +143,14 @@ def test_m3_prefill_32k():
 
 
 def test_fp8_prefill_128k():
-    case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long", every=256)
+    case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long", every=64)
     assert chosen == msa.MSA_KV_OUTER
     compare(case, lists, rows, out, o_s, lse_s)
 
 
 def test_fp8_proxies_prefill_128k():
     """The 128K fp8 workload with its proxies quantised to e4m3 too (8-bit MFMA scoring)."""
-    case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long_i8", every=256)
+    case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long_i8", every=64)
     assert chosen == msa.MSA_KV_OUTER
     compare(case, lists, rows, out, o_s, lse_s)
 

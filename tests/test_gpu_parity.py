@@ -15,8 +15,8 @@ from oracle import msa_case, msa_ref as ref
 from synth import msa_inputs as mi
 from synth.msa_inputs import widen
 
-from gpu_util import (compare_lists, err_stats, gpu_attention, gpu_index, near_tie_bound,
-                      proxies, shape_of, upload)
+from gpu_util import (compare_lists, err_stats, gpu_attention, gpu_index, proxies,
+                      proxy_score_errors, shape_of, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,15 +38,18 @@ def _oracle_index_scores(case):
     return out, scores
 
 
-def _bound_fn(case):
+def _err_fn(case):
+    """(row, group) -> per-block error bounds of the computed proxy scores (fp64)."""
     qi, ki = proxies(case)
     seq_of = np.searchsorted(case.cu_q, np.arange(case.total_q), side="right") - 1
 
-    def bound(i, g):
+    def err(i, g):
         s = seq_of[i]
-        return near_tie_bound(qi[i, g], ki[case.cu_k[s]:case.cu_k[s + 1], g],
-                              case.cfg.idx_dtype == "fp8")
-    return bound
+        k0, k1 = case.cu_k[s], case.cu_k[s + 1]
+        pos = (k1 - k0) - (case.cu_q[s + 1] - case.cu_q[s]) + (i - case.cu_q[s])
+        return proxy_score_errors(qi[i, g], ki[k0:k1, g], int(pos) if case.cfg.causal else None,
+                                  case.cfg.idx_dtype == "fp8")
+    return err
 
 
 # ------------------------------------------------------------------ index branch
@@ -95,7 +98,7 @@ def test_index_topk_gaussian_certified(cfgname):
     case = mi.make_case(cfgname, seed=0)
     got, _ = gpu_index(case, upload(case))
     out, scores = _oracle_index_scores(case)
-    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _bound_fn(case))
+    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _err_fn(case))
     _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
     assert not bad, f"uncertified list differences at {bad[:5]}"
 
@@ -115,6 +118,29 @@ FP8_INDEX_CASES = [
 
 
 @pytest.mark.parametrize("name,kw", FP8_INDEX_CASES, ids=[c[0] for c in FP8_INDEX_CASES])
+def test_index_topk_fp8_bit_exact_on_exact_arithmetic(name, kw):
+    """e4m3 proxies holding grid values (codes {-16..16}/4, descale 1): every product is a
+    multiple of 2^-4 below 2^4, so the 8-bit MFMA's sums are exact and the lists and scores
+    must equal the oracle's bit for bit, ties included."""
+    _say(f"[index fp8 exact] {name}")
+    kw = dict(kw, proxy="grid")
+    kw.pop("lowrank", None)
+    case = mi.make_case(mi.custom(name=name, idx_dtype="fp8", **kw), seed=3)
+    assert case.idx_descale == (1.0, 1.0)
+    got, got_sc = gpu_index(case, upload(case))
+    out = msa_case.run(case, want_output=False)
+    n_diff, _, bad = compare_lists(got, out.topk_idx)
+    assert n_diff == 0, f"{n_diff} rows differ, first {bad[:5]}"
+    seq_of = np.searchsorted(case.cu_q, np.arange(case.total_q), side="right") - 1
+    for i in range(0, case.total_q, 5):
+        s = seq_of[i]
+        for g in range(case.cfg.hkv):
+            for k, b in enumerate(got[i, g]):
+                want = out.scores[s][i - case.cu_q[s], g, b] if b >= 0 else -np.inf
+                assert got_sc[i, g, k] == want
+
+
+@pytest.mark.parametrize("name,kw", FP8_INDEX_CASES, ids=[c[0] for c in FP8_INDEX_CASES])
 def test_index_topk_fp8_proxies_certified(name, kw):
     """e4m3 proxies: lists equal the oracle's on the dequantised proxies up to certified
     near-ties; reported scores are the oracle's block maxima within the fp32 summation bound."""
@@ -122,8 +148,8 @@ def test_index_topk_fp8_proxies_certified(name, kw):
     case = mi.make_case(mi.custom(name=name, idx_dtype="fp8", **kw), seed=2)
     got, got_sc = gpu_index(case, upload(case))
     out, scores = _oracle_index_scores(case)
-    bound = _bound_fn(case)
-    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, bound)
+    err = _err_fn(case)
+    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, err)
     _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
     assert not bad, f"uncertified list differences at {bad[:5]}"
     n_checked = 0
@@ -134,7 +160,7 @@ def test_index_topk_fp8_proxies_certified(name, kw):
                 if not np.isfinite(want):
                     assert got_sc[i, g, k] == want
                     continue
-                tol = bound(i, g) / 2 + 2.0 ** -22 * abs(want)    # one dot product's bound
+                tol = err(i, g)[b] + 2.0 ** -22 * abs(want)    # block b's score bound
                 assert abs(got_sc[i, g, k] - want) <= tol, (i, g, k, got_sc[i, g, k], want)
                 n_checked += 1
     assert n_checked > 0
@@ -194,16 +220,21 @@ def test_layer_matches_oracle(name, cfg, seed, mode):
 
 
 def test_index_then_layer_end_to_end():
+    """The index branch's own lists feed the main branch. Lists: bit-exact, or a certified
+    near-tie (capped in number); outputs: the oracle's attention over the GPU's lists on every
+    row (so rows with a certified swap are checked too)."""
     _say("[e2e] tiny")
     case = mi.make_case("tiny", seed=0)
     dev = upload(case)
     got, _ = gpu_index(case, dev)
-    out = msa_case.run(case)
-    same = np.all(got == out.topk_idx, axis=(1, 2))
+    out, scores = _oracle_index_scores(case)
+    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _err_fn(case))
+    _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
+    assert not bad, f"uncertified list differences at {bad[:5]}"
+    ref = msa_case.run(case, lists=got)
     o, lse = gpu_attention(case, dev, torch.from_numpy(got).cuda(), msa.MSA_AUTO)
-    st = err_stats(o[same], out.o[same], lse[same], out.lse[same])
-    _say(st, "rows compared", int(same.sum()))
-    assert same.mean() > 0.99
+    st = err_stats(o, ref.o, lse, ref.lse)
+    _say(st)
     assert st["max_abs"] <= 2e-2 and st["max_dlse"] <= 1e-2
 
 
@@ -360,7 +391,7 @@ def test_per_query_lists_edge_cases_and_empty_sequence():
     dev = upload(case)
     got, _ = gpu_index(case, dev)
     out, scores = _oracle_index_scores(case)
-    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _bound_fn(case))
+    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _err_fn(case))
     assert not bad, f"uncertified list differences at {bad[:5]}"
     lists = _mutate_per_query_lists(case, out.topk_idx, np.random.default_rng(7))
     ref = msa_case.run(case, lists=lists)
@@ -402,7 +433,7 @@ def test_decode_q_outer_splits():
     dev = upload(case)
     got, _ = gpu_index(case, dev)
     out, scores = _oracle_index_scores(case)
-    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _bound_fn(case))
+    n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, _err_fn(case))
     assert not bad
     full = msa_case.run(case)
     for mode in (msa.MSA_AUTO, msa.MSA_KV_OUTER):
@@ -438,3 +469,30 @@ def test_constant_values_and_invariants():
     for mode in (msa.MSA_KV_OUTER, msa.MSA_Q_OUTER):
         o, _ = gpu_attention(case, dev, torch.from_numpy(got).cuda(), mode)
         assert np.max(np.abs(o - 1.0)) <= 2 ** -7
+
+
+@pytest.mark.parametrize("mode", [msa.MSA_KV_OUTER, msa.MSA_Q_OUTER], ids=["kv", "q"])
+def test_topk1_local_only_is_block_diagonal_attention(mode):
+    """topK = 1: the index branch keeps only the forced local block, so the layer is causal
+    attention masked to the query's own 128-key block. The GPU index branch and main branch
+    run end to end; the lists must be exactly the local block, and the output is compared
+    with torch's scaled_dot_product_attention (CPU, float64) under the block-diagonal causal
+    mask, computed independently of the oracle."""
+    _say(f"[topk=1] mode={mode}")
+    case = mi.make_case(mi.custom(name="k1", n_q=(700,), hq=8, hkv=2, topk=1, dp=32), seed=8)
+    dev = upload(case)
+    got, _ = gpu_index(case, dev)
+    n = case.total_q
+    assert np.array_equal(got[:, :, 0], np.repeat((np.arange(n) // 128)[:, None], 2, axis=1))
+    o, lse = gpu_attention(case, dev, torch.from_numpy(got).cuda(), mode)
+    q = torch.from_numpy(widen(case.q)).permute(1, 0, 2)                      # [Hq, N, D]
+    kv_rep = case.cfg.hq // case.cfg.hkv
+    k = torch.from_numpy(widen(case.k)).permute(1, 0, 2).repeat_interleave(kv_rep, dim=0)
+    v = torch.from_numpy(widen(case.v)).permute(1, 0, 2).repeat_interleave(kv_rep, dim=0)
+    i = torch.arange(n)
+    mask = (i[None, :] <= i[:, None]) & (i[None, :] // 128 == i[:, None] // 128)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=mask, scale=case.softmax_scale).permute(1, 0, 2).numpy()
+    err = float(np.max(np.abs(o - want)))
+    _say(f"max |O - O_sdpa| = {err:.3e}")
+    assert err <= 2e-2

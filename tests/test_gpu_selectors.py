@@ -4,7 +4,8 @@ fp64 oracle, and the selector -> per-tile attention pipeline.
 Lists must equal the oracle's up to certified near-ties: the GPU averages bf16 tokens and
 forms the dot products in fp32, so a representative's error is within gamma_128 of the mean
 of |x| per dimension and a score's within 3 gamma_128 sum_d A_d B_d (A, B: means of |q|,
-|k|); the test allows twice 4 gamma_128 |A|_2 |B|_2 between two swapped blocks."""
+|k|); each block's score is taken within 4 gamma_128 |A|_2 |B|_2 of the oracle's, and a
+differing list must be the selection of some scores within those bounds (capped in number)."""
 import numpy as np
 import pytest
 import torch
@@ -88,7 +89,7 @@ def test_selector_matches_oracle(name, kw, reps):
     got = got.cpu().numpy()
     want, scores, bounds = oracle_select(case, reps)
     n_diff, n_tie, bad = compare_lists(got, want, lambda i, g: scores[(i, g)],
-                                       lambda i, g: bounds[(i, g)])
+                                       lambda i, g: bounds[(i, g)] / 2)
     _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
     assert not bad, f"uncertified list differences at {bad[:5]}"
     # reported scores: the oracle's within one score's bound; -inf on empty slots
@@ -106,8 +107,8 @@ def test_selector_matches_oracle(name, kw, reps):
 
 @pytest.mark.parametrize("reps", [1, 4])
 def test_selector_then_tile_attention(reps):
-    """R1 / R4 lists feed the per-tile attention; outputs against the oracle on its own lists
-    (tiles whose lists differ by a certified near-tie are left out)."""
+    """R1 / R4 lists feed the per-tile attention; lists against the oracle's (exact or
+    certified near-ties), outputs against the oracle's attention over the GPU's lists."""
     _say(f"[selector pipeline] R{reps}")
     case = mi.make_case(mi.custom(name="sp", n_q=(640, 200), n_k=(2500, 900), hq=8, hkv=2,
                                   topk=6, causal=False, list_q=128, selector=reps), seed=6)
@@ -116,17 +117,13 @@ def test_selector_then_tile_attention(reps):
     want, scores, bounds = oracle_select(case, reps)
     g_np = got.cpu().numpy()
     n_diff, n_tie, bad = compare_lists(g_np, want, lambda i, g: scores[(i, g)],
-                                       lambda i, g: bounds[(i, g)])
+                                       lambda i, g: bounds[(i, g)] / 2)
     assert not bad
-    case.lists = want
+    _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
+    # the oracle's attention over the lists the GPU selected, on every query
+    case.lists = g_np
     out = msa_case.run(case)
     o, lse = gpu_attention(case, dev, got, msa.MSA_AUTO)
-    tiles_max = -(-case.max_q // 128)
-    same_row = np.all(g_np == want, axis=(1, 2))
-    seq = np.searchsorted(case.cu_q, np.arange(case.total_q), side="right") - 1
-    row = seq * tiles_max + (np.arange(case.total_q) - case.cu_q[seq]) // 128
-    keep = same_row[row]
-    st = err_stats(o[keep], out.o[keep], lse[keep], out.lse[keep])
-    _say(st, "queries compared", int(keep.sum()))
-    assert keep.mean() > 0.9
+    st = err_stats(o, out.o, lse, out.lse)
+    _say(st)
     assert st["max_abs"] <= 2e-2 and st["max_dlse"] <= 1e-2 and st["lse_inf_match"]

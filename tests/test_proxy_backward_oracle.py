@@ -96,3 +96,29 @@ def test_proxy_equal_to_the_main_attention_has_zero_loss_and_gradient():
     assert abs(loss) < 1e-12
     assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
     assert np.all(np.isfinite(lsep))
+
+
+def test_row_and_column_gradients_match_the_whole_sequence_proxy_backward():
+    """dq_idx and LSEp of sampled rows alone, and dk_idx of one (group, block) column alone
+    (used at full size), equal the whole-sequence proxy backward's values."""
+    from oracle import msa_case
+    from synth import msa_inputs as mi
+    from synth.msa_inputs import widen
+    cfg = mi.custom("pcols", n_q=(300,), n_k=(600,), hq=8, hkv=2, topk=3, dp=32)
+    case = mi.make_case(cfg, seed=6)
+    q, k = widen(case.q), widen(case.k)
+    qi, ki = widen(case.q_idx), widen(case.k_idx)
+    lists = msa_case.run(case, want_output=False).topk_idx
+    ps = 1.0 / np.sqrt(32)
+    dqi, dki, _, lsep = PB.proxy_backward(q, k, qi, ki, lists, case.softmax_scale, ps, 128, True)
+    rows = np.array([0, 7, 128, 299])
+    gq, gl = PB.proxy_rows_gradient(q, k, qi, ki, lists[rows], rows, case.softmax_scale, ps,
+                                    128, True)
+    np.testing.assert_allclose(gq, dqi[rows], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(gl, lsep[rows], rtol=1e-13)
+    for g in range(2):
+        for b in range(5):
+            got = PB.proxy_key_block_gradient(q, k, qi, ki, lists, g, b, case.softmax_scale, ps,
+                                              128, True)
+            lo, hi = 128 * b, min(128 * b + 128, 600)
+            np.testing.assert_allclose(got, dki[lo:hi, g], rtol=1e-12, atol=1e-14)
