@@ -108,7 +108,8 @@ def test_selector_matches_oracle(name, kw, reps):
 @pytest.mark.parametrize("reps", [1, 4])
 def test_selector_then_tile_attention(reps):
     """R1 / R4 lists feed the per-tile attention; lists against the oracle's (exact or
-    certified near-ties), outputs against the oracle's attention over the GPU's lists."""
+    certified near-ties, capped), outputs against the oracle's on the queries whose tile
+    lists equal the oracle's."""
     _say(f"[selector pipeline] R{reps}")
     case = mi.make_case(mi.custom(name="sp", n_q=(640, 200), n_k=(2500, 900), hq=8, hkv=2,
                                   topk=6, causal=False, list_q=128, selector=reps), seed=6)
@@ -120,10 +121,14 @@ def test_selector_then_tile_attention(reps):
                                        lambda i, g: bounds[(i, g)] / 2)
     assert not bad
     _say(f"rows differing {n_diff}, certified near-ties {n_tie}")
-    # the oracle's attention over the lists the GPU selected, on every query
-    case.lists = g_np
+    case.lists = want
     out = msa_case.run(case)
     o, lse = gpu_attention(case, dev, got, msa.MSA_AUTO)
-    st = err_stats(o, out.o, lse, out.lse)
-    _say(st)
+    # queries of tiles with a certified swap ran on other lists than the oracle's: left out
+    tiles_max = -(-case.max_q // 128)
+    same_row = np.all(g_np == want, axis=(1, 2))
+    seq = np.searchsorted(case.cu_q, np.arange(case.total_q), side="right") - 1
+    keep = same_row[seq * tiles_max + (np.arange(case.total_q) - case.cu_q[seq]) // 128]
+    st = err_stats(o[keep], out.o[keep], lse[keep], out.lse[keep])
+    _say(st, "queries compared", int(keep.sum()))
     assert st["max_abs"] <= 2e-2 and st["max_dlse"] <= 1e-2 and st["lse_inf_match"]
