@@ -32,8 +32,18 @@ from synth import msa_inputs as mi    # noqa: E402
 PEAK_HBM = 8.0e12            # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15           # dense bf16 MFMA FLOP/s
 PEAK_FP8 = 5.0e15            # dense fp8 MFMA FLOP/s
-KERNEL_SOURCES = ("block_sparse_gqa_amd/csrc/attn_kv.hip", "block_sparse_gqa_amd/csrc/attn_tile.h",
-                  "block_sparse_gqa_amd/csrc/msa_device.h")
+CSRC = "block_sparse_gqa_amd/csrc"
+# sources each call's kernels are built from (a traffic figure is kept only while they are
+# unchanged)
+COMMON = (f"{CSRC}/msa_device.h", f"{CSRC}/msa_internal.h")
+CALL_SOURCES = {
+    "index": (f"{CSRC}/index_topk.hip",) + COMMON,
+    "select": (f"{CSRC}/select_tiles.hip",) + COMMON,
+    "plan": (f"{CSRC}/plan.hip",) + COMMON,
+    "attn_main": (f"{CSRC}/attn_kv.hip", f"{CSRC}/attn_tile.h") + COMMON,
+    "attn_q": (f"{CSRC}/attn_q.hip", f"{CSRC}/attn_tile.h") + COMMON,
+    "combine": (f"{CSRC}/combine.hip",) + COMMON,
+}
 
 WORKLOADS = {
     # name -> (config key, description)
@@ -58,9 +68,14 @@ WORKLOADS = {
 }
 
 
-def kernel_sha() -> str:
+def kernel_sha(paths=None) -> str:
+    """Hash of the given sources (default: every source of the library and its header)."""
+    if paths is None:
+        d = os.path.join(ROOT, CSRC)
+        paths = [os.path.join(CSRC, f) for f in sorted(os.listdir(d))
+                 if f.endswith((".hip", ".h"))] + ["include/msa.h"]
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -206,15 +221,58 @@ def cpu_baseline(case, budget_s: float) -> dict:
                       f"fp64 NumPy, {t_used:.1f} s wall on {platform.processor() or 'host'}"}
 
 
-def load_traffic(workload: str, launches_bytes_alg: float):
-    path = os.path.join(ROOT, "profiles", f"attn_kv_traffic_{workload}.json")
+def load_traffic(workload: str) -> dict:
+    """HBM bytes per launch of each call (FETCH_SIZE and WRITE_SIZE, scaled by what the same
+    counters read for a device copy of known size), from profiles/traffic_<workload>.json;
+    a call whose sources changed since the counters were taken gets None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_sha():
-        return None
-    return t.get("traffic_bytes_per_launch")
+    out = {}
+    for call, e in t.get("calls", {}).items():
+        ok = call in CALL_SOURCES and e.get("sha") == kernel_sha(CALL_SOURCES[call])
+        out[call] = e.get("traffic_bytes") if ok else None
+    return out
+
+
+def measure_ceilings(dev, mib: int = 2048) -> dict:
+    """Memory ceilings measured on this GPU: torch's fill (write), copy (read + write) and sum
+    (read) over a buffer of `mib` MiB, best of five after warm-up, in GB/s."""
+    n = (mib << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+
+    def best(fn, nbytes):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return nbytes / min(ts) / 1e9
+    nb = n * 4
+    out = {"write_gbps": best(lambda: a.fill_(2.0), nb),
+           "copy_gbps": best(lambda: b.copy_(a), 2 * nb),
+           "read_gbps": best(lambda: a.sum(), nb),
+           "buffer_mib": mib, "how": "torch fill_ / copy_ / sum on one buffer, best of 5"}
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def mix_ceiling(ceil: dict, read_bytes: float, write_bytes: float) -> float:
+    """Measured ceiling (GB/s) for a kernel that reads and writes these amounts: the time the
+    measured read and write rates need for them, as one rate."""
+    t = read_bytes / ceil["read_gbps"] + write_bytes / ceil["write_gbps"]
+    return (read_bytes + write_bytes) / t if t > 0 else 0.0
 
 
 def bench_backward(args, case, shape, desc, t) -> None:
@@ -351,6 +409,202 @@ def cpu_baseline_backward(case, lists: np.ndarray, dout, budget_s: float) -> dic
                       f"NumPy, {t_used:.1f} s wall"}
 
 
+def prepare(workload: str, seed: int, mode_name: str, dev: str) -> dict:
+    """Seeded inputs of a workload, uploaded to HBM, with the buffers of one layer call."""
+    cfg_key, desc = WORKLOADS[workload]
+    t_gen = time.perf_counter()
+    case = mi.make_case(cfg_key, seed=seed)
+    t_gen = time.perf_counter() - t_gen
+    cfg = case.cfg
+    dtype = msa.MSA_FP8_E4M3 if cfg.dtype == "fp8" else msa.MSA_BF16
+    shape = msa.make_shape(batch=len(case.cu_q) - 1, total_q=case.total_q, total_k=case.total_k,
+                           max_q=case.max_q, max_k=case.max_k, hq=cfg.hq, hkv=cfg.hkv,
+                           topk=cfg.topk, dp=cfg.dp, causal=cfg.causal, dtype=dtype,
+                           list_q=cfg.list_q)
+    mode = {"auto": msa.MSA_AUTO, "kv": msa.MSA_KV_OUTER, "q": msa.MSA_Q_OUTER}[mode_name]
+    chosen = msa.msa_resolve_mode(shape, mode)
+    up = lambda t: None if t is None else t.contiguous().to(dev)
+    c = dict(workload=workload, desc=desc, case=case, cfg=cfg, dtype=dtype, shape=shape,
+             chosen=chosen, t_gen=t_gen)
+    c["q"], c["k"], c["v"] = up(case.q), up(case.k), up(case.v)
+    c["q_idx"], c["k_idx"] = up(case.q_idx), up(case.k_idx)
+    c["idx8"] = cfg.idx_dtype == "fp8"
+    c["idx_descale"] = (torch.tensor(case.idx_descale, dtype=torch.float32, device=dev)
+                        if c["idx8"] else None)
+    c["cu_q"] = torch.from_numpy(case.cu_q).to(dev)
+    c["cu_k"] = torch.from_numpy(case.cu_k).to(dev)
+    c["descale"] = torch.tensor(case.descale, dtype=torch.float32, device=dev) if dtype else None
+    c["given"] = torch.from_numpy(case.lists).to(dev) if case.lists is not None else None
+    sel = c["sel"] = cfg.selector              # per-tile lists from the R1 / R4 selector
+    c["n_lists"] = (case.total_q if cfg.list_q == 1
+                    else (len(case.cu_q) - 1) * -(-case.max_q // 128))
+    c["topk"] = c["given"] if c["given"] is not None else torch.empty(
+        (c["n_lists"], cfg.hkv, cfg.topk), dtype=torch.int32, device=dev)
+    c["iws"] = torch.empty(max(msa.msa_index_workspace_size(shape)
+                               if c["given"] is None and not sel else 0, 256),
+                           dtype=torch.uint8, device=dev)
+    c["sws"] = torch.empty(msa.msa_select_workspace_size(shape, sel) if sel else 256,
+                           dtype=torch.uint8, device=dev)
+    c["ws"] = torch.empty(msa.msa_workspace_size(shape, chosen), dtype=torch.uint8, device=dev)
+    c["o"] = torch.empty((case.total_q, cfg.hq, 128), dtype=torch.bfloat16, device=dev)
+    c["lse"] = torch.empty((case.total_q, cfg.hq), dtype=torch.float32, device=dev)
+    return c
+
+
+def make_step(c: dict):
+    """One layer call on the workload's buffers, HIP events recorded between its calls (on
+    torch's current stream, the one the library launches on)."""
+    shape, chosen, scale = c["shape"], c["chosen"], c["case"].softmax_scale
+    given, sel, idx8 = c["given"], c["sel"], c["idx8"]
+    q, k, v, topk, ws, o, lse = c["q"], c["k"], c["v"], c["topk"], c["ws"], c["o"], c["lse"]
+    cu_q, cu_k = c["cu_q"], c["cu_k"]
+    kv = chosen == msa.MSA_KV_OUTER
+    first = (["select"] if sel else ["index"]) if given is None else []
+    names = first + (["plan", "attn_main"] if kv else ["attn_q"]) + ["combine"]
+
+    def step(evs=None):
+        i = 0
+        if evs:
+            evs[0].record()
+        if given is None and sel:
+            msa.msa_select_tiles(shape, sel, q, k, cu_q, cu_k, topk, None, c["sws"])
+        elif given is None and idx8:
+            msa.msa_index_topk_fp8(shape, c["q_idx"], c["k_idx"], c["idx_descale"], cu_q, cu_k,
+                                   topk, None, c["iws"])
+        elif given is None:
+            msa.msa_index_topk(shape, c["q_idx"], c["k_idx"], cu_q, cu_k, topk, None, c["iws"])
+        if given is None and evs:
+            i += 1
+            evs[i].record()
+        if kv:
+            msa.msa_plan(shape, topk, cu_q, cu_k, ws)
+            if evs:
+                i += 1
+                evs[i].record()
+            msa.msa_attn_main(shape, q, k, v, c["descale"], scale, cu_q, cu_k, ws)
+        else:
+            msa.msa_sparse_attn_fwd(shape, q, k, v, c["descale"], scale, topk, cu_q, cu_k, chosen,
+                                    ws, o, lse)
+        if evs:
+            i += 1
+            evs[i].record()
+        msa.msa_combine(shape, chosen, ws, o, lse)
+        if evs:
+            i += 1
+            evs[i].record()
+    return step, names
+
+
+def run_forward(c: dict, steps: int, warmup: int, ceil: dict | None) -> dict:
+    """Time `steps` layer calls after `warmup`; the result line of the workload."""
+    case, cfg, dtype, chosen = c["case"], c["cfg"], c["dtype"], c["chosen"]
+    step, names = make_step(c)
+    timer = Timer(names)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: every kernel bracketed by HIP events on the stream the library launches on
+    # (torch's current stream), the whole region by the host clock
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer.step())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    kms = timer.ms()
+
+    kv = chosen == msa.MSA_KV_OUTER
+    given, sel = c["given"], c["sel"]
+    lists_np = c["topk"].cpu().numpy()
+    pairs, nsb = useful_pairs(cfg, case.cu_q, case.cu_k, lists_np, cfg.list_q)
+    flops = 4.0 * 128 * pairs
+    g = cfg.hq // cfg.hkv
+    eb = 1 if dtype else 2
+    peak_mma = PEAK_FP8 if dtype else PEAK_BF16
+    n_ent = int(c["ws"][:4].view(torch.int32)[0].item()) if kv else 0
+    traffic = load_traffic(c["workload"])
+    res = {
+        "metric": "main-attn TFLOP/s (useful pairs) + % MFMA/HBM roofline; ms per layer call",
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if dtype else "bf16",
+        "data": "synthetic (seeded NumPy draws, see DESIGN.md input recipe)",
+        "config": {"workload": c["workload"], "description": c["desc"],
+                   "mode": {1: "kv_outer", 2: "q_outer"}[chosen],
+                   "global_batch": len(case.cu_q) - 1, "seq_len": case.max_q,
+                   "hq": cfg.hq, "hkv": cfg.hkv, "d": 128, "block": 128, "topk": cfg.topk,
+                   "dp": cfg.dp, "causal": cfg.causal, "parallelism": "single GPU"},
+        "kernel_ms": kms,
+        "useful_gflop": flops / 1e9,
+        "nsb": nsb, "nsb_over_n": nsb / max(1, case.total_q), "entries": n_ent,
+    }
+    main_name = "attn_main" if kv else "attn_q"
+    t_main = kms[main_name] * 1e-3
+    res["main_attn_tflops"] = flops / t_main / 1e12
+    res["main_attn_mfma_frac"] = flops / t_main / peak_mma
+    kr = {}
+    if given is None and sel:
+        # representatives read Q and K once; the lists are written
+        kr["select"] = roof(kms["select"], "hbm", (case.total_q * cfg.hq + case.total_k * cfg.hkv)
+                            * 128 * 2 + c["n_lists"] * cfg.hkv * cfg.topk * 4)
+    elif given is None:
+        ifl, ib = index_work(cfg, case.cu_q, case.cu_k)
+        pk = PEAK_FP8 if cfg.idx_dtype == "fp8" else PEAK_BF16
+        kr["index"] = roof(kms["index"], "mfma", ifl, pk) if ifl / ib > pk / PEAK_HBM else \
+            roof(kms["index"], "hbm", ib)
+    if kv:
+        q_bytes = case.total_q * cfg.hq * 128 * eb          # Q, each query once
+        kv_bytes = nsb * 2 * 128 * 128 * eb                 # selected K and V blocks once
+        part_bytes = n_ent * g * 128 * 2 + n_ent * g * 4    # bf16 partial O, fp32 LSE written
+        alg = q_bytes + kv_bytes + part_bytes
+        kname = "attn_kv_f8_kernel" if dtype else "attn_kv_tiled_kernel"
+        res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": alg / t_main / 1e9,
+                           "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": alg / t_main / PEAK_HBM,
+                           "traffic": traffic.get("attn_main"), "algorithmic_bytes": alg}
+        if ceil:
+            pm = mix_ceiling(ceil, q_bytes + kv_bytes, part_bytes)
+            res["roofline"]["peak_measured"] = pm
+            res["roofline"]["frac_measured"] = alg / t_main / 1e9 / pm
+        comb_read = n_ent * g * (128 * 2 + 4) + case.total_q * cfg.hkv * cfg.topk * 4
+        comb_write = case.total_q * cfg.hq * (128 * 2 + 4)
+        comb_alg = comb_read + comb_write
+        res["combine_gbps"] = comb_alg / (kms["combine"] * 1e-3) / 1e9
+        e_max = case.total_q * cfg.hkv * cfg.topk
+        kr["plan"] = roof(kms["plan"], "hbm", e_max * 4 + n_ent * 8 + e_max * 4)
+        kr["attn_main"] = roof(kms["attn_main"], "hbm", alg)
+        kr["combine"] = roof(kms["combine"], "hbm", comb_alg)
+        if ceil:
+            kr["attn_main"]["peak_measured"] = res["roofline"]["peak_measured"]
+            kr["combine"]["peak_measured"] = mix_ceiling(ceil, comb_read, comb_write)
+            kr["combine"]["frac_measured"] = (comb_alg / (kms["combine"] * 1e-3) / 1e9
+                                              / kr["combine"]["peak_measured"])
+    else:
+        qbytes = nsb * 2 * 128 * 128 * eb + case.total_q * cfg.hq * 128 * (eb + 2)
+        if flops / qbytes > peak_mma / PEAK_HBM:
+            res["roofline"] = {"bound": "mfma", "kernel": "attn_q_kernel",
+                               "achieved": flops / t_main / 1e12, "peak": peak_mma / 1e12,
+                               "unit": "TFLOP/s", "frac": flops / t_main / peak_mma,
+                               "traffic": traffic.get("attn_q")}
+            kr["attn_q"] = roof(kms["attn_q"], "mfma", flops, peak_mma)
+        else:
+            res["roofline"] = {"bound": "hbm", "kernel": "attn_q_kernel",
+                               "achieved": qbytes / t_main / 1e9, "peak": PEAK_HBM / 1e9,
+                               "unit": "GB/s", "frac": qbytes / t_main / PEAK_HBM,
+                               "traffic": traffic.get("attn_q"), "algorithmic_bytes": qbytes}
+            kr["attn_q"] = roof(kms["attn_q"], "hbm", qbytes)
+        kr["combine"] = {"ms": kms["combine"]}
+    for call, e in kr.items():
+        if call in traffic:
+            e["traffic"] = traffic[call]
+    res["kernels"] = kr
+    res["kernel_sha"] = kernel_sha()
+    res["gen_seconds"] = round(c["t_gen"], 1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,6 +615,11 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--secondary", default="m3_fp8_long",
+                    help="a second workload timed in the same run and reported under "
+                         "'secondary' (only with the default workload; 'none' to skip)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured memory ceilings")
     ap.add_argument("--backward", action="store_true",
                     help="time the main-branch backward (msa_sparse_attn_bwd) instead")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -374,173 +633,18 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = "cuda"
-    cfg_key, desc = WORKLOADS[args.workload]
-    t_gen = time.perf_counter()
-    case = mi.make_case(cfg_key, seed=args.seed)
-    t_gen = time.perf_counter() - t_gen
-    cfg = case.cfg
-    dtype = msa.MSA_FP8_E4M3 if cfg.dtype == "fp8" else msa.MSA_BF16
-    shape = msa.make_shape(batch=len(case.cu_q) - 1, total_q=case.total_q, total_k=case.total_k,
-                           max_q=case.max_q, max_k=case.max_k, hq=cfg.hq, hkv=cfg.hkv,
-                           topk=cfg.topk, dp=cfg.dp, causal=cfg.causal, dtype=dtype,
-                           list_q=cfg.list_q)
-    mode = {"auto": msa.MSA_AUTO, "kv": msa.MSA_KV_OUTER, "q": msa.MSA_Q_OUTER}[args.mode]
-    chosen = msa.msa_resolve_mode(shape, mode)
-
-    up = lambda t: None if t is None else t.contiguous().to(dev)
-    q, k, v = up(case.q), up(case.k), up(case.v)
-    q_idx, k_idx = up(case.q_idx), up(case.k_idx)
-    idx8 = cfg.idx_dtype == "fp8"
-    idx_descale = torch.tensor(case.idx_descale, dtype=torch.float32, device=dev) if idx8 else None
-    cu_q = torch.from_numpy(case.cu_q).to(dev)
-    cu_k = torch.from_numpy(case.cu_k).to(dev)
-    descale = torch.tensor(case.descale, dtype=torch.float32, device=dev) if dtype else None
-    given = torch.from_numpy(case.lists).to(dev) if case.lists is not None else None
-    sel = cfg.selector                         # per-tile lists from the R1 / R4 selector
-    n_lists = case.total_q if cfg.list_q == 1 else (len(case.cu_q) - 1) * -(-case.max_q // 128)
-    topk = given if given is not None else torch.empty((n_lists, cfg.hkv, cfg.topk),
-                                                      dtype=torch.int32, device=dev)
-    iws = torch.empty(max(msa.msa_index_workspace_size(shape)
-                          if given is None and not sel else 0, 256), dtype=torch.uint8,
-                      device=dev)
-    sws = torch.empty(msa.msa_select_workspace_size(shape, sel) if sel else 256,
-                      dtype=torch.uint8, device=dev)
-    ws = torch.empty(msa.msa_workspace_size(shape, chosen), dtype=torch.uint8, device=dev)
-    o = torch.empty((case.total_q, cfg.hq, 128), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((case.total_q, cfg.hq), dtype=torch.float32, device=dev)
-    scale = case.softmax_scale
-
-    kv = chosen == msa.MSA_KV_OUTER
-    first = (["select"] if sel else ["index"]) if given is None else []
-    names = first + (["plan", "attn_main"] if kv else ["attn_q"]) + ["combine"]
-    timer = Timer(names)
-
-    def step(evs=None):
-        i = 0
-        rec = (lambda: evs[i].record()) if evs else (lambda: None)
-        if evs:
-            evs[0].record()
-        if given is None and sel:
-            msa.msa_select_tiles(shape, sel, q, k, cu_q, cu_k, topk, None, sws)
-        elif given is None and idx8:
-            msa.msa_index_topk_fp8(shape, q_idx, k_idx, idx_descale, cu_q, cu_k, topk, None, iws)
-        elif given is None:
-            msa.msa_index_topk(shape, q_idx, k_idx, cu_q, cu_k, topk, None, iws)
-        if given is None:
-            if evs:
-                i += 1
-                evs[i].record()
-        if kv:
-            msa.msa_plan(shape, topk, cu_q, cu_k, ws)
-            if evs:
-                i += 1
-                evs[i].record()
-            msa.msa_attn_main(shape, q, k, v, descale, scale, cu_q, cu_k, ws)
-        else:
-            msa.msa_sparse_attn_fwd(shape, q, k, v, descale, scale, topk, cu_q, cu_k, chosen, ws,
-                                    o, lse)
-        if evs:
-            i += 1
-            evs[i].record()
-        msa.msa_combine(shape, chosen, ws, o, lse)
-        if evs:
-            i += 1
-            evs[i].record()
-
+    c = prepare(args.workload, args.seed, args.mode, dev)
     if args.backward:
+        step, _ = make_step(c)
         step()                                 # lists, O and LSE of the forward
-        bench_backward(args, case, shape, desc, (q, k, v, o, lse, topk, cu_q, cu_k, q_idx, k_idx))
+        bench_backward(args, c["case"], c["shape"], c["desc"],
+                       (c["q"], c["k"], c["v"], c["o"], c["lse"], c["topk"], c["cu_q"],
+                        c["cu_k"], c["q_idx"], c["k_idx"]))
         return
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed region: every kernel bracketed by HIP events on the stream the library launches on
-    # (torch's current stream), the whole region by the host clock
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(timer.step())
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    kms = timer.ms()
-
-    lists_np = topk.cpu().numpy()
-    pairs, nsb = useful_pairs(cfg, case.cu_q, case.cu_k, lists_np, cfg.list_q)
-    flops = 4.0 * 128 * pairs
-    g = cfg.hq // cfg.hkv
-    eb = 1 if dtype else 2
-    n_ent = int(ws[:4].view(torch.int32)[0].item()) if kv else 0
-    res = {
-        "metric": "main-attn TFLOP/s (useful pairs) + % MFMA/HBM roofline; ms per layer call",
-        "value": flops / (ms_per_step * 1e-3) / 1e12,
-        "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8" if dtype else "bf16",
-        "data": "synthetic (seeded NumPy draws, see DESIGN.md input recipe)",
-        "config": {"workload": args.workload, "description": desc, "mode": {1: "kv_outer", 2: "q_outer"}[chosen],
-                   "global_batch": len(case.cu_q) - 1, "seq_len": case.max_q,
-                   "hq": cfg.hq, "hkv": cfg.hkv, "d": 128, "block": 128, "topk": cfg.topk,
-                   "dp": cfg.dp, "causal": cfg.causal, "parallelism": "single GPU"},
-        "kernel_ms": kms,
-        "useful_gflop": flops / 1e9,
-        "nsb": nsb, "nsb_over_n": nsb / max(1, case.total_q), "entries": n_ent,
-    }
-    main_name = "attn_main" if kv else "attn_q"
-    t_main = kms[main_name] * 1e-3
-    res["main_attn_tflops"] = flops / t_main / 1e12
-    res["main_attn_mfma_frac"] = flops / t_main / PEAK_BF16
-    if kv:
-        alg = (case.total_q * cfg.hq * 128 * eb            # Q, each query once
-               + nsb * 2 * 128 * 128 * eb                   # selected K and V blocks once
-               + n_ent * g * 128 * 2                        # bf16 partial O written
-               + n_ent * g * 4)                             # fp32 partial LSE written
-        kname = "attn_kv_f8_kernel" if dtype else "attn_kv_tiled_kernel"
-        res["roofline"] = {"bound": "hbm", "kernel": kname, "achieved": alg / t_main / 1e9,
-                           "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": alg / t_main / PEAK_HBM,
-                           "traffic": load_traffic(args.workload, alg),
-                           "algorithmic_bytes": alg}
-        comb_alg = n_ent * g * (128 * 2 + 4) + case.total_q * cfg.hkv * cfg.topk * 4 \
-            + case.total_q * cfg.hq * (128 * 2 + 4)
-        res["combine_gbps"] = comb_alg / (kms["combine"] * 1e-3) / 1e9
-    else:
-        qbytes = nsb * 2 * 128 * 128 * eb + case.total_q * cfg.hq * 128 * (eb + 2)
-        if flops / qbytes > PEAK_BF16 / PEAK_HBM:
-            res["roofline"] = {"bound": "mfma", "kernel": "attn_q_kernel",
-                               "achieved": flops / t_main / 1e12, "peak": PEAK_BF16 / 1e12,
-                               "unit": "TFLOP/s", "frac": flops / t_main / PEAK_BF16,
-                               "traffic": None}
-        else:
-            res["roofline"] = {"bound": "hbm", "kernel": "attn_q_kernel",
-                               "achieved": qbytes / t_main / 1e9, "peak": PEAK_HBM / 1e9,
-                               "unit": "GB/s", "frac": qbytes / t_main / PEAK_HBM,
-                               "traffic": None, "algorithmic_bytes": qbytes}
-    # every call of the step against its own roofline
-    kr = {}
-    if given is None and sel:
-        # representatives read Q and K once; the lists are written
-        kr["select"] = roof(kms["select"], "hbm", (case.total_q * cfg.hq + case.total_k * cfg.hkv)
-                            * 128 * 2 + n_lists * cfg.hkv * cfg.topk * 4)
-    elif given is None:
-        ifl, ib = index_work(cfg, case.cu_q, case.cu_k)
-        pk = PEAK_FP8 if cfg.idx_dtype == "fp8" else PEAK_BF16
-        ridge = pk / PEAK_HBM
-        kr["index"] = roof(kms["index"], "mfma", ifl, pk) if ifl / ib > ridge else \
-            roof(kms["index"], "hbm", ib)
-    if kv:
-        e_max = case.total_q * cfg.hkv * cfg.topk
-        kr["plan"] = roof(kms["plan"], "hbm", e_max * 4 + n_ent * 8 + e_max * 4)
-        kr["attn_main"] = roof(kms["attn_main"], "hbm", alg)
-        kr["combine"] = roof(kms["combine"], "hbm", comb_alg)
-    else:
-        qbytes = nsb * 2 * 128 * 128 * eb + case.total_q * cfg.hq * 128 * (eb + 2)
-        kr["attn_q"] = roof(kms["attn_q"], "mfma", flops) if flops / qbytes > PEAK_BF16 / PEAK_HBM \
-            else roof(kms["attn_q"], "hbm", qbytes)
-        kr["combine"] = {"ms": kms["combine"]}
-    res["kernels"] = kr
-    res["kernel_sha"] = kernel_sha()
-    res["gen_seconds"] = round(t_gen, 1)
+    ceil = None if args.no_ceilings else measure_ceilings(dev)
+    res = run_forward(c, args.steps, args.warmup, ceil)
+    if ceil:
+        res["ceilings_measured"] = ceil
     if args.copy_probe:
         n = args.copy_probe << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -555,6 +659,21 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         res["copy_probe"] = {"bytes_each_way": n, "gbps": 2 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9}
+        del a, b
+    case = c["case"]
+    del c
+    torch.cuda.empty_cache()
+    if args.workload == "m3" and args.secondary != "none":
+        # the largest workload, fp8 at 128K tokens, timed in the same run
+        c2 = prepare(args.secondary, args.seed, args.mode, dev)
+        sec = run_forward(c2, max(5, args.steps // 2), max(1, args.warmup), ceil)
+        res["secondary"] = {k: sec[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup",
+                                                "dtype", "config", "kernel_ms", "roofline",
+                                                "kernels", "main_attn_tflops",
+                                                "main_attn_mfma_frac", "useful_gflop", "nsb",
+                                                "entries", "gen_seconds")}
+        del c2
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(res), flush=True)

@@ -59,33 +59,6 @@ __device__ __forceinline__ float exp_step(const f32x16 sc[4], int s, float sl2, 
   return l;
 }
 
-// Output staging: the wave's 32 rows x 256 B, 16-byte chunk c of row R at R*16 + (c ^ (R%16)).
-// Lane (col, hf) deposits dims 32*dt + 16*hf .. +15 of row col (chunks 4dt+2hf, +1).
-__device__ __forceinline__ void stage_o(u32x4* buf, const f32x16& o, int dt, int col, int hf) {
-  // opaque copies: the addresses are recomputed here instead of being held (or spilled)
-  // across the caller's loop
-  asm volatile("" : "+v"(col), "+v"(hf));
-  const int x = (2 * hf) ^ (col & 15);   // c ^ (col % 16) == (4dt + h2) ^ x
-  u32x4* const row = buf + col * 16;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[8 * h2 + 2 * i], o[8 * h2 + 2 * i + 1]);
-    row[(4 * dt + h2) ^ x] = w;
-  }
-}
-
-// Read-back i (0..7): lane l takes chunk l%16 of row R = 4i + l/16, so the 64 lanes hold
-// 1 KiB of consecutive output bytes. With R % 16 = 4 (i % 4) + l/16 the slot is
-// (l%16) ^ (l/16) ^ 4 (i % 4): the lane's address for read-back i is ub[i % 4] + 256 (i / 4).
-__device__ __forceinline__ void unstage_bases(int lane, int ub[4]) {
-  asm volatile("" : "+v"(lane));
-  const int lq = lane >> 4, x = (lane & 15) ^ lq;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ub[j] = (4 * j + lq) * 16 + (x ^ (4 * j));
-}
-
 // B operand of S^T from the staging buffer (chunk c of row R in slot c ^ (R % 16)):
 // elements 16*st + 8*hf .. +7 of the lane's row.
 __device__ __forceinline__ void read_q(const u32x4* buf, bf16x8 bq[8], int col, int hf) {
@@ -360,6 +333,82 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t srd(const void* p, int bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(q, 0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
 }
 
+// Lane offset that the buffer range check drops (a padding row, or no previous tile).
+constexpr int kOffDrop = 0x40000000;
+
+// Byte offset of the lane's row in the 8-row group layout of the partials, counted from the
+// group of the wave's first row o_row0 (the store descriptor's base), plus the lane's half
+// of a dim tile (chunks 4 dt + 2 hf + {0, 1}: 256 hf bytes); kOffDrop for rows past o_nrow.
+__device__ __forceinline__ int store_lane_offset(size_t o_row0, int o_nrow, int col, int hf) {
+  const int rr = (int)(o_row0 & 7) + col;
+  return col < o_nrow ? ((rr >> 3) << 11) + ((rr & 7) << 4) + (hf << 8) : kOffDrop;
+}
+
+// Dim tile dt of a wave's output (lane (col, hf) holds dims 32 dt + 16 hf .. +15 of row col)
+// from registers to the partial buffer: chunk 4 dt + 2 hf + j of each row, two stores that
+// each cover 8 whole 128-byte lines when the rows fill their groups. Streaming stores: the
+// partials are read once, by the combine kernel. The descriptor spans the (at most five)
+// groups the wave's 32 rows touch; offsets past it (kOffDrop) are dropped by the hardware.
+__device__ __forceinline__ void store_o_tile(char* part_o_b, size_t o_row0, const f32x16& o,
+                                             int dt, int voff) {
+  const __amdgpu_buffer_rsrc_t ro = srd(part_o_b + (o_row0 >> 3) * 2048, 5 * 2048);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[8 * j + 2 * i], o[8 * j + 2 * i + 1]);
+    __builtin_amdgcn_raw_buffer_store_b128(w, ro, voff + (4 * dt + j) * 128, 0, 2);
+  }
+}
+
+// fp8 output read-back i (0..7) from the wave's staging buffer (chunk c of row R at
+// R*16 + (c ^ (R % 16))): lane l takes row R = 8 (i / 2) + l % 8, chunk c = 8 (i % 2) + l / 8,
+// so that with the first row at a group boundary the 64 lanes hold the 1 KiB at i KiB of the
+// wave's 8 KiB in the group layout. Its LDS index is rb_lane + rb_step(i) (R % 16 = 8 ((i/2) % 2)
+// + l % 8 and c ^ (R % 16) = 8 ((i ^ i/2) % 2) + ((l / 8) ^ (l % 8)); l / 8, l % 8 < 8).
+__device__ __forceinline__ int readback_lane(int lane) {
+  return 16 * (lane & 7) + ((lane >> 3) ^ (lane & 7));
+}
+__device__ __forceinline__ constexpr int readback_step(int i) {
+  return 128 * (i >> 1) + 8 * ((i ^ (i >> 1)) & 1);
+}
+// Byte offset of the lane's chunk in read-back i from the group of the wave's first row:
+// sv_lane + 1024 i when no padding row is involved. The row R = 8 (i / 2) + l % 8 lies at
+// (r0 + R) = rr_lane + 8 (i / 2) with rr_lane = r0 + l % 8, so its group offset is
+// ((rr_lane / 8) + i / 2) * 2048 and its row in the group rr_lane % 8.
+__device__ __forceinline__ int readback_sv_lane(size_t o_row0, int lane) {
+  const int rr = (int)(o_row0 & 7) + (lane & 7);
+  return ((rr >> 3) << 11) + ((rr & 7) << 4) + ((lane >> 3) << 7);
+}
+
+// The wave's staged 8 KiB (fp8 kernel) read back and stored in the 8-row group layout. With
+// G >= 8 the wave's rows are whole groups from a group boundary and its real rows end on a
+// group boundary too: the descriptor's byte range (o_nrow * 256) drops exactly the padding
+// groups, and each store writes 1 KiB of consecutive bytes. Smaller groups compute each
+// lane's row and drop padding rows lane by lane.
+template <int G>
+__device__ __forceinline__ void store_staged_f8(const u32x4* obuf, char* part_o_b, size_t o_row0,
+                                                int o_nrow, int rb_lane, int lane) {
+  if constexpr (G >= 8) {
+    const __amdgpu_buffer_rsrc_t ro = srd(part_o_b + (o_row0 >> 3) * 2048, o_nrow * 256);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(obuf[rb_lane + readback_step(i)], ro,
+                                             lane * 16 + i * 1024, 0, 2);
+  } else {
+    const __amdgpu_buffer_rsrc_t ro = srd(part_o_b + (o_row0 >> 3) * 2048, 5 * 2048);
+    const int sv = readback_sv_lane(o_row0, lane);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int R = 8 * (i >> 1) + (lane & 7);
+      __builtin_amdgcn_raw_buffer_store_b128(obuf[rb_lane + readback_step(i)], ro,
+                                             R < o_nrow ? sv + (i >> 1) * 2048 + (i & 1) * 1024
+                                                        : kOffDrop,
+                                             0, 2);
+    }
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   constexpr int MQ = 256 / G;          // entries per tile
@@ -382,12 +431,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   const uint32_t kv_row = (uint32_t)a.hkv * kD;
   int vl[4];
   v_lane_offsets(lane, vl);
-  int ub[4];
-  unstage_bases(lane, ub);
   int qo[4];
   q_lane_offsets(lane, qo);
-  // byte offset of the lane's 16 bytes in read-back i < 4 (i >= 4: + 4 KiB)
-  const int o_voff = (lane >> 4) * 256 + (lane & 15) * 16;
+  char* const part_o_b = reinterpret_cast<char*>(a.part_o);
 
   // (sequence, group) of a phase
   auto seq_of = [&](int p, int* h) {
@@ -424,9 +470,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
   float o_l = 0.f, o_lse = 0.f;
-  // the previous tile's output rows: first partial row and row count (none yet)
+  // the previous tile's output rows: first partial row, row count (none yet) and the lane's
+  // byte offset in the 8-row group layout from the group of the first row
   size_t o_row0 = 0;
-  int o_nrow = 0;
+  int o_nrow = 0, o_voff = kOffDrop;
 
   while (true) {
     const bool trans = d1.n != 0 && (d1.b != d0.b || d1.p != d0.p);
@@ -456,43 +503,25 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
     const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs]);
     k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[0], 0, rp, sw, hf);
 
-    // ---- phase A: QK^T(j) | O(j-1) through LDS to memory: packed into LDS in steps 0-1,
-    // read back one step ahead of its stores in steps 2-6; the staging buffer is then free
-    // and the next tile's Q rows are requested in step 6
+    // ---- phase A: QK^T(j) | O(j-1) from registers to memory in steps 0-3 (dim tile st:
+    // two 16-byte chunks per lane, each store 8 whole 128-byte lines of the group layout);
+    // the next tile's Q rows are requested in step 4, when this tile's Q operands have been
+    // read (LDS reads complete in order, and the K operands of step 1 were read after them)
     f32x16 sc[4];
-    u32x4 wb[2];
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       if (st < 7) k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[(st + 1) & 1], st + 1, rp, sw, hf);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
-      if (st < 2) {
-        stage_o(obuf, oacc[2 * st], 2 * st, col, hf);
-        stage_o(obuf, oacc[2 * st + 1], 2 * st + 1, col, hf);
-      } else if (st < 7) {
-        if (st > 2) {
-          // streaming stores: the partials are read once, by the combine kernel
-          const __amdgpu_buffer_rsrc_t ro = srd(a.part_o + o_row0 * kD, o_nrow * kD * 2);
-#pragma unroll
-          for (int i2 = 0; i2 < 2; ++i2)
-            __builtin_amdgcn_raw_buffer_store_b128(wb[i2], ro, o_voff + (2 * (st - 3) + i2) * 1024, 0, 2);
-        }
-        if (st < 6) {
-#pragma unroll
-          for (int i2 = 0; i2 < 2; ++i2) {
-            const int i = 2 * (st - 2) + i2;
-            wb[i2] = obuf[ub[i & 3] + 256 * (i >> 2)];
-          }
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                                srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                                srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
-          // Q of the next tile into the staging buffer, whose read-back is complete (the
-          // stores above took its data from registers)
-          tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
-        }
+      if (st < 4) {
+        store_o_tile(part_o_b, o_row0, oacc[st], st, o_voff);
+      } else if (st == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                              srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                              srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+        tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
       }
       MSA_INTERLEAVE(1, 6);
     }
@@ -537,6 +566,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
     o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
     o_nrow = max(0, min(32, d0.n * G - wave * 32));
     o_row0 = (size_t)d0.e0 * G + wave * 32;
+    o_voff = store_lane_offset(o_row0, o_nrow, col, hf);
     if (d1.n == 0) break;
     if (trans) {
       const int k2 = fs;
@@ -555,13 +585,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   // output of the last tile (after the last, unused, Q load into the buffer)
   wait_vm0();
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) stage_o(obuf, oacc[dt], dt, col, hf);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
-    __builtin_amdgcn_raw_buffer_store_b128(w, srd(a.part_o + o_row0 * kD, o_nrow * kD * 2),
-                                           o_voff + i * 1024, 0, 2);
-  }
+  for (int dt = 0; dt < 4; ++dt) store_o_tile(part_o_b, o_row0, oacc[dt], dt, o_voff);
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
                                         srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
@@ -761,9 +785,8 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   const uint8_t* const kb = reinterpret_cast<const uint8_t*>(a.k);
   const uint8_t* const vb = reinterpret_cast<const uint8_t*>(a.v);
   const uint32_t kv_row = (uint32_t)a.hkv * kD;   // bytes between consecutive keys
-  int ub[4];
-  unstage_bases(lane, ub);
-  const int o_voff = (lane >> 4) * 256 + (lane & 15) * 16;
+  char* const part_o_b = reinterpret_cast<char*>(a.part_o);
+  const int rb_lane = readback_lane(lane);
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
 
@@ -855,13 +878,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       }
     }
     {
-      const __amdgpu_buffer_rsrc_t ro = srd(a.part_o + o_row0 * kD, o_nrow * kD * 2);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
-        // streaming store: the partials are read once, by the combine kernel
-        __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_voff + i * 1024, 0, 2);
-      }
+      // read back in the 8-row group layout; streaming stores: the partials are read once,
+      // by the combine kernel
+      store_staged_f8<G>(obuf, part_o_b, o_row0, o_nrow, rb_lane, lane);
       const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
       const float o_lse =
           o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
@@ -942,12 +961,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       row[2 * ((4 * dt + a4) ^ (col & 15)) + hf] = w;
     }
   }
-  const __amdgpu_buffer_rsrc_t ro = srd(a.part_o + o_row0 * kD, o_nrow * kD * 2);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const u32x4 w = obuf[ub[i & 3] + 256 * (i >> 2)];
-    __builtin_amdgcn_raw_buffer_store_b128(w, ro, o_voff + i * 1024, 0, 2);
-  }
+  store_staged_f8<G>(obuf, part_o_b, o_row0, o_nrow, rb_lane, lane);
   const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
   const float o_lse =
       o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();

@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
     if (hf == 0 && a.lse) a.lse[(size_t)t * a.hq + hh] = lse_v;
   } else {
     const size_t pe = ((size_t)t * a.hkv + h) * a.splits + split;
-    store_o_row(a.part_o + (pe * G + g) * kD, oacc, inv, hf);
+    store_o_part(a.part_o, pe * G + g, oacc, inv, hf);
     if (hf == 0) {
       a.part_lse[pe * G + g] = lse_v;
       a.part_l[pe * G + g] = 1.f;           // the partial output is already normalised

@@ -449,4 +449,21 @@ __device__ __forceinline__ void store_o_row(uint16_t* orow, const f32x16 o[4], f
   }
 }
 
+// The same row as a partial output (row p of the partial buffer, 8-row group layout).
+__device__ __forceinline__ void store_o_part(uint16_t* part_o, size_t p, const f32x16 o[4],
+                                             float mul, int hf) {
+  char* const base = reinterpret_cast<char*>(part_o);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = pack_bf16x2(o[dt][8 * h2 + 2 * i] * mul, o[dt][8 * h2 + 2 * i + 1] * mul);
+      *reinterpret_cast<u32x4*>(base + part_chunk_offset(p, 4 * dt + 2 * hf + h2)) = w;
+    }
+  }
+}
+
 }  // namespace msa

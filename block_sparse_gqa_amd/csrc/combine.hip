@@ -7,7 +7,7 @@
 //
 // A thread owns 8 output dims (16 bytes) of one (query, head): it reads the slot LSEs and
 // weight sums, then issues all of its slot loads before accumulating, so each wave keeps 16
-// independent 1 KiB gathers in flight. A partial is stored unnormalised (its output times its
+// independent 1 KiB gathers in flight. Partials are read in their 8-row group layout. A partial is stored unnormalised (its output times its
 // weight sum l), so slot k enters with coefficient exp(lse_k - m) / l_k.
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -28,7 +28,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   constexpr int BOXES = 256 / TPB;
   const int tid = threadIdx.x;
   const int box = blockIdx.x * BOXES + tid / TPB;
-  const int g = (tid / 16) % G, c = tid % 16;
+  // the thread's (head, 16-byte chunk): with G >= 8 an entry's G rows are whole 8-row groups
+  // of the partial layout and thread j of the box reads its bytes 16 j .. 16 j + 15 (each
+  // wave 1 KiB of consecutive bytes; its output stores fill 8 whole rows' halves)
+  const int j = tid % TPB;
+  const int g = G >= 8 ? 8 * (j >> 7) + (j & 7) : j % G;
+  const int c = G >= 8 ? (j >> 3) & 15 : j / G;
   const int t = box / hkv, h = box % hkv;
   if (t >= total_q) return;
   const int n_ent = counters[0];
@@ -54,8 +59,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       l = part_lse[(size_t)es[k] * G + g];
       w = part_l[(size_t)es[k] * G + g];
       // streaming load: each partial is read exactly once
-      v = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(part_o + ((size_t)es[k] * G + g) * kD + 8 * c));
+      v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const char*>(part_o) + part_chunk_offset((size_t)es[k] * G + g, c)));
     }
     ls[k] = l;
     lw[k] = w;

@@ -140,7 +140,8 @@ Layout layout(const msa_shape& s, msa_mode mode) {
   }
   L.part_lse = take((size_t)g.e_max * g.group * 4);
   L.part_l = take((size_t)g.e_max * g.group * 4);
-  L.part_o = take((size_t)g.e_max * g.group * s.d * 2);
+  // partial rows in groups of 8 (see the partial layout of the kernels)
+  L.part_o = take((size_t)((g.e_max * g.group + 7) / 8 * 8) * s.d * 2);
   L.total = off;
   return L;
 }

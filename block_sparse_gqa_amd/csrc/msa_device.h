@@ -140,6 +140,15 @@ __device__ __forceinline__ float wave_max_from(float v) {
   return fmaxf(v, shfl_xor_f(v, 32));
 }
 
+// Partial outputs (bf16, 256 bytes per row) are stored in groups of 8 rows: chunk c (dims
+// 8c .. 8c+7) of partial row p sits at byte ((p / 8) * 16 + c) * 128 + (p % 8) * 16, so chunk
+// c of 8 consecutive rows is one 128-byte line. A wave holding whole rows of 8-row groups
+// then writes 1 KiB of consecutive bytes per store instruction straight from its MFMA
+// registers, and the combine reads an entry of G >= 8 heads as G * 256 consecutive bytes.
+__device__ __forceinline__ size_t part_chunk_offset(size_t p, int c) {
+  return ((p >> 3) << 11) + ((size_t)c << 7) + ((p & 7) << 4);
+}
+
 // Per-sequence geometry read from the cumulative length arrays.
 struct Seq {
   int q0, nq, k0, nk;

@@ -108,10 +108,13 @@ typedef struct {
                           positive factor of the kernel's choosing that part_o carries too
                           (bf16: 1; fp8: 2^8 / sigma, with the V descale = sigma * 2^k,
                           sigma in [1, 2)); 1 where the partial output is already normalised */
-  size_t part_o;       /* bf16 [E, hq/hkv, d]: partial output before normalisation, i.e. the
-                          partial's attention output times part_l ("Kernel optimization
-                          ...", section 2: unnormalised accumulators, normalised in the
-                          combine) */
+  size_t part_o;       /* bf16, E * hq/hkv rows of d: partial output before normalisation,
+                          i.e. the partial's attention output times part_l ("Kernel
+                          optimization ...", section 2: unnormalised accumulators, normalised
+                          in the combine). Row p = e * (hq/hkv) + head is stored in groups of 8
+                          rows: dims 8c .. 8c+7 of row p at byte ((p / 8) * 16 + c) * 128 +
+                          (p % 8) * 16, so that dims 8c .. 8c+7 of 8 consecutive rows fill one
+                          128-byte line (the rows are padded to a multiple of 8) */
   size_t total;        /* bytes needed */
   int32_t slots;       /* slots per (query, group) in cmap */
   int32_t n_words;     /* bitmap words (0 for Q-outer) */

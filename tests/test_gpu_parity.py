@@ -258,7 +258,10 @@ def test_partials_match_oracle_partials(dtype):
     cmap = cmap.numpy().reshape(case.total_q, case.cfg.hkv, case.cfg.topk)
     plse = wsn[L.part_lse:L.part_lse + n_ent * G * 4].view(torch.float32).numpy().reshape(n_ent, G)
     pl = wsn[L.part_l:L.part_l + n_ent * G * 4].view(torch.float32).numpy().reshape(n_ent, G)
-    po = wsn[L.part_o:L.part_o + n_ent * G * 256].view(torch.bfloat16).float().numpy()
+    # 8-row groups: chunk c (dims 8c..8c+7) of row p at byte ((p // 8) * 16 + c) * 128 + (p % 8) * 16
+    n_grp = -(-n_ent * G // 8)
+    po = wsn[L.part_o:L.part_o + n_grp * 2048].view(torch.bfloat16).float().numpy()
+    po = po.reshape(n_grp, 16, 8, 8).transpose(0, 2, 1, 3).reshape(n_grp * 8, 128)[:n_ent * G]
     # stored unnormalised: output times the weight sum (a block always has a visible key here)
     assert np.all(pl >= 1.0)
     po = po.reshape(n_ent, G, 128) / pl[:, :, None]
