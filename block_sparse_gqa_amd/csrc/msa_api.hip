@@ -172,6 +172,44 @@ int device_cu_count() {
 
 }  // namespace msa
 
+
+// Scratch of the allocation-free main-branch call: one array per device, kept until the
+// process ends. In host code `scratch` names a host-side stand-in, not device memory: every
+// host use goes through the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+namespace msa {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device (nullptr and an error text on failure).
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {nullptr};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_error = e != hipSuccess ? hipGetErrorString(e) : "device index out of range";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_error = e != hipSuccess ? hipGetErrorString(e) : "scratch has no device address";
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+}  // namespace
+}  // namespace msa
+
 using namespace msa;
 
 extern "C" {
@@ -541,6 +579,34 @@ msa_status msa_combine(const msa_shape* shape, msa_mode mode, const void* worksp
     return MSA_ERR_LAUNCH;
   }
   return MSA_OK;
+}
+
+
+msa_status msa_sparse_attn_fwd_noalloc(const msa_shape* shape, const void* q, const void* k,
+                                       const void* v, const float* descale_qkv,
+                                       float softmax_scale, const int32_t* topk_idx,
+                                       const int32_t* cu_q, const int32_t* cu_k, msa_mode mode,
+                                       void* o, float* lse, hipStream_t stream) {
+  msa_status st = check_shape(shape);
+  if (st != MSA_OK) return st;
+  msa_mode m;
+  st = check_mode(*shape, mode, &m);
+  if (st != MSA_OK) return st;
+  const size_t need = layout(*shape, m).total;
+  if (need > (size_t)MSA_NOALLOC_SCRATCH_BYTES) {
+    g_last_error = "the shape needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                   std::to_string((size_t)MSA_NOALLOC_SCRATCH_BYTES) + " the library holds";
+    return MSA_ERR_WORKSPACE;
+  }
+  if (shape->total_q > 0 && !o) return MSA_ERR_NULL;
+  void* ws = scratch_ptr();
+  if (!ws) return MSA_ERR_LAUNCH;
+  // the same two calls as the workspace form, on the static scratch (nothing in it needs to
+  // start at zero: the plan and the Q-outer kernels write every value the later kernels read)
+  st = msa_sparse_attn_fwd(shape, q, k, v, descale_qkv, softmax_scale, topk_idx, cu_q, cu_k, m,
+                           ws, MSA_NOALLOC_SCRATCH_BYTES, o, lse, stream);
+  if (st != MSA_OK) return st;
+  return msa_combine(shape, m, ws, MSA_NOALLOC_SCRATCH_BYTES, o, lse, stream);
 }
 
 }  // extern "C"

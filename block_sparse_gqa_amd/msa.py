@@ -25,7 +25,8 @@ SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace
            "msa_index_topk", "msa_index_topk_fp8", "msa_sparse_attn_fwd", "msa_plan",
            "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles",
            "msa_bwd_workspace_size", "msa_sparse_attn_bwd", "msa_proxy_bwd_workspace_size",
-           "msa_proxy_attn_bwd", "msa_train_bwd_workspace_size", "msa_train_bwd")
+           "msa_proxy_attn_bwd", "msa_train_bwd_workspace_size", "msa_train_bwd",
+           "msa_sparse_attn_fwd_noalloc")
 
 
 class Shape(ctypes.Structure):
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
             "msa_plan": [sp, vp, vp, vp, vp, sz, vp],
             "msa_attn_main": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp],
             "msa_combine": [sp, i32, vp, sz, vp, vp, vp],
+            "msa_sparse_attn_fwd_noalloc": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, i32,
+                                            vp, vp, vp],
             "msa_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
             "msa_proxy_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
             "msa_train_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
@@ -98,7 +101,7 @@ def _check(st: int, where: str) -> None:
     if st != MSA_OK:
         L = lib()
         detail = L.msa_status_string(st).decode()
-        if st == MSA_ERR_LAUNCH:
+        if st == MSA_ERR_LAUNCH or (st == MSA_ERR_WORKSPACE and where.endswith("_noalloc")):
             detail += ": " + L.msa_last_error().decode()
         raise MSAError(st, where, detail)
 
@@ -218,6 +221,14 @@ def msa_attn_main(shape, q, k, v, descale_qkv, softmax_scale, cu_q, cu_k, worksp
 def msa_combine(shape, mode, workspace, o, lse, stream=None) -> None:
     _check(lib().msa_combine(ctypes.byref(shape), mode, _p(workspace), _nbytes(workspace), _p(o),
                              _p(lse), _stream(stream)), "msa_combine")
+
+
+def msa_sparse_attn_fwd_noalloc(shape, q, k, v, descale_qkv, softmax_scale, topk_idx, cu_q, cu_k,
+                                mode, o, lse, stream=None) -> None:
+    _check(lib().msa_sparse_attn_fwd_noalloc(ctypes.byref(shape), _p(q), _p(k), _p(v),
+                                             _p(descale_qkv), float(softmax_scale), _p(topk_idx),
+                                             _p(cu_q), _p(cu_k), mode, _p(o), _p(lse),
+                                             _stream(stream)), "msa_sparse_attn_fwd_noalloc")
 
 
 def msa_bwd_workspace_size(shape) -> int:

@@ -257,6 +257,24 @@ msa_status msa_attn_main(const msa_shape* shape, const void* q, const void* k, c
 msa_status msa_combine(const msa_shape* shape, msa_mode mode, const void* workspace,
                        size_t ws_bytes, void* o, float* lse, hipStream_t stream);
 
+/* Allocation-free form of the main branch, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Runs msa_sparse_attn_fwd followed by msa_combine with the same arguments, its workspace
+ * being a scratch array the library holds on each device (MSA_NOALLOC_SCRATCH_BYTES bytes per
+ * device, kept until the process ends), so `o` and `lse` (nullable) receive the final O and LSE
+ * whichever schedule `mode` resolves to. Calls no allocating routine. Errors: those of the two
+ * calls, and MSA_ERR_WORKSPACE (with the byte counts in msa_last_error) when
+ * msa_workspace_size(shape, mode) exceeds MSA_NOALLOC_SCRATCH_BYTES (a tiny prefill of 2048
+ * queries with 16 heads and topK 4 needs about 36 MB; 64 decode requests well under 8 MB).
+ * Every call on one device shares that device's scratch: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must be serialised by the caller. */
+#define MSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+msa_status msa_sparse_attn_fwd_noalloc(const msa_shape* shape, const void* q, const void* k,
+                                       const void* v, const float* descale_qkv,
+                                       float softmax_scale, const int32_t* topk_idx,
+                                       const int32_t* cu_q, const int32_t* cu_k, msa_mode mode,
+                                       void* o, float* lse, hipStream_t stream);
+
 /* Main-branch backward ("Flash-MSA: accelerating million-token training": the selected block
  * ids and the main branch's LSE are kept for the backward; the gradients are those of the
  * exact attention over each query's union of selected keys, as in msa_sparse_attn_fwd; the

@@ -345,3 +345,19 @@ def test_proxy_backward_argument_checks(L):
     assert pb(s, dki=None) == msa.MSA_ERR_NULL
     assert pb(s, nbytes=need - 1) == msa.MSA_ERR_WORKSPACE
     assert pb(s, ws=None) == msa.MSA_ERR_WORKSPACE
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_without_a_gpu(L):
+    """The allocation-free call checks the shape and the scratch size on the host first: a
+    shape whose workspace exceeds MSA_NOALLOC_SCRATCH_BYTES returns MSA_ERR_WORKSPACE with the
+    byte counts in msa_last_error, before any device call."""
+    import ctypes
+    big = msa.make_shape(batch=1, total_q=32768, total_k=32768, max_q=32768, max_k=32768,
+                         hq=64, hkv=4, topk=16, dp=64)
+    st = L.msa_sparse_attn_fwd_noalloc(ctypes.byref(big), None, None, None, None, 0.1, None,
+                                       None, None, msa.MSA_KV_OUTER, None, None, None)
+    assert st == msa.MSA_ERR_WORKSPACE
+    assert b"scratch" in L.msa_last_error()
+    st = L.msa_sparse_attn_fwd_noalloc(None, None, None, None, None, 0.1, None, None, None,
+                                       msa.MSA_KV_OUTER, None, None, None)
+    assert st == msa.MSA_ERR_NULL
