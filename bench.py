@@ -605,6 +605,93 @@ def run_forward(c: dict, steps: int, warmup: int, ceil: dict | None) -> dict:
     return res
 
 
+def calibrate(dev) -> dict:
+    """Read bandwidth of HBM (a 4 GiB working set) and of the caches (working sets of 16 MiB,
+    which fits the 4 MiB L2 of each of the 8 XCDs, and 64 to 192 MiB, within the 256 MiB
+    last-level cache), each the best of five probe launches reading 16 GiB."""
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device=dev)
+    total = 16 << 30
+    out = {}
+    for name, ws in (("hbm_4096mib", 4 << 30), ("mall_192mib", 192 << 20),
+                     ("mall_128mib", 128 << 20), ("mall_64mib", 64 << 20),
+                     ("l2_16mib", 16 << 20)):
+        for _ in range(2):
+            msa.msa_probe_read(buf, ws, total, sink)
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            msa.msa_probe_read(buf, ws, total, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        out[name + "_gbps"] = total / min(ts) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    out["beta_mall"] = out["mall_128mib_gbps"] / out["hbm_4096mib_gbps"]
+    return out
+
+
+def crossover_sweep(args, dev) -> dict:
+    """KV-outer against Q-outer across block reuse: 2048 queries in requests of n_q queries
+    that share one list of 16 blocks per group (each request its own 2048-key cache, every
+    block listed: nsb / N = 64 / n_q), Hq = 64, Hkv = 4, D = 128, bf16, non-causal. Each point
+    times the main branch and the combine of both schedules on the same inputs."""
+    n_total, nk, hq, hkv, topk = 2048, 2048, 64, 4, 16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    q = torch.randn((n_total, hq, 128), generator=gen, device=dev).to(torch.bfloat16)
+    k = torch.randn((n_total * nk, hkv, 128), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((n_total * nk, hkv, 128), generator=gen, device=dev).to(torch.bfloat16)
+    o = torch.empty((n_total, hq, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((n_total, hq), dtype=torch.float32, device=dev)
+    points = []
+    n_q = 1
+    while n_q <= n_total:
+        n_req = n_total // n_q
+        cu_q = torch.arange(0, n_total + 1, n_q, dtype=torch.int32, device=dev)
+        cu_k = torch.arange(0, n_req * nk + 1, nk, dtype=torch.int32, device=dev)
+        lists = torch.from_numpy(mi.shared_lists(n_q, n_req, nk // 128, hkv, topk,
+                                                 args.seed)).to(dev)
+        shape = msa.make_shape(batch=n_req, total_q=n_total, total_k=n_req * nk, max_q=n_q,
+                               max_k=nk, hq=hq, hkv=hkv, topk=topk, dp=64, causal=False)
+        row = {"n_q": n_q, "requests": n_req, "nsb_over_n": hkv * topk / n_q}
+        for mode, name in ((msa.MSA_KV_OUTER, "kv_outer_ms"), (msa.MSA_Q_OUTER, "q_outer_ms")):
+            ws = torch.empty(msa.msa_workspace_size(shape, mode), dtype=torch.uint8, device=dev)
+
+            def call():
+                msa.msa_sparse_attn_fwd(shape, q, k, v, None, 1.0 / math.sqrt(128), lists, cu_q,
+                                        cu_k, mode, ws, o, lse)
+                msa.msa_combine(shape, mode, ws, o, lse)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            row[name] = e0.elapsed_time(e1) / 10
+            del ws
+        row["auto"] = {1: "kv_outer", 2: "q_outer"}[msa.msa_resolve_mode(shape, msa.MSA_AUTO)]
+        row["model_x"] = msa.msa_crossover(shape, 1.0, 0.0)
+        points.append(row)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        n_q *= 2
+    # measured crossover: where log(kv / q) changes sign, interpolated in log(nsb / N)
+    cross = None
+    for a, b in zip(points, points[1:]):
+        ra = math.log(a["kv_outer_ms"] / a["q_outer_ms"])
+        rb = math.log(b["kv_outer_ms"] / b["q_outer_ms"])
+        if (ra > 0) != (rb > 0):
+            xa, xb = math.log(a["nsb_over_n"]), math.log(b["nsb_over_n"])
+            cross = math.exp(xa + (xb - xa) * ra / (ra - rb))
+    return {"points": points, "measured_crossover_nsb_over_n": cross}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,6 +711,10 @@ def main():
                     help="time the main-branch backward (msa_sparse_attn_bwd) instead")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also time a plain device copy of this many MiB (counter scaling)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="measure HBM and cache read bandwidth with the library's probe")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time KV-outer against Q-outer across block reuse levels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -633,6 +724,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = "cuda"
+    if args.calibrate or args.crossover:
+        res = {"metric": "memory bandwidth and schedule crossover", "n_gpus": 1}
+        if args.calibrate:
+            res["bandwidth"] = calibrate(dev)
+        if args.crossover:
+            res["crossover"] = crossover_sweep(args, dev)
+        print(json.dumps(res), flush=True)
+        return
     c = prepare(args.workload, args.seed, args.mode, dev)
     if args.backward:
         step, _ = make_step(c)

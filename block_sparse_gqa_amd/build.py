@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libmsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["msa_api.hip", "index_topk.hip", "plan.hip", "attn_kv.hip", "attn_q.hip",
-           "combine.hip", "select_tiles.hip", "backward.hip"]
+           "combine.hip", "select_tiles.hip", "backward.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -117,6 +117,10 @@ hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
                          const void* q, const void* k, const void* v, const float* descale,
                          float scale, const int32_t* lists, const int32_t* cu_q,
                          const int32_t* cu_k, char* ws, void* o, float* lse, hipStream_t st);
+// Read-bandwidth probe: kProbeGrid workgroups of 256 threads, 4 KiB per workgroup and pass.
+constexpr int kProbeGrid = 1024;
+hipError_t launch_probe_read(const void* buf, size_t working_set, size_t total, float* sink,
+                             hipStream_t st);
 hipError_t launch_combine(const msa_shape& s, const Geometry& g, const Layout& L,
                           const char* ws, void* o, float* lse, hipStream_t st);
 // Main-branch backward: workspace = the KV-outer plan, bf16 dQ partials [E, group, d], the

@@ -26,7 +26,7 @@ SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace
            "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles",
            "msa_bwd_workspace_size", "msa_sparse_attn_bwd", "msa_proxy_bwd_workspace_size",
            "msa_proxy_attn_bwd", "msa_train_bwd_workspace_size", "msa_train_bwd",
-           "msa_sparse_attn_fwd_noalloc")
+           "msa_sparse_attn_fwd_noalloc", "msa_probe_read")
 
 
 class Shape(ctypes.Structure):
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "msa_plan": [sp, vp, vp, vp, vp, sz, vp],
             "msa_attn_main": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, sz, vp],
             "msa_combine": [sp, i32, vp, sz, vp, vp, vp],
+            "msa_probe_read": [vp, sz, sz, vp, vp],
             "msa_sparse_attn_fwd_noalloc": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, i32,
                                             vp, vp, vp],
             "msa_bwd_workspace_size": [sp, ctypes.POINTER(sz)],
@@ -229,6 +230,11 @@ def msa_sparse_attn_fwd_noalloc(shape, q, k, v, descale_qkv, softmax_scale, topk
                                              _p(descale_qkv), float(softmax_scale), _p(topk_idx),
                                              _p(cu_q), _p(cu_k), mode, _p(o), _p(lse),
                                              _stream(stream)), "msa_sparse_attn_fwd_noalloc")
+
+
+def msa_probe_read(buf, working_set_bytes, total_bytes, sink, stream=None) -> None:
+    _check(lib().msa_probe_read(_p(buf), int(working_set_bytes), int(total_bytes), _p(sink),
+                                _stream(stream)), "msa_probe_read")
 
 
 def msa_bwd_workspace_size(shape) -> int:

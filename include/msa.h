@@ -154,7 +154,9 @@ msa_status msa_resolve_mode(const msa_shape* shape, msa_mode mode, msa_mode* cho
  * element, partials bf16 and LSE fp32, per query token:
  *   kv_per_n = hq*d*e + hq*topk*(2*2*d + 2*4) + hq*d*2 ;  q_per_n = hkv*topk*2*block*d*e + hq*d*(e+2)
  *   X = (q_per_n * bw_hbm / bw_cache - kv_per_n) / (2*block*d*e).
- * bw_* in any common unit; bw_cache = 0 selects the MI355X default ratio (2.0). */
+ * bw_* in any common unit; bw_cache = 0 selects the MI355X default ratio 2.32, measured (the
+ * ratio at which this model reproduces the crossover of the two schedules timed over block
+ * reuse on MI355X; its last-level cache alone reads 1.32x the HBM rate). AUTO uses it. */
 msa_status msa_crossover(const msa_shape* shape, double bw_hbm, double bw_cache, double* x);
 
 const char* msa_status_string(msa_status st);
@@ -256,6 +258,18 @@ msa_status msa_attn_main(const msa_shape* shape, const void* q, const void* k, c
  * schedule already wrote O. */
 msa_status msa_combine(const msa_shape* shape, msa_mode mode, const void* workspace,
                        size_t ws_bytes, void* o, float* lse, hipStream_t stream);
+
+/* Read-bandwidth probe for the schedule choice ("Kernel optimization ...", section 1 and
+ * appendix: the KV-outer / Q-outer crossover scales with the measured ratio of cache to HBM
+ * bandwidth). Reads total_bytes of the device buffer `buf` by sweeping its first
+ * working_set_bytes over and over, each sweep one coalesced pass of 1024 workgroups of 4 KiB
+ * each, and writes 1024 * 256 floats (checksums) to the device buffer `sink`. A working set
+ * larger than the last-level cache (256 MB on MI355X) streams from HBM, one within it from the
+ * cache. Time it with events on `stream`. Requires working_set_bytes >= 4 MiB and a multiple of
+ * 4096, total_bytes >= 4 MiB (read in whole passes of 4 MiB); SHAPE otherwise, NULL for a
+ * missing buffer. */
+msa_status msa_probe_read(const void* buf, size_t working_set_bytes, size_t total_bytes,
+                          float* sink, hipStream_t stream);
 
 /* Allocation-free form of the main branch, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).

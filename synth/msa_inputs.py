@@ -356,3 +356,15 @@ def grad_output(case: Case, seed: Optional[int] = None) -> torch.Tensor:
     cfg = case.cfg
     ss = _stream(case.seed if seed is None else seed, "dout")
     return to_bf16(normal_f32(ss, (case.total_q, cfg.hq, cfg.d)))
+
+
+def shared_lists(n_q: int, n_req: int, n_blocks: int, hkv: int, topk: int, seed: int) -> np.ndarray:
+    """Per-query block lists [n_req * n_q, hkv, topk] in which the n_q queries of each request
+    share one list per group: topk distinct blocks of the request's n_blocks, drawn uniformly
+    without replacement and sorted (a workload whose block reuse nsb / N is hkv * topk / n_q)."""
+    rng = np.random.default_rng(_stream(seed, "lists"))
+    out = np.empty((n_req * n_q, hkv, topk), dtype=np.int32)
+    for r in range(n_req):
+        for g in range(hkv):
+            out[r * n_q:(r + 1) * n_q, g] = np.sort(rng.choice(n_blocks, topk, replace=False))
+    return out

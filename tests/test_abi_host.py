@@ -361,3 +361,31 @@ def test_noalloc_rejects_shapes_beyond_its_scratch_without_a_gpu(L):
     st = L.msa_sparse_attn_fwd_noalloc(None, None, None, None, None, 0.1, None, None, None,
                                        msa.MSA_KV_OUTER, None, None, None)
     assert st == msa.MSA_ERR_NULL
+
+
+def test_probe_argument_checks(L):
+    """The bandwidth probe rejects missing buffers and working sets below one pass (4 MiB) or
+    not a multiple of 4 KiB, before any launch."""
+    import ctypes
+    one = ctypes.c_void_p(1)
+    assert L.msa_probe_read(None, 4 << 20, 4 << 20, one, None) == msa.MSA_ERR_NULL
+    assert L.msa_probe_read(one, 4 << 20, 4 << 20, None, None) == msa.MSA_ERR_NULL
+    assert L.msa_probe_read(one, (4 << 20) - 4096, 4 << 20, one, None) == msa.MSA_ERR_SHAPE
+    assert L.msa_probe_read(one, (4 << 20) + 100, 8 << 20, one, None) == msa.MSA_ERR_SHAPE
+    assert L.msa_probe_read(one, 4 << 20, (4 << 20) - 1, one, None) == msa.MSA_ERR_SHAPE
+
+
+def test_default_cache_ratio_is_the_measured_one():
+    """bw_cache = 0 selects the ratio measured on MI355X (2.32: the model's crossover then
+    equals the one timed there, nsb/N = 19.2), and AUTO decides with it."""
+    s = m3_shape()
+    x_default = msa.msa_crossover(s, 1.0, 0.0)
+    assert abs(x_default - msa.msa_crossover(s, 1.0, 2.32)) < 1e-9
+    assert abs(x_default - 19.2) < 0.1
+    # a list reuse just above / below the crossover picks Q-outer / KV-outer
+    def reuse_shape(n_q):
+        n = 2048
+        return msa.make_shape(batch=n // n_q, total_q=n, total_k=n // n_q * 2048, max_q=n_q,
+                              max_k=2048, hq=64, hkv=4, topk=16, causal=False)
+    assert msa.msa_resolve_mode(reuse_shape(2), msa.MSA_AUTO) == msa.MSA_Q_OUTER    # 32
+    assert msa.msa_resolve_mode(reuse_shape(4), msa.MSA_AUTO) == msa.MSA_KV_OUTER   # 16
