@@ -64,6 +64,44 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+
+
+def asan_runtime() -> str | None:
+    """The AddressSanitizer runtime of the compiler hipcc drives (to preload into a host)."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(
+        hipcc()))), "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    hits += sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[0] if hits else None
+
+
+def build_asan() -> str:
+    """A copy of the library whose host code (argument checks, workspace plan, launchers) is
+    built with AddressSanitizer; the device code is built as usual (no GPU sanitizer). For
+    host-only tests: load it with the runtime from asan_runtime() preloaded."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g", "-Xarch_host",
+                                                       "-fsanitize=address", "-shared-libasan"]
+
+    def one(src):
+        obj = os.path.join(ASAN_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *flags, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (asan) failed on {src}:\n{r.stderr}")
+        return obj
+    with ThreadPoolExecutor(max(1, min(len(SOURCES), os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(ASAN_DIR, "libmsa_asan.so")
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-shared-libasan", *objs, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (asan) failed:\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
