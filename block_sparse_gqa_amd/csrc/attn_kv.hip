@@ -361,51 +361,33 @@ __device__ __forceinline__ void store_o_tile(char* part_o_b, size_t o_row0, cons
   }
 }
 
-// fp8 output read-back i (0..7) from the wave's staging buffer (chunk c of row R at
-// R*16 + (c ^ (R % 16))): lane l takes row R = 8 (i / 2) + l % 8, chunk c = 8 (i % 2) + l / 8,
-// so that with the first row at a group boundary the 64 lanes hold the 1 KiB at i KiB of the
-// wave's 8 KiB in the group layout. Its LDS index is rb_lane + rb_step(i) (R % 16 = 8 ((i/2) % 2)
-// + l % 8 and c ^ (R % 16) = 8 ((i ^ i/2) % 2) + ((l / 8) ^ (l % 8)); l / 8, l % 8 < 8).
-__device__ __forceinline__ int readback_lane(int lane) {
-  return 16 * (lane & 7) + ((lane >> 3) ^ (lane & 7));
-}
-__device__ __forceinline__ constexpr int readback_step(int i) {
-  return 128 * (i >> 1) + 8 * ((i ^ (i >> 1)) & 1);
-}
-// Byte offset of the lane's chunk in read-back i from the group of the wave's first row:
-// sv_lane + 1024 i when no padding row is involved. The row R = 8 (i / 2) + l % 8 lies at
-// (r0 + R) = rr_lane + 8 (i / 2) with rr_lane = r0 + l % 8, so its group offset is
-// ((rr_lane / 8) + i / 2) * 2048 and its row in the group rr_lane % 8.
-__device__ __forceinline__ int readback_sv_lane(size_t o_row0, int lane) {
-  const int rr = (int)(o_row0 & 7) + (lane & 7);
-  return ((rr >> 3) << 11) + ((rr & 7) << 4) + ((lane >> 3) << 7);
+// fp8 kernel: lane (col, hf) holds dims 32 dt + 8 a + 4 hf .. +3 of row col in
+// oacc[dt][4 a ..], half a 16-byte chunk. Exchanging the packed pieces of a = 2k and 2k + 1
+// between lanes l and l + 32 (v_permlane32_swap: the upper half-wave of the first operand
+// trades with the lower half-wave of the second) leaves lane (col, hf) with all of chunk
+// 4 dt + 2k + hf of its row, so that, as in the bf16 kernel, each store writes 8 whole
+// 128-byte lines of the group layout.
+__device__ __forceinline__ int store_lane_offset_f8(size_t o_row0, int o_nrow, int col, int hf) {
+  const int rr = (int)(o_row0 & 7) + col;
+  return col < o_nrow ? ((rr >> 3) << 11) + ((rr & 7) << 4) + (hf << 7) : kOffDrop;
 }
 
-// The wave's staged 8 KiB (fp8 kernel) read back and stored in the 8-row group layout. With
-// G >= 8 the wave's rows are whole groups from a group boundary and its real rows end on a
-// group boundary too: the descriptor's byte range (o_nrow * 256) drops exactly the padding
-// groups, and each store writes 1 KiB of consecutive bytes. Smaller groups compute each
-// lane's row and drop padding rows lane by lane.
-template <int G>
-__device__ __forceinline__ void store_staged_f8(const u32x4* obuf, char* part_o_b, size_t o_row0,
-                                                int o_nrow, int rb_lane, int lane) {
-  if constexpr (G >= 8) {
-    const __amdgpu_buffer_rsrc_t ro = srd(part_o_b + (o_row0 >> 3) * 2048, o_nrow * 256);
+__device__ __forceinline__ void store_o_tile_f8(char* part_o_b, size_t o_row0, const f32x16& o,
+                                                int dt, int voff) {
+  const __amdgpu_buffer_rsrc_t ro = srd(part_o_b + (o_row0 >> 3) * 2048, 5 * 2048);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_buffer_store_b128(obuf[rb_lane + readback_step(i)], ro,
-                                             lane * 16 + i * 1024, 0, 2);
-  } else {
-    const __amdgpu_buffer_rsrc_t ro = srd(part_o_b + (o_row0 >> 3) * 2048, 5 * 2048);
-    const int sv = readback_sv_lane(o_row0, lane);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int R = 8 * (i >> 1) + (lane & 7);
-      __builtin_amdgcn_raw_buffer_store_b128(obuf[rb_lane + readback_step(i)], ro,
-                                             R < o_nrow ? sv + (i >> 1) * 2048 + (i & 1) * 1024
-                                                        : kOffDrop,
-                                             0, 2);
-    }
+  for (int k = 0; k < 2; ++k) {
+    // packed pieces a = 2k (x) and a = 2k + 1 (y), two dwords each
+    const uint32_t x0 = pack_bf16x2(o[8 * k + 0], o[8 * k + 1]);
+    const uint32_t x1 = pack_bf16x2(o[8 * k + 2], o[8 * k + 3]);
+    const uint32_t y0 = pack_bf16x2(o[8 * k + 4], o[8 * k + 5]);
+    const uint32_t y1 = pack_bf16x2(o[8 * k + 6], o[8 * k + 7]);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    // hf = 0: its own piece 2k (dims +0..3) then the partner's (+4..7); hf = 1: the
+    // partner's piece 2k + 1 (+0..3) then its own (+4..7)
+    const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(w, ro, voff + (4 * dt + 2 * k) * 128, 0, 2);
   }
 }
 
@@ -786,7 +768,6 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   const uint8_t* const vb = reinterpret_cast<const uint8_t*>(a.v);
   const uint32_t kv_row = (uint32_t)a.hkv * kD;   // bytes between consecutive keys
   char* const part_o_b = reinterpret_cast<char*>(a.part_o);
-  const int rb_lane = readback_lane(lane);
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
 
@@ -827,7 +808,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   float o_c = 0.f;
   bool o_any = false;
   size_t o_row0 = 0;
-  int o_nrow = 0;
+  int o_nrow = 0, o_voff = kOffDrop;
 
   while (true) {
     const bool trans = d1.n != 0 && (d1.b != d0.b || d1.p != d0.p);
@@ -854,8 +835,8 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
     const u32x4* const kslot = kvs[ks_];
     const uint8_t* const vslot = reinterpret_cast<const uint8_t*>(kvs[vs_]);
 
-    // ---- phase A: QK^T(j) (8 MFMAs) | O(j-1) through LDS to memory (8-byte pieces: lane
-    // (col, hf) holds dims 32 dt + 8 a + 4 hf .. +3 of row col in oacc[dt][4 a ..])
+    // ---- phase A: QK^T(j) (8 MFMAs) | O(j-1) from registers to memory, dim tile kt after
+    // the MFMAs of key tile kt (see store_o_tile_f8)
     f32x16 sc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -863,24 +844,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       const i32x8 k1 = read_k8(kslot, kt, 1, rp, hf);
       sc[kt] = mfma8(k0, bq0, f32x16{});
       sc[kt] = mfma8(k1, bq1, sc[kt]);
-      // stage dim tile kt of the previous output
-      {
-        int cc = col;
-        asm volatile("" : "+v"(cc));
-        u32x2* const row = reinterpret_cast<u32x2*>(obuf + cc * 16);
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[kt][4 * a4], oacc[kt][4 * a4 + 1]);
-          w[1] = pack_bf16x2(oacc[kt][4 * a4 + 2], oacc[kt][4 * a4 + 3]);
-          row[2 * ((4 * kt + a4) ^ (cc & 15)) + hf] = w;
-        }
-      }
+      store_o_tile_f8(part_o_b, o_row0, oacc[kt], kt, o_voff);
     }
     {
-      // read back in the 8-row group layout; streaming stores: the partials are read once,
-      // by the combine kernel
-      store_staged_f8<G>(obuf, part_o_b, o_row0, o_nrow, rb_lane, lane);
       const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
       const float o_lse =
           o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
@@ -894,7 +860,8 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       dma_block8<true>(kvs[ks_], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
                        wave, lane);
     }
-    // Q of the next tile into the staging buffer, whose read-back is complete
+    // Q of the next tile into the staging buffer: this tile's Q operands were read before the K
+    // operands that the MFMAs above waited for (LDS reads complete in order)
     tq1.dma(obuf, a.q, a.hq, h1, g, lane);
     // ---- row max of S(j)
     if (need_mask) {
@@ -933,6 +900,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
     o_any = any;
     o_nrow = max(0, min(32, d0.n * G - wave * 32));
     o_row0 = (size_t)d0.e0 * G + wave * 32;
+    o_voff = store_lane_offset_f8(o_row0, o_nrow, col, hf);
     if (d1.n == 0) break;
     if (trans) {
       const int k2 = fs_;
@@ -951,17 +919,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   // output of the last tile (after the last, unused, Q load into the buffer)
   wait_vm0();
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    u32x2* const row = reinterpret_cast<u32x2*>(obuf + col * 16);
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[dt][4 * a4], oacc[dt][4 * a4 + 1]);
-      w[1] = pack_bf16x2(oacc[dt][4 * a4 + 2], oacc[dt][4 * a4 + 3]);
-      row[2 * ((4 * dt + a4) ^ (col & 15)) + hf] = w;
-    }
-  }
-  store_staged_f8<G>(obuf, part_o_b, o_row0, o_nrow, rb_lane, lane);
+  for (int dt = 0; dt < 4; ++dt) store_o_tile_f8(part_o_b, o_row0, oacc[dt], dt, o_voff);
   const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
   const float o_lse =
       o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
