@@ -499,10 +499,12 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
       if (st < 4) {
         store_o_tile(part_o_b, o_row0, oacc[st], st, o_voff);
       } else if (st == 4) {
+        // LSE and weight sum, streaming like the partials (both are read once, by the
+        // combine): lines kept in L2 would only push out the phase's Q rows
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                              srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                              srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                              srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                              srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
         tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
       }
       MSA_INTERLEAVE(1, 6);
@@ -569,9 +571,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) store_o_tile(part_o_b, o_row0, oacc[dt], dt, o_voff);
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                        srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                        srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                        srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                        srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
 }
 
 // ======================================================================================
@@ -851,9 +853,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       const float o_lse =
           o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                            srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                            srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                            srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                            srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
     }
     if (trans) {
       __syncthreads();        // every wave is done with this bucket's K
@@ -924,9 +926,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   const float o_lse =
       o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                        srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                        srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                        srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 0);
+                                        srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
 }
 
 template <int G>

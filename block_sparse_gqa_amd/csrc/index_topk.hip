@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   constexpr int PER_T = 128 * CH / 256;   // direct-to-LDS loads per thread per block
   const char* const q_idx = reinterpret_cast<const char*>(q_idx_);
   const char* const k_idx = reinterpret_cast<const char*>(k_idx_);
-  constexpr int NBUF = 4;          // ring of key blocks: three in flight while one is scored
+  constexpr int NBUF = 4;          // ring of key blocks: two pairs
   __shared__ u32x4 kl[NBUF][128 * CH];
 
   const int s = blockIdx.z, h = blockIdx.y;
@@ -176,15 +176,15 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     }
   };
 
-  for (int j = jbeg; j < min(jend, jbeg + NBUF - 1); ++j) dma_block(j);
-  for (int j = jbeg; j < jend; ++j) {
-    // block j has landed once at most the later blocks' loads are outstanding
-    const int later = min(jend - 1 - j, NBUF - 2);
-    if (later >= 2) wait_vm<2 * PER_T>();
-    else if (later == 1) wait_vm<PER_T>();
-    else wait_vm<0>();
-    __syncthreads();   // every thread's part of block j is in LDS; slot (j-1) % NBUF is free
-    if (j + NBUF - 1 < jend) dma_block(j + NBUF - 1);
+  // Blocks go through the ring in pairs: pair (jp, jp + 1) is scored while the next pair
+  // loads into the two slots the previous pair has just left, so one wait and one barrier
+  // serve two blocks.
+  for (int j = jbeg; j < min(jend, jbeg + 2); ++j) dma_block(j);
+  for (int jp = jbeg; jp < jend; jp += 2) {
+    wait_vm<0>();      // this thread's parts of the pair have landed (nothing else in flight)
+    __syncthreads();   // every thread's parts are in LDS; the previous pair's slots are free
+    for (int j = jp + 2; j < min(jp + 4, jend); ++j) dma_block(j);
+    for (int j = jp; j < min(jp + 2, jend); ++j) {
     const int buf = j % NBUF;
 
     f32x16 acc[2][4];
@@ -236,6 +236,7 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     const bool ins = qvalid && (causal ? (j < c) : (j != c)) && mx > tl.sc[kMaxTopK - 1];
     if (__any(ins)) {
       if (ins) tl.insert(mx, j);
+    }
     }
   }
 
