@@ -126,6 +126,7 @@ struct KvTArgs {
   float* part_lse;
   float* part_l;
   uint16_t* part_o;
+  const uint16_t* vw;     // fp8: V widened to bf16 (exactly) in the workspace
   int total_q, total_k, max_q, max_k;
   int hq, hkv, nb_max, n_r, n_phase, n_xcd, n_share, causal;
 };
@@ -361,36 +362,6 @@ __device__ __forceinline__ void store_o_tile(char* part_o_b, size_t o_row0, cons
   }
 }
 
-// fp8 kernel: lane (col, hf) holds dims 32 dt + 8 a + 4 hf .. +3 of row col in
-// oacc[dt][4 a ..], half a 16-byte chunk. Exchanging the packed pieces of a = 2k and 2k + 1
-// between lanes l and l + 32 (v_permlane32_swap: the upper half-wave of the first operand
-// trades with the lower half-wave of the second) leaves lane (col, hf) with all of chunk
-// 4 dt + 2k + hf of its row, so that, as in the bf16 kernel, each store writes 8 whole
-// 128-byte lines of the group layout.
-__device__ __forceinline__ int store_lane_offset_f8(size_t o_row0, int o_nrow, int col, int hf) {
-  const int rr = (int)(o_row0 & 7) + col;
-  return col < o_nrow ? ((rr >> 3) << 11) + ((rr & 7) << 4) + (hf << 7) : kOffDrop;
-}
-
-__device__ __forceinline__ void store_o_tile_f8(char* part_o_b, size_t o_row0, const f32x16& o,
-                                                int dt, int voff) {
-  const __amdgpu_buffer_rsrc_t ro = srd(part_o_b + (o_row0 >> 3) * 2048, 5 * 2048);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    // packed pieces a = 2k (x) and a = 2k + 1 (y), two dwords each
-    const uint32_t x0 = pack_bf16x2(o[8 * k + 0], o[8 * k + 1]);
-    const uint32_t x1 = pack_bf16x2(o[8 * k + 2], o[8 * k + 3]);
-    const uint32_t y0 = pack_bf16x2(o[8 * k + 4], o[8 * k + 5]);
-    const uint32_t y1 = pack_bf16x2(o[8 * k + 6], o[8 * k + 7]);
-    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-    // hf = 0: its own piece 2k (dims +0..3) then the partner's (+4..7); hf = 1: the
-    // partner's piece 2k + 1 (+0..3) then its own (+4..7)
-    const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
-    __builtin_amdgcn_raw_buffer_store_b128(w, ro, voff + (4 * dt + 2 * k) * 128, 0, 2);
-  }
-}
-
 template <int G>
 __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   constexpr int MQ = 256 / G;          // entries per tile
@@ -577,23 +548,18 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
 }
 
 // ======================================================================================
-// fp8: the tiled schedule on fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4)
+// fp8: the tiled schedule with QK^T on the 8-bit MFMA (v_mfma_scale_f32_32x32x64_f8f6f4)
 //
-// Q, K and V stay OCP e4m3 in LDS (16 KiB per block, 4 KiB of Q rows per wave), half the bytes
-// of the bf16 kernel, and each MFMA covers 64 of the contraction at twice the bf16 rate. For
-// the 32x32x64 8-bit MFMA, lane l supplies row l % 32 of A (and column l % 32 of B) at
-// contraction indices 32 (l / 32) .. +31, 32 bytes; the result has the 32x32 layout of the
-// bf16 MFMA. QK^T: A = K rows (key order rowperm, as in the bf16 kernel), B = Q rows, D = 64
-// per MFMA (two MFMAs per 128 dims). PV: the probabilities (scaled by 2^8, which the weight
-// sum divides out) become two e4m3 operands, hi and the rounded remainder lo, which serve as
-// B with each lane's own 32 keys of a 64-key step, each against the same rows of V^T: those
-// come from four 8-byte transpose loads (ds_read_b64_tr_b8: within a 16-lane group, lane j
-// receives byte j % 8 of the blocks addressed by lanes 2t + j / 8, t = 0..7), one run of 8
-// keys each. An A operand of ones gives the weight sum of exactly the quantised probabilities
-// on the MFMA pipe.
+// Q and K stay OCP e4m3 in LDS (16 KiB per K block, 4 KiB of Q rows per wave), and each QK^T
+// MFMA covers 64 of the contraction at twice the bf16 rate. For the 32x32x64 8-bit MFMA, lane l
+// supplies row l % 32 of A (and column l % 32 of B) at contraction indices 32 (l / 32) .. +31,
+// 32 bytes; the result has the 32x32 layout of the bf16 MFMA. QK^T: A = K rows (key order
+// rowperm, as in the bf16 kernel), B = Q rows, D = 64 per MFMA (two MFMAs per 128 dims). The
+// probabilities are rounded to bf16 and PV runs on bf16 MFMA, as in the bf16 kernel, against
+// V widened to bf16 (exactly: every e4m3 value is a bf16 value) by a pass over V before the
+// attention kernel; the V descale divides the stored weight sum instead of scaling V.
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c,
                                         int scale_a = 127) {
@@ -603,19 +569,17 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
 
 // LDS layouts (16-byte chunks, 8 per 128-byte row): chunk c of row r at slot c ^ f(r).
 __device__ __forceinline__ int f8_swz_k(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
-__device__ __forceinline__ int f8_swz_v(int r) { return (r >> 1) & 3; }
 __device__ __forceinline__ int f8_swz_q(int r) { return (r ^ (r >> 3)) & 7; }
 
-// An fp8 K or V block into an LDS slot by the workgroup's 512 threads, 2 direct loads each:
-// load p of wave w fills rows 64p + 8w .. +7. Rows at or past nk_rel repeat the last key.
-template <bool V>
+// An fp8 K block into an LDS slot by the workgroup's 512 threads, 2 direct loads each: load p
+// of wave w fills rows 64p + 8w .. +7. Rows at or past nk_rel repeat the last key.
 __device__ __forceinline__ void dma_block8(u32x4* dst, const uint8_t* base, uint32_t row_stride,
                                            int nk_rel, int wave, int lane) {
   const int slot = lane & 7;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int row = 64 * p + 8 * wave + (lane >> 3);
-    const int f = V ? f8_swz_v(row) : f8_swz_k(row);
+    const int f = f8_swz_k(row);
     const uint32_t r = (uint32_t)min(row, nk_rel - 1);
     dma16s(base, r * row_stride + (uint32_t)((slot ^ f) * 16), lds_addr(dst + p * 512 + wave * 64));
   }
@@ -690,62 +654,10 @@ __device__ __forceinline__ i32x8 read_k8(const u32x4* kb, int kt, int ds, int rp
   const u32x4 hi = kb[r * 8 + ((4 * ds + 2 * hf + 1) ^ f)];
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
-// A operand of O^T for dim tile dt, key step ks: V^T[32 dt + m][keys of run q = 0..3], run q of
-// lane half hf covering keys 32 (2 ks + q / 2) + 16 hf + 8 (q % 2) .. +7, the keys the lane's
-// own probabilities stand for. In 16-lane group gl (= lane / 16), supplier lane i = 2t + p
-// addresses key row k0 + t, dims 32 dt + 16 (gl % 2) + 8 p .. +7; receiving lane j gets dim
-// 32 dt + 16 (gl % 2) + j of keys k0 .. k0 + 7. Lane offsets depend on (q, t, p) only.
-__device__ __forceinline__ i32x8 read_v8(const uint8_t* vb, int dt, int ks, int lane) {
-  const int gl = lane >> 4, j = lane & 15;
-  const int t = j >> 1, p = j & 1, hf = gl >> 1;
-  i32x8 out;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 32 * (2 * ks + (q >> 1)) + 16 * hf + 8 * (q & 1) + t;
-    const int chunk = (2 * dt + (gl & 1)) ^ f8_swz_v(row);
-    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (__attribute__((address_space(3))) i32x2*)(vb + row * 128 + chunk * 16 + 8 * p));
-    out[2 * q] = v[0];
-    out[2 * q + 1] = v[1];
-  }
-  return out;
-}
-
-// Probabilities of key step ks, scaled by 2^8, as a sum of two e4m3 operands: hi = e4m3(x)
-// and lo = e4m3(x - hi), so that hi + lo carries x to about 2^-8 relative (one e4m3 term
-// alone is 2^-4). Byte 8 q + u of the lane is key 32 (2 ks + q / 2) + 16 hf + 8 (q % 2) + u,
-// i.e. sc[2 ks + q / 2][8 (q % 2) + u].
-__device__ __forceinline__ void pack_p8(const f32x16 sc[4], int ks, float sl2, float c, i32x8& hi,
-                                        i32x8& lo) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int kt = 2 * ks + (q >> 1), b = 8 * (q & 1);
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      float x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        x[u] = __builtin_amdgcn_exp2f(fmaf(sc[kt][b + 4 * w + u], sl2, 8.f - c));
-      // the first conversion of a pair writes the low half and keeps the high half of its
-      // third operand, which the second conversion overwrites: any dead value serves there
-      int d = __builtin_amdgcn_cvt_pk_fp8_f32(
-          x[0], x[1], __builtin_bit_cast(int, sc[kt][b + 4 * w]), false);
-      d = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], d, true);
-      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-      const float r0 = x[0] - h01[0];
-      int e = __builtin_amdgcn_cvt_pk_fp8_f32(r0, x[1] - h01[1], __builtin_bit_cast(int, r0), false);
-      e = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] - h23[0], x[3] - h23[1], e, true);
-      hi[2 * q + w] = d;
-      lo[2 * q + w] = e;
-    }
-  }
-}
-
 template <int G>
 __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
-  __shared__ u32x4 kvs[3][128 * 8];    // rotating fp8 K / V slots, 16 KiB each
-  __shared__ u32x4 obuf_all[8][32 * 16];
+  __shared__ u32x4 kvs[3][128 * 16];   // rotating slots: fp8 K (first 16 KiB) or bf16 V
+  __shared__ u32x4 obuf_all[8][32 * 8];
 
   const int E = a.counters[0];
   if (E <= 0) return;
@@ -758,28 +670,29 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   u32x4* const obuf = obuf_all[wave];
   const int xcd = blockIdx.x % a.n_xcd, j = blockIdx.x / a.n_xcd;
   const float sl2 = a.scale_log2 * a.descale[0] * a.descale[1];
-  // V descale dv = sigma * 2^kv, sigma in [1, 2) for normal dv: 2^kv is applied by the PV MFMAs'
-  // A scale, sigma by dividing the stored weight sum (the output over the weight sum carries
-  // dv, the log-sum-exp does not depend on it). dv = 0 gives an infinite weight sum, i.e. a
-  // zero contribution with the right log-sum-exp.
-  const float dv = a.descale[2];
-  const int kv = min((int)((__builtin_bit_cast(uint32_t, dv) >> 23) & 0xff) - 127, 127);
-  const int v_scale = 127 + kv;
-  const float inv_sigma = 1.f / ldexpf(dv, -kv);
+  // The partial output is accumulated against the raw e4m3 values of V (widened exactly to
+  // bf16); its weight sum is stored divided by the V descale dv, so that output over weight
+  // sum carries dv. dv = 0 gives an infinite weight sum: a zero contribution with the right
+  // log-sum-exp.
+  const float inv_dv = 1.f / a.descale[2];
   const uint8_t* const kb = reinterpret_cast<const uint8_t*>(a.k);
-  const uint8_t* const vb = reinterpret_cast<const uint8_t*>(a.v);
-  const uint32_t kv_row = (uint32_t)a.hkv * kD;   // bytes between consecutive keys
+  const uint16_t* const vwb = a.vw;
+  const uint32_t k_row = (uint32_t)a.hkv * kD;     // bytes between consecutive fp8 keys
+  const uint32_t v_row = (uint32_t)a.hkv * kD;     // bf16 elements between consecutive keys
   char* const part_o_b = reinterpret_cast<char*>(a.part_o);
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+  int vl[4];
+  v_lane_offsets(lane, vl);
 
   auto seq_of = [&](int p, int* h) {
     *h = (p / a.n_r) % a.hkv;
     return load_seq_clamped(a.cu_q, a.cu_k, p / (a.n_r * a.hkv), a.total_q, a.total_k, a.max_q,
                             a.max_k);
   };
-  auto kv_base = [&](const uint8_t* base, const Seq& sq, int h, int b) {
-    return base + ((size_t)(sq.k0 + b * kBlock) * a.hkv + h) * kD;
+  auto k_base = [&](const Seq& sq, int h, int bb) {
+    return kb + ((size_t)(sq.k0 + bb * kBlock) * a.hkv + h) * kD;
+  };
+  auto v_base = [&](const Seq& sq, int h, int bb) {
+    return vwb + ((size_t)(sq.k0 + bb * kBlock) * a.hkv + h) * kD;
   };
 
   TileIt it{xcd, 0, 0};
@@ -793,22 +706,19 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   int h0;
   Seq sq0 = seq_of(d0.p, &h0);
   int ks_ = 0, vs_ = 1, fs_ = 2;
-  dma_block8<false>(kvs[ks_], kv_base(kb, sq0, h0, d0.b), kv_row, sq0.nk - d0.b * kBlock, wave, lane);
-  dma_block8<true>(kvs[vs_], kv_base(vb, sq0, h0, d0.b), kv_row, sq0.nk - d0.b * kBlock, wave, lane);
+  dma_block8(kvs[ks_], k_base(sq0, h0, d0.b), k_row, sq0.nk - d0.b * kBlock, wave, lane);
+  dma_block<true>(kvs[vs_], v_base(sq0, h0, d0.b), v_row, sq0.nk - d0.b * kBlock, wave, lane);
   TileQ8<G> tq0, tq1;
   tq0.load(a.entry_q, d0, wave, rent);
   wait_vm0();
   tq0.dma(obuf, a.q, a.hq, h0, g, lane);
   bool opened = true;
 
+  bf16x8 fr[2][4];
   f32x16 oacc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
-  // weight sum and max of the previous tile, read where its outputs are stored (the weight
-  // sum's MFMA chain then completes under the next tile's QK^T)
-  f32x16 o_lacc = {};
-  float o_c = 0.f;
-  bool o_any = false;
+  float o_l = 0.f, o_lse = 0.f;
   size_t o_row0 = 0;
   int o_nrow = 0, o_voff = kOffDrop;
 
@@ -830,15 +740,14 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
     const TileD d3 = it_decode(r3, it, a, E);
     r3 = it_fetch(it, a, j);
     if (trans)
-      dma_block8<false>(kvs[fs_], kv_base(kb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
-                        wave, lane);
+      dma_block8(kvs[fs_], k_base(sq1, h1, d1.b), k_row, sq1.nk - d1.b * kBlock, wave, lane);
     const i32x8 bq0 = read_q8(obuf, 0, col, hf);
     const i32x8 bq1 = read_q8(obuf, 1, col, hf);
     const u32x4* const kslot = kvs[ks_];
-    const uint8_t* const vslot = reinterpret_cast<const uint8_t*>(kvs[vs_]);
+    const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs_]);
 
-    // ---- phase A: QK^T(j) (8 MFMAs) | O(j-1) from registers to memory, dim tile kt after
-    // the MFMAs of key tile kt (see store_o_tile_f8)
+    // ---- phase A: QK^T(j) on the 8-bit MFMA (8 MFMAs) | O(j-1) from registers to memory,
+    // dim tile kt after the MFMAs of key tile kt
     f32x16 sc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -846,21 +755,16 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       const i32x8 k1 = read_k8(kslot, kt, 1, rp, hf);
       sc[kt] = mfma8(k0, bq0, f32x16{});
       sc[kt] = mfma8(k1, bq1, sc[kt]);
-      store_o_tile_f8(part_o_b, o_row0, oacc[kt], kt, o_voff);
+      store_o_tile(part_o_b, o_row0, oacc[kt], kt, o_voff);
     }
-    {
-      const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
-      const float o_lse =
-          o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                            srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                            srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
-    }
+    // LSE and weight sum, streaming like the partials
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                          srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                          srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
     if (trans) {
       __syncthreads();        // every wave is done with this bucket's K
-      dma_block8<true>(kvs[ks_], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
-                       wave, lane);
+      dma_block<true>(kvs[ks_], v_base(sq1, h1, d1.b), v_row, sq1.nk - d1.b * kBlock, wave, lane);
     }
     // Q of the next tile into the staging buffer: this tile's Q operands were read before the K
     // operands that the MFMAs above waited for (LDS reads complete in order)
@@ -881,28 +785,26 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
     m = fmaxf(m, shfl_xor_f(m, 32));
     const bool any = m > -__builtin_inff();
     const float c = any ? m * sl2 : 0.f;
-    // ---- phase B: PV(j) and the weight sum (ones) on the MFMA pipe
-    f32x16 lacc = {};
+    // ---- phase B: PV(j) on bf16 MFMA against the widened V | exp of the next key-step
+    v_frags_tr(vslot, fr[0], 0, vl);
+    u32x4 pk[8];
+    float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      i32x8 phi, plo;
-      pack_p8(sc, ks, sl2, c, phi, plo);
+    for (int st = 0; st < 8; ++st) {
+      if (st < 7) v_frags_tr(vslot, fr[(st + 1) & 1], st + 1, vl);
+      const bf16x8 bp = as_bf16x8(pk[st]);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const i32x8 va = read_v8(vslot, dt, ks, lane);
-        oacc[dt] = mfma8(va, phi, ks == 0 ? f32x16{} : oacc[dt], v_scale);
-        oacc[dt] = mfma8(va, plo, oacc[dt], v_scale);
-      }
-      lacc = mfma8(ones, phi, lacc);
-      lacc = mfma8(ones, plo, lacc);
+      for (int dt = 0; dt < 4; ++dt)
+        oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
+      if (st + 1 < 8) l = exp_step(sc, st + 1, sl2, c, pk[st + 1], l);
+      MSA_INTERLEAVE(2, 7);
     }
-    // lacc: sum of the quantised, 2^8-scaled probabilities of the lane's row (every element)
-    o_lacc = lacc;
-    o_c = c;
-    o_any = any;
+    l += shfl_xor_f(l, 32);
+    o_l = any ? l * inv_dv : 0.f;
+    o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
     o_nrow = max(0, min(32, d0.n * G - wave * 32));
     o_row0 = (size_t)d0.e0 * G + wave * 32;
-    o_voff = store_lane_offset_f8(o_row0, o_nrow, col, hf);
+    o_voff = store_lane_offset(o_row0, o_nrow, col, hf);
     if (d1.n == 0) break;
     if (trans) {
       const int k2 = fs_;
@@ -921,14 +823,27 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   // output of the last tile (after the last, unused, Q load into the buffer)
   wait_vm0();
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) store_o_tile_f8(part_o_b, o_row0, oacc[dt], dt, o_voff);
-  const float o_l = o_any ? o_lacc[0] * inv_sigma : 0.f;
-  const float o_lse =
-      o_any ? (o_c + log2f(o_lacc[0]) - 8.f) * 0.69314718055994531f : -__builtin_inff();
+  for (int dt = 0; dt < 4; ++dt) store_o_tile(part_o_b, o_row0, oacc[dt], dt, o_voff);
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
                                         srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
                                         srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
+}
+
+// V (e4m3) widened to bf16, exactly: 16 elements per thread.
+__global__ __launch_bounds__(256) void widen_v_kernel(const uint8_t* __restrict__ v,
+                                                      uint16_t* __restrict__ vw, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const u32x4 x = reinterpret_cast<const u32x4*>(v)[i];
+  u32x4 lo, hi;
+  const u32x2 a0 = fp8x4_to_bf16x4(x[0]), a1 = fp8x4_to_bf16x4(x[1]);
+  const u32x2 a2 = fp8x4_to_bf16x4(x[2]), a3 = fp8x4_to_bf16x4(x[3]);
+  lo = u32x4{a0[0], a0[1], a1[0], a1[1]};
+  hi = u32x4{a2[0], a2[1], a3[0], a3[1]};
+  u32x4* out = reinterpret_cast<u32x4*>(vw) + 2 * i;
+  __builtin_nontemporal_store(lo, out);
+  __builtin_nontemporal_store(hi, out + 1);
 }
 
 template <int G>
@@ -978,7 +893,16 @@ hipError_t launch_attn_kv(const msa_shape& s, const Geometry& g, const Layout& L
   t.n_xcd = device_xcd_count();
   t.n_share = n_wg / t.n_xcd;
   t.causal = s.causal;
+  t.vw = reinterpret_cast<const uint16_t*>(ws + L.v_wide);
   if (s.dtype == MSA_FP8_E4M3) {
+    const int64_t n16 = (int64_t)s.total_k * s.hkv * s.d / 16;
+    if (n16 > 0) {
+      hipLaunchKernelGGL(widen_v_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,
+                         reinterpret_cast<const uint8_t*>(v), reinterpret_cast<uint16_t*>(ws + L.v_wide),
+                         n16);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     switch (g.group) {
       case 1: return launch_kv_f8_g<1>(t, n_wg, st);
       case 2: return launch_kv_f8_g<2>(t, n_wg, st);

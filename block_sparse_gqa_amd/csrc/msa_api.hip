@@ -140,10 +140,11 @@ Layout layout(const msa_shape& s, msa_mode mode) {
     L.tile_off = take((size_t)g.n_buckets * 4);
     L.phase_base = take((size_t)(g.n_phase + 1) * 8);
     L.tiles = take((size_t)g.n_tiles_max * 8);
+    L.v_wide = take(s.dtype == MSA_FP8_E4M3 ? (size_t)s.total_k * s.hkv * s.d * 2 : 0);
   } else {
     L.slots = g.splits;
     L.masks = L.offsets = L.scan_sums = L.entry_q = L.entry_bucket = off;
-    L.tile_off = L.phase_base = L.tiles = off;
+    L.tile_off = L.phase_base = L.tiles = L.v_wide = off;
     L.cmap = take(g.splits > 1 ? (size_t)s.total_q * s.hkv * g.splits * 4 : 0);
   }
   L.part_lse = take((size_t)g.e_max * g.group * 4);
@@ -274,6 +275,7 @@ msa_status msa_workspace_layout_of(const msa_shape* shape, msa_mode mode,
   out->part_lse = L.part_lse;
   out->part_l = L.part_l;
   out->part_o = L.part_o;
+  out->v_wide = L.v_wide;
   out->total = L.total;
   out->slots = L.slots;
   out->n_words = (int32_t)g.n_words;

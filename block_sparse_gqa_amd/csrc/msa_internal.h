@@ -72,6 +72,7 @@ struct Layout {
   size_t phase_base;    // int32  [2 * (n_phase + 1)]: first tile record of each phase,
                         //   then the tile count of each phase
   size_t tiles;         // int2   [n_tiles_max]: (first entry, block << 8 | entries - 1)
+  size_t v_wide;        // bf16   [total_k * hkv * d]: fp8 V widened (KV-outer fp8 only)
   size_t part_lse;      // float  [e_max * group]
   size_t part_l;        // float  [e_max * group]: weight sums (partials are unnormalised)
   size_t part_o;        // bf16   [e_max * group * d]

@@ -38,7 +38,7 @@ class Shape(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "counters", "masks", "offsets", "scan_sums", "entry_q", "entry_bucket", "cmap",
-        "part_lse", "part_l", "part_o", "total")] + [(n, ctypes.c_int32) for n in (
+        "part_lse", "part_l", "part_o", "v_wide", "total")] + [(n, ctypes.c_int32) for n in (
             "slots", "n_words", "w_max", "nb_max", "words_per_bucket", "n_ranges")]
 
 

@@ -103,11 +103,11 @@ typedef struct {
   size_t entry_bucket; /* int32 [E]: bucket ((s * hkv + g) * n_ranges + r) * nb_max + b */
   size_t cmap;         /* int32 [total_q, hkv, slots]: partial index of each slot, -1 = none */
   size_t part_lse;     /* float [E, hq/hkv]: log-sum-exp of each partial */
-  size_t part_l;       /* float [E, hq/hkv]: sum of each partial's softmax weights, each
-                          weight taken relative to the partial's maximum and multiplied by a
-                          positive factor of the kernel's choosing that part_o carries too
-                          (bf16: 1; fp8: 2^8 / sigma, with the V descale = sigma * 2^k,
-                          sigma in [1, 2)); 1 where the partial output is already normalised */
+  size_t part_l;       /* float [E, hq/hkv]: sum of each partial's softmax weights (as rounded
+                          for the PV product), each taken relative to the partial's maximum and
+                          divided by a positive factor that part_o carries too (bf16: 1; fp8:
+                          the V descale, part_o holding the output against the raw e4m3 values
+                          of V); 1 where the partial output is already normalised */
   size_t part_o;       /* bf16, E * hq/hkv rows of d: partial output before normalisation,
                           i.e. the partial's attention output times part_l ("Kernel
                           optimization ...", section 2: unnormalised accumulators, normalised
@@ -115,6 +115,8 @@ typedef struct {
                           rows: dims 8c .. 8c+7 of row p at byte ((p / 8) * 16 + c) * 128 +
                           (p % 8) * 16, so that dims 8c .. 8c+7 of 8 consecutive rows fill one
                           128-byte line (the rows are padded to a multiple of 8) */
+  size_t v_wide;       /* bf16 [total_k, hkv, d]: V widened exactly from e4m3 for the fp8
+                          KV-outer kernel's PV product (size 0 otherwise) */
   size_t total;        /* bytes needed */
   int32_t slots;       /* slots per (query, group) in cmap */
   int32_t n_words;     /* bitmap words (0 for Q-outer) */
@@ -128,8 +130,9 @@ typedef struct {
 
 /* Bytes of workspace msa_sparse_attn_fwd and msa_combine need for `shape` under `mode`.
  * KV-outer holds the inverted index (bitmaps, scan, entry list, combine map) and E bf16
- * partials of (hq/hkv) x d plus fp32 LSEs, E <= total_q * hkv * topk. Errors: NULL, SHAPE,
- * DTYPE, MODE. */
+ * partials of (hq/hkv) x d plus fp32 LSEs and weight sums, E <= total_q * hkv * topk; with
+ * fp8 Q/K/V also a bf16 copy of V (total_k * hkv * d * 2 bytes). Errors: NULL, SHAPE, DTYPE,
+ * MODE. */
 msa_status msa_workspace_size(const msa_shape* shape, msa_mode mode, size_t* bytes);
 
 /* Region offsets of that workspace (same errors). */

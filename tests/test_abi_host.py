@@ -220,6 +220,17 @@ def test_kv_outer_workspace_layout_m3():
     assert msa.msa_workspace_size(s, msa.MSA_KV_OUTER) == lay.total
 
 
+def test_fp8_workspace_holds_the_widened_v():
+    """fp8 KV-outer: a bf16 copy of V (total_k * hkv * d * 2 bytes) before the partials; bf16:
+    no such region."""
+    s8 = m3_shape(dtype=msa.MSA_FP8_E4M3)
+    lay = msa.msa_workspace_layout_of(s8, msa.MSA_KV_OUTER)
+    assert lay.cmap < lay.v_wide < lay.part_lse and lay.v_wide % 256 == 0
+    assert lay.part_lse - lay.v_wide >= 32768 * 4 * 128 * 2
+    lb = msa.msa_workspace_layout_of(m3_shape(), msa.MSA_KV_OUTER)
+    assert lb.part_lse - lb.v_wide < 256        # empty (alignment only)
+
+
 def test_partial_memory_ratio_matches_the_pages():
     """bf16 partials of every selected block take topk times the bf16 output."""
     g = json.load(open(GOLDEN))["partial_memory_ratio"]
