@@ -558,6 +558,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
 // probabilities are rounded to bf16 and PV runs on bf16 MFMA, as in the bf16 kernel, against
 // V widened to bf16 (exactly: every e4m3 value is a bf16 value) by a pass over V before the
 // attention kernel; the V descale divides the stored weight sum instead of scaling V.
+// Four 32 KiB slots (K in the first half of one): when the next tile opens a new bucket, its K
+// and V blocks are both requested at the start of the current tile into the two slots the
+// previous bucket left (released by the barrier that opened the current bucket), so a bucket
+// change takes one barrier.
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -656,7 +660,7 @@ __device__ __forceinline__ i32x8 read_k8(const u32x4* kb, int kt, int ds, int rp
 }
 template <int G>
 __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
-  __shared__ u32x4 kvs[3][128 * 16];   // rotating slots: fp8 K (first 16 KiB) or bf16 V
+  __shared__ u32x4 kvs[4][128 * 16];   // fp8 K (first 16 KiB of a slot) and bf16 V slots
   __shared__ u32x4 obuf_all[8][32 * 8];
 
   const int E = a.counters[0];
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
 
   int h0;
   Seq sq0 = seq_of(d0.p, &h0);
-  int ks_ = 0, vs_ = 1, fs_ = 2;
+  int ks_ = 0, vs_ = 1, fk_ = 2, fv_ = 3;
   dma_block8(kvs[ks_], k_base(sq0, h0, d0.b), k_row, sq0.nk - d0.b * kBlock, wave, lane);
   dma_block<true>(kvs[vs_], v_base(sq0, h0, d0.b), v_row, sq0.nk - d0.b * kBlock, wave, lane);
   TileQ8<G> tq0, tq1;
@@ -739,8 +743,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
     if (d1.n) tq1.load(a.entry_q, d1, wave, rent);
     const TileD d3 = it_decode(r3, it, a, E);
     r3 = it_fetch(it, a, j);
-    if (trans)
-      dma_block8(kvs[fs_], k_base(sq1, h1, d1.b), k_row, sq1.nk - d1.b * kBlock, wave, lane);
+    if (trans) {
+      dma_block8(kvs[fk_], k_base(sq1, h1, d1.b), k_row, sq1.nk - d1.b * kBlock, wave, lane);
+      dma_block<true>(kvs[fv_], v_base(sq1, h1, d1.b), v_row, sq1.nk - d1.b * kBlock, wave, lane);
+    }
     const i32x8 bq0 = read_q8(obuf, 0, col, hf);
     const i32x8 bq1 = read_q8(obuf, 1, col, hf);
     const u32x4* const kslot = kvs[ks_];
@@ -762,10 +768,6 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
                                           srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
                                           srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
-    if (trans) {
-      __syncthreads();        // every wave is done with this bucket's K
-      dma_block<true>(kvs[ks_], v_base(sq1, h1, d1.b), v_row, sq1.nk - d1.b * kBlock, wave, lane);
-    }
     // Q of the next tile into the staging buffer: this tile's Q operands were read before the K
     // operands that the MFMAs above waited for (LDS reads complete in order)
     tq1.dma(obuf, a.q, a.hq, h1, g, lane);
@@ -807,10 +809,12 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
     o_voff = store_lane_offset(o_row0, o_nrow, col, hf);
     if (d1.n == 0) break;
     if (trans) {
-      const int k2 = fs_;
-      fs_ = vs_;
-      vs_ = ks_;
-      ks_ = k2;
+      int x = ks_;
+      ks_ = fk_;
+      fk_ = x;
+      x = vs_;
+      vs_ = fv_;
+      fv_ = x;
     }
     opened = trans;
     d0 = d1;

@@ -21,12 +21,13 @@ constexpr int kWordQ = 64;
 // kernels hand each (s, group, range) phase to one XCD, whose workgroups split the phase's
 // tiles. Longer ranges hold more queries per bucket (fuller tiles, fewer K/V loads) but more
 // Q rows per phase: bf16 takes up to 1024 queries (16 heads x 256 B x 1024 = 4 MiB, one XCD's
-// L2: at the M3 shape 3.21 ms with 512, 3.10 with 1024, 3.11 with 2048), fp8, whose kernel is
-// bound by issue rather than memory, up to 4096; either as long as the schedule keeps at least
-// 128 phases (16 per XCD) to spread, and never below 512.
+// L2: at the M3 shape 3.21 ms with 512, 3.10 with 1024, 3.11 with 2048), fp8 up to 2048 (the
+// same 4 MiB of e4m3 rows: at 128K tokens 10.23 / 9.80 / 9.91 ms with 1024 / 2048 / 4096);
+// either as long as the schedule keeps at least 128 phases (16 per XCD) to spread, and never
+// below 512.
 constexpr int kRangeQMin = 512;
 constexpr int kRangeQBf16Max = 1024;
-constexpr int kRangeQFp8Max = 4096;
+constexpr int kRangeQFp8Max = 2048;
 constexpr int64_t kMinPhases = 128;
 inline int range_q(const msa_shape& s) {
   int r = s.dtype == MSA_FP8_E4M3 ? kRangeQFp8Max : kRangeQBf16Max;

@@ -242,7 +242,7 @@ def test_partial_memory_ratio_matches_the_pages():
 
 
 def test_query_range_rule():
-    """Ranges hold the longest of 1024 (bf16) or 4096 (fp8) .. 512 queries that leaves at least
+    """Ranges hold the longest of 1024 (bf16) or 2048 (fp8) .. 512 queries that leaves at least
     128 (sequence, group, range) phases."""
     def q_range(s):
         lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
@@ -250,7 +250,7 @@ def test_query_range_rule():
     fp8 = msa.MSA_FP8_E4M3
     assert q_range(m3_shape()) == (1024, 32)                     # 4 groups x 32 ranges
     long = dict(total_q=131072, total_k=131072, max_q=131072, max_k=131072)
-    assert q_range(m3_shape(dtype=fp8, **long)) == (4096, 32)
+    assert q_range(m3_shape(dtype=fp8, **long)) == (2048, 64)
     assert q_range(m3_shape(**long)) == (1024, 128)
     assert q_range(m3_shape(total_q=4096, total_k=4096, max_q=4096, max_k=4096)) == (512, 8)
     assert q_range(m3_shape(dtype=fp8)) == (1024, 32)            # 4 groups x 32 ranges
