@@ -12,6 +12,7 @@ recorded on the stream the library launches on.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
@@ -268,6 +269,99 @@ def measure_ceilings(dev, mib: int = 2048) -> dict:
     return out
 
 
+def _amdgpu_files() -> dict | None:
+    """sysfs files of the one AMD GPU: hwmon power reading and cap (microwatts), current
+    graphics clock level. None when there is not exactly one such device."""
+    devs = [d for d in glob.glob("/sys/class/drm/card*/device")
+            if os.path.exists(os.path.join(d, "vendor"))
+            and open(os.path.join(d, "vendor")).read().strip() == "0x1002"
+            and glob.glob(os.path.join(d, "hwmon", "hwmon*", "power1_input"))]
+    if len(devs) != 1:
+        return None
+    hw = glob.glob(os.path.join(devs[0], "hwmon", "hwmon*"))[0]
+    return {"power": os.path.join(hw, "power1_input"), "cap": os.path.join(hw, "power1_cap"),
+            "sclk": os.path.join(devs[0], "pp_dpm_sclk")}
+
+
+def _read_sclk(path: str):
+    """Current graphics clock (MHz): the level marked '*' in pp_dpm_sclk."""
+    try:
+        for line in open(path):
+            if "*" in line:
+                num = "".join(ch if ch.isdigit() else " " for ch in line.split(":", 1)[-1]).split()
+                return float(num[0]) if num else None
+    except OSError:
+        return None
+    return None
+
+
+def power_sample(fn, secs: float = 6.0, settle: float = 2.5) -> dict | None:
+    """Socket power and graphics clock while `fn` (one call, launched asynchronously) runs
+    back to back for `secs` seconds: amdgpu's hwmon reading is taken between batches of calls
+    after `settle` seconds (the power manager's steady state), the median reported. Files
+    are read, no tool is run. None when the GPU's sysfs files are not there."""
+    f = _amdgpu_files()
+    if f is None:
+        return None
+    fn()
+    torch.cuda.synchronize()
+    watts, mhz = [], []
+    n, t0 = 0, time.perf_counter()
+    while True:
+        for _ in range(8):
+            fn()
+        n += 8
+        el = time.perf_counter() - t0
+        if el > settle:
+            try:
+                watts.append(int(open(f["power"]).read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+            c = _read_sclk(f["sclk"])
+            if c:
+                mhz.append(c)
+        torch.cuda.synchronize()
+        if el > secs:
+            break
+    el = time.perf_counter() - t0
+    try:
+        cap = int(open(f["cap"]).read()) / 1e6
+    except (OSError, ValueError):
+        cap = None
+    if not watts:
+        return None
+    w = float(np.median(watts))
+    ms = el * 1e3 / n
+    return {"socket_w": w, "cap_w": cap, "gfx_mhz": float(np.median(mhz)) if mhz else None,
+            "ms_per_call": ms, "joule_per_call": w * ms * 1e-3, "samples": len(watts),
+            "how": "calls back to back; amdgpu hwmon power1_input and pp_dpm_sclk, median"}
+
+
+def gemm_ceiling(dev, n: int = 8192, secs: float = 5.0) -> dict:
+    """bf16 MFMA ceiling measured on this GPU under its power manager: torch.matmul (the
+    vendor BLAS) on n x n x n bf16 back to back for `secs` seconds, the rate taken from the
+    host clock over all the calls; the power and clock seen meanwhile."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    t0 = time.perf_counter()
+    k = 0
+    pw = power_sample(lambda: torch.matmul(a, b, out=c), secs=secs, settle=secs / 2)
+    if pw is None:            # no power reading: time the loop alone
+        while time.perf_counter() - t0 < secs:
+            for _ in range(8):
+                torch.matmul(a, b, out=c)
+            torch.cuda.synchronize()
+            k += 8
+        ms = (time.perf_counter() - t0) * 1e3 / k
+    else:
+        ms = pw["ms_per_call"]
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"gemm_bf16_tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12, "n": n, "power": pw,
+            "how": "torch.matmul bf16 %d^3 back to back for %.0f s, host clock" % (n, secs)}
+
+
 def mix_ceiling(ceil: dict, read_bytes: float, write_bytes: float) -> float:
     """Measured ceiling (GB/s) for a kernel that reads and writes these amounts: the time the
     measured read and write rates need for them, as one rate."""
@@ -495,6 +589,64 @@ def make_step(c: dict):
     return step, names
 
 
+def call_fns(c: dict) -> dict:
+    """Each call of a step as a function of no arguments, on the workload's buffers (the
+    workspace must hold a plan for attn_main and partials for combine: run a step first)."""
+    shape, chosen, scale = c["shape"], c["chosen"], c["case"].softmax_scale
+    q, k, v, topk, ws, o, lse = c["q"], c["k"], c["v"], c["topk"], c["ws"], c["o"], c["lse"]
+    cu_q, cu_k = c["cu_q"], c["cu_k"]
+    fns = {}
+    if c["given"] is None and c["sel"]:
+        fns["select"] = lambda: msa.msa_select_tiles(shape, c["sel"], q, k, cu_q, cu_k, topk,
+                                                     None, c["sws"])
+    elif c["given"] is None and c["idx8"]:
+        fns["index"] = lambda: msa.msa_index_topk_fp8(shape, c["q_idx"], c["k_idx"],
+                                                      c["idx_descale"], cu_q, cu_k, topk, None,
+                                                      c["iws"])
+    elif c["given"] is None:
+        fns["index"] = lambda: msa.msa_index_topk(shape, c["q_idx"], c["k_idx"], cu_q, cu_k,
+                                                  topk, None, c["iws"])
+    if chosen == msa.MSA_KV_OUTER:
+        fns["plan"] = lambda: msa.msa_plan(shape, topk, cu_q, cu_k, ws)
+        fns["attn_main"] = lambda: msa.msa_attn_main(shape, q, k, v, c["descale"], scale, cu_q,
+                                                     cu_k, ws)
+    else:
+        fns["attn_q"] = lambda: msa.msa_sparse_attn_fwd(shape, q, k, v, c["descale"], scale,
+                                                        topk, cu_q, cu_k, chosen, ws, o, lse)
+    fns["combine"] = lambda: msa.msa_combine(shape, chosen, ws, o, lse)
+    return fns
+
+
+def power_table(c: dict, dev, secs: float = 6.0) -> dict:
+    """Power and clock of each call of the step run back to back, of the whole step, of the
+    vendor bf16 GEMM and of a 2 GiB device copy; the idle reading first."""
+    f = _amdgpu_files()
+    out = {"metric": "socket power and graphics clock per call", "workload": c["workload"],
+           "description": c["desc"]}
+    if f is None:
+        out["error"] = "no amdgpu hwmon power reading"
+        return out
+    torch.cuda.synchronize()
+    time.sleep(3.0)
+    out["idle_w"] = int(open(f["power"]).read()) / 1e6
+    step, _ = make_step(c)
+    step()
+    torch.cuda.synchronize()
+    calls = {name: power_sample(fn, secs) for name, fn in call_fns(c).items()}
+    calls["step"] = power_sample(step, secs)
+    out["calls"] = calls
+    out["gemm"] = gemm_ceiling(dev)
+    x = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    pw = power_sample(lambda: y.copy_(x), secs)
+    if pw:
+        pw["gbps"] = 2 * x.numel() / (pw["ms_per_call"] * 1e-3) / 1e9
+    out["copy_2gib"] = pw
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_forward(c: dict, steps: int, warmup: int, ceil: dict | None) -> dict:
     """Time `steps` layer calls after `warmup`; the result line of the workload."""
     case, cfg, dtype, chosen = c["case"], c["cfg"], c["dtype"], c["chosen"]
@@ -600,6 +752,21 @@ def run_forward(c: dict, steps: int, warmup: int, ceil: dict | None) -> dict:
         if call in traffic:
             e["traffic"] = traffic[call]
     res["kernels"] = kr
+    if ceil is not None:
+        # the main call back to back after the timed region: power and clock it runs at
+        shape, scale = c["shape"], case.softmax_scale
+        if kv:
+            fn = lambda: msa.msa_attn_main(shape, c["q"], c["k"], c["v"], c["descale"], scale,
+                                           c["cu_q"], c["cu_k"], c["ws"])
+        else:
+            fn = lambda: msa.msa_sparse_attn_fwd(shape, c["q"], c["k"], c["v"], c["descale"],
+                                                 scale, c["topk"], c["cu_q"], c["cu_k"], chosen,
+                                                 c["ws"], c["o"], c["lse"])
+        res["roofline"]["power"] = power_sample(fn)
+        gem = ceil.get("gemm")
+        if gem and not dtype:
+            res["roofline"]["mfma_ceiling_measured_tflops"] = gem["gemm_bf16_tflops"]
+            res["roofline"]["mfma_frac_measured"] = flops / t_main / 1e12 / gem["gemm_bf16_tflops"]
     res["kernel_sha"] = kernel_sha()
     res["gen_seconds"] = round(c["t_gen"], 1)
     return res
@@ -706,7 +873,7 @@ def main():
                     help="a second workload timed in the same run and reported under "
                          "'secondary' (only with the default workload; 'none' to skip)")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the measured memory ceilings")
+                    help="skip the measured memory and GEMM ceilings and the power samples")
     ap.add_argument("--backward", action="store_true",
                     help="time the main-branch backward (msa_sparse_attn_bwd) instead")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -715,6 +882,9 @@ def main():
                     help="measure HBM and cache read bandwidth with the library's probe")
     ap.add_argument("--crossover", action="store_true",
                     help="time KV-outer against Q-outer across block reuse levels")
+    ap.add_argument("--power", action="store_true",
+                    help="power and clock of each call run back to back (amdgpu hwmon), "
+                         "with the GEMM and copy references, instead of the timed run")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -733,6 +903,9 @@ def main():
         print(json.dumps(res), flush=True)
         return
     c = prepare(args.workload, args.seed, args.mode, dev)
+    if args.power:
+        print(json.dumps(power_table(c, dev)), flush=True)
+        return
     if args.backward:
         step, _ = make_step(c)
         step()                                 # lists, O and LSE of the forward
@@ -740,7 +913,10 @@ def main():
                        (c["q"], c["k"], c["v"], c["o"], c["lse"], c["topk"], c["cu_q"],
                         c["cu_k"], c["q_idx"], c["k_idx"]))
         return
-    ceil = None if args.no_ceilings else measure_ceilings(dev)
+    ceil = None
+    if not args.no_ceilings:
+        ceil = measure_ceilings(dev)
+        ceil["gemm"] = gemm_ceiling(dev)
     res = run_forward(c, args.steps, args.warmup, ceil)
     if ceil:
         res["ceilings_measured"] = ceil
