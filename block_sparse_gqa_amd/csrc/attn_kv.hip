@@ -451,74 +451,93 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
     if (trans)
       dma_block<false>(kvs[fs], kv_base(kb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock, wave,
                        lane);
-    read_q(obuf, bq, col, hf);
     const u32x4* const kslot = kvs[ks];
     const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs]);
-    k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[0], 0, rp, sw, hf);
-
-    // ---- phase A: QK^T(j) | O(j-1) from registers to memory in steps 0-3 (dim tile st:
-    // two 16-byte chunks per lane, each store 8 whole 128-byte lines of the group layout);
-    // the next tile's Q rows are requested in step 4, when this tile's Q operands have been
-    // read (LDS reads complete in order, and the K operands of step 1 were read after them)
-    f32x16 sc[4];
+    // A wave whose 32 rows all lie past the tile's entries (the last tile of a bucket) skips
+    // the tile's math and Q rows: it only stores the previous tile's output and takes part in
+    // the K/V loads and barriers.
+    const bool act = d0.n * G > wave * 32;
+    const bool act1 = d1.n * G > wave * 32;
+    if (act) {
+      f32x16 sc[4];
+      read_q(obuf, bq, col, hf);
+      k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[0], 0, rp, sw, hf);
+      // ---- phase A: QK^T(j) | O(j-1) from registers to memory in steps 0-3 (dim tile st:
+      // two 16-byte chunks per lane, each store 8 whole 128-byte lines of the group layout);
+      // the next tile's Q rows are requested in step 4, when this tile's Q operands have been
+      // read (LDS reads complete in order, and the K operands of step 1 were read after them)
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (st < 7) k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[(st + 1) & 1], st + 1, rp, sw, hf);
+      for (int st = 0; st < 8; ++st) {
+        if (st < 7) k_frags(*reinterpret_cast<const KVLds*>(kslot), fr[(st + 1) & 1], st + 1, rp, sw, hf);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
-      if (st < 4) {
-        store_o_tile(part_o_b, o_row0, oacc[st], st, o_voff);
-      } else if (st == 4) {
-        // LSE and weight sum, streaming like the partials (both are read once, by the
-        // combine): lines kept in L2 would only push out the phase's Q rows
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                              srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                              srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
-        tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
+        for (int kt = 0; kt < 4; ++kt)
+          sc[kt] = mfma32(fr[st & 1][kt], bq[st], st == 0 ? f32x16{} : sc[kt]);
+        if (st < 4) {
+          store_o_tile(part_o_b, o_row0, oacc[st], st, o_voff);
+        } else if (st == 4) {
+          // LSE and weight sum, streaming like the partials (both are read once, by the
+          // combine): lines kept in L2 would only push out the phase's Q rows
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                                srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                                srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
+          if (act1) tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
+        }
+        MSA_INTERLEAVE(1, 6);
       }
-      MSA_INTERLEAVE(1, 6);
-    }
-    if (trans) {
-      __syncthreads();        // every wave is done with this bucket's K
-      dma_block<true>(kvs[ks], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock, wave,
-                      lane);
-    }
-    // ---- row max of S(j)
-    if (need_mask) {
+      if (trans) {
+        __syncthreads();        // every wave is done with this bucket's K
+        dma_block<true>(kvs[ks], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
+                        wave, lane);
+      }
+      // ---- row max of S(j)
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sc[kt][i] = (kt * 32 + 16 * hf + i <= kmax) ? sc[kt][i] : -__builtin_inff();
+      }
+      float m = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          sc[kt][i] = (kt * 32 + 16 * hf + i <= kmax) ? sc[kt][i] : -__builtin_inff();
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      const bool any = m > -__builtin_inff();
+      const float c = any ? m * sl2 : 0.f;
+      // ---- phase B: PV(j) | exp of the next key-step
+      v_frags_tr(vslot, fr[0], 0, vl);
+      u32x4 pk[8];
+      float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st < 7) v_frags_tr(vslot, fr[(st + 1) & 1], st + 1, vl);
+        const bf16x8 bp = as_bf16x8(pk[st]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
+        if (st + 1 < 8) l = exp_step(sc, st + 1, sl2, c, pk[st + 1], l);
+        MSA_INTERLEAVE(2, 7);
+      }
+      l += shfl_xor_f(l, 32);
+      // the output of tile j is stored during the next tile's phase A
+      o_l = any ? l : 0.f;
+      o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) store_o_tile(part_o_b, o_row0, oacc[dt], dt, o_voff);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                            srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                            srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
+      if (act1) tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
+      if (trans) {
+        __syncthreads();
+        dma_block<true>(kvs[ks], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
+                        wave, lane);
+      }
     }
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
-    m = fmaxf(m, shfl_xor_f(m, 32));
-    const bool any = m > -__builtin_inff();
-    const float c = any ? m * sl2 : 0.f;
-    // ---- phase B: PV(j) | exp of the next key-step
-    v_frags_tr(vslot, fr[0], 0, vl);
-    u32x4 pk[8];
-    float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (st < 7) v_frags_tr(vslot, fr[(st + 1) & 1], st + 1, vl);
-      const bf16x8 bp = as_bf16x8(pk[st]);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
-      if (st + 1 < 8) l = exp_step(sc, st + 1, sl2, c, pk[st + 1], l);
-      MSA_INTERLEAVE(2, 7);
-    }
-    l += shfl_xor_f(l, 32);
-    // the output of tile j is stored during the next tile's phase A
-    o_l = any ? l : 0.f;
-    o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
     o_nrow = max(0, min(32, d0.n * G - wave * 32));
     o_row0 = (size_t)d0.e0 * G + wave * 32;
     o_voff = store_lane_offset(o_row0, o_nrow, col, hf);
@@ -747,63 +766,76 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       dma_block8(kvs[fk_], k_base(sq1, h1, d1.b), k_row, sq1.nk - d1.b * kBlock, wave, lane);
       dma_block<true>(kvs[fv_], v_base(sq1, h1, d1.b), v_row, sq1.nk - d1.b * kBlock, wave, lane);
     }
-    const i32x8 bq0 = read_q8(obuf, 0, col, hf);
-    const i32x8 bq1 = read_q8(obuf, 1, col, hf);
     const u32x4* const kslot = kvs[ks_];
     const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs_]);
+    // waves whose rows all lie past the tile's entries skip the tile's math and Q rows
+    const bool act = d0.n * G > wave * 32;
+    const bool act1 = d1.n * G > wave * 32;
+    if (act) {
+      const i32x8 bq0 = read_q8(obuf, 0, col, hf);
+      const i32x8 bq1 = read_q8(obuf, 1, col, hf);
 
-    // ---- phase A: QK^T(j) on the 8-bit MFMA (8 MFMAs) | O(j-1) from registers to memory,
-    // dim tile kt after the MFMAs of key tile kt
-    f32x16 sc[4];
+      // ---- phase A: QK^T(j) on the 8-bit MFMA (8 MFMAs) | O(j-1) from registers to memory,
+      // dim tile kt after the MFMAs of key tile kt
+      f32x16 sc[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const i32x8 k0 = read_k8(kslot, kt, 0, rp, hf);
-      const i32x8 k1 = read_k8(kslot, kt, 1, rp, hf);
-      sc[kt] = mfma8(k0, bq0, f32x16{});
-      sc[kt] = mfma8(k1, bq1, sc[kt]);
-      store_o_tile(part_o_b, o_row0, oacc[kt], kt, o_voff);
-    }
-    // LSE and weight sum, streaming like the partials
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
-                                          srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
-                                          srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
-    // Q of the next tile into the staging buffer: this tile's Q operands were read before the K
-    // operands that the MFMAs above waited for (LDS reads complete in order)
-    tq1.dma(obuf, a.q, a.hq, h1, g, lane);
-    // ---- row max of S(j)
-    if (need_mask) {
+      for (int kt = 0; kt < 4; ++kt) {
+        const i32x8 k0 = read_k8(kslot, kt, 0, rp, hf);
+        const i32x8 k1 = read_k8(kslot, kt, 1, rp, hf);
+        sc[kt] = mfma8(k0, bq0, f32x16{});
+        sc[kt] = mfma8(k1, bq1, sc[kt]);
+        store_o_tile(part_o_b, o_row0, oacc[kt], kt, o_voff);
+      }
+      // LSE and weight sum, streaming like the partials
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                            srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                            srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
+      // Q of the next tile into the staging buffer: this tile's Q operands were read before the K
+      // operands that the MFMAs above waited for (LDS reads complete in order)
+      if (act1) tq1.dma(obuf, a.q, a.hq, h1, g, lane);
+      // ---- row max of S(j)
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sc[kt][i] = (kt * 32 + 16 * hf + i <= kmax) ? sc[kt][i] : -__builtin_inff();
+      }
+      float m = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          sc[kt][i] = (kt * 32 + 16 * hf + i <= kmax) ? sc[kt][i] : -__builtin_inff();
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      const bool any = m > -__builtin_inff();
+      const float c = any ? m * sl2 : 0.f;
+      // ---- phase B: PV(j) on bf16 MFMA against the widened V | exp of the next key-step
+      v_frags_tr(vslot, fr[0], 0, vl);
+      u32x4 pk[8];
+      float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st < 7) v_frags_tr(vslot, fr[(st + 1) & 1], st + 1, vl);
+        const bf16x8 bp = as_bf16x8(pk[st]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
+        if (st + 1 < 8) l = exp_step(sc, st + 1, sl2, c, pk[st + 1], l);
+        MSA_INTERLEAVE(2, 7);
+      }
+      l += shfl_xor_f(l, 32);
+      o_l = any ? l * inv_dv : 0.f;
+      o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) store_o_tile(part_o_b, o_row0, oacc[dt], dt, o_voff);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_lse),
+                                            srd(a.part_lse + o_row0, o_nrow * 4), col * 4, 0, 2);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o_l),
+                                            srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
+      if (act1) tq1.dma(obuf, a.q, a.hq, h1, g, lane);
     }
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[kt][i]);
-    m = fmaxf(m, shfl_xor_f(m, 32));
-    const bool any = m > -__builtin_inff();
-    const float c = any ? m * sl2 : 0.f;
-    // ---- phase B: PV(j) on bf16 MFMA against the widened V | exp of the next key-step
-    v_frags_tr(vslot, fr[0], 0, vl);
-    u32x4 pk[8];
-    float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (st < 7) v_frags_tr(vslot, fr[(st + 1) & 1], st + 1, vl);
-      const bf16x8 bp = as_bf16x8(pk[st]);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        oacc[dt] = mfma32(fr[st & 1][dt], bp, st == 0 ? f32x16{} : oacc[dt]);
-      if (st + 1 < 8) l = exp_step(sc, st + 1, sl2, c, pk[st + 1], l);
-      MSA_INTERLEAVE(2, 7);
-    }
-    l += shfl_xor_f(l, 32);
-    o_l = any ? l * inv_dv : 0.f;
-    o_lse = any ? (c + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
     o_nrow = max(0, min(32, d0.n * G - wave * 32));
     o_row0 = (size_t)d0.e0 * G + wave * 32;
     o_voff = store_lane_offset(o_row0, o_nrow, col, hf);
