@@ -239,8 +239,9 @@ def load_traffic(workload: str) -> dict:
 
 
 def measure_ceilings(dev, mib: int = 2048) -> dict:
-    """Memory ceilings measured on this GPU: torch's fill (write), copy (read + write) and sum
-    (read) over a buffer of `mib` MiB, best of five after warm-up, in GB/s."""
+    """Memory ceilings measured on this GPU over a buffer of `mib` MiB, best of five after
+    warm-up, in GB/s: torch's fill (write) and copy (read + write), the library's read probe
+    (read; torch's sum, a slower reader, beside it)."""
     n = (mib << 20) // 4
     a = torch.empty(n, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
@@ -260,11 +261,16 @@ def measure_ceilings(dev, mib: int = 2048) -> dict:
             ts.append(e0.elapsed_time(e1) * 1e-3)
         return nbytes / min(ts) / 1e9
     nb = n * 4
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device=dev)
     out = {"write_gbps": best(lambda: a.fill_(2.0), nb),
            "copy_gbps": best(lambda: b.copy_(a), 2 * nb),
-           "read_gbps": best(lambda: a.sum(), nb),
-           "buffer_mib": mib, "how": "torch fill_ / copy_ / sum on one buffer, best of 5"}
-    del a, b
+           "read_gbps": best(lambda: msa.msa_probe_read(a, nb, 4 * nb, sink), 4 * nb),
+           "torch_sum_gbps": best(lambda: a.sum(), nb),
+           "buffer_mib": mib,
+           "how": "torch fill_ (write) and copy_ (read + write) on one buffer; read: the "
+                  "library's read probe over the same buffer (far beyond the 256 MiB "
+                  "last-level cache), 4 passes; best of 5 each"}
+    del a, b, sink
     torch.cuda.empty_cache()
     return out
 
