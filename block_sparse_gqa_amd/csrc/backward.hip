@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) void bwd_clear_kernel(int32_t* __restrict__ p,
 // branch: T = the main weights averaged over the group's G heads (recomputed from Q, K and
 // the main LSE; held fixed), Pp = exp(tau_p z - LSEp) with z = q_idx . k_idx, and the
 // gradients of sum KL(T || Pp): dz = tau_p (Pp - T), dq_idx = dz k_idx, dk_idx = dz^T q_idx.
-// The proxy LSE is recomputed over the sparse keys first (one wave per (query, group)).
+// The proxy LSE is recomputed over the sparse keys first, block by block over the plan.
 
 struct ProxyArgs {
   BwdArgs b;                   // main-branch fields: Q, K, main LSE, plan, chunks
@@ -490,78 +490,114 @@ struct ProxyArgs {
   float pscale, pscale_log2;
 };
 
+// Proxy LSE in the KV-stationary order of the plan: per chunk of a (sequence, group, block)
+// column, each wave holds the block's proxy keys as MFMA operands (key 32 kt + lane % 32, dims
+// 16 ks + 8 (lane / 32) .. +7) and reduces the proxy scores of 32 entries at a time over the
+// block's visible keys to a (max, sum) pair per entry, in log2 units: the block's proxy keys
+// are read once per chunk, not once per query that selected the block. The pairs of a
+// (query, group) are merged by proxy_lse_merge_kernel through the combine map.
 template <int DP>
-__global__ __launch_bounds__(256) void proxy_lse_kernel(ProxyArgs pa, const int32_t* lists,
-                                                        float* lsep, int topk, int list_q,
-                                                        int tiles_max, int batch) {
+__global__ __launch_bounds__(256) void proxy_lse_part_kernel(ProxyArgs pa, float* __restrict__ pm,
+                                                             float* __restrict__ pl) {
   const BwdArgs& a = pa.b;
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t = gw / a.hkv, g = gw % a.hkv;
-  if (t >= a.total_q) return;
-  // the sequence holding row t (cu_q non-decreasing)
-  int lo = 0, hi = batch;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu_q[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int s = lo;
+  const int chunk = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int cl = a.col_of[chunk];
+  if (cl < 0) return;
+  const int b = cl % a.nb_max, g = (cl / a.nb_max) % a.hkv, s = cl / (a.nb_max * a.hkv);
+  const int j = chunk - a.chunk_base[cl];
+  const int lo = j * a.chunk_e, hi = lo + a.chunk_e;
   const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
-  const int il = t - sq.q0;
-  float m = -__builtin_inff(), l = 0.f;
-  if (il >= 0 && il < sq.nq) {
-    float qv[DP];
+  const int u0 = b * kBlock;
+  bf16x8 kf[4][DP / 16];
 #pragma unroll
-    for (int c = 0; c < DP / 8; ++c) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(pa.q_idx + ((size_t)t * a.hkv + g) * DP + 8 * c);
+  for (int kt = 0; kt < 4; ++kt) {
+    const int u = min(u0 + 32 * kt + col, sq.nk - 1);
+    const uint16_t* kr = pa.k_idx + ((size_t)(sq.k0 + u) * a.hkv + g) * DP + 8 * hf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qv[8 * c + 2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-        qv[8 * c + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    for (int ks = 0; ks < DP / 16; ++ks)
+      kf[kt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + 16 * ks));
+  }
+  TileIt it{0, 0, 0, 0};
+  while (next_segment(a, s, g, b, lo, hi, it)) {
+    for (int et = it.et + 32 * wave; et < it.e1; et += 128) {
+      const int e = et + col;
+      const int t = e < it.e1 ? a.entry_q[e] : -1;
+      bf16x8 qf[DP / 16];
+#pragma unroll
+      for (int ks = 0; ks < DP / 16; ++ks) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (t >= 0)
+          w = *reinterpret_cast<const u32x4*>(pa.q_idx + ((size_t)t * a.hkv + g) * DP + 16 * ks +
+                                              8 * hf);
+        qf[ks] = as_bf16x8(w);
       }
-    }
-    const int64_t row = list_q == 1 ? (int64_t)t : (int64_t)s * tiles_max + il / list_q;
-    const int32_t* L = lists + (row * a.hkv + g) * topk;
-    const int nb = (sq.nk + kBlock - 1) / kBlock;
-    const int pos = sq.nk - sq.nq + il;
-    for (int k = 0; k < topk; ++k) {
-      const int b = L[k];
-      bool ok = b >= 0 && b < nb && !(a.causal && b * kBlock > pos);
-      for (int p = 0; p < k && ok; ++p) ok = L[p] != b;
-      if (!ok) continue;
+      f32x16 z[4];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int u = b * kBlock + lane + 64 * jj;
-        if (u >= sq.nk || (a.causal && u > pos)) continue;
-        const uint16_t* kr = pa.k_idx + ((size_t)(sq.k0 + u) * a.hkv + g) * DP;
-        float z = 0.f;
+      for (int kt = 0; kt < 4; ++kt) {
+        z[kt] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < DP / 8; ++c) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(kr + 8 * c);
+        for (int ks = 0; ks < DP / 16; ++ks) z[kt] = mfma32(kf[kt][ks], qf[ks], z[kt]);
+      }
+      // visible keys of the entry: in the sequence and, causal, not after its query
+      const int pos = sq.nk - sq.nq + (t - sq.q0);
+      int kmax = min(kBlock - 1, sq.nk - 1 - u0);
+      if (a.causal) kmax = min(kmax, pos - u0);
+      if (t < 0) kmax = -1;
+      float m = -__builtin_inff();
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            z = fmaf(qv[8 * c + 2 * i], bf16_bits_to_f32(w[i] & 0xFFFFu), z);
-            z = fmaf(qv[8 * c + 2 * i + 1], bf16_bits_to_f32(w[i] >> 16), z);
-          }
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int key = 32 * kt + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+          if (key <= kmax) m = fmaxf(m, z[kt][rr] * pa.pscale_log2);
         }
-        const float zs = z * pa.pscale_log2;
-        const float mn = fmaxf(m, zs);
-        l = l * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(zs - mn);
-        m = mn;
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      float l = 0.f;
+      if (m > -__builtin_inff()) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int key = 32 * kt + 8 * (rr >> 2) + 4 * hf + (rr & 3);
+            if (key <= kmax) l += __builtin_amdgcn_exp2f(fmaf(z[kt][rr], pa.pscale_log2, -m));
+          }
+      }
+      l += shfl_xor_f(l, 32);
+      if (hf == 0 && t >= 0) {
+        pm[e] = m;
+        pl[e] = l;
       }
     }
   }
-  // wave reduction of (max, sum)
-  float mw = m;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) mw = fmaxf(mw, shfl_xor_f(mw, off));
-  float lw = mw == -__builtin_inff() ? 0.f : l * __builtin_amdgcn_exp2f(m - mw);
-  if (m == -__builtin_inff()) lw = 0.f;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) lw += shfl_xor_f(lw, off);
-  if (lane == 0)
-    lsep[(size_t)t * a.hkv + g] =
-        mw == -__builtin_inff() ? -__builtin_inff() : (mw + log2f(lw)) * 0.6931471805599453f;
+}
+
+// Proxy LSE of each (query, group) (natural log): its entries' (max, sum) pairs merged in slot
+// order through the combine map; -inf when no selected key is visible.
+__global__ __launch_bounds__(256) void proxy_lse_merge_kernel(const int32_t* __restrict__ cmap,
+                                                              const int32_t* __restrict__ counters,
+                                                              const float* __restrict__ pm,
+                                                              const float* __restrict__ pl,
+                                                              float* __restrict__ lsep, int64_t n,
+                                                              int topk) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int n_ent = counters[0];
+  const int32_t* cm = cmap + i * topk;
+  float m = -__builtin_inff();
+  for (int k = 0; k < topk; ++k) {
+    const int e = cm[k];
+    if (e >= 0 && e < n_ent) m = fmaxf(m, pm[e]);
+  }
+  float l = 0.f;
+  if (m > -__builtin_inff())
+    for (int k = 0; k < topk; ++k) {
+      const int e = cm[k];
+      if (e >= 0 && e < n_ent && pm[e] > -__builtin_inff())
+        l += pl[e] * __builtin_amdgcn_exp2f(pm[e] - m);
+    }
+  lsep[i] = m > -__builtin_inff() ? (m + log2f(l)) * 0.6931471805599453f : -__builtin_inff();
 }
 
 template <int G, int DP>
@@ -825,7 +861,7 @@ BwdGeometry bwd_geometry(const msa_shape& s) {
 
 struct ProxyGeometry {
   int64_t n_cols, chunks_max;
-  size_t off_dqi, off_base, off_col, off_dki, off_lsep, total;
+  size_t off_dqi, off_base, off_col, off_dki, off_lsep, off_pm, off_pl, total;
 };
 
 ProxyGeometry proxy_geometry(const msa_shape& s) {
@@ -845,6 +881,8 @@ ProxyGeometry proxy_geometry(const msa_shape& s) {
   b.off_col = take((size_t)b.chunks_max * 4);
   b.off_dki = take((size_t)b.chunks_max * kBlock * s.dp * 4);
   b.off_lsep = take((size_t)s.total_q * s.hkv * 4);
+  b.off_pm = take((size_t)g.e_max * 4);
+  b.off_pl = take((size_t)g.e_max * 4);
   b.total = off;
   return b;
 }
@@ -918,23 +956,32 @@ hipError_t launch_proxy_bwd(const msa_shape& s, const void* q, const void* k, co
   pa.dk_idx = dk_idx;
   pa.pscale = proxy_scale;
   pa.pscale_log2 = proxy_scale * 1.4426950408889634f;
-  const int64_t waves = (int64_t)s.total_q * s.hkv;
-  if (waves > 0) {
-    const dim3 grid((unsigned)((waves + 3) / 4));
-    if (s.dp == 32)
-      hipLaunchKernelGGL(proxy_lse_kernel<32>, grid, dim3(256), 0, st, pa, lists, lsep, s.topk,
-                         s.list_q, (int)g.tiles_max, s.batch);
-    else
-      hipLaunchKernelGGL(proxy_lse_kernel<64>, grid, dim3(256), 0, st, pa, lists, lsep, s.topk,
-                         s.list_q, (int)g.tiles_max, s.batch);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  float* const pm = reinterpret_cast<float*>(ws + pg.off_pm);
+  float* const pl = reinterpret_cast<float*>(ws + pg.off_pl);
   if (pg.n_cols > 0) {
     hipLaunchKernelGGL(bwd_chunks_kernel, dim3(1), dim3(256), 0, st, a,
                        reinterpret_cast<int32_t*>(ws + pg.off_base),
                        reinterpret_cast<int32_t*>(ws + pg.off_col), (int)pg.n_cols,
                        (int)pg.chunks_max);
+    if (s.dp == 32)
+      hipLaunchKernelGGL(proxy_lse_part_kernel<32>, dim3((unsigned)pg.chunks_max), dim3(256), 0,
+                         st, pa, pm, pl);
+    else
+      hipLaunchKernelGGL(proxy_lse_part_kernel<64>, dim3((unsigned)pg.chunks_max), dim3(256), 0,
+                         st, pa, pm, pl);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t rows = (int64_t)s.total_q * s.hkv;
+  if (rows > 0) {
+    hipLaunchKernelGGL(proxy_lse_merge_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       st, reinterpret_cast<const int32_t*>(ws + L.cmap),
+                       reinterpret_cast<const int32_t*>(ws + L.counters), pm, pl, lsep, rows,
+                       s.topk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pg.n_cols > 0) {
     e = s.dp == 32 ? launch_proxy_dp<32>(pa, g.group, pg.chunks_max, st)
                    : launch_proxy_dp<64>(pa, g.group, pg.chunks_max, st);
     if (e != hipSuccess) return e;
