@@ -447,6 +447,8 @@ def bench_backward(args, case, shape, desc, t) -> None:
         torch.cuda.synchronize()
         res["proxy_backward_ms"] = sum(pev[i].elapsed_time(pev[i + 1])
                                        for i in range(args.steps)) / args.steps
+        if not args.no_ceilings:
+            res["power"] = {"backward": power_sample(bwd), "proxy_backward": power_sample(pbwd)}
         del pws
         # both backward passes in one call (msa_train_bwd)
         tws = torch.empty(msa.msa_train_bwd_workspace_size(shape), dtype=torch.uint8,
