@@ -48,11 +48,14 @@ __device__ __forceinline__ bf16x8 read_rows(const uint16_t* buf, int rs, int r0,
                                                    8 * (lane >> 5)));
 }
 
-// 128-wide bf16 tiles in LDS are stored with their 16-byte chunks XOR-swizzled by the row
-// (chunk c of row r at c ^ (r % 16)), so that the 32 rows one fragment read touches, and the
-// 4 rows of each transpose load, fall in different banks.
+// 128-wide bf16 tiles in LDS are stored with their 16-byte chunks XOR-swizzled by the row:
+// chunk c of row r at c ^ f(r), f(r) = 4 (r % 4) + (r / 4) % 4, a permutation of 0..15 over
+// 16 consecutive rows. A fragment read (32 rows, one chunk) then meets each of the 16 chunk
+// positions twice, and a transpose load (4 consecutive rows x 4 consecutive chunks per half
+// wave) all 16 once: r % 4 moves the chunk by whole groups of four.
 __device__ __forceinline__ int sw(int row, int col) {
-  return row * kD + ((((col >> 3) ^ row) & 15) << 3) + (col & 7);
+  const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+  return row * kD + ((((col >> 3) ^ f) & 15) << 3) + (col & 7);
 }
 
 __device__ __forceinline__ bf16x8 read_rows_sw(const uint16_t* buf, int r0, int c0, int lane) {
@@ -71,6 +74,31 @@ __device__ __forceinline__ bf16x8 read_tr_sw(const uint16_t* buf, int r0, int c0
         (__attribute__((address_space(3))) s4*)(buf + sw(row, col)));
   }
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 32 x 32 bf16 tiles [row][key] (P and dS) with the 16-byte chunks of a row XOR-swizzled by
+// row / 4, so that the row-per-lane writes and reads and the 4-row transpose loads, whose rows
+// lie 64 bytes apart, spread over the banks.
+__device__ __forceinline__ int pswz(int row, int key) {
+  return row * 32 + ((((key >> 3) ^ (row >> 2)) & 3) << 3) + (key & 7);
+}
+
+// read_tr and read_rows over a pswz tile.
+__device__ __forceinline__ bf16x8 read_tr_p(const uint16_t* buf, int r0, int c0, int lane) {
+  const int i = lane & 15, grp = (lane >> 4) & 1, kb = lane >> 5;
+  const int col = c0 + 16 * grp + 4 * (i & 3);
+  s4 r[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int row = r0 + 8 * kb + 4 * h2 + (i >> 2);
+    r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4*)(buf + pswz(row, col)));
+  }
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 read_rows_p(const uint16_t* buf, int c0, int lane) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + pswz(lane & 31, c0 + 8 * (lane >> 5))));
 }
 
 // D[t, h] = sum_d dO[t, h, d] O[t, h, d] (fp32): 16 lanes per row of 128, 16-byte loads.
@@ -142,17 +170,21 @@ __device__ __forceinline__ bool next_segment(const BwdArgs& a, int s, int g, int
 }
 
 template <int G>
-__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
-  constexpr int TE = 32 / G;                 // entries per tile of 32 rows
-  __shared__ uint16_t kb[kBlock * kD];       // K_b, V_b, row-major
+__global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
+  constexpr int TE = 64 / G;                 // entries per tile of 64 rows
+  __shared__ uint16_t kb[kBlock * kD];       // K_b, V_b (swizzled)
   __shared__ uint16_t vb[kBlock * kD];
-  __shared__ uint16_t qt[2][32 * kD];        // the tile's Q and dO rows, double-buffered
-  __shared__ uint16_t dot[2][32 * kD];
-  __shared__ uint16_t pbuf[4][32 * 32];      // per wave: P and dS of its keys, [row][key]
-  __shared__ uint16_t sbuf[4][32 * 32];
+  __shared__ uint16_t qt[2][64 * kD];        // the tile's Q and dO rows, double-buffered
+  __shared__ uint16_t dot[2][64 * kD];
+  __shared__ uint16_t pbuf[8][32 * 32];      // per wave: P and dS of its keys and rows,
+  __shared__ uint16_t sbuf[8][32 * 32];      //   [row][key]
 
   const int chunk = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wave w: keys 32 kw .. +31 of the block; rows 32 hw .. +31 of the tile for S, dP and dQ;
+  // dims 64 hw .. +63 of dK and dV (the two waves of a key quarter split the dims)
+  const int kw = wave & 3, hw = wave >> 2;
   const int col = lane & 31, hf = lane >> 5;
   const int cl = a.col_of[chunk];            // -1: past the last chunk
   if (cl < 0) return;
@@ -164,38 +196,40 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
   const int u0 = b * kBlock;
 
   // K_b and V_b (rows past the sequence repeat its last key; their weights are masked)
-  for (int i = tid; i < kBlock * kD / 8; i += 256) {
+  for (int i = tid; i < kBlock * kD / 8; i += 512) {
     const int row = i / (kD / 8), c = i % (kD / 8);
     const size_t src = ((size_t)(sq.k0 + min(u0 + row, sq.nk - 1)) * a.hkv + g) * kD + 8 * c;
     *reinterpret_cast<u32x4*>(kb + sw(row, 8 * c)) = *reinterpret_cast<const u32x4*>(a.k + src);
     *reinterpret_cast<u32x4*>(vb + sw(row, 8 * c)) = *reinterpret_cast<const u32x4*>(a.v + src);
   }
 
-  f32x16 dk_acc[4], dv_acc[4];
+  f32x16 dk_acc[2], dv_acc[2];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < 2; ++dt) {
     dk_acc[dt] = f32x16{};
     dv_acc[dt] = f32x16{};
   }
-  const int key0 = 32 * wave;                // this wave's keys within the block
+  const int key0 = 32 * kw;                  // this wave's keys within the block
+  const int row0 = 32 * hw;                  // this wave's rows within the tile
 
-  // Staging rows of this thread: n = tid / 16 + 16 k (k = 0, 1), 16-byte column tid % 16.
-  // Compute row of this lane: n = col. Loads of a tile: entry rows first, then Q, dO, LSE, D.
+  // Staging rows of this thread: n = tid / 16 + 32 k (k = 0, 1), 16-byte column tid % 16.
+  // Compute row of this lane: n = row0 + col. Loads of a tile: entry rows first, then Q, dO,
+  // LSE, D.
   const int c16 = tid % 16;
   auto load_rows = [&](int et, int e1, int eq[2], int& eqc) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int e = et + (tid / 16 + 16 * k) / G;
+      const int e = et + (tid / 16 + 32 * k) / G;
       eq[k] = e < e1 ? a.entry_q[e] : -1;
     }
-    const int e = et + col / G;
+    const int e = et + (row0 + col) / G;
     eqc = e < e1 ? a.entry_q[e] : -1;
   };
   auto load_data = [&](const int eq[2], int eqc, u32x4 qv[2], u32x4 ov[2], float& lse2,
                        float& dsum) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int n = tid / 16 + 16 * k;
+      const int n = tid / 16 + 32 * k;
       qv[k] = u32x4{0u, 0u, 0u, 0u};
       ov[k] = u32x4{0u, 0u, 0u, 0u};
       if (eq[k] >= 0) {
@@ -207,7 +241,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     lse2 = 0.f;
     dsum = 0.f;
     if (eqc >= 0) {
-      const size_t hrow = (size_t)eqc * a.hq + g * G + col % G;
+      const size_t hrow = (size_t)eqc * a.hq + g * G + (row0 + col) % G;
       lse2 = a.lse[hrow] * 1.4426950408889634f;
       dsum = a.dsum[hrow];
     }
@@ -215,20 +249,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
   auto store_slot = [&](int slot, const u32x4 qv[2], const u32x4 ov[2]) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int n = tid / 16 + 16 * k;
+      const int n = tid / 16 + 32 * k;
       *reinterpret_cast<u32x4*>(qt[slot] + sw(n, 8 * c16)) = qv[k];
       *reinterpret_cast<u32x4*>(dot[slot] + sw(n, 8 * c16)) = ov[k];
     }
   };
 
   __syncthreads();                           // K_b, V_b staged
-  // the wave's K and V rows as A operands of S^T and dP^T, kept for the whole chunk
-  bf16x8 kf[kD / 16], vf[kD / 16];
+  // the wave's K rows as A operands of S^T, kept for the whole chunk (V's are read from LDS)
+  bf16x8 kf[kD / 16];
 #pragma unroll
-  for (int ks = 0; ks < kD / 16; ++ks) {
-    kf[ks] = read_rows_sw(kb, key0, 16 * ks, lane);
-    vf[ks] = read_rows_sw(vb, key0, 16 * ks, lane);
-  }
+  for (int ks = 0; ks < kD / 16; ++ks) kf[ks] = read_rows_sw(kb, key0, 16 * ks, lane);
 
   TileIt it{0, 0, 0, 0};
   bool have = next_segment(a, s, g, b, lo, hi, it);
@@ -257,14 +288,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     const int pos = sq.nk - sq.nq + (cur_t - sq.q0);
     const uint16_t* const qs = qt[slot];
     const uint16_t* const os = dot[slot];
-    // S^T and dP^T for the wave's 32 keys x the tile's 32 rows
+    // S^T and dP^T for the wave's 32 keys x its 32 rows of the tile
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
-      const bf16x8 qb = read_rows_sw(qs, 0, 16 * ks, lane);
-      const bf16x8 ob = read_rows_sw(os, 0, 16 * ks, lane);
+      const bf16x8 qb = read_rows_sw(qs, row0, 16 * ks, lane);
+      const bf16x8 ob = read_rows_sw(os, row0, 16 * ks, lane);
       st = mfma32(kf[ks], qb, st);
-      dpt = mfma32(vf[ks], ob, dpt);
+      dpt = mfma32(read_rows_sw(vb, key0, 16 * ks, lane), ob, dpt);
     }
     // P = exp(tau S - LSE) on visible keys; dS = P (dP - D); both to the wave's buffers as
     // [row][key] (lane (row col, half hf) holds keys 8 (r / 4) + 4 hf + r % 4 in st[r])
@@ -282,49 +313,47 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
         p[i] = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
         d[i] = p[i] * (dpt[4 * q4 + i] - dsum);
       }
-      u32x2 pw, sw;
+      u32x2 pw, sw2;
       pw[0] = pack_bf16x2(p[0], p[1]);
       pw[1] = pack_bf16x2(p[2], p[3]);
-      sw[0] = pack_bf16x2(d[0], d[1]);
-      sw[1] = pack_bf16x2(d[2], d[3]);
-      *reinterpret_cast<u32x2*>(pb + col * 32 + 8 * q4 + 4 * hf) = pw;
-      *reinterpret_cast<u32x2*>(sb + col * 32 + 8 * q4 + 4 * hf) = sw;
+      sw2[0] = pack_bf16x2(d[0], d[1]);
+      sw2[1] = pack_bf16x2(d[2], d[3]);
+      *reinterpret_cast<u32x2*>(pb + pswz(col, 8 * q4 + 4 * hf)) = pw;
+      *reinterpret_cast<u32x2*>(sb + pswz(col, 8 * q4 + 4 * hf)) = sw2;
     }
     // the following tile's data, in flight during the products below
     if (have_next) load_data(nq, nqc, qv, ov, lse2, dsum);
     __syncthreads();                         // P, dS of every wave written
 
-    // dV += P^T dO, dK += dS^T Q: contraction over the tile's 32 rows (2 steps of 16)
+    // dV += P^T dO, dK += dS^T Q for the wave's keys and dims 64 hw .. +63: contraction over
+    // the tile's 64 rows (rows 0-31 in the buffers of waves kw, rows 32-63 in those of kw + 4)
 #pragma unroll
-    for (int kr = 0; kr < 2; ++kr) {
-      const bf16x8 pa = read_tr(pb, 32, 16 * kr, 0, lane);   // P^T[key][rows]
-      const bf16x8 sa = read_tr(sb, 32, 16 * kr, 0, lane);   // dS^T[key][rows]
+    for (int kr = 0; kr < 4; ++kr) {
+      const int src = kw + 4 * (kr >> 1);
+      const bf16x8 pa = read_tr_p(pbuf[src], 16 * (kr & 1), 0, lane);   // P^T[key][rows]
+      const bf16x8 sa = read_tr_p(sbuf[src], 16 * (kr & 1), 0, lane);   // dS^T[key][rows]
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 ob = read_tr_sw(os, 16 * kr, 32 * dt, lane);   // dO[rows][dims]
-        const bf16x8 qb = read_tr_sw(qs, 16 * kr, 32 * dt, lane);   // Q[rows][dims]
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8 ob = read_tr_sw(os, 16 * kr, 64 * hw + 32 * dt, lane);   // dO[rows][dims]
+        const bf16x8 qb = read_tr_sw(qs, 16 * kr, 64 * hw + 32 * dt, lane);   // Q[rows][dims]
         dv_acc[dt] = mfma32(pa, ob, dv_acc[dt]);
         dk_acc[dt] = mfma32(sa, qb, dk_acc[dt]);
       }
     }
-    // dQ of the tile's rows, dims 32 wave .. +31, over all 128 keys: dS[rows][keys] K[keys][dims]
-    f32x16 dq0 = {}, dq1 = {};
+    // dQ of the wave's 32 rows, dims 32 kw .. +31, over all 128 keys: dS[rows][keys] K[keys][dims]
+    f32x16 dq = {};
 #pragma unroll
-    for (int kk = 0; kk < kBlock / 16; kk += 2) {
-      const bf16x8 s0 = read_rows(sbuf[kk >> 1], 32, 0, 0, lane);
-      const bf16x8 k0 = read_tr_sw(kb, 16 * kk, 32 * wave, lane);
-      const bf16x8 s1 = read_rows(sbuf[kk >> 1], 32, 0, 16, lane);
-      const bf16x8 k1 = read_tr_sw(kb, 16 * kk + 16, 32 * wave, lane);
-      dq0 = mfma32(s0, k0, dq0);
-      dq1 = mfma32(s1, k1, dq1);
+    for (int kk = 0; kk < kBlock / 16; ++kk) {
+      const bf16x8 s0 = read_rows_p(sbuf[(kk >> 1) + 4 * hw], 16 * (kk & 1), lane);
+      const bf16x8 k0 = read_tr_sw(kb, 16 * kk, 32 * kw, lane);
+      dq = mfma32(s0, k0, dq);
     }
-    const f32x16 dq = dq0 + dq1;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int n = 8 * (rr / 4) + 4 * hf + rr % 4;
+      const int n = row0 + 8 * (rr / 4) + 4 * hf + rr % 4;
       const int e = cur_et + n / G;
       if (e < cur_e1)
-        a.dq_part[((size_t)e * G + n % G) * kD + 32 * wave + col] =
+        a.dq_part[((size_t)e * G + n % G) * kD + 32 * kw + col] =
             (uint16_t)f32_to_bf16_bits(dq[rr] * a.scale);
     }
     if (have_next) store_slot(slot ^ 1, qv, ov);
@@ -344,9 +373,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     for (int rr = 0; rr < 16; ++rr) {
       const int m = key0 + 8 * (rr / 4) + 4 * hf + rr % 4;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        pk[m * kD + 32 * dt + col] = dk_acc[dt][rr] * a.scale;
-        pk[(kBlock + m) * kD + 32 * dt + col] = dv_acc[dt][rr];
+      for (int dt = 0; dt < 2; ++dt) {
+        pk[m * kD + 64 * hw + 32 * dt + col] = dk_acc[dt][rr] * a.scale;
+        pk[(kBlock + m) * kD + 64 * hw + 32 * dt + col] = dv_acc[dt][rr];
       }
     }
     return;
@@ -355,9 +384,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
   for (int rr = 0; rr < 16; ++rr) {
     const int u = u0 + key0 + 8 * (rr / 4) + 4 * hf + rr % 4;
     if (u < sq.nk) {
-      const size_t row = ((size_t)(sq.k0 + u) * a.hkv + g) * kD;
+      const size_t row = ((size_t)(sq.k0 + u) * a.hkv + g) * kD + 64 * hw;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+      for (int dt = 0; dt < 2; ++dt) {
         a.dk[row + 32 * dt + col] = dk_acc[dt][rr] * a.scale;
         a.dv[row + 32 * dt + col] = dv_acc[dt][rr];
       }
@@ -735,14 +764,14 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
       u32x2 w;
       w[0] = pack_bf16x2(d[0], d[1]);
       w[1] = pack_bf16x2(d[2], d[3]);
-      *reinterpret_cast<u32x2*>(zb + col * 32 + 8 * q4 + 4 * hf) = w;
+      *reinterpret_cast<u32x2*>(zb + pswz(col, 8 * q4 + 4 * hf)) = w;
     }
     if (have_next) load_data(nq, nqi, nqc, qv, pv, lse2, lsep2);
     __syncthreads();                         // dz of every wave written
     // dk_idx += (dz / G)^T q_idx over the tile's 32 rows (each entry counted G times)
 #pragma unroll
     for (int kr = 0; kr < 2; ++kr) {
-      const bf16x8 za = read_tr(zb, 32, 16 * kr, 0, lane);
+      const bf16x8 za = read_tr_p(zb, 16 * kr, 0, lane);
 #pragma unroll
       for (int dt = 0; dt < DP / 32; ++dt)
         acc[dt] = mfma32(za, read_tr(qit[slot], DP, 16 * kr, 32 * dt, lane), acc[dt]);
@@ -752,7 +781,7 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
       f32x16 dq = {};
 #pragma unroll
       for (int kk = 0; kk < kBlock / 16; ++kk)
-        dq = mfma32(read_rows(zbuf[kk >> 1], 32, 0, 16 * (kk & 1), lane),
+        dq = mfma32(read_rows_p(zbuf[kk >> 1], 16 * (kk & 1), lane),
                     read_tr(kib, DP, 16 * kk, 32 * wave, lane), dq);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
@@ -827,7 +856,7 @@ __global__ __launch_bounds__(256) void proxy_dq_kernel(const int32_t* __restrict
 
 template <int G>
 hipError_t launch_kv_g(const BwdArgs& a, int64_t chunks_max, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_kv_kernel<G>), dim3((unsigned)chunks_max), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bwd_kv_kernel<G>), dim3((unsigned)chunks_max), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
