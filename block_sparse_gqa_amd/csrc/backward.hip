@@ -469,30 +469,46 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a) {
   }
 }
 
-// dQ[t, h] = sum over the (query, group)'s entries of their partials (the combine map), one
-// thread per 4 dims of a (query, head) row.
+// dQ[t, h] = sum over the (query, group)'s entries of their partials (the combine map), in slot
+// order. A thread owns 8 dims (16 bytes of a partial row) of one head; the partial loads of
+// every slot are issued before any is added, each wave reading whole 256-byte head rows.
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ cmap,
                                                      const uint16_t* __restrict__ dq_part,
                                                      float* __restrict__ dq, int64_t n, int hq,
                                                      int group, int topk) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const int c = (int)(i % 32);
-  const int64_t row = i / 32;                // query row * hq + head
+  const int c = (int)(i % 16);
+  const int64_t row = i / 16;                // query row * hq + head
   const int head = (int)(row % hq), h = head / group, gi = head % group;
   const int64_t t = row / hq;
   const int32_t* cm = cmap + (t * (hq / group) + h) * topk;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < topk; ++k) {
-    const int e = cm[k];
-    if (e < 0) continue;
-    const u32x2 w = *reinterpret_cast<const u32x2*>(dq_part + ((size_t)e * group + gi) * kD + 4 * c);
-    acc[0] += bf16_bits_to_f32(w[0] & 0xFFFFu);
-    acc[1] += bf16_bits_to_f32(w[0] >> 16);
-    acc[2] += bf16_bits_to_f32(w[1] & 0xFFFFu);
-    acc[3] += bf16_bits_to_f32(w[1] >> 16);
+  int es[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) es[k] = k < topk ? cm[k] : -1;
+  u32x4 w[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    w[k] = u32x4{0u, 0u, 0u, 0u};
+    if (es[k] >= 0)
+      w[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+          dq_part + ((size_t)es[k] * group + gi) * kD + 8 * c));
   }
-  *reinterpret_cast<f32x4*>(dq + row * kD + 4 * c) = acc;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    a0[0] += bf16_bits_to_f32(w[k][0] & 0xFFFFu);
+    a0[1] += bf16_bits_to_f32(w[k][0] >> 16);
+    a0[2] += bf16_bits_to_f32(w[k][1] & 0xFFFFu);
+    a0[3] += bf16_bits_to_f32(w[k][1] >> 16);
+    a1[0] += bf16_bits_to_f32(w[k][2] & 0xFFFFu);
+    a1[1] += bf16_bits_to_f32(w[k][2] >> 16);
+    a1[2] += bf16_bits_to_f32(w[k][3] & 0xFFFFu);
+    a1[3] += bf16_bits_to_f32(w[k][3] >> 16);
+  }
+  f32x4* const out = reinterpret_cast<f32x4*>(dq + row * kD + 8 * c);
+  out[0] = a0;
+  out[1] = a1;
 }
 
 // The combine map of rows that lie in no sequence is never written by the plan: clear it.
@@ -1109,7 +1125,7 @@ hipError_t launch_bwd(const msa_shape& s, const void* q, const void* k, const vo
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t n = (int64_t)rows * 32;
+  const int64_t n = (int64_t)rows * 16;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<const int32_t*>(ws + L.cmap), a.dq_part, dq, n, s.hq,
