@@ -157,18 +157,18 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
   return pre + x - v;
 }
 
+// Word popcounts of a tile, summed. Loads are coalesced: word base + 256 i + thread.
 __global__ __launch_bounds__(256) void scan_reduce_kernel(const unsigned long long* __restrict__ masks,
                                                           int64_t n_words, int32_t* __restrict__ sums) {
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kPer;
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x;
   int v = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (base + i < n_words) v += __popcll(masks[base + i]);
+    if (base + 256 * i < n_words) v += __popcll(masks[base + 256 * i]);
   int tot;
   block_exclusive_scan(v, &tot);
   if (threadIdx.x == 0) sums[blockIdx.x] = tot;
 }
-
 __global__ __launch_bounds__(256) void scan_top_kernel(int32_t* __restrict__ sums, int64_t n_blocks,
                                                        int32_t* __restrict__ counters,
                                                        int32_t* __restrict__ offsets_end) {
@@ -187,23 +187,38 @@ __global__ __launch_bounds__(256) void scan_top_kernel(int32_t* __restrict__ sum
   }
 }
 
+// Offsets of a tile's words: wave w scans words w kScanTile / 4 .. +kScanTile / 4 - 1 of the
+// tile in kPer rounds of 64 consecutive words (coalesced loads and stores), carrying the
+// running sum from round to round; the waves' totals order the four segments.
 __global__ __launch_bounds__(256) void scan_down_kernel(const unsigned long long* __restrict__ masks,
                                                         int64_t n_words, const int32_t* __restrict__ sums,
                                                         int32_t* __restrict__ offsets) {
-  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * kPer;
+  __shared__ int wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + wave * (kScanTile / 4) + lane;
   int cnt[kPer];
-  int v = 0;
+  int tot = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    cnt[i] = (base + i < n_words) ? __popcll(masks[base + i]) : 0;
-    v += cnt[i];
+    cnt[i] = (base + 64 * i < n_words) ? __popcll(masks[base + 64 * i]) : 0;
+    tot += cnt[i];
   }
-  int tot;
-  int run = block_exclusive_scan(v, &tot) + sums[blockIdx.x];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o, 64);
+  if (lane == 0) wsum[wave] = tot;
+  __syncthreads();
+  int run = sums[blockIdx.x];
+  for (int w = 0; w < wave; ++w) run += wsum[w];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    if (base + i < n_words) offsets[base + i] = run;
-    run += cnt[i];
+    int x = cnt[i];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (base + 64 * i < n_words) offsets[base + 64 * i] = run + x - cnt[i];
+    run += __shfl(x, 63, 64);
   }
 }
 
