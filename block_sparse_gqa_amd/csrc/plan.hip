@@ -62,8 +62,20 @@ __device__ __forceinline__ void entry_blocks(const PlanArgs& a, const Seq& sq, i
   const int nb = min((sq.nk + kBlock - 1) / kBlock, a.nb_max);
   const int pos = sq.nk - sq.nq + il;
   int raw[kMaxTopK];
+  if (a.topk == kMaxTopK && ((uintptr_t)L & 15) == 0) {
+    // a whole 64-byte list row in four 16-byte loads
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) raw[k] = k < a.topk ? L[k] : -1;
+    for (int c = 0; c < kMaxTopK / 4; ++c) {
+      const int4 v = reinterpret_cast<const int4*>(L)[c];
+      raw[4 * c] = v.x;
+      raw[4 * c + 1] = v.y;
+      raw[4 * c + 2] = v.z;
+      raw[4 * c + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) raw[k] = k < a.topk ? L[k] : -1;
+  }
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) {
     const int b = raw[k];
@@ -117,9 +129,9 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(PlanArgs a) {
     const int w = il / kWordQ;
     const unsigned long long below = (1ull << (il % kWordQ)) - 1ull;
     int32_t* cm = a.cmap + ((size_t)(sq.q0 + il) * a.hkv + h) * a.topk;
+    int ent[kMaxTopK];
 #pragma unroll
     for (int k = 0; k < kMaxTopK; ++k) {
-      if (k >= a.topk) break;
       int e = -1;
       if (blk[k] >= 0) {
         const size_t wi = word_index(a, s, h, w, blk[k]);
@@ -127,7 +139,17 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(PlanArgs a) {
         a.entry_q[e] = sq.q0 + il;
         a.entry_bucket[e] = (int)bucket_of(a, s, h, w, blk[k]);
       }
-      cm[k] = e;
+      ent[k] = e;
+    }
+    if (a.topk == kMaxTopK && ((uintptr_t)cm & 15) == 0) {
+#pragma unroll
+      for (int c = 0; c < kMaxTopK / 4; ++c)
+        reinterpret_cast<int4*>(cm)[c] = make_int4(ent[4 * c], ent[4 * c + 1], ent[4 * c + 2],
+                                                   ent[4 * c + 3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k)
+        if (k < a.topk) cm[k] = ent[k];
     }
   }
 }
