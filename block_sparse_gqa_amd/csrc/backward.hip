@@ -301,15 +301,16 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     // [row][key] (lane (row col, half hf) holds keys 8 (r / 4) + 4 hf + r % 4 in st[r])
     uint16_t* const pb = pbuf[wave];
     uint16_t* const sb = sbuf[wave];
+    // the row's visible keys among the wave's: key0 + m with m <= kmax
+    int kmax = min(kBlock - 1, sq.nk - 1 - u0) - key0;
+    if (a.causal) kmax = min(kmax, pos - u0 - key0);
+    if (!(row_ok && lse2 > -__builtin_inff())) kmax = -1;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       float p[4], d[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 8 * q4 + 4 * hf + i;
-        const int u = u0 + key0 + m;
-        const bool vis = row_ok && u < sq.nk && !(a.causal && u > pos) &&
-                         lse2 > -__builtin_inff();
+        const bool vis = 8 * q4 + 4 * hf + i <= kmax;
         p[i] = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
         d[i] = p[i] * (dpt[4 * q4 + i] - dsum);
       }
@@ -762,20 +763,23 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
     for (int ks = 0; ks < DP / 16; ++ks)
       zt = mfma32(kif[ks], read_rows(qit[slot], DP, 0, 16 * ks, lane), zt);
     uint16_t* const zb = zbuf[wave];
+    // the row's visible keys among the wave's: key0 + m with m <= kmax (in the sequence and,
+    // causal, not after the query; none for a padding row or a row without visible keys)
+    int kmax = min(kBlock - 1, sq.nk - 1 - u0) - key0;
+    if (a.causal) kmax = min(kmax, pos - u0 - key0);
+    if (!(row_ok && lse2 > -__builtin_inff() && lsep2 > -__builtin_inff())) kmax = -1;
+    const float c1 = pa.pscale * (1.f / G), c2 = pa.pscale * (1.f / (G * G));
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       float d[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = 8 * q4 + 4 * hf + i;
-        const int u = u0 + key0 + m;
-        const bool vis = row_ok && u < sq.nk && !(a.causal && u > pos) &&
-                         lse2 > -__builtin_inff() && lsep2 > -__builtin_inff();
+        const bool vis = 8 * q4 + 4 * hf + i <= kmax;
         float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
         p = group_sum<G>(p);                 // sum over the entry's heads (DPP network)
         const float pp =
             vis ? __builtin_amdgcn_exp2f(fmaf(zt[4 * q4 + i], pa.pscale_log2, -lsep2)) : 0.f;
-        d[i] = pa.pscale * (pp - p * (1.f / G)) * (1.f / G);
+        d[i] = fmaf(c1, pp, -c2 * p);        // tau_p (Pp - T) / G, T = p / G
       }
       u32x2 w;
       w[0] = pack_bf16x2(d[0], d[1]);
