@@ -101,6 +101,22 @@ __device__ __forceinline__ bf16x8 read_rows_p(const uint16_t* buf, int c0, int l
   return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + pswz(lane & 31, c0 + 8 * (lane >> 5))));
 }
 
+// Sum over aligned groups of N lanes (N <= 16, within a DPP row) as fused DPP adds: the moved
+// operand is taken with a zero fill, which none of these in-row patterns ever uses, so the
+// compiler folds each move into its add (v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp_z(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_z<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_z<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_z<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_z<kDppMirror>(v);
+  return v;
+}
+
 // D[t, h] = sum_d dO[t, h, d] O[t, h, d] (fp32): 16 lanes per row of 128, 16-byte loads.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
@@ -776,7 +792,7 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
       for (int i = 0; i < 4; ++i) {
         const bool vis = 8 * q4 + 4 * hf + i <= kmax;
         float p = vis ? __builtin_amdgcn_exp2f(fmaf(st[4 * q4 + i], a.scale_log2, -lse2)) : 0.f;
-        p = group_sum<G>(p);                 // sum over the entry's heads (DPP network)
+        p = lane_group_sum<G>(p);            // sum over the entry's heads (DPP network)
         const float pp =
             vis ? __builtin_amdgcn_exp2f(fmaf(zt[4 * q4 + i], pa.pscale_log2, -lsep2)) : 0.f;
         d[i] = fmaf(c1, pp, -c2 * p);        // tau_p (Pp - T) / G, T = p / G
