@@ -27,7 +27,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   constexpr int TPB = G * 16;               // threads per (query, group) box
   constexpr int BOXES = 256 / TPB;
   const int tid = threadIdx.x;
-  const int box = blockIdx.x * BOXES + tid / TPB;
+  // Boxes from the last query backwards: the partials the attention kernel wrote last (the
+  // final query ranges) are then read first, while some are still in the last-level cache.
+  const int64_t n_boxes = (int64_t)total_q * hkv;
+  const int64_t idx = (int64_t)blockIdx.x * BOXES + tid / TPB;
+  if (idx >= n_boxes) return;
+  const int box = (int)(n_boxes - 1 - idx);
   // the thread's (head, 16-byte chunk): with G >= 8 an entry's G rows are whole 8-row groups
   // of the partial layout and thread j of the box reads its bytes 16 j .. 16 j + 15 (each
   // wave 1 KiB of consecutive bytes; its output stores fill 8 whole rows' halves)
@@ -35,7 +40,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int g = G >= 8 ? 8 * (j >> 7) + (j & 7) : j % G;
   const int c = G >= 8 ? (j >> 3) & 15 : j / G;
   const int t = box / hkv, h = box % hkv;
-  if (t >= total_q) return;
   const int n_ent = counters[0];
   const int hq = hkv * G;
   const int32_t* cm = cmap + ((size_t)t * hkv + h) * slots;
