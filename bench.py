@@ -743,14 +743,17 @@ def run_forward(c: dict, steps: int, warmup: int, ceil: dict | None) -> dict:
                                               / kr["combine"]["peak_measured"])
     else:
         qbytes = nsb * 2 * 128 * 128 * eb + case.total_q * cfg.hq * 128 * (eb + 2)
+        # the Q-outer kernel that runs: bf16 per-tile lists, bf16 per-query lists, fp8 lists
+        qname = ("attn_q_kernel" if dtype else
+                 "attn_qt_kernel" if cfg.list_q > 1 else "attn_qd_kernel")
         if flops / qbytes > peak_mma / PEAK_HBM:
-            res["roofline"] = {"bound": "mfma", "kernel": "attn_q_kernel",
+            res["roofline"] = {"bound": "mfma", "kernel": qname,
                                "achieved": flops / t_main / 1e12, "peak": peak_mma / 1e12,
                                "unit": "TFLOP/s", "frac": flops / t_main / peak_mma,
                                "traffic": traffic.get("attn_q")}
             kr["attn_q"] = roof(kms["attn_q"], "mfma", flops, peak_mma)
         else:
-            res["roofline"] = {"bound": "hbm", "kernel": "attn_q_kernel",
+            res["roofline"] = {"bound": "hbm", "kernel": qname,
                                "achieved": qbytes / t_main / 1e9, "peak": PEAK_HBM / 1e9,
                                "unit": "GB/s", "frac": qbytes / t_main / PEAK_HBM,
                                "traffic": traffic.get("attn_q"), "algorithmic_bytes": qbytes}

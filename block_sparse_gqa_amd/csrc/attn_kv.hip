@@ -228,7 +228,7 @@ __device__ __forceinline__ void dma_block(u32x4* dst, const uint16_t* base, uint
 
 // V^T operands (A) of key-step s (keys 32kt + 16hf + 8ks .. +7, kt = s/2, ks = s%2) for the
 // 4 output-dim tiles, from the row-major V block by transpose loads; `vl` is the lane's
-// element offset within the slot (see pv_block_tr).
+// element offset within the slot (see pv_half_tr).
 __device__ __forceinline__ void v_frags_tr(const unsigned short* vb, bf16x8 a[4], int s,
                                            const int vl[4]) {
   typedef short s4 __attribute__((ext_vector_type(4)));

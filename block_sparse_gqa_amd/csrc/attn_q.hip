@@ -98,8 +98,12 @@ __device__ __forceinline__ int visit_list_lanes(const int32_t* list, int topk, i
   return __builtin_amdgcn_ds_permute(dst * 4, b);
 }
 
+// fp8 lists (per-tile or per-query): e4m3 K and V are widened to bf16 while staged through
+// registers into LDS, one block at a time. bf16 lists run in attn_qd_kernel (per query) and
+// attn_qt_kernel (per tile).
 template <bool FP8, int G>
 __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
+  static_assert(FP8, "bf16 lists run in attn_qd_kernel and attn_qt_kernel");
   constexpr int EB = FP8 ? 1 : 2;
   __shared__ KVLds L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -210,56 +214,6 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
         pv_block<false>(L, pk, oacc, col, hf);
       });
     }
-  } else {
-    // bf16: K and V of block j+1 stream into LDS by direct loads while block j is computed.
-    // K(j+1) is issued once every wave has finished QK(j); V(j+1) once PV(j) is done.
-    const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k);
-    const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v);
-    auto dma_k = [&](int j) {
-      const int u0 = vis[j] * kBlock;
-      dma_rows<false>(L.k, kp + (kv_head + (size_t)u0 * a.hkv) * kD, kv_row, sq.nk - u0);
-    };
-    auto dma_v = [&](int j) {
-      const int u0 = vis[j] * kBlock;
-      dma_rows<true>(L.vt, vp + (kv_head + (size_t)u0 * a.hkv) * kD, kv_row, sq.nk - u0);
-    };
-    if (nv > 0) {
-      dma_k(0);
-      dma_v(0);
-    }
-    for (int j = 0; j < nv; ++j) {
-      const int u0 = vis[j] * kBlock;
-      const int nk_rel = sq.nk - u0;
-      wait_vm<8>();          // K(j) landed (only V(j), 8 loads, may still be in flight)
-      __syncthreads();
-      f32x16 sacc[4];
-      if (wave_rows) qk_block(L, bq, sacc, col, hf);
-      __syncthreads();       // K buffer free
-      const bool more = j + 1 < nv;
-      if (more) dma_k(j + 1);
-      u32x4 pk[4][2];
-      if (wave_rows) {
-        int kmax = min(127, nk_rel - 1);
-        if (a.causal) kmax = min(kmax, pos - u0);
-        const float mb = mask_max(sacc, kmax, __any(kmax < 127), hf);
-        const float m_new = fmaxf(m_run, mb);          // raw-score units
-        const float c = m_new > ninf ? m_new * sl2 : 0.f;
-        const float alpha = m_run > ninf ? __builtin_amdgcn_exp2f(m_run * sl2 - c) : 0.f;
-        const float lb = exp_pack(sacc, sl2, c, pk);
-        l_run = l_run * alpha + lb;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-        m_run = m_new;
-      }
-      if (more) wait_vm<8>();   // V(j) landed (K(j+1) may still be in flight)
-      else wait_vm<0>();
-      __syncthreads();
-      if (wave_rows) pv_block_tr<false>(L, pk, oacc, lane);
-      __syncthreads();       // V buffer free
-      if (more) dma_v(j + 1);
-    }
   }
 
   if (a.splits > 1 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0)
@@ -274,6 +228,149 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
     if (hf == 0 && a.lse) a.lse[(size_t)t * a.hq + hh] = lse_v;
   } else {
     const size_t pe = ((size_t)t * a.hkv + h) * a.splits + split;
+    store_o_part(a.part_o, pe * G + g, oacc, inv, hf);
+    if (hf == 0) {
+      a.part_lse[pe * G + g] = lse_v;
+      a.part_l[pe * G + g] = 1.f;           // the partial output is already normalised
+      if (g == 0) a.cmap[pe] = (int)pe;
+    }
+  }
+}
+
+// Per-query lists, bf16: the G heads of one query over the listed blocks of a split, on two
+// waves that take the two key halves of every block (wave w: keys 64 w .. 64 w + 63), each with
+// its own running max, sum and output, merged once at the end; K and V are double-buffered in
+// LDS (128 KiB, one workgroup per CU). At the top of step j the workgroup waits for block j,
+// crosses its one barrier of the step and issues block j + 1 from all four waves, so a whole
+// block is in flight while block j is computed. The running max is raised only when a block's
+// max exceeds it by more than 2^8 in probability, as in the per-tile kernel below.
+template <int G>
+__global__ __launch_bounds__(256, 1) void attn_qd_kernel(QArgs a) {
+  __shared__ KVLds L[2];
+  __shared__ int vis[kMaxTopK];
+  __shared__ int n_vis;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const bool math = wave < 2;
+  const int kt0 = 2 * (wave & 1);
+  const int tq = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
+  if (tq >= a.total_q) return;
+  const int s = seq_of_row(a.cu_q, a.batch, tq);
+  const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
+  const bool valid = col < G && tq - sq.q0 < sq.nq;
+  const int hh = h * G + (col < G ? col : 0);
+  const int pos = sq.nk - sq.nq + (tq - sq.q0);
+  const int nb = (sq.nk + kBlock - 1) / kBlock;
+  const int32_t* list = a.lists + ((size_t)tq * a.hkv + h) * a.topk;
+
+  const float sl2 = a.scale_log2;
+  bf16x8 bq[8];
+  if (math)
+    load_q_operand<false>(bq, reinterpret_cast<const char*>(a.q) + ((size_t)tq * a.hq + hh) * kD * 2, hf);
+
+  const int per = (a.topk + a.splits - 1) / a.splits;
+  const int slot0 = split * per, slot1 = min(a.topk, slot0 + per);
+  if (tid < 64) visit_list(list, a.topk, slot0, slot1, nb, a.causal, pos, vis, &n_vis);
+  // every load so far (Q rows, list, sequence bounds) completes here, before any K/V load is
+  // issued: the compiler then has no load of its own pending inside the loop, where a wait of
+  // its would also cover the K/V loads in flight
+  if (math) hold_q(bq);
+  wait_vm<0>();
+  __syncthreads();
+  const int nv = n_vis;
+
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v);
+  const uint32_t kv_row = (uint32_t)a.hkv * kD;
+  const size_t kv_head = (size_t)sq.k0 * a.hkv + h;     // row of key 0 of the sequence, head h
+  auto dma = [&](int j) {
+    const int u0 = vis[j] * kBlock;
+    const size_t off = (kv_head + (size_t)u0 * a.hkv) * kD;
+    dma_rows<false>(L[j & 1].k, kp + off, kv_row, sq.nk - u0);
+    dma_rows<true>(L[j & 1].vt, vp + off, kv_row, sq.nk - u0);
+  };
+
+  const float ninf = -__builtin_inff();
+  // c_run: reference max in scaled (log2) units; l_run: this lane's share of the row sum
+  float c_run = ninf, l_run = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+
+  if (nv > 0) dma(0);
+  for (int j = 0; j < nv; ++j) {
+    wait_vm<0>();            // this thread's loads of block j landed
+    __syncthreads();         // ... everyone's; step j - 1 is done, its buffer free
+    if (j + 1 < nv) dma(j + 1);
+    if (math) {
+      const KVLds& B = L[j & 1];
+      const int u0 = vis[j] * kBlock;
+      f32x16 sc[2];
+      qk_half(B.k, bq, sc, kt0, col, hf);
+      int kmax = min(127, sq.nk - u0 - 1);
+      if (a.causal) kmax = min(kmax, pos - u0);
+      const float mb = mask_max_half(sc, kt0, kmax, __any(kmax < kt0 * 32 + 63), hf);
+      const float mbs = mb * sl2;                        // -inf stays -inf (sl2 > 0)
+      const bool grow = mbs > c_run + 8.f;
+      if (__any(grow)) {
+        const float c_new = grow ? mbs : c_run;
+        const float alpha = grow ? (c_run > ninf ? __builtin_amdgcn_exp2f(c_run - c_new) : 0.f) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        c_run = c_new;
+      }
+      u32x4 pk[2][2];
+      l_run += exp_pack_half(sc, sl2, c_run > ninf ? c_run : 0.f, pk);
+      pv_half_tr(B.vt, pk, oacc, kt0, lane);
+    }
+  }
+  l_run += shfl_xor_f(l_run, 32);            // the row's sum over the wave's keys
+
+  if (a.splits > 1 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0)
+    a.counters[0] = a.total_q * a.hkv * a.splits;
+  // merge the key halves: wave 1 hands its (max, sum, output) to wave 0 through LDS (no load
+  // is in flight: the last step issues none)
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(&L[0]);          // [4 dt][4][64 lanes][4]
+  float* xc = xo + 4 * 4 * 64 * 4;                      // [64 lanes] max, then sum
+  if (wave == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 w = {oacc[dt][4 * q], oacc[dt][4 * q + 1], oacc[dt][4 * q + 2], oacc[dt][4 * q + 3]};
+        *reinterpret_cast<f32x4*>(xo + ((dt * 4 + q) * 64 + lane) * 4) = w;
+      }
+    xc[lane] = c_run;
+    xc[64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (wave != 0 || !valid) return;
+  const float c1 = xc[lane], l1 = xc[64 + lane];
+  const float cm = fmaxf(c_run, c1);
+  const float w0 = c_run > ninf ? __builtin_amdgcn_exp2f(c_run - cm) : 0.f;
+  const float w1 = c1 > ninf ? __builtin_amdgcn_exp2f(c1 - cm) : 0.f;
+  const float l = w0 * l_run + w1 * l1;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(xo + ((dt * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[dt][4 * q + i] = w0 * oacc[dt][4 * q + i] + w1 * x[i];
+    }
+  const bool any = l > 0.f;
+  const float inv = any ? 1.f / l : 0.f;
+  const float lse_v = any ? (cm + log2f(l)) * 0.69314718055994531f : ninf;
+  const int g = hh - h * G;
+  if (a.splits == 1) {
+    store_o_row(a.o + ((size_t)tq * a.hq + hh) * kD, oacc, inv, hf);
+    if (hf == 0 && a.lse) a.lse[(size_t)tq * a.hq + hh] = lse_v;
+  } else {
+    const size_t pe = ((size_t)tq * a.hkv + h) * a.splits + split;
     store_o_part(a.part_o, pe * G + g, oacc, inv, hf);
     if (hf == 0) {
       a.part_lse[pe * G + g] = lse_v;
@@ -349,9 +446,7 @@ __global__ __launch_bounds__(512, 1) void attn_qt_kernel(QArgs a) {
       const char* src = kvb + head_off + (size_t)u0 * row_bytes;
 #pragma unroll
       for (int p = 0; p < 8; ++p)
-        __builtin_amdgcn_global_load_lds(
-            src + p * 16 * row_bytes + col_off[p & 1],
-            (__attribute__((address_space(3))) void*)(dst + p * 256 + half_wave * 64), 16, 0, 0);
+        lds_dma16(src + p * 16 * row_bytes + col_off[p & 1], dst + p * 256 + half_wave * 64);
     } else {
       const uint16_t* base = reinterpret_cast<const uint16_t*>(kvb + head_off + (size_t)u0 * row_bytes);
       if (v_part) dma_rows_t<true>(dst, base, row_bytes / 2, nk_rel, u);
@@ -374,6 +469,7 @@ __global__ __launch_bounds__(512, 1) void attn_qt_kernel(QArgs a) {
   }
   for (int j = 0; j < nv; ++j) {
     wait_vm<0>();                            // this thread's K(j) and V(j) landed
+    hold_q(bq);
     __syncthreads();                         // ... everyone's; step j-1 done by every wave
     const int u0 = vis(j) * kBlock;
     if (j + 1 < nv) {
@@ -440,6 +536,18 @@ __global__ __launch_bounds__(512, 1) void attn_qt_kernel(QArgs a) {
   if (hf == 0 && a.lse) a.lse[(size_t)t * a.hq + hh] = any ? (cm + log2f(l)) * 0.69314718055994531f : ninf;
 }
 
+hipError_t launch_qd_g(const QArgs& a, int group, dim3 grid, hipStream_t st) {
+  dim3 blk(256);
+  switch (group) {
+    case 1: hipLaunchKernelGGL(attn_qd_kernel<1>, grid, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(attn_qd_kernel<2>, grid, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL(attn_qd_kernel<4>, grid, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL(attn_qd_kernel<8>, grid, blk, 0, st, a); break;
+    default: hipLaunchKernelGGL(attn_qd_kernel<16>, grid, blk, 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <bool FP8>
 hipError_t launch_q_g(const QArgs& a, int group, dim3 grid, hipStream_t st) {
   dim3 blk(256);
@@ -498,9 +606,9 @@ hipError_t launch_attn_q(const msa_shape& s, const Geometry& g, const Layout& L,
   } else {
     if (s.total_q == 0) return hipSuccess;
     grid = dim3((unsigned)s.total_q, s.hkv, g.splits);
+    if (s.dtype == MSA_BF16) return launch_qd_g(a, g.group, grid, st);
   }
-  return s.dtype == MSA_FP8_E4M3 ? launch_q_g<true>(a, g.group, grid, st)
-                                 : launch_q_g<false>(a, g.group, grid, st);
+  return launch_q_g<true>(a, g.group, grid, st);
 }
 
 }  // namespace msa

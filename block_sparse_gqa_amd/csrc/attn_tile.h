@@ -198,10 +198,32 @@ __device__ __forceinline__ void pv_block(const KVLds& L, const u32x4 p[4][2], f3
 __device__ __forceinline__ int swz_v(int key) { return (key & 3) << 2; }
 
 // s_waitcnt vmcnt(n): direct-to-LDS loads are not tracked by the compiler's own waits.
+// The count has 6 bits: bits 3:0 of the immediate and bits 15:14.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory to LDS address `lds` + 16 * lane (`lds` wave-uniform),
+// as inline assembly. The compiler does not see these loads, so it adds no wait for them before
+// later LDS reads: with the builtin it waits for every direct-to-LDS load in flight, the next
+// block's included, before the first LDS read of the current block, which serialises the
+// prefetch with the math. The caller makes the data visible (wait_vm<n>() and a barrier).
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  const uint32_t a = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a)
+               : "memory", "m0");
+}
+
+// Marks the Q operand as used at this point. Called right after the caller has waited for
+// every load in flight, it places the compiler's own wait for the Q loads there instead of at
+// the first MFMA, which comes after the next block's loads have been issued (the compiler's
+// wait counts only the loads it knows of, so it would wait for those too).
+__device__ __forceinline__ void hold_q(bf16x8 bq[8]) {
+#pragma unroll
+  for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(bq[st]));
 }
 
 // One 128-row x 256-byte block (rows at or past nk_rel repeat row nk_rel - 1; the caller masks
@@ -218,9 +240,7 @@ __device__ __forceinline__ void dma_rows_t(u32x4* dst, const uint16_t* base, uin
     const int f = V ? swz_v(row0)
                     : ((row0 & 3) | ((p & 1) << 2) | (((row0 >> 2) & 1) << 3));
     const uint32_t r = (uint32_t)min(row, nk_rel - 1);
-    __builtin_amdgcn_global_load_lds(
-        base + r * row_stride + (uint32_t)((slot ^ f) * 8),
-        (__attribute__((address_space(3))) void*)(dst + p * 256 + wave * 64), 16, 0, 0);
+    lds_dma16(base + r * row_stride + (uint32_t)((slot ^ f) * 8), dst + p * 256 + wave * 64);
   }
 }
 
@@ -229,46 +249,6 @@ template <bool V>
 __device__ __forceinline__ void dma_rows(u32x4* dst, const uint16_t* base, uint32_t row_stride,
                                          int nk_rel) {
   dma_rows_t<V>(dst, base, row_stride, nk_rel, (int)threadIdx.x);
-}
-
-// O^T (+)= V^T P^T with V row-major in LDS. The LDS transpose load gives lane j of each
-// 16-lane group elements from the 16 rows x 4 columns its group's lanes address: lane s of
-// the group addresses key row k0 + s/4 at dims D(s%4) .. +3 with D = {0, 16, 4, 20} (+8 for
-// the group of lanes 16..31), and lane j receives dims D(j/4) + j%4 = rowperm(j) of keys
-// k0 .. k0+3, i.e. its A-operand row for four consecutive keys.
-template <bool INIT>
-__device__ __forceinline__ void pv_block_tr(const KVLds& L, const u32x4 p[4][2], f32x16 o[4],
-                                            int lane) {
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  asm volatile("" : "+v"(lane));
-  const int s = lane & 15, grp = (lane >> 4) & 1, hf = lane >> 5;
-  const int dsel = s & 3, k_lane = s >> 2;
-  const int d_lane = ((dsel & 1) << 4) + ((dsel >> 1) << 2) + 8 * grp;   // D(s%4) + 8*grp
-  // element (key 16*hf + k_lane, dim 32*dt + d_lane); chunk (dim / 8) ^ (4 * k_lane)
-  const unsigned short* vrow = reinterpret_cast<const unsigned short*>(L.vt);
-  const unsigned short* base[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    base[dt] = vrow + (16 * hf + k_lane) * 128 + (4 * (dt ^ k_lane) + (d_lane >> 3)) * 8 +
-               (d_lane & 7);
-#pragma unroll
-  for (int step = 0; step < 8; ++step) {
-    const int kt = step >> 1, ks = step & 1;
-    bf16x8 a[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      s4 r[2];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s4*)(base[dt] + (32 * kt + 8 * ks + 4 * h2) * 128));
-      a[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    const bf16x8 bp = as_bf16x8(p[kt][ks]);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-      o[dt] = mfma32(a[dt], bp, (INIT && step == 0) ? f32x16{} : o[dt]);
-  }
 }
 
 // ---- half blocks: a wave covering keys [32*kt0, 32*kt0 + 64) of a staged block
@@ -303,6 +283,11 @@ __device__ __forceinline__ void qk_half(const u32x4* kb, const bf16x8 bq[8], f32
 
 // O^T += V^T P^T over keys 32*kt0 .. +63 of the row-major V block in `vb` (layout of
 // dma_rows<true>): 16 MFMAs; p[i][ks] holds keys 32*(kt0 + i) + 16*(l/32) + 8*ks + 2j, +1.
+// The LDS transpose load gives lane j of each 16-lane group elements from the 16 rows x 4
+// columns its group's lanes address: lane s of the group addresses key row k0 + s/4 at dims
+// D(s%4) .. +3 with D = {0, 16, 4, 20} (+8 for the group of lanes 16..31), and lane j receives
+// dims D(j/4) + j%4 = rowperm(j) of keys k0 .. k0+3, i.e. its A-operand row for four
+// consecutive keys.
 __device__ __forceinline__ void pv_half_tr(const u32x4* vb, const u32x4 p[2][2], f32x16 o[4],
                                            int kt0, int lane) {
   typedef short s4 __attribute__((ext_vector_type(4)));

@@ -39,11 +39,14 @@ msa_status check_shape(const msa_shape* s) {
 }
 
 // Splits of each per-query list for the Q-outer kernel: the smallest power of two giving about
-// 512 workgroups (two per compute unit of a 256-CU part), so that each workgroup streams a few
-// blocks back to back. Shape-only, so the workspace size depends on the shape alone.
+// one workgroup per compute unit of a 256-CU part for bf16 (its kernel holds two blocks in
+// LDS, one workgroup per CU) and two for fp8 (one block, two workgroups per CU), so that each
+// workgroup streams its blocks back to back. Shape-only, so the workspace size depends on the
+// shape alone.
 int choose_splits(const msa_shape& s) {
+  const int64_t target = s.dtype == MSA_BF16 ? 256 : 512;
   int ns = 1;
-  while (ns * 2 <= s.topk && (int64_t)s.total_q * s.hkv * ns < 512) ns *= 2;
+  while (ns * 2 <= s.topk && (int64_t)s.total_q * s.hkv * ns < target) ns *= 2;
   return ns;
 }
 

@@ -264,9 +264,22 @@ def test_query_range_rule():
 
 
 def test_q_outer_workspace():
+    # bf16 per-query lists: splits up to one workgroup per CU of a 256-CU part (the bf16 kernel
+    # holds two blocks in LDS); 64 requests x 4 groups already fill it, so the output is
+    # written directly
     s = decode_shape()
     lay = msa.msa_workspace_layout_of(s, msa.MSA_Q_OUTER)
-    assert lay.slots >= 2                       # decode splits each list
+    assert lay.slots == 1 and lay.total <= 1024
+    few = msa.make_shape(batch=8, total_q=8, total_k=8 * 70000, max_q=1, max_k=131072,
+                         hq=64, hkv=4, topk=16, dp=64)
+    lay = msa.msa_workspace_layout_of(few, msa.MSA_Q_OUTER)
+    assert lay.slots == 8                       # 8 x 4 x 8 = 256 workgroups
+    assert lay.part_o - lay.part_lse >= 8 * 4 * lay.slots * 16 * 4
+    # fp8 (one block in LDS, two workgroups per CU): about 512 workgroups
+    f8 = msa.make_shape(batch=64, total_q=64, total_k=64 * 70000, max_q=1, max_k=131072,
+                        hq=64, hkv=4, topk=16, dp=64, dtype=msa.MSA_FP8_E4M3)
+    lay = msa.msa_workspace_layout_of(f8, msa.MSA_Q_OUTER)
+    assert lay.slots == 2
     assert lay.part_o - lay.part_lse >= 64 * 4 * lay.slots * 16 * 4
     tiles = msa.make_shape(batch=1, total_q=8192, total_k=8192, max_q=8192, max_k=8192, hq=16,
                            hkv=16, topk=16, causal=False, list_q=128)
