@@ -38,6 +38,15 @@ __device__ __forceinline__ void k_frags(const KVLds& L, bf16x8 a[4], int st, int
   for (int kt = 0; kt < 4; ++kt) a[kt] = as_bf16x8(L.k[(kt * 32 + rp) * 16 + cc]);
 }
 
+// V^T operands (A) of key-step s (keys 32kt + 16hf + 8ks .. +7, kt = s/2, ks = s%2) for the
+// 4 output-dim tiles, from a V^T block (row = head dim, 128 keys) in the layout of k_frags.
+__device__ __forceinline__ void v_frags(const u32x4* vt, bf16x8 a[4], int s, int rp, int sw,
+                                        int hf) {
+  const int cc = (4 * (s >> 1) + 2 * hf + (s & 1)) ^ sw;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) a[dt] = as_bf16x8(vt[(dt * 32 + rp) * 16 + cc]);
+}
+
 // exp2 of the 8 scores of key-step s, packed to bf16 into pk; their sum is added to l. The
 // sum is taken over the bf16-rounded weights (one bf16 dot product per pair), the exact
 // weights the PV product uses.
@@ -99,8 +108,9 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 // tile starts a new bucket, its K block is loaded at the start of the current tile into the
 // free slot (the V slot of the previous bucket, released by the barrier that opened the
 // current bucket) and its V block, after a barrier, into the K slot of the current bucket once
-// every wave has finished QK^T; the next tile starts after one more barrier. V stays
-// row-major and is read with the LDS transpose load. Output stores go through buffer
+// every wave has finished QK^T; the next tile starts after one more barrier. V comes from a
+// transposed copy (transpose_v_kernel, one pass over V before the attention kernel), so its
+// PV operands are plain 16-byte LDS reads like K's. Output stores go through buffer
 // descriptors whose record count covers the tile's real rows: stores of padding rows are
 // dropped by the hardware range check.
 //
@@ -126,9 +136,10 @@ struct KvTArgs {
   float* part_lse;
   float* part_l;
   uint16_t* part_o;
-  const uint16_t* vw;     // fp8: V widened to bf16 (exactly) in the workspace
+  const uint16_t* vw;     // bf16 V^T of each (group, key block) (fp8: widened exactly)
   int total_q, total_k, max_q, max_k;
   int hq, hkv, nb_max, n_r, n_phase, n_xcd, n_share, causal;
+  int nbt;                // blocks per group of the transposed V (see transpose_v_kernel)
 };
 
 // 16 bytes per lane from global memory to LDS address m0 + 16 * lane (m0 wave-uniform).
@@ -208,50 +219,22 @@ __device__ __forceinline__ TileD it_decode(const TileRaw& x, TileIt& it, const K
   return d;
 }
 
-// K (layout of k_frags) or V (row-major, transposed reads) of one block into an LDS slot by
-// the workgroup's 512 threads, 4 direct loads each: load p of wave w fills rows
+// A K block or a V^T block (128 rows of 256 bytes, the layout of k_frags and v_frags) into an
+// LDS slot by the workgroup's 512 threads, 4 direct loads each: load p of wave w fills rows
 // 32p + 4w .. +3, lane l fetching the chunk that belongs in its slot. Rows at or past nk_rel
-// repeat the last key (their scores are masked).
-template <bool V>
+// repeat the last one (K: keys past the sequence's end, whose scores are masked; a V^T block
+// has all 128 rows).
 __device__ __forceinline__ void dma_block(u32x4* dst, const uint16_t* base, uint32_t row_stride,
                                           int nk_rel, int wave, int lane) {
   const int slot = lane & 15;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int row = 32 * p + 4 * wave + (lane >> 4);
-    const int f = V ? swz_v(row) : swz(row);
+    const int f = swz(row);
     const uint32_t r = (uint32_t)min(row, nk_rel - 1);
     dma16s(base, (r * row_stride + (uint32_t)((slot ^ f) * 8)) * 2,
            lds_addr(dst + p * 512 + wave * 64));
   }
-}
-
-// V^T operands (A) of key-step s (keys 32kt + 16hf + 8ks .. +7, kt = s/2, ks = s%2) for the
-// 4 output-dim tiles, from the row-major V block by transpose loads; `vl` is the lane's
-// element offset within the slot (see pv_half_tr).
-__device__ __forceinline__ void v_frags_tr(const unsigned short* vb, bf16x8 a[4], int s,
-                                           const int vl[4]) {
-  typedef short s4 __attribute__((ext_vector_type(4)));
-  const int kt = s >> 1, ks = s & 1;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    s4 r[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-      r[h2] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s4*)(vb + vl[dt] + (32 * kt + 8 * ks + 4 * h2) * 128));
-    a[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
-  }
-}
-
-__device__ __forceinline__ void v_lane_offsets(int lane, int vl[4]) {
-  asm volatile("" : "+v"(lane));
-  const int s = lane & 15, grp = (lane >> 4) & 1, hf = lane >> 5;
-  const int dsel = s & 3, k_lane = s >> 2;
-  const int d_lane = ((dsel & 1) << 4) + ((dsel >> 1) << 2) + 8 * grp;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    vl[dt] = (16 * hf + k_lane) * 128 + (4 * (dt ^ k_lane) + (d_lane >> 3)) * 8 + (d_lane & 7);
 }
 
 // Query rows of one tile's entries for one wave (rows 32w .. 32w + 31 = entries
@@ -380,10 +363,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   const int xcd = blockIdx.x % a.n_xcd, j = blockIdx.x / a.n_xcd;
   const float sl2 = a.scale_log2;
   const uint16_t* const kb = reinterpret_cast<const uint16_t*>(a.k);
-  const uint16_t* const vb = reinterpret_cast<const uint16_t*>(a.v);
   const uint32_t kv_row = (uint32_t)a.hkv * kD;
-  int vl[4];
-  v_lane_offsets(lane, vl);
   int qo[4];
   q_lane_offsets(lane, qo);
   char* const part_o_b = reinterpret_cast<char*>(a.part_o);
@@ -397,6 +377,11 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   auto kv_base = [&](const uint16_t* base, const Seq& sq, int h, int b) {
     return base + ((size_t)(sq.k0 + b * kBlock) * a.hkv + h) * kD;
   };
+  // V^T of block b of phase p's sequence, group h (blocks numbered as transpose_v_kernel does)
+  auto vt_base = [&](int p, const Seq& sq, int h, int b) {
+    const int s = p / (a.n_r * a.hkv);
+    return a.vw + ((size_t)h * a.nbt + (size_t)(sq.k0 >> 7) + s + b) * (kD * kBlock);
+  };
 
   TileIt it{xcd, 0, 0};
   it_enter(it, a, j);
@@ -409,8 +394,8 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
   int h0;
   Seq sq0 = seq_of(d0.p, &h0);
   int ks = 0, vs = 1, fs = 2;
-  dma_block<false>(kvs[ks], kv_base(kb, sq0, h0, d0.b), kv_row, sq0.nk - d0.b * kBlock, wave, lane);
-  dma_block<true>(kvs[vs], kv_base(vb, sq0, h0, d0.b), kv_row, sq0.nk - d0.b * kBlock, wave, lane);
+  dma_block(kvs[ks], kv_base(kb, sq0, h0, d0.b), kv_row, sq0.nk - d0.b * kBlock, wave, lane);
+  dma_block(kvs[vs], vt_base(d0.p, sq0, h0, d0.b), kBlock, kD, wave, lane);
   TileQ<G> tq0, tq1;
   tq0.load(a.entry_q, d0, wave, rent);
   wait_vm0();
@@ -449,10 +434,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
     const TileD d3 = it_decode(r3, it, a, E);
     r3 = it_fetch(it, a, j);
     if (trans)
-      dma_block<false>(kvs[fs], kv_base(kb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock, wave,
+      dma_block(kvs[fs], kv_base(kb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock, wave,
                        lane);
     const u32x4* const kslot = kvs[ks];
-    const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs]);
+    const u32x4* const vslot = kvs[vs];
     // A wave whose 32 rows all lie past the tile's entries (the last tile of a bucket) skips
     // the tile's math and Q rows: it only stores the previous tile's output and takes part in
     // the K/V loads and barriers.
@@ -487,8 +472,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
       }
       if (trans) {
         __syncthreads();        // every wave is done with this bucket's K
-        dma_block<true>(kvs[ks], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
-                        wave, lane);
+        dma_block(kvs[ks], vt_base(d1.p, sq1, h1, d1.b), kBlock, kD, wave, lane);
       }
       // ---- row max of S(j)
       if (need_mask) {
@@ -507,12 +491,12 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
       const bool any = m > -__builtin_inff();
       const float c = any ? m * sl2 : 0.f;
       // ---- phase B: PV(j) | exp of the next key-step
-      v_frags_tr(vslot, fr[0], 0, vl);
+      v_frags(vslot, fr[0], 0, rp, sw, hf);
       u32x4 pk[8];
       float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        if (st < 7) v_frags_tr(vslot, fr[(st + 1) & 1], st + 1, vl);
+        if (st < 7) v_frags(vslot, fr[(st + 1) & 1], st + 1, rp, sw, hf);
         const bf16x8 bp = as_bf16x8(pk[st]);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -534,8 +518,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
       if (act1) tq1.dma(obuf, a.q, a.hq, h1, g, qo, lane);
       if (trans) {
         __syncthreads();
-        dma_block<true>(kvs[ks], kv_base(vb, sq1, h1, d1.b), kv_row, sq1.nk - d1.b * kBlock,
-                        wave, lane);
+        dma_block(kvs[ks], vt_base(d1.p, sq1, h1, d1.b), kBlock, kD, wave, lane);
       }
     }
     o_nrow = max(0, min(32, d0.n * G - wave * 32));
@@ -575,8 +558,9 @@ __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
 // 32 bytes; the result has the 32x32 layout of the bf16 MFMA. QK^T: A = K rows (key order
 // rowperm, as in the bf16 kernel), B = Q rows, D = 64 per MFMA (two MFMAs per 128 dims). The
 // probabilities are rounded to bf16 and PV runs on bf16 MFMA, as in the bf16 kernel, against
-// V widened to bf16 (exactly: every e4m3 value is a bf16 value) by a pass over V before the
-// attention kernel; the V descale divides the stored weight sum instead of scaling V.
+// V widened to bf16 (exactly: every e4m3 value is a bf16 value) and transposed by the pass over
+// V before the attention kernel; the V descale divides the stored weight sum instead of
+// scaling V.
 // Four 32 KiB slots (K in the first half of one): when the next tile opens a new bucket, its K
 // and V blocks are both requested at the start of the current tile into the two slots the
 // previous bucket left (released by the barrier that opened the current bucket), so a bucket
@@ -689,7 +673,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   const int col = lane & 31, hf = lane >> 5;
   const int r = wave * 32 + col;       // row of the tile
   const int rent = r / G, g = r % G;
-  const int rp = rowperm(col);
+  const int rp = rowperm(col), vsw = swz(rp);
   u32x4* const obuf = obuf_all[wave];
   const int xcd = blockIdx.x % a.n_xcd, j = blockIdx.x / a.n_xcd;
   const float sl2 = a.scale_log2 * a.descale[0] * a.descale[1];
@@ -699,12 +683,8 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   // log-sum-exp.
   const float inv_dv = 1.f / a.descale[2];
   const uint8_t* const kb = reinterpret_cast<const uint8_t*>(a.k);
-  const uint16_t* const vwb = a.vw;
   const uint32_t k_row = (uint32_t)a.hkv * kD;     // bytes between consecutive fp8 keys
-  const uint32_t v_row = (uint32_t)a.hkv * kD;     // bf16 elements between consecutive keys
   char* const part_o_b = reinterpret_cast<char*>(a.part_o);
-  int vl[4];
-  v_lane_offsets(lane, vl);
 
   auto seq_of = [&](int p, int* h) {
     *h = (p / a.n_r) % a.hkv;
@@ -714,8 +694,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   auto k_base = [&](const Seq& sq, int h, int bb) {
     return kb + ((size_t)(sq.k0 + bb * kBlock) * a.hkv + h) * kD;
   };
-  auto v_base = [&](const Seq& sq, int h, int bb) {
-    return vwb + ((size_t)(sq.k0 + bb * kBlock) * a.hkv + h) * kD;
+  // V^T (widened) of block bb of phase p's sequence, group h (numbered as transpose_v_kernel does)
+  auto vt_base = [&](int p, const Seq& sq, int h, int bb) {
+    const int s = p / (a.n_r * a.hkv);
+    return a.vw + ((size_t)h * a.nbt + (size_t)(sq.k0 >> 7) + s + bb) * (kD * kBlock);
   };
 
   TileIt it{xcd, 0, 0};
@@ -730,7 +712,7 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
   Seq sq0 = seq_of(d0.p, &h0);
   int ks_ = 0, vs_ = 1, fk_ = 2, fv_ = 3;
   dma_block8(kvs[ks_], k_base(sq0, h0, d0.b), k_row, sq0.nk - d0.b * kBlock, wave, lane);
-  dma_block<true>(kvs[vs_], v_base(sq0, h0, d0.b), v_row, sq0.nk - d0.b * kBlock, wave, lane);
+  dma_block(kvs[vs_], vt_base(d0.p, sq0, h0, d0.b), kBlock, kD, wave, lane);
   TileQ8<G> tq0, tq1;
   tq0.load(a.entry_q, d0, wave, rent);
   wait_vm0();
@@ -764,10 +746,10 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
     r3 = it_fetch(it, a, j);
     if (trans) {
       dma_block8(kvs[fk_], k_base(sq1, h1, d1.b), k_row, sq1.nk - d1.b * kBlock, wave, lane);
-      dma_block<true>(kvs[fv_], v_base(sq1, h1, d1.b), v_row, sq1.nk - d1.b * kBlock, wave, lane);
+      dma_block(kvs[fv_], vt_base(d1.p, sq1, h1, d1.b), kBlock, kD, wave, lane);
     }
     const u32x4* const kslot = kvs[ks_];
-    const unsigned short* const vslot = reinterpret_cast<const unsigned short*>(kvs[vs_]);
+    const u32x4* const vslot = kvs[vs_];
     // waves whose rows all lie past the tile's entries skip the tile's math and Q rows
     const bool act = d0.n * G > wave * 32;
     const bool act1 = d1.n * G > wave * 32;
@@ -811,12 +793,12 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
       const bool any = m > -__builtin_inff();
       const float c = any ? m * sl2 : 0.f;
       // ---- phase B: PV(j) on bf16 MFMA against the widened V | exp of the next key-step
-      v_frags_tr(vslot, fr[0], 0, vl);
+      v_frags(vslot, fr[0], 0, rp, vsw, hf);
       u32x4 pk[8];
       float l = exp_step(sc, 0, sl2, c, pk[0], 0.f);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        if (st < 7) v_frags_tr(vslot, fr[(st + 1) & 1], st + 1, vl);
+        if (st < 7) v_frags(vslot, fr[(st + 1) & 1], st + 1, rp, vsw, hf);
         const bf16x8 bp = as_bf16x8(pk[st]);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -866,20 +848,54 @@ __global__ __launch_bounds__(512, 1) void attn_kv_f8_kernel(KvTArgs a) {
                                         srd(a.part_l + o_row0, o_nrow * 4), col * 4, 0, 2);
 }
 
-// V (e4m3) widened to bf16, exactly: 16 elements per thread.
-__global__ __launch_bounds__(256) void widen_v_kernel(const uint8_t* __restrict__ v,
-                                                      uint16_t* __restrict__ vw, int64_t n16) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n16) return;
-  const u32x4 x = reinterpret_cast<const u32x4*>(v)[i];
-  u32x4 lo, hi;
-  const u32x2 a0 = fp8x4_to_bf16x4(x[0]), a1 = fp8x4_to_bf16x4(x[1]);
-  const u32x2 a2 = fp8x4_to_bf16x4(x[2]), a3 = fp8x4_to_bf16x4(x[3]);
-  lo = u32x4{a0[0], a0[1], a1[0], a1[1]};
-  hi = u32x4{a2[0], a2[1], a3[0], a3[1]};
-  u32x4* out = reinterpret_cast<u32x4*>(vw) + 2 * i;
-  __builtin_nontemporal_store(lo, out);
-  __builtin_nontemporal_store(hi, out + 1);
+// V of every (sequence, group, key block) transposed for the PV operands, which are then read
+// like K's (16 consecutive bytes per lane, no transpose loads); e4m3 V is widened to bf16 on
+// the way (exactly: every e4m3 value is a bf16 value):
+// vt[h][n][d][j] = V[k0 + 128 b + j][h][d] for block b of sequence s, n = k0 / 128 + s + b
+// (k0 the sequence's first key: the blocks of different sequences are disjoint and
+// n < ceil(total_k / 128) + batch), zero for keys past the sequence's end. One 128 x 128 tile
+// per workgroup through LDS.
+template <bool FP8>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const void* __restrict__ v,
+                                                          uint16_t* __restrict__ vt,
+                                                          const int32_t* cu_q, const int32_t* cu_k,
+                                                          int total_q, int total_k, int max_q,
+                                                          int max_k, int hkv, int nbt) {
+  constexpr int TS = kD + 2;            // LDS row pitch (elements) of the [key][dim] tile
+  __shared__ uint32_t t[kBlock * TS / 2];
+  const int b = blockIdx.x, h = blockIdx.y, s = blockIdx.z, tid = threadIdx.x;
+  const Seq sq = load_seq_clamped(cu_q, cu_k, s, total_q, total_k, max_q, max_k);
+  if (b * kBlock >= sq.nk) return;
+  const int c = tid & 15;               // 8 dims 8c .. 8c + 7 of a key
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int key = 16 * p + (tid >> 4);
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (b * kBlock + key < sq.nk) {
+      const size_t e = ((size_t)(sq.k0 + b * kBlock + key) * hkv + h) * kD + 8 * c;
+      if constexpr (FP8) {
+        const u32x2 y = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(v) + e);
+        const u32x2 lo = fp8x4_to_bf16x4(y[0]), hi = fp8x4_to_bf16x4(y[1]);
+        x = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(v) + e);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[(key * TS + 8 * c) / 2 + i] = x[i];
+  }
+  __syncthreads();
+  const uint16_t* th = reinterpret_cast<const uint16_t*>(t);
+  uint16_t* out = vt + ((size_t)h * nbt + (size_t)(sq.k0 >> 7) + s + b) * (kD * kBlock);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int d = 16 * p + (tid >> 4);
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)th[(8 * c + 2 * i) * TS + d] | ((uint32_t)th[(8 * c + 2 * i + 1) * TS + d] << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(out + d * kBlock + 8 * c));
+  }
 }
 
 template <int G>
@@ -930,15 +946,18 @@ hipError_t launch_attn_kv(const msa_shape& s, const Geometry& g, const Layout& L
   t.n_share = n_wg / t.n_xcd;
   t.causal = s.causal;
   t.vw = reinterpret_cast<const uint16_t*>(ws + L.v_wide);
+  t.nbt = (int)(cdiv(s.total_k, kBlock) + s.batch);
+  const dim3 tgrid((unsigned)g.nb_max, s.hkv, s.batch);
+  uint16_t* const vt = reinterpret_cast<uint16_t*>(ws + L.v_wide);
+  if (s.dtype == MSA_FP8_E4M3)
+    hipLaunchKernelGGL(transpose_v_kernel<true>, tgrid, dim3(256), 0, st, v, vt, cu_q, cu_k,
+                       s.total_q, s.total_k, s.max_q, s.max_k, s.hkv, t.nbt);
+  else
+    hipLaunchKernelGGL(transpose_v_kernel<false>, tgrid, dim3(256), 0, st, v, vt, cu_q, cu_k,
+                       s.total_q, s.total_k, s.max_q, s.max_k, s.hkv, t.nbt);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (s.dtype == MSA_FP8_E4M3) {
-    const int64_t n16 = (int64_t)s.total_k * s.hkv * s.d / 16;
-    if (n16 > 0) {
-      hipLaunchKernelGGL(widen_v_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st,
-                         reinterpret_cast<const uint8_t*>(v), reinterpret_cast<uint16_t*>(ws + L.v_wide),
-                         n16);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
     switch (g.group) {
       case 1: return launch_kv_f8_g<1>(t, n_wg, st);
       case 2: return launch_kv_f8_g<2>(t, n_wg, st);

@@ -143,7 +143,9 @@ Layout layout(const msa_shape& s, msa_mode mode) {
     L.tile_off = take((size_t)g.n_buckets * 4);
     L.phase_base = take((size_t)(g.n_phase + 1) * 8);
     L.tiles = take((size_t)g.n_tiles_max * 8);
-    L.v_wide = take(s.dtype == MSA_FP8_E4M3 ? (size_t)s.total_k * s.hkv * s.d * 2 : 0);
+    // bf16 V^T of every (group, key block) (e4m3 V widened exactly), blocks numbered per
+    // sequence from its first key: ceil(total_k / 128) + batch per group
+    L.v_wide = take((size_t)s.hkv * (cdiv(s.total_k, s.block) + s.batch) * s.block * s.d * 2);
   } else {
     L.slots = g.splits;
     L.masks = L.offsets = L.scan_sums = L.entry_q = L.entry_bucket = off;

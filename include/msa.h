@@ -115,8 +115,13 @@ typedef struct {
                           rows: dims 8c .. 8c+7 of row p at byte ((p / 8) * 16 + c) * 128 +
                           (p % 8) * 16, so that dims 8c .. 8c+7 of 8 consecutive rows fill one
                           128-byte line (the rows are padded to a multiple of 8) */
-  size_t v_wide;       /* bf16 [total_k, hkv, d]: V widened exactly from e4m3 for the fp8
-                          KV-outer kernel's PV product (size 0 otherwise) */
+  size_t v_wide;       /* KV-outer: bf16 V^T of every (kv head, key block), the PV operand
+                          of the attention kernels (e4m3 V widened exactly): block b of
+                          sequence s and kv head h is the 128 x 128 array
+                          [h][cu_k[s] / 128 + s + b][d][key], keys past the sequence's end
+                          zero; hkv * (ceil(total_k / 128) + batch) blocks. Written by
+                          msa_sparse_attn_fwd before its attention kernel (size 0 for
+                          Q-outer) */
   size_t total;        /* bytes needed */
   int32_t slots;       /* slots per (query, group) in cmap */
   int32_t n_words;     /* bitmap words (0 for Q-outer) */

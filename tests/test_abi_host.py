@@ -220,15 +220,21 @@ def test_kv_outer_workspace_layout_m3():
     assert msa.msa_workspace_size(s, msa.MSA_KV_OUTER) == lay.total
 
 
-def test_fp8_workspace_holds_the_widened_v():
-    """fp8 KV-outer: a bf16 copy of V (total_k * hkv * d * 2 bytes) before the partials; bf16:
-    no such region."""
-    s8 = m3_shape(dtype=msa.MSA_FP8_E4M3)
-    lay = msa.msa_workspace_layout_of(s8, msa.MSA_KV_OUTER)
-    assert lay.cmap < lay.v_wide < lay.part_lse and lay.v_wide % 256 == 0
-    assert lay.part_lse - lay.v_wide >= 32768 * 4 * 128 * 2
-    lb = msa.msa_workspace_layout_of(m3_shape(), msa.MSA_KV_OUTER)
-    assert lb.part_lse - lb.v_wide < 256        # empty (alignment only)
+def test_kv_outer_workspace_holds_the_transposed_v():
+    """KV-outer, bf16 and fp8 alike: a bf16 V^T of every (group, key block) before the partials,
+    hkv * (ceil(total_k / 128) + batch) blocks of 128 x 128 elements (the blocks of each
+    sequence numbered from its first key); Q-outer: no such region."""
+    for s in (m3_shape(), m3_shape(dtype=msa.MSA_FP8_E4M3)):
+        lay = msa.msa_workspace_layout_of(s, msa.MSA_KV_OUTER)
+        assert lay.cmap < lay.v_wide < lay.part_lse and lay.v_wide % 256 == 0
+        need = 4 * (32768 // 128 + 1) * 128 * 128 * 2
+        assert need <= lay.part_lse - lay.v_wide < need + 256
+    ragged = msa.make_shape(batch=3, total_q=700, total_k=1000, max_q=400, max_k=500, hq=8,
+                            hkv=2, topk=4, dp=32)
+    lay = msa.msa_workspace_layout_of(ragged, msa.MSA_KV_OUTER)
+    assert lay.part_lse - lay.v_wide >= 2 * (8 + 3) * 128 * 128 * 2
+    lq = msa.msa_workspace_layout_of(m3_shape(), msa.MSA_Q_OUTER)
+    assert lq.v_wide == 0 or lq.part_lse - lq.v_wide < 256
 
 
 def test_partial_memory_ratio_matches_the_pages():
