@@ -365,13 +365,20 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
       const bf16x8 k0 = read_tr_sw(kb, 16 * kk, 32 * kw, lane);
       dq = mfma32(s0, k0, dq);
     }
+    // stores: the lanes of dims 2c and 2c + 1 swap one value per pair of rows (DPP), so that
+    // each writes two adjacent dims of one row as a 4-byte piece (half the store instructions)
+    const bool odd = col & 1;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
+    for (int i = 0; i < 8; ++i) {
+      const float lo = dq[2 * i] * a.scale, hi = dq[2 * i + 1] * a.scale;
+      const float got = __int_as_float(
+          __builtin_amdgcn_mov_dpp(__float_as_int(odd ? lo : hi), 0xB1, 0xF, 0xF, false));
+      const int rr = 2 * i + (odd ? 1 : 0);
       const int n = row0 + 8 * (rr / 4) + 4 * hf + rr % 4;
       const int e = cur_et + n / G;
       if (e < cur_e1)
-        a.dq_part[((size_t)e * G + n % G) * kD + 32 * kw + col] =
-            (uint16_t)f32_to_bf16_bits(dq[rr] * a.scale);
+        *reinterpret_cast<uint32_t*>(a.dq_part + ((size_t)e * G + n % G) * kD + 32 * kw + (col & ~1)) =
+            odd ? pack_bf16x2(got, hi) : pack_bf16x2(lo, got);
     }
     if (have_next) store_slot(slot ^ 1, qv, ov);
     slot ^= 1;
