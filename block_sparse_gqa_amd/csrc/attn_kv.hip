@@ -347,7 +347,6 @@ __device__ __forceinline__ void store_o_tile(char* part_o_b, size_t o_row0, cons
 
 template <int G>
 __global__ __launch_bounds__(512, 1) void attn_kv_tiled_kernel(KvTArgs a) {
-  constexpr int MQ = 256 / G;          // entries per tile
   __shared__ u32x4 kvs[3][128 * 16];   // rotating K / V slots
   __shared__ u32x4 obuf_all[8][32 * 16];
 

@@ -179,7 +179,6 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(QArgs a) {
   if (tid < 64) visit_list(list, a.topk, slot0, slot1, nb, a.causal, pos_max, vis, &n_vis);
   __syncthreads();
   const int nv = n_vis;
-  const size_t kv_head = (size_t)sq.k0 * a.hkv + h;     // row of key 0 of the sequence, head h
 
   auto fold = [&](int u0, int nk_rel, auto&& pv) {
     f32x16 sacc[4];

@@ -480,7 +480,7 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a) {
   if (c1 - c0 < 2) return;
   const int b = cl % a.nb_max, g = (cl / a.nb_max) % a.hkv, s = cl / (a.nb_max * a.hkv);
   const Seq sq = load_seq_clamped(a.cu_q, a.cu_k, s, a.total_q, a.total_k, a.max_q, a.max_k);
-  for (int i = blockIdx.y * kPer + tid; i < (blockIdx.y + 1) * kPer; i += 256) {
+  for (int i = (int)blockIdx.y * kPer + tid; i < ((int)blockIdx.y + 1) * kPer; i += 256) {
     const int m = (i / (kD / 4)) % kBlock, which = i / (kBlock * kD / 4);
     const int u = b * kBlock + m;
     if (u >= sq.nk) continue;

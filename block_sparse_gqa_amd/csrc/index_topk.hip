@@ -121,7 +121,6 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   const bool qvalid = il < sq.nq;
   const int pos = sq.nk - sq.nq + il;
   const int c = floordiv(pos, kBlock);
-  const int nb = (sq.nk + kBlock - 1) / kBlock;
 
   const int jbeg = 0, jend = tile_blocks(sq, tile, causal);
 

@@ -81,7 +81,6 @@ __device__ __forceinline__ float fp8e4m3_to_f32(uint32_t b) {
 // value): the gfx950 scaled pack conversion with scale 1. Checked on the device against
 // fp8e4m3_to_f32 for all 256 codes in every byte position (NaN codes stay NaN).
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   u32x2 r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
   r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
