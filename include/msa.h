@@ -230,8 +230,9 @@ msa_status msa_select_tiles(const msa_shape* shape, int reps, const void* q, con
  * values are scaled by descale_v. Lists: topk_idx as described for list_q; entries outside
  * [0, ceil(Nk/block)), repeated entries, and (causal) blocks wholly after the query are
  * ignored.
- * KV_OUTER: builds the block -> query inverted index in the workspace, then one kernel loads
- * each selected block once and writes, for every (query-group, block) entry, contiguously
+ * KV_OUTER: builds the block -> query inverted index in the workspace and a transposed bf16
+ * copy of V (v_wide, the PV operand layout), then one kernel loads each selected block once
+ * and writes, for every (query-group, block) entry, contiguously
  * in entry order: the UNNORMALISED partial output (bf16, part_o: the block's attention output
  * times its weight sum), the weight sum (fp32, part_l) and the partial's LSE (fp32,
  * part_lse); see msa_workspace_layout. msa_combine, which must follow on the same stream,
@@ -248,8 +249,9 @@ msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void
                                size_t ws_bytes, void* o, float* lse, hipStream_t stream);
 
 /* KV-outer halves of msa_sparse_attn_fwd, for timing the inverted-index build and the
- * attention kernel separately. msa_plan(...) followed by msa_attn_main(...) with the same
- * arguments is exactly msa_sparse_attn_fwd(..., MSA_KV_OUTER, ...). */
+ * attention kernels separately (msa_attn_main: the transposed V copy, then the attention
+ * kernel). msa_plan(...) followed by msa_attn_main(...) with the same arguments is exactly
+ * msa_sparse_attn_fwd(..., MSA_KV_OUTER, ...). */
 msa_status msa_plan(const msa_shape* shape, const int32_t* topk_idx, const int32_t* cu_q,
                     const int32_t* cu_k, void* workspace, size_t ws_bytes, hipStream_t stream);
 msa_status msa_attn_main(const msa_shape* shape, const void* q, const void* k, const void* v,
