@@ -342,22 +342,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     if (have_next) load_data(nq, nqc, qv, ov, lse2, dsum);
     __syncthreads();                         // P, dS of every wave written
 
-    // dV += P^T dO, dK += dS^T Q for the wave's keys and dims 64 hw .. +63: contraction over
-    // the tile's 64 rows (rows 0-31 in the buffers of waves kw, rows 32-63 in those of kw + 4)
-#pragma unroll
-    for (int kr = 0; kr < 4; ++kr) {
-      const int src = kw + 4 * (kr >> 1);
-      const bf16x8 pa = read_tr_p(pbuf[src], 16 * (kr & 1), 0, lane);   // P^T[key][rows]
-      const bf16x8 sa = read_tr_p(sbuf[src], 16 * (kr & 1), 0, lane);   // dS^T[key][rows]
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const bf16x8 ob = read_tr_sw(os, 16 * kr, 64 * hw + 32 * dt, lane);   // dO[rows][dims]
-        const bf16x8 qb = read_tr_sw(qs, 16 * kr, 64 * hw + 32 * dt, lane);   // Q[rows][dims]
-        dv_acc[dt] = mfma32(pa, ob, dv_acc[dt]);
-        dk_acc[dt] = mfma32(sa, qb, dk_acc[dt]);
-      }
-    }
     // dQ of the wave's 32 rows, dims 32 kw .. +31, over all 128 keys: dS[rows][keys] K[keys][dims]
+    // (before dK / dV, so that its partial stores drain under the dK / dV products)
     f32x16 dq = {};
 #pragma unroll
     for (int kk = 0; kk < kBlock / 16; ++kk) {
@@ -379,6 +365,21 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
       if (e < cur_e1)
         *reinterpret_cast<uint32_t*>(a.dq_part + ((size_t)e * G + n % G) * kD + 32 * kw + (col & ~1)) =
             odd ? pack_bf16x2(got, hi) : pack_bf16x2(lo, got);
+    }
+    // dV += P^T dO, dK += dS^T Q for the wave's keys and dims 64 hw .. +63: contraction over
+    // the tile's 64 rows (rows 0-31 in the buffers of waves kw, rows 32-63 in those of kw + 4)
+#pragma unroll
+    for (int kr = 0; kr < 4; ++kr) {
+      const int src = kw + 4 * (kr >> 1);
+      const bf16x8 pa = read_tr_p(pbuf[src], 16 * (kr & 1), 0, lane);   // P^T[key][rows]
+      const bf16x8 sa = read_tr_p(sbuf[src], 16 * (kr & 1), 0, lane);   // dS^T[key][rows]
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8 ob = read_tr_sw(os, 16 * kr, 64 * hw + 32 * dt, lane);   // dO[rows][dims]
+        const bf16x8 qb = read_tr_sw(qs, 16 * kr, 64 * hw + 32 * dt, lane);   // Q[rows][dims]
+        dv_acc[dt] = mfma32(pa, ob, dv_acc[dt]);
+        dk_acc[dt] = mfma32(sa, qb, dk_acc[dt]);
+      }
     }
     if (have_next) store_slot(slot ^ 1, qv, ov);
     slot ^= 1;
