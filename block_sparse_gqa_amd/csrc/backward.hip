@@ -362,9 +362,12 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
       const int rr = 2 * i + (odd ? 1 : 0);
       const int n = row0 + 8 * (rr / 4) + 4 * hf + rr % 4;
       const int e = cur_et + n / G;
+      // streaming stores: each partial is read once, by bwd_dq_kernel; lines kept in L2 would
+      // only push out the tiles' Q and dO rows
       if (e < cur_e1)
-        *reinterpret_cast<uint32_t*>(a.dq_part + ((size_t)e * G + n % G) * kD + 32 * kw + (col & ~1)) =
-            odd ? pack_bf16x2(got, hi) : pack_bf16x2(lo, got);
+        __builtin_nontemporal_store(
+            odd ? pack_bf16x2(got, hi) : pack_bf16x2(lo, got),
+            reinterpret_cast<uint32_t*>(a.dq_part + ((size_t)e * G + n % G) * kD + 32 * kw + (col & ~1)));
     }
     // dV += P^T dO, dK += dS^T Q for the wave's keys and dims 64 hw .. +63: contraction over
     // the tile's 64 rows (rows 0-31 in the buffers of waves kw, rows 32-63 in those of kw + 4)
@@ -399,8 +402,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
       const int m = key0 + 8 * (rr / 4) + 4 * hf + rr % 4;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        pk[m * kD + 64 * hw + 32 * dt + col] = dk_acc[dt][rr] * a.scale;
-        pk[(kBlock + m) * kD + 64 * hw + 32 * dt + col] = dv_acc[dt][rr];
+        __builtin_nontemporal_store(dk_acc[dt][rr] * a.scale, pk + m * kD + 64 * hw + 32 * dt + col);
+        __builtin_nontemporal_store(dv_acc[dt][rr], pk + (kBlock + m) * kD + 64 * hw + 32 * dt + col);
       }
     }
     return;
@@ -831,7 +834,8 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
       for (int rr = 0; rr < 16; ++rr) {
         const int n = 8 * (rr / 4) + 4 * hf + rr % 4;
         const int e = cur_et + n / G;
-        if (n % G == 0 && e < cur_e1) pa.dqi_part[(size_t)e * DP + 32 * wave + col] = dq[rr] * G;
+        if (n % G == 0 && e < cur_e1)
+          __builtin_nontemporal_store(dq[rr] * G, pa.dqi_part + (size_t)e * DP + 32 * wave + col);
       }
     }
     if (have_next) store_slot(slot ^ 1, qv, pv);
@@ -852,7 +856,7 @@ __global__ __launch_bounds__(256, 1) void proxy_bwd_kernel(ProxyArgs pa) {
 #pragma unroll
     for (int dt = 0; dt < DP / 32; ++dt) {
       if (split)
-        pa.dki_part[((size_t)chunk * kBlock + m) * DP + 32 * dt + col] = acc[dt][rr];
+        __builtin_nontemporal_store(acc[dt][rr], pa.dki_part + ((size_t)chunk * kBlock + m) * DP + 32 * dt + col);
       else if (u < sq.nk)
         pa.dk_idx[((size_t)(sq.k0 + u) * a.hkv + g) * DP + 32 * dt + col] = acc[dt][rr];
     }
