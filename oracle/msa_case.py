@@ -12,6 +12,7 @@ import numpy as np
 
 from synth.msa_inputs import Case, widen
 from . import msa_ref as ref
+from . import mxfp4
 
 
 @dataclass
@@ -58,8 +59,13 @@ def run(case: Case, rows: np.ndarray | None = None, lists: np.ndarray | None = N
     # Chapter 4: the low-precision scorer compares quantised index vectors; the selection rule
     # is unchanged)
     dqi, dki = case.idx_descale
-    qi = widen(case.q_idx, dqi) if case.q_idx is not None else None
-    ki = widen(case.k_idx, dki) if case.k_idx is not None else None
+    if cfg.idx_dtype == "mxfp4":
+        # 4-bit codes times their E8M0 group scales ("Sparse Attention", Chapter 4, FP4)
+        qi = mxfp4.dequantize(case.q_idx.numpy(), case.q_idx_scale.numpy())
+        ki = mxfp4.dequantize(case.k_idx.numpy(), case.k_idx_scale.numpy())
+    else:
+        qi = widen(case.q_idx, dqi) if case.q_idx is not None else None
+        ki = widen(case.k_idx, dki) if case.k_idx is not None else None
     out_rows, out_sel, out_s, out_o, out_l = [], [], [], [], []
     for s, q0, q1, k0, k1, loc in seq_rows(case, rows):
         if loc.size == 0:

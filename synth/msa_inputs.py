@@ -97,6 +97,37 @@ def to_fp8(x: np.ndarray) -> tuple[torch.Tensor, float]:
     return t.to(torch.float8_e4m3fn), scale
 
 
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # magnitudes of codes 0..7
+
+
+def to_mxfp4(x: np.ndarray) -> tuple[torch.Tensor, torch.Tensor]:
+    """Prepares 4-bit index vectors (OCP MXFP4) from float32 rows [..., dp], dp % 32 == 0.
+
+    Every 32 consecutive elements share the scale 2^X with X = floor(log2(amax)) - 2 (the
+    largest E2M1 exponent), clamped to [-127, 127], X = 0 for an all-zero group; each element
+    x / 2^X is rounded to the nearest E2M1 magnitude, ties to the code with a zero mantissa
+    bit, magnitudes past 6 saturating to 6; the sign bit is set for negative x. Returns
+    (packed codes uint8 [..., dp / 2], element 2i in the low nibble of byte i; E8M0 scale codes
+    uint8 [..., dp / 32] = X + 127).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dp = x.shape[-1]
+    assert dp % 32 == 0, dp
+    g = x.reshape(x.shape[:-1] + (dp // 32, 32))
+    amax = np.abs(g).max(axis=-1)
+    _, e = np.frexp(amax)                         # amax = f * 2^e, f in [0.5, 1)
+    xexp = np.where(amax > 0, np.clip(e - 1 - 2, -127, 127), 0)
+    mag = np.abs(g) / np.exp2(xexp)[..., None]
+    mid = (E2M1_GRID[1:] + E2M1_GRID[:-1]) / 2
+    lo = np.searchsorted(mid, mag, side="left")
+    hi = np.searchsorted(mid, mag, side="right")
+    k = np.where((lo != hi) & (lo % 2 == 1), hi, lo)   # a tie takes the even code
+    codes = (k | np.where(g < 0, 8, 0)).astype(np.uint8).reshape(x.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return (torch.from_numpy(np.ascontiguousarray(packed)),
+            torch.from_numpy(np.ascontiguousarray((xexp + 127).astype(np.uint8))))
+
+
 def widen(t: torch.Tensor, descale: float = 1.0) -> np.ndarray:
     """Exact value of a stored bf16/fp8 tensor as float64 (times its descale)."""
     a = t.to(torch.float64).numpy()
@@ -119,7 +150,7 @@ class Config:
     dp: int = 64
     causal: bool = True
     dtype: str = "bf16"     # "bf16" or "fp8" for Q/K/V
-    idx_dtype: str = "bf16"  # "bf16" or "fp8" (e4m3fn, per-tensor scale) for the proxies
+    idx_dtype: str = "bf16"  # "bf16", "fp8" (e4m3fn, per-tensor scale) or "mxfp4" proxies
     lowrank: bool = False   # rank-8 per-group bias giving block reuse
     list_q: int = 1         # 1: per-query selection by the index branch; 128: given per-tile lists
     list_pool: int = 0      # per-tile lists: blocks drawn from range(list_pool)
@@ -165,6 +196,11 @@ CONFIGS = {
                            lowrank=True, dtype="fp8", idx_dtype="fp8"),
     "decode_i8": Config(name="decode_i8", batch=64, n_q=(), n_k=(), hq=64, hkv=4, topk=16, dp=64,
                         length_seed_draw=(64, 128, 1024), idx_dtype="fp8"),
+    # and with 4-bit (MXFP4) proxies ("Sparse Attention", Chapter 4: the FP4 scorer)
+    "m3_fp8_long_i4": _cfg("m3_fp8_long_i4", 131072, 131072, hq=64, hkv=4, topk=16, dp=64,
+                           lowrank=True, dtype="fp8", idx_dtype="mxfp4"),
+    "decode_i4": Config(name="decode_i4", batch=64, n_q=(), n_k=(), hq=64, hkv=4, topk=16, dp=64,
+                        length_seed_draw=(64, 128, 1024), idx_dtype="mxfp4"),
 }
 
 
@@ -193,12 +229,14 @@ class Case:
     k: torch.Tensor             # [Tk, Hkv, D]
     v: torch.Tensor             # [Tk, Hkv, D]
     descale: tuple              # (dq, dk, dv); (1,1,1) for bf16
-    q_idx: Optional[torch.Tensor] = None   # [Tq, Hkv, dp] bf16 or float8_e4m3fn
+    q_idx: Optional[torch.Tensor] = None   # [Tq, Hkv, dp] bf16 / float8_e4m3fn, mxfp4: uint8 [.., dp/2]
     k_idx: Optional[torch.Tensor] = None   # [Tk, Hkv, dp]
     lists: Optional[np.ndarray] = None     # [Tq/list_q, Hkv, K] int32 for given lists
     softmax_scale: float = 0.0
     meta: dict = field(default_factory=dict)
     idx_descale: tuple = (1.0, 1.0)        # (descale of q_idx, of k_idx); (1, 1) for bf16
+    q_idx_scale: Optional[torch.Tensor] = None   # mxfp4: E8M0 codes uint8 [Tq, Hkv, dp / 32]
+    k_idx_scale: Optional[torch.Tensor] = None   # mxfp4: [Tk, Hkv, dp / 32]
 
     @property
     def total_q(self) -> int:
@@ -299,6 +337,7 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
         with_proxies = cfg.list_q == 1
     q_idx = k_idx = None
     idx_descale = (1.0, 1.0)
+    q_isc = k_isc = None
     if with_proxies:
         if cfg.proxy == "grid":
             qi = grid_f32(_stream(seed, "q_idx"), (tq, hkv, dp))
@@ -319,6 +358,9 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
             q_idx, dqi = to_fp8(qi)
             k_idx, dki = to_fp8(ki)
             idx_descale = (dqi, dki)
+        elif cfg.idx_dtype == "mxfp4":
+            q_idx, q_isc = to_mxfp4(qi)
+            k_idx, k_isc = to_mxfp4(ki)
         elif cfg.idx_dtype == "bf16":
             q_idx, k_idx = to_bf16(qi), to_bf16(ki)
         else:
@@ -330,7 +372,8 @@ def make_case(cfg: Config | str, seed: int = 0, with_proxies: Optional[bool] = N
 
     return Case(cfg=cfg, seed=seed, cu_q=cu_q, cu_k=cu_k, q=qs, k=ks, v=vs, descale=descale,
                 q_idx=q_idx, k_idx=k_idx, lists=lists,
-                softmax_scale=1.0 / math.sqrt(d), idx_descale=idx_descale)
+                softmax_scale=1.0 / math.sqrt(d), idx_descale=idx_descale,
+                q_idx_scale=q_isc, k_idx_scale=k_isc)
 
 
 def tile_lists(cfg: Config, cu_q: np.ndarray, seed: int) -> np.ndarray:
