@@ -33,6 +33,7 @@ from synth import msa_inputs as mi    # noqa: E402
 PEAK_HBM = 8.0e12            # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15           # dense bf16 MFMA FLOP/s
 PEAK_FP8 = 5.0e15            # dense fp8 MFMA FLOP/s
+PEAK_FP4 = 10.1e15           # dense fp4 MFMA FLOP/s
 CSRC = "block_sparse_gqa_amd/csrc"
 # sources each call's kernels are built from (a traffic figure is kept only while they are
 # unchanged)
@@ -66,6 +67,11 @@ WORKLOADS = {
     "m3_fp8_long_i8": ("m3_fp8_long_i8", "long-context fp8 MSA prefill as m3_fp8_long, proxies "
                                          "fp8 e4m3 with per-tensor scales"),
     "decode_i8": ("decode_i8", "MSA decode as decode, proxies fp8 e4m3 with per-tensor scales"),
+    # and with 4-bit MXFP4 proxies (E2M1 codes, one E8M0 scale per 32 elements)
+    "m3_fp8_long_i4": ("m3_fp8_long_i4", "long-context fp8 MSA prefill as m3_fp8_long, proxies "
+                                         "MXFP4 (4-bit, one scale per 32 elements)"),
+    "decode_i4": ("decode_i4", "MSA decode as decode, proxies MXFP4 (4-bit, one scale per 32 "
+                               "elements)"),
 }
 
 
@@ -117,7 +123,7 @@ def index_work(cfg, cu_q, cu_k) -> tuple[float, float]:
     """(proxy FLOPs, proxy bytes) the index branch must do: 2*dp per (query, group, key) over
     the keys of every visible block other than the local one; q_idx and those k_idx rows once
     (eb bytes per element), plus the lists written."""
-    eb = 1.0 if cfg.idx_dtype == "fp8" else 2.0
+    eb = {"fp8": 1.0, "mxfp4": 0.5 + 1.0 / 32}.get(cfg.idx_dtype, 2.0)
     flops, kbytes = 0.0, 0.0
     for s in range(len(cu_q) - 1):
         nq = int(cu_q[s + 1] - cu_q[s])
@@ -531,6 +537,8 @@ def prepare(workload: str, seed: int, mode_name: str, dev: str) -> dict:
     c["q"], c["k"], c["v"] = up(case.q), up(case.k), up(case.v)
     c["q_idx"], c["k_idx"] = up(case.q_idx), up(case.k_idx)
     c["idx8"] = cfg.idx_dtype == "fp8"
+    c["idx4"] = cfg.idx_dtype == "mxfp4"
+    c["q_isc"], c["k_isc"] = up(case.q_idx_scale), up(case.k_idx_scale)
     c["idx_descale"] = (torch.tensor(case.idx_descale, dtype=torch.float32, device=dev)
                         if c["idx8"] else None)
     c["cu_q"] = torch.from_numpy(case.cu_q).to(dev)
@@ -573,6 +581,9 @@ def make_step(c: dict):
         elif given is None and idx8:
             msa.msa_index_topk_fp8(shape, c["q_idx"], c["k_idx"], c["idx_descale"], cu_q, cu_k,
                                    topk, None, c["iws"])
+        elif given is None and c["idx4"]:
+            msa.msa_index_topk_mxfp4(shape, c["q_idx"], c["q_isc"], c["k_idx"], c["k_isc"], cu_q,
+                                     cu_k, topk, None, c["iws"])
         elif given is None:
             msa.msa_index_topk(shape, c["q_idx"], c["k_idx"], cu_q, cu_k, topk, None, c["iws"])
         if given is None and evs:
@@ -611,6 +622,10 @@ def call_fns(c: dict) -> dict:
         fns["index"] = lambda: msa.msa_index_topk_fp8(shape, c["q_idx"], c["k_idx"],
                                                       c["idx_descale"], cu_q, cu_k, topk, None,
                                                       c["iws"])
+    elif c["given"] is None and c["idx4"]:
+        fns["index"] = lambda: msa.msa_index_topk_mxfp4(shape, c["q_idx"], c["q_isc"],
+                                                        c["k_idx"], c["k_isc"], cu_q, cu_k,
+                                                        topk, None, c["iws"])
     elif c["given"] is None:
         fns["index"] = lambda: msa.msa_index_topk(shape, c["q_idx"], c["k_idx"], cu_q, cu_k,
                                                   topk, None, c["iws"])
@@ -712,7 +727,7 @@ def run_forward(c: dict, steps: int, warmup: int, ceil: dict | None) -> dict:
                             * 128 * 2 + c["n_lists"] * cfg.hkv * cfg.topk * 4)
     elif given is None:
         ifl, ib = index_work(cfg, case.cu_q, case.cu_k)
-        pk = PEAK_FP8 if cfg.idx_dtype == "fp8" else PEAK_BF16
+        pk = {"fp8": PEAK_FP8, "mxfp4": PEAK_FP4}.get(cfg.idx_dtype, PEAK_BF16)
         kr["index"] = roof(kms["index"], "mfma", ifl, pk) if ifl / ib > pk / PEAK_HBM else \
             roof(kms["index"], "hbm", ib)
     if kv:

@@ -25,6 +25,19 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kIndexTileQ = 256;   // queries per workgroup of the tile kernel (64 per wave)
 
+// Proxy precisions: bf16, OCP fp8 e4m3 with per-tensor descales, OCP MXFP4 (E2M1 codes, two
+// per byte with the even element in the low nibble, one E8M0 scale byte per 32 elements).
+enum : int { kPrBf16 = 0, kPrFp8 = 1, kPrFp4 = 2 };
+// bytes of one proxy row of DP elements
+template <int PR>
+constexpr int proxy_row_bytes(int dp) {
+  return PR == kPrBf16 ? 2 * dp : (PR == kPrFp8 ? dp : dp / 2);
+}
+// E8M0 code -> its power of two (code 0: 2^-127, a subnormal)
+__device__ __forceinline__ float e8m0_to_f32(unsigned e) {
+  return e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
+}
+
 // Blocks the tile kernel scores for query tile `tile` of a sequence: those before the local
 // block of the tile's last query (causal), or all of them.
 __device__ __forceinline__ int tile_blocks(const Seq& sq, int tile, int causal) {
@@ -71,6 +84,12 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, f32x16{}, 0, 0, 0, 127, 0, 127);
 }
+// The same MFMA on MXFP4 operands: lane l supplies 32 E2M1 codes (16 bytes; the instruction
+// reads four registers) of row l % 32 at contraction indices 32 (l / 32) .. +31, which is one
+// scale group, and that group's E8M0 scale byte (sa for A, sb for B).
+__device__ __forceinline__ f32x16 mfma_f4(const i32x8& a, const i32x8& b, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, f32x16{}, 4, 4, 0, sa, 0, sb);
+}
 __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -83,17 +102,24 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 // one 8-bit MFMA per 32 x 32 score tile over the whole proxy dim (dp = 32 fills the upper
 // half of the 64-long contraction with zeros); scores are the raw dot products times the two
 // descales, applied where they are written (a positive factor does not change the order).
-template <int DP, bool FP8>
+// FP4: MXFP4 proxies ("Sparse Attention", Chapter 4: the scorer on 4-bit index vectors), one
+// scaled 4-bit MFMA per score tile, each lane's scale byte beside its 32 codes; the key
+// blocks' scale bytes are read into registers one pair of blocks ahead.
+template <int DP, int PR>
 __global__ __launch_bounds__(256) void index_tile_kernel(
     const void* __restrict__ q_idx_, const void* __restrict__ k_idx_,
+    const uint8_t* __restrict__ q_sc, const uint8_t* __restrict__ k_sc,
     const float* __restrict__ descale_idx, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_score, int hkv, int topk, int causal, int total_q, int total_k,
     int max_q, int max_k, int one_round) {
-  constexpr int EB = FP8 ? 1 : 2;  // bytes per proxy element
-  constexpr int CH = DP * EB / 16; // 16-byte chunks per proxy key row
+  constexpr bool FP8 = PR == kPrFp8, FP4 = PR == kPrFp4;
+  constexpr int RB = proxy_row_bytes<PR>(DP);   // bytes per proxy row
+  constexpr int CH = RB / 16;      // 16-byte chunks per proxy key row
   constexpr int STEPS = DP / 16;   // bf16 MFMA k-steps over the proxy dim
-  constexpr int PER_T = 128 * CH / 256;   // direct-to-LDS loads per thread per block
+  constexpr int NCK = 128 * CH;    // chunks per key block
+  constexpr int PER_T = NCK >= 256 ? NCK / 256 : 1;   // direct-to-LDS loads per thread per block
+  constexpr int NSC = DP / 32;     // FP4: scale bytes per proxy row
   const char* const q_idx = reinterpret_cast<const char*>(q_idx_);
   const char* const k_idx = reinterpret_cast<const char*>(k_idx_);
   constexpr int NBUF = 4;          // ring of key blocks: two pairs
@@ -126,12 +152,23 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
 
   bf16x8 bq[2][STEPS];
   i32x8 bq8[2];
+  int qsc[2] = {127, 127};   // FP4: this lane's query scale byte per half
 #pragma unroll
   for (int qh = 0; qh < 2; ++qh) {
     const int iq = q_wave + qh * 32 + col;
     const bool ok = iq < sq.nq;
-    const char* qrow = q_idx + ((size_t)(sq.q0 + (ok ? iq : 0)) * hkv + h) * DP * EB;
-    if constexpr (FP8) {
+    const size_t qr = (size_t)(sq.q0 + (ok ? iq : 0)) * hkv + h;
+    const char* qrow = q_idx + qr * RB;
+    if constexpr (FP4) {
+      // bytes 16 hf .. 16 hf + 15 of the row: scale group hf (dp = 32: half 1 holds zeros)
+      u32x4 w = {0u, 0u, 0u, 0u};
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      if (ok && (DP == 64 || hf == 0)) {
+        w = *reinterpret_cast<const u32x4*>(qrow + 16 * hf);
+        qsc[qh] = q_sc[qr * NSC + hf];
+      }
+      bq8[qh] = cat8(w, z);
+    } else if constexpr (FP8) {
       // bytes 32 hf .. 32 hf + 31 of the row (dp = 32: the lanes of half 1 hold zeros)
       u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
       if (ok && (DP == 64 || hf == 0)) {
@@ -161,9 +198,10 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
   // swizzle term (row / 2) % CH is the same for all of them.
   const unsigned row0 = (unsigned)tid / CH;
   const unsigned cc0 = ((unsigned)tid % CH) ^ ((row0 >> 1) & (CH - 1));
-  const size_t krow = (size_t)hkv * DP * EB;            // bytes between consecutive keys
-  const char* const kh = k_idx + (size_t)h * DP * EB + cc0 * 16;
+  const size_t krow = (size_t)hkv * RB;                 // bytes between consecutive keys
+  const char* const kh = k_idx + (size_t)h * RB + cc0 * 16;
   auto dma_block = [&](int j) {
+    if (NCK < 256 && wave >= NCK / 64) return;   // fewer chunks than threads (fp4, dp = 32)
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
       const unsigned row = row0 + (256 / CH) * p;
@@ -175,19 +213,55 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
     }
   };
 
+  // FP4: the scale bytes this lane's K operands need in block j (key rows kt * 32 + col,
+  // scale group hf; the last key repeats past the end, like the rows)
+  int ksc[2][4], ksc_next[2][4];
+  auto load_ksc = [&](int j, int (&dst)[4]) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int u = min(j * kBlock + kt * 32 + col, sq.nk - 1);
+      dst[kt] = (DP == 64 || hf == 0) ? (int)k_sc[((size_t)(sq.k0 + u) * hkv + h) * NSC + hf]
+                                      : 127;
+    }
+  };
+
   // Blocks go through the ring in pairs: pair (jp, jp + 1) is scored while the next pair
   // loads into the two slots the previous pair has just left, so one wait and one barrier
   // serve two blocks.
   for (int j = jbeg; j < min(jend, jbeg + 2); ++j) dma_block(j);
+  // (constant register indices and clamped block numbers: a load into a runtime-indexed
+  // register array would be waited for at once, together with the block loads before it)
+  if constexpr (FP4) {
+    if (jend > jbeg) {
+      load_ksc(jbeg, ksc[0]);
+      load_ksc(min(jbeg + 1, jend - 1), ksc[1]);
+    }
+  }
   for (int jp = jbeg; jp < jend; jp += 2) {
     wait_vm<0>();      // this thread's parts of the pair have landed (nothing else in flight)
     __syncthreads();   // every thread's parts are in LDS; the previous pair's slots are free
     for (int j = jp + 2; j < min(jp + 4, jend); ++j) dma_block(j);
+    if constexpr (FP4) {
+      load_ksc(min(jp + 2, jend - 1), ksc_next[0]);
+      load_ksc(min(jp + 3, jend - 1), ksc_next[1]);
+    }
     for (int j = jp; j < min(jp + 2, jend); ++j) {
     const int buf = j % NBUF;
 
     f32x16 acc[2][4];
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int row = kt * 32 + col;
+        const int sw = (row >> 1) & (CH - 1);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 w = kl[buf][row * CH + ((DP == 64 ? hf : 0) ^ sw)];
+        const i32x8 ka = (DP == 64 || hf == 0) ? cat8(w, z) : cat8(z, z);
+        const int sa = (j - jp) ? ksc[1][kt] : ksc[0][kt];
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) acc[qh][kt] = mfma_f4(ka, bq8[qh], sa, qsc[qh]);
+      }
+    } else if constexpr (FP8) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const int row = kt * 32 + col;
@@ -237,6 +311,12 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
       if (ins) tl.insert(mx, j);
     }
     }
+    if constexpr (FP4) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) ksc[b][kt] = ksc_next[b][kt];
+    }
   }
 
   if (qvalid) {
@@ -254,16 +334,19 @@ __global__ __launch_bounds__(256) void index_tile_kernel(
 // the groups' interleaved proxy-key rows of the same keys together, i.e. one contiguous span
 // of memory (the scan is bound by HBM bandwidth). Dot products on the VALUs; the chunk's list
 // of each group (merged in LDS over the waves sharing the group) goes to the workspace.
-template <int DP, bool FP8>
+template <int DP, int PR>
 __global__ __launch_bounds__(256) void index_split_kernel(
     const void* __restrict__ q_idx_, const void* __restrict__ k_idx_,
+    const uint8_t* __restrict__ q_sc, const uint8_t* __restrict__ k_sc,
     const float* __restrict__ descale_idx, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, float* __restrict__ part_sc, int32_t* __restrict__ part_id,
     int hkv, int max_q, int causal, int n_chunks, int chunk_blocks, int total_q, int total_k,
     int max_k) {
-  constexpr int EB = FP8 ? 1 : 2;  // bytes per proxy element
-  constexpr int VPL = 16 / EB;     // proxy elements per lane (16 bytes)
-  constexpr int LPK = DP / VPL;    // lanes per key row
+  constexpr bool FP8 = PR == kPrFp8, FP4 = PR == kPrFp4;
+  constexpr int RB = proxy_row_bytes<PR>(DP);   // bytes per proxy row
+  constexpr int VPL = FP4 ? 32 : (FP8 ? 16 : 8);  // proxy elements per lane (16 bytes)
+  constexpr int LPK = RB / 16;     // lanes per key row
+  constexpr int NSC = DP / 32;     // FP4: scale bytes per row (lane dc holds scale group dc)
   constexpr int KPI = 64 / LPK;    // keys per wave instruction
   const char* const q_idx = reinterpret_cast<const char*>(q_idx_);
   const char* const k_idx = reinterpret_cast<const char*>(k_idx_);
@@ -287,11 +370,25 @@ __global__ __launch_bounds__(256) void index_split_kernel(
   const int kk = lane / LPK, dc = lane % LPK;
 
   // this wave's best blocks of group h over blocks j0 + sub, j0 + sub + wph, ...
-  // the 16 bytes of a lane as VPL floats (bf16, or e4m3 codes)
+  // the 16 bytes of a lane as VPL floats (bf16, e4m3 codes or E2M1 codes, unscaled)
   auto unpack = [](const u32x4& w, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if constexpr (FP8) {
+      if constexpr (FP4) {
+        // byte b of the word: elements 2b (low nibble) and 2b + 1
+        const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.f, 0);
+        const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.f, 1);
+        const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.f, 2);
+        const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[i], 1.f, 3);
+        f[8 * i] = v0[0];
+        f[8 * i + 1] = v0[1];
+        f[8 * i + 2] = v1[0];
+        f[8 * i + 3] = v1[1];
+        f[8 * i + 4] = v2[0];
+        f[8 * i + 5] = v2[1];
+        f[8 * i + 6] = v3[0];
+        f[8 * i + 7] = v3[1];
+      } else if constexpr (FP8) {
         const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
         const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
         f[4 * i] = lo[0];
@@ -306,11 +403,14 @@ __global__ __launch_bounds__(256) void index_split_kernel(
   };
   auto scan = [&](int h, int sub, TopList& tl) {
     float qv[VPL];
+    float qs = 1.f;   // FP4: the query's scale of group dc
     {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (qvalid)
-        w = *reinterpret_cast<const u32x4*>(q_idx + (((size_t)(sq.q0 + il) * hkv + h) * DP) * EB +
-                                            dc * 16);
+      const size_t qr = (size_t)(sq.q0 + il) * hkv + h;
+      if (qvalid) {
+        w = *reinterpret_cast<const u32x4*>(q_idx + qr * RB + dc * 16);
+        if constexpr (FP4) qs = e8m0_to_f32(q_sc[qr * NSC + dc]);
+      }
       unpack(w, qv);
     }
     tl.init();
@@ -319,13 +419,17 @@ __global__ __launch_bounds__(256) void index_split_kernel(
       float mx = kNegInf;
       constexpr int IT = kBlock / KPI;
       u32x4 kvv[IT];
+      unsigned ksv[IT];
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int u = j * kBlock + it * KPI + kk;
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (u < sq.nk)
-          w = *reinterpret_cast<const u32x4*>(k_idx + (((size_t)(sq.k0 + u) * hkv + h) * DP) * EB +
-                                              dc * 16);
+        ksv[it] = 127u;
+        if (u < sq.nk) {
+          const size_t kr = (size_t)(sq.k0 + u) * hkv + h;
+          w = *reinterpret_cast<const u32x4*>(k_idx + kr * RB + dc * 16);
+          if constexpr (FP4) ksv[it] = k_sc[kr * NSC + dc];
+        }
         kvv[it] = w;
       }
 #pragma unroll
@@ -335,6 +439,9 @@ __global__ __launch_bounds__(256) void index_split_kernel(
         float dot = 0.f;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) dot = fmaf(qv[i], kv[i], dot);
+        // FP4: the group's products are exact and so is their sum (multiples of 1/4 below
+        // 2^11); the two scales are powers of two, so only the sum over groups rounds
+        if constexpr (FP4) dot = dot * qs * e8m0_to_f32(ksv[it]);
         dot = group_sum<LPK>(dot);
         const int u = j * kBlock + it * KPI + kk;
         if (u >= sq.nk) dot = kNegInf;
@@ -514,52 +621,65 @@ static hipError_t launch_index_merge(const msa_shape& s, const float* part_sc,
   return hipGetLastError();
 }
 
-template <int DP, bool FP8>
-static void launch_tile_t(const msa_shape& s, dim3 grid, const void* q_idx, const void* k_idx,
-                          const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
-                          int32_t* topk_idx, float* topk_score, int one_round, hipStream_t st) {
-  hipLaunchKernelGGL((index_tile_kernel<DP, FP8>), grid, dim3(256), 0, st, q_idx, k_idx,
-                     descale_idx, cu_q, cu_k, topk_idx, topk_score, s.hkv, s.topk, s.causal,
-                     s.total_q, s.total_k, s.max_q, s.max_k, one_round);
+template <int DP, int PR>
+static void launch_tile_t(const msa_shape& s, dim3 grid, const IndexProxies& px,
+                          const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                          float* topk_score, int one_round, hipStream_t st) {
+  hipLaunchKernelGGL((index_tile_kernel<DP, PR>), grid, dim3(256), 0, st, px.q_idx, px.k_idx,
+                     px.q_scale, px.k_scale, px.descale, cu_q, cu_k, topk_idx, topk_score, s.hkv,
+                     s.topk, s.causal, s.total_q, s.total_k, s.max_q, s.max_k, one_round);
 }
 
-hipError_t launch_index_tile(const msa_shape& s, bool fp8, const void* q_idx, const void* k_idx,
-                             const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
-                             int32_t* topk_idx, float* topk_score, hipStream_t st) {
+template <int PR>
+static void launch_tile_p(const msa_shape& s, dim3 grid, const IndexProxies& px,
+                          const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                          float* topk_score, int one_round, hipStream_t st) {
+  if (s.dp == 64)
+    launch_tile_t<64, PR>(s, grid, px, cu_q, cu_k, topk_idx, topk_score, one_round, st);
+  else
+    launch_tile_t<32, PR>(s, grid, px, cu_q, cu_k, topk_idx, topk_score, one_round, st);
+}
+
+hipError_t launch_index_tile(const msa_shape& s, const IndexProxies& px, const int32_t* cu_q,
+                             const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
+                             hipStream_t st) {
   const int tiles = (s.max_q + kIndexTileQ - 1) / kIndexTileQ;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, s.hkv, s.batch);
   const int one_round = (int64_t)tiles * s.hkv * s.batch <= 2 * (int64_t)device_cu_count();
-  if (fp8) {
-    if (s.dp == 64)
-      launch_tile_t<64, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
-                              topk_score, one_round, st);
-    else
-      launch_tile_t<32, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
-                              topk_score, one_round, st);
-  } else {
-    if (s.dp == 64)
-      launch_tile_t<64, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
-                               topk_score, one_round, st);
-    else
-      launch_tile_t<32, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx,
-                               topk_score, one_round, st);
+  switch (px.prec) {
+    case kIdxFp8:
+      launch_tile_p<kPrFp8>(s, grid, px, cu_q, cu_k, topk_idx, topk_score, one_round, st);
+      break;
+    case kIdxMxfp4:
+      launch_tile_p<kPrFp4>(s, grid, px, cu_q, cu_k, topk_idx, topk_score, one_round, st);
+      break;
+    default:
+      launch_tile_p<kPrBf16>(s, grid, px, cu_q, cu_k, topk_idx, topk_score, one_round, st);
   }
   return hipGetLastError();
 }
 
-template <int DP, bool FP8>
-static void launch_split_t(const msa_shape& s, dim3 grid, const void* q_idx, const void* k_idx,
-                           const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
-                           float* part_sc, int32_t* part_id, int n_chunks, int cb,
-                           hipStream_t st) {
-  hipLaunchKernelGGL((index_split_kernel<DP, FP8>), grid, dim3(256), 0, st, q_idx, k_idx,
-                     descale_idx, cu_q, cu_k, part_sc, part_id, s.hkv, s.max_q, s.causal,
-                     n_chunks, cb, s.total_q, s.total_k, s.max_k);
+template <int DP, int PR>
+static void launch_split_t(const msa_shape& s, dim3 grid, const IndexProxies& px,
+                           const int32_t* cu_q, const int32_t* cu_k, float* part_sc,
+                           int32_t* part_id, int n_chunks, int cb, hipStream_t st) {
+  hipLaunchKernelGGL((index_split_kernel<DP, PR>), grid, dim3(256), 0, st, px.q_idx, px.k_idx,
+                     px.q_scale, px.k_scale, px.descale, cu_q, cu_k, part_sc, part_id, s.hkv,
+                     s.max_q, s.causal, n_chunks, cb, s.total_q, s.total_k, s.max_k);
 }
 
-hipError_t launch_index_split(const msa_shape& s, bool fp8, const void* q_idx,
-                              const void* k_idx, const float* descale_idx, const int32_t* cu_q,
+template <int PR>
+static void launch_split_p(const msa_shape& s, dim3 grid, const IndexProxies& px,
+                           const int32_t* cu_q, const int32_t* cu_k, float* part_sc,
+                           int32_t* part_id, int n_chunks, int cb, hipStream_t st) {
+  if (s.dp == 64)
+    launch_split_t<64, PR>(s, grid, px, cu_q, cu_k, part_sc, part_id, n_chunks, cb, st);
+  else
+    launch_split_t<32, PR>(s, grid, px, cu_q, cu_k, part_sc, part_id, n_chunks, cb, st);
+}
+
+hipError_t launch_index_split(const msa_shape& s, const IndexProxies& px, const int32_t* cu_q,
                               const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
                               void* ws, hipStream_t st) {
   if (s.max_q == 0) return hipSuccess;
@@ -571,20 +691,15 @@ hipError_t launch_index_split(const msa_shape& s, bool fp8, const void* q_idx,
   int32_t* part_id = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + n * 4);
   if (n_chunks > 0) {
     dim3 grid(n_chunks, s.batch * s.max_q);
-    if (fp8) {
-      if (s.dp == 64)
-        launch_split_t<64, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
-                                 part_id, n_chunks, cb, st);
-      else
-        launch_split_t<32, true>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
-                                 part_id, n_chunks, cb, st);
-    } else {
-      if (s.dp == 64)
-        launch_split_t<64, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
-                                  part_id, n_chunks, cb, st);
-      else
-        launch_split_t<32, false>(s, grid, q_idx, k_idx, descale_idx, cu_q, cu_k, part_sc,
-                                  part_id, n_chunks, cb, st);
+    switch (px.prec) {
+      case kIdxFp8:
+        launch_split_p<kPrFp8>(s, grid, px, cu_q, cu_k, part_sc, part_id, n_chunks, cb, st);
+        break;
+      case kIdxMxfp4:
+        launch_split_p<kPrFp4>(s, grid, px, cu_q, cu_k, part_sc, part_id, n_chunks, cb, st);
+        break;
+      default:
+        launch_split_p<kPrBf16>(s, grid, px, cu_q, cu_k, part_sc, part_id, n_chunks, cb, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -308,19 +308,21 @@ msa_status msa_index_workspace_size(const msa_shape* shape, size_t* bytes) {
   return MSA_OK;
 }
 
-static msa_status index_topk(const msa_shape* shape, bool fp8, const void* q_idx,
-                             const void* k_idx, const float* descale_idx, const int32_t* cu_q,
-                             const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
-                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+static msa_status index_topk(const msa_shape* shape, const IndexProxies& px,
+                             const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
+                             float* topk_score, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
   msa_status st = check_shape(shape);
   if (st != MSA_OK) return st;
   const msa_shape& s = *shape;
   if (s.list_q != 1 || (s.dp != 32 && s.dp != 64)) return MSA_ERR_SHAPE;
   if ((int64_t)s.total_q * s.hkv * s.dp > kInt32Max * 2LL) return MSA_ERR_SHAPE;
   if (!cu_q || !cu_k || !topk_idx) return MSA_ERR_NULL;
-  if (s.total_q > 0 && !q_idx) return MSA_ERR_NULL;
-  if (s.total_k > 0 && !k_idx) return MSA_ERR_NULL;
-  if (fp8 && !descale_idx) return MSA_ERR_NULL;
+  if (s.total_q > 0 && !px.q_idx) return MSA_ERR_NULL;
+  if (s.total_k > 0 && !px.k_idx) return MSA_ERR_NULL;
+  if (px.prec == kIdxFp8 && !px.descale) return MSA_ERR_NULL;
+  if (px.prec == kIdxMxfp4 && ((s.total_q > 0 && !px.q_scale) || (s.total_k > 0 && !px.k_scale)))
+    return MSA_ERR_NULL;
   hipError_t e;
   if (s.max_q <= kSplitIndexMaxQ) {
     // key chunks merged by one wave per (query, group): at most 512 per query
@@ -328,11 +330,9 @@ static msa_status index_topk(const msa_shape* shape, bool fp8, const void* q_idx
     if ((int64_t)s.batch * s.max_q > 65535) return MSA_ERR_SHAPE;      // grid y of the split kernel
     const size_t need = index_workspace_bytes(s);
     if (!workspace || ws_bytes < need) return MSA_ERR_WORKSPACE;
-    e = launch_index_split(s, fp8, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score,
-                           workspace, stream);
+    e = launch_index_split(s, px, cu_q, cu_k, topk_idx, topk_score, workspace, stream);
   } else {
-    e = launch_index_tile(s, fp8, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score,
-                          stream);
+    e = launch_index_tile(s, px, cu_q, cu_k, topk_idx, topk_score, stream);
   }
   if (e != hipSuccess) {
     fail_launch(e);
@@ -345,16 +345,25 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
                           const int32_t* cu_q, const int32_t* cu_k, int32_t* topk_idx,
                           float* topk_score, void* workspace, size_t ws_bytes,
                           hipStream_t stream) {
-  return index_topk(shape, false, q_idx, k_idx, nullptr, cu_q, cu_k, topk_idx, topk_score,
-                    workspace, ws_bytes, stream);
+  const IndexProxies px{kIdxBf16, q_idx, k_idx, nullptr, nullptr, nullptr};
+  return index_topk(shape, px, cu_q, cu_k, topk_idx, topk_score, workspace, ws_bytes, stream);
 }
 
 msa_status msa_index_topk_fp8(const msa_shape* shape, const void* q_idx, const void* k_idx,
                               const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
                               int32_t* topk_idx, float* topk_score, void* workspace,
                               size_t ws_bytes, hipStream_t stream) {
-  return index_topk(shape, true, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, topk_score,
-                    workspace, ws_bytes, stream);
+  const IndexProxies px{kIdxFp8, q_idx, k_idx, nullptr, nullptr, descale_idx};
+  return index_topk(shape, px, cu_q, cu_k, topk_idx, topk_score, workspace, ws_bytes, stream);
+}
+
+msa_status msa_index_topk_mxfp4(const msa_shape* shape, const void* q_idx,
+                                const uint8_t* q_scale, const void* k_idx,
+                                const uint8_t* k_scale, const int32_t* cu_q, const int32_t* cu_k,
+                                int32_t* topk_idx, float* topk_score, void* workspace,
+                                size_t ws_bytes, hipStream_t stream) {
+  const IndexProxies px{kIdxMxfp4, q_idx, k_idx, q_scale, k_scale, nullptr};
+  return index_topk(shape, px, cu_q, cu_k, topk_idx, topk_score, workspace, ws_bytes, stream);
 }
 
 msa_status msa_select_workspace_size(const msa_shape* shape, int reps, size_t* bytes) {

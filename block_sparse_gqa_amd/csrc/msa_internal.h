@@ -86,12 +86,22 @@ Layout layout(const msa_shape& s, msa_mode mode);
 size_t index_workspace_bytes(const msa_shape& s);
 
 // ----- launchers (return hipSuccess or the launch error)
-// fp8: e4m3 proxies with device descales descale_idx[0] (q_idx), [1] (k_idx)
-hipError_t launch_index_tile(const msa_shape& s, bool fp8, const void* q_idx, const void* k_idx,
-                             const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
-                             int32_t* topk_idx, float* topk_score, hipStream_t st);
-hipError_t launch_index_split(const msa_shape& s, bool fp8, const void* q_idx,
-                              const void* k_idx, const float* descale_idx, const int32_t* cu_q,
+// Proxies of the index branch: bf16; fp8 e4m3 with device descales descale[0] (q_idx),
+// descale[1] (k_idx); MXFP4 codes (two per byte, even element in the low nibble) with one
+// E8M0 scale byte per 32 elements in q_scale / k_scale ([token, group, dp / 32]).
+enum IndexPrec : int { kIdxBf16 = 0, kIdxFp8 = 1, kIdxMxfp4 = 2 };
+struct IndexProxies {
+  IndexPrec prec;
+  const void* q_idx;
+  const void* k_idx;
+  const uint8_t* q_scale;
+  const uint8_t* k_scale;
+  const float* descale;
+};
+hipError_t launch_index_tile(const msa_shape& s, const IndexProxies& px, const int32_t* cu_q,
+                             const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
+                             hipStream_t st);
+hipError_t launch_index_split(const msa_shape& s, const IndexProxies& px, const int32_t* cu_q,
                               const int32_t* cu_k, int32_t* topk_idx, float* topk_score,
                               void* ws, hipStream_t st);
 

@@ -22,7 +22,7 @@ MSA_AUTO, MSA_KV_OUTER, MSA_Q_OUTER = 0, 1, 2
 
 SYMBOLS = ("msa_workspace_size", "msa_workspace_layout_of", "msa_index_workspace_size",
            "msa_resolve_mode", "msa_crossover", "msa_status_string", "msa_last_error",
-           "msa_index_topk", "msa_index_topk_fp8", "msa_sparse_attn_fwd", "msa_plan",
+           "msa_index_topk", "msa_index_topk_fp8", "msa_index_topk_mxfp4", "msa_sparse_attn_fwd", "msa_plan",
            "msa_attn_main", "msa_combine", "msa_select_workspace_size", "msa_select_tiles",
            "msa_bwd_workspace_size", "msa_sparse_attn_bwd", "msa_proxy_bwd_workspace_size",
            "msa_proxy_attn_bwd", "msa_train_bwd_workspace_size", "msa_train_bwd",
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "msa_crossover": [sp, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)],
             "msa_index_topk": [sp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_index_topk_fp8": [sp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "msa_index_topk_mxfp4": [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_select_workspace_size": [sp, i32, ctypes.POINTER(sz)],
             "msa_select_tiles": [sp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_sparse_attn_fwd": [sp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, i32, vp, sz,
@@ -183,6 +184,15 @@ def msa_index_topk_fp8(shape, q_idx, k_idx, descale_idx, cu_q, cu_k, topk_idx, t
                                     _p(cu_q), _p(cu_k), _p(topk_idx), _p(topk_score),
                                     _p(workspace), _nbytes(workspace), _stream(stream)),
            "msa_index_topk_fp8")
+
+
+def msa_index_topk_mxfp4(shape, q_idx, q_scale, k_idx, k_scale, cu_q, cu_k, topk_idx,
+                         topk_score=None, workspace=None, stream=None) -> None:
+    _check(lib().msa_index_topk_mxfp4(ctypes.byref(shape), _p(q_idx), _p(q_scale), _p(k_idx),
+                                      _p(k_scale), _p(cu_q), _p(cu_k), _p(topk_idx),
+                                      _p(topk_score), _p(workspace), _nbytes(workspace),
+                                      _stream(stream)),
+           "msa_index_topk_mxfp4")
 
 
 def msa_select_workspace_size(shape, reps) -> int:

@@ -8,6 +8,7 @@
  *
  *   msa_index_topk       index branch: max-pooled proxy scores + top-K, local block forced
  *   msa_index_topk_fp8   the same on fp8 e4m3 proxies (8-bit MFMA scoring)
+ *   msa_index_topk_mxfp4 the same on 4-bit MXFP4 proxies (scaled 4-bit MFMA scoring)
  *   msa_select_tiles     per-Q-tile lists from block representatives (R1 / R4 selectors)
  *   msa_sparse_attn_fwd  main branch: KV-outer partials (or Q-outer output) over the lists
  *   msa_combine          log-sum-exp merge of the per-slot partials into O and LSE
@@ -80,8 +81,9 @@ typedef struct {
   int32_t block;    /* KV block size: 128 */
   int32_t topk;     /* selected blocks per list: 1..16 */
   int32_t causal;   /* 1: key u visible to a query at position pos iff u <= pos */
-  int32_t dtype;    /* msa_dtype of Q/K/V. Proxies are bf16 for msa_index_topk and e4m3fn
-                       (with their own descales) for msa_index_topk_fp8 */
+  int32_t dtype;    /* msa_dtype of Q/K/V. Proxies are bf16 for msa_index_topk, e4m3fn
+                       (with their own descales) for msa_index_topk_fp8 and MXFP4 (codes
+                       and E8M0 group scales) for msa_index_topk_mxfp4 */
   int32_t list_q;   /* 1: per-query lists topk_idx [total_q, hkv, topk];
                        128: per-Q-tile lists [batch * ceil(max_q/128), hkv, topk], row
                        s * ceil(max_q/128) + t holds the list of queries [128t, 128t+128)
@@ -201,6 +203,26 @@ msa_status msa_index_topk_fp8(const msa_shape* shape, const void* q_idx, const v
                               const float* descale_idx, const int32_t* cu_q, const int32_t* cu_k,
                               int32_t* topk_idx, float* topk_score, void* workspace,
                               size_t ws_bytes, hipStream_t stream);
+
+/* 4-bit index scoring ("Sparse Attention", Chapter 4: the FP4 scorer, 4-bit index vectors
+ * with scales prepared before the call; one score per (query, key), the block keeps its
+ * largest). The format is OCP MXFP4, the 4-bit form gfx950's scaled MFMA takes. The same
+ * selection, arguments, workspace and errors as msa_index_topk, except:
+ *  - q_idx [total_q, hkv, dp / 2] and k_idx [total_k, hkv, dp / 2] bytes hold E2M1 codes,
+ *    element 2i of a row in the low nibble of byte i;
+ *  - q_scale [total_q, hkv, dp / 32] and k_scale [total_k, hkv, dp / 32] (DEVICE uint8) hold
+ *    the E8M0 scale of elements 32b .. 32b + 31 of each row (value 2^(code - 127); code 255,
+ *    NaN in the format, is not checked and gives undefined scores); NULL with a non-empty
+ *    side: MSA_ERR_NULL.
+ *  - A proxy element is its code's value times its group's scale. Per group the products are
+ *    exact and summed exactly; only the sum over the dp / 32 groups rounds (fp32), so scores
+ *    are exact whenever the exact value is an fp32 number. Block scores, and topk_score, are
+ *    max(q.k), unscaled. */
+msa_status msa_index_topk_mxfp4(const msa_shape* shape, const void* q_idx,
+                                const uint8_t* q_scale, const void* k_idx,
+                                const uint8_t* k_scale, const int32_t* cu_q, const int32_t* cu_k,
+                                int32_t* topk_idx, float* topk_score, void* workspace,
+                                size_t ws_bytes, hipStream_t stream);
 
 /* Per-Q-tile block selectors R1 and R4 ("Sparse Attention", Chapter 4: one or four
  * representatives). Every 128-query tile of a sequence and every 128-key block is summarised,

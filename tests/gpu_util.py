@@ -23,6 +23,8 @@ class Dev:
     lists: torch.Tensor | None
     descale: torch.Tensor | None
     idx_descale: torch.Tensor | None = None   # fp8 proxies: device [descale q_idx, k_idx]
+    q_idx_scale: torch.Tensor | None = None   # MXFP4 proxies: E8M0 group scales
+    k_idx_scale: torch.Tensor | None = None
 
 
 def upload(case: Case, device="cuda") -> Dev:
@@ -38,7 +40,8 @@ def upload(case: Case, device="cuda") -> Dev:
     return Dev(q=up(case.q), k=up(case.k), v=up(case.v), q_idx=up(case.q_idx),
                k_idx=up(case.k_idx), cu_q=torch.from_numpy(case.cu_q).to(device),
                cu_k=torch.from_numpy(case.cu_k).to(device), lists=lists, descale=ds,
-               idx_descale=ids)
+               idx_descale=ids, q_idx_scale=up(case.q_idx_scale),
+               k_idx_scale=up(case.k_idx_scale))
 
 
 def shape_of(case: Case, list_q=None) -> msa.Shape:
@@ -51,8 +54,12 @@ def shape_of(case: Case, list_q=None) -> msa.Shape:
 
 
 def run_index(case: Case, dev: Dev, s, topk, score, ws) -> None:
-    """The index branch for the case's proxy type (bf16, or fp8 with its descales)."""
-    if case.cfg.idx_dtype == "fp8":
+    """The index branch for the case's proxy type (bf16, fp8 with its descales, or MXFP4 codes
+    with their group scales)."""
+    if case.cfg.idx_dtype == "mxfp4":
+        msa.msa_index_topk_mxfp4(s, dev.q_idx, dev.q_idx_scale, dev.k_idx, dev.k_idx_scale,
+                                 dev.cu_q, dev.cu_k, topk, score, ws)
+    elif case.cfg.idx_dtype == "fp8":
         msa.msa_index_topk_fp8(s, dev.q_idx, dev.k_idx, dev.idx_descale, dev.cu_q, dev.cu_k,
                                topk, score, ws)
     else:
@@ -60,8 +67,13 @@ def run_index(case: Case, dev: Dev, s, topk, score, ws) -> None:
 
 
 def proxies(case: Case) -> tuple[np.ndarray, np.ndarray]:
-    """The proxies' exact values as float64 (fp8 codes times their descales)."""
+    """The proxies' exact values as float64 (fp8 codes times their descales, MXFP4 codes
+    times their group scales)."""
     from synth.msa_inputs import widen
+    if case.cfg.idx_dtype == "mxfp4":
+        from oracle import mxfp4
+        return (mxfp4.dequantize(case.q_idx.numpy(), case.q_idx_scale.numpy()),
+                mxfp4.dequantize(case.k_idx.numpy(), case.k_idx_scale.numpy()))
     dqi, dki = case.idx_descale
     return widen(case.q_idx, dqi), widen(case.k_idx, dki)
 

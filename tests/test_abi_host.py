@@ -141,6 +141,13 @@ def test_null_device_pointers_and_small_workspace(L):
                                 0, None) == msa.MSA_ERR_NULL
     assert L.msa_index_topk_fp8(ctypes.byref(s_dp), fake, fake, fake, fake, fake, fake, None,
                                 None, 0, None) == msa.MSA_ERR_SHAPE
+    # MXFP4 proxies: both scale arrays are required, dp as for the other precisions
+    assert L.msa_index_topk_mxfp4(ctypes.byref(s), fake, None, fake, fake, fake, fake, fake,
+                                  None, None, 0, None) == msa.MSA_ERR_NULL
+    assert L.msa_index_topk_mxfp4(ctypes.byref(s), fake, fake, fake, None, fake, fake, fake,
+                                  None, None, 0, None) == msa.MSA_ERR_NULL
+    assert L.msa_index_topk_mxfp4(ctypes.byref(s_dp), fake, fake, fake, fake, fake, fake, fake,
+                                  None, None, 0, None) == msa.MSA_ERR_SHAPE
     # main branch: workspace checks come first, then pointers
     assert L.msa_sparse_attn_fwd(ctypes.byref(s), fake, fake, fake, None, 0.1, fake, fake, fake,
                                  msa.MSA_AUTO, fake, need - 1, fake, None,

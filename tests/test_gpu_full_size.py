@@ -94,7 +94,7 @@ def run_workload(cfgname, every, seed=0, max_rows=None):
     return case, chosen, lists, rows, out, o_s, lse_s
 
 
-def compare(case, lists, rows, out, o_s, lse_s):
+def compare(case, lists, rows, out, o_s, lse_s, exact_lists=False):
     """Sampled rows: lists bit-exact or certified near-ties (capped in number); outputs
     against the oracle's on every sampled row whose list equals the oracle's."""
     c = case.cfg
@@ -124,6 +124,8 @@ def compare(case, lists, rows, out, o_s, lse_s):
         n_diff, n_tie, bad = compare_lists(got, out.topk_idx, scores, err)
         _say(f"rows differing {n_diff}, certified near-ties {n_tie} of {got.shape[0] * c.hkv}")
         assert not bad, f"uncertified list differences at {bad[:5]}"
+        if exact_lists:
+            assert n_diff == 0, f"{n_diff} (row, group) lists differ"
         # rows with a certified swap ran on other lists than the oracle's: left out
         same = np.all(got == out.topk_idx, axis=(1, 2))
     else:
@@ -151,6 +153,20 @@ def test_fp8_proxies_prefill_128k():
     case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long_i8", every=64)
     assert chosen == msa.MSA_KV_OUTER
     compare(case, lists, rows, out, o_s, lse_s)
+
+
+def test_mxfp4_proxies_prefill_128k():
+    """The 128K fp8 workload with 4-bit MXFP4 proxies: exact scores, so the lists must equal
+    the oracle's on every sampled row, with no near-tie allowance."""
+    case, chosen, lists, rows, out, o_s, lse_s = run_workload("m3_fp8_long_i4", every=64)
+    assert chosen == msa.MSA_KV_OUTER
+    compare(case, lists, rows, out, o_s, lse_s, exact_lists=True)
+
+
+def test_mxfp4_proxies_decode_64_requests():
+    case, chosen, lists, rows, out, o_s, lse_s = run_workload("decode_i4", every=1)
+    assert chosen == msa.MSA_Q_OUTER
+    compare(case, lists, rows, out, o_s, lse_s, exact_lists=True)
 
 
 def test_decode_64_requests():

@@ -166,6 +166,42 @@ def test_index_topk_fp8_proxies_certified(name, kw):
     assert n_checked > 0
 
 
+MXFP4_INDEX_CASES = FP8_INDEX_CASES + [
+    # ragged sequences in one call, one group, a last block of 1 key
+    ("tile_ragged_g1", dict(n_q=(300, 129, 700), n_k=(300, 2049, 700), hq=4, hkv=1, topk=9,
+                            dp=64)),
+    ("split_g8_decode", dict(n_q=(1, 1), n_k=(3000, 12000), hq=16, hkv=8, topk=16, dp=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", MXFP4_INDEX_CASES, ids=[c[0] for c in MXFP4_INDEX_CASES])
+def test_index_topk_mxfp4_bit_exact(name, kw):
+    """MXFP4 proxies ("Sparse Attention", Chapter 4: the FP4 scorer): every product of two
+    E2M1 values is a multiple of 1/4 below 36, a 32-element group sums exactly, the scales are
+    powers of two, so each score is exact whenever its exact value is an fp32 number (checked
+    here on the oracle's scores). Lists and scores must then equal the oracle's bit for bit,
+    ties included, with no near-tie allowance."""
+    _say(f"[index mxfp4] {name}")
+    case = mi.make_case(mi.custom(name=name, idx_dtype="mxfp4", **kw), seed=4)
+    got, got_sc = gpu_index(case, upload(case))
+    out = msa_case.run(case, want_output=False)
+    for sc in out.scores:
+        fin = sc[np.isfinite(sc)]
+        assert np.array_equal(fin.astype(np.float32).astype(np.float64), fin)
+    n_diff, _, bad = compare_lists(got, out.topk_idx)
+    assert n_diff == 0, f"{n_diff} rows differ, first {bad[:5]}"
+    seq_of = np.searchsorted(case.cu_q, np.arange(case.total_q), side="right") - 1
+    n_checked = 0
+    for i in range(0, case.total_q, 3):
+        s = seq_of[i]
+        for g in range(case.cfg.hkv):
+            for k, b in enumerate(got[i, g]):
+                want = out.scores[s][i - case.cu_q[s], g, b] if b >= 0 else -np.inf
+                assert got_sc[i, g, k] == want, (i, g, k, got_sc[i, g, k], want)
+                n_checked += 1
+    assert n_checked > 0
+
+
 # ------------------------------------------------------------------ whole layer
 
 LAYER_CASES = [
