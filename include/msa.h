@@ -192,8 +192,8 @@ msa_status msa_index_topk(const msa_shape* shape, const void* q_idx, const void*
 
 /* Low-precision index scoring ("Sparse Attention", Chapter 4: a scorer that compares
  * quantised index vectors, token by token, and keeps each block's largest score; the pages
- * use 4-bit inputs, this call OCP fp8 e4m3fn). The same selection, arguments, workspace and
- * errors as msa_index_topk, except:
+ * use 4-bit inputs, as msa_index_topk_mxfp4 does; this call takes OCP fp8 e4m3fn). The same
+ * selection, arguments, workspace and errors as msa_index_topk, except:
  *  - q_idx and k_idx hold e4m3fn codes; descale_idx is a DEVICE float[2] with their positive
  *    per-tensor descales (proxy value = code * descale), NULL: MSA_ERR_NULL.
  *  - Each proxy dot product is the exact products of the codes summed in fp32 (an 8-bit MFMA
