@@ -600,7 +600,7 @@ __global__ __launch_bounds__(64) void index_merge_kernel(
 // Key chunks of the split kernel (short-query calls) per (sequence, query, group).
 static int64_t index_chunks(const msa_shape& s) {
   const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
-  const int cb = split_index_chunk(nb_max, true);   // the most chunks of any precision
+  const int cb = split_index_chunk(nb_max);
   return std::max<int64_t>(1, (nb_max + cb - 1) / cb);
 }
 
@@ -684,7 +684,7 @@ hipError_t launch_index_split(const msa_shape& s, const IndexProxies& px, const 
                               void* ws, hipStream_t st) {
   if (s.max_q == 0) return hipSuccess;
   const int64_t nb_max = (s.max_k + s.block - 1) / s.block;
-  const int cb = split_index_chunk(nb_max, px.prec == kIdxMxfp4);
+  const int cb = split_index_chunk(nb_max);
   const int n_chunks = (int)((nb_max + cb - 1) / cb);
   const int64_t n = (int64_t)s.batch * s.max_q * s.hkv * n_chunks * kMaxTopK;
   float* part_sc = reinterpret_cast<float*>(ws);

@@ -428,10 +428,9 @@ def test_default_cache_ratio_is_the_measured_one():
     assert msa.msa_resolve_mode(reuse_shape(4), msa.MSA_AUTO) == msa.MSA_KV_OUTER   # 16
 
 
-def test_index_workspace_covers_the_smallest_key_chunks():
+def test_index_workspace_covers_every_key_chunk():
     """Short-query calls write one top-16 list (score + id, 8 bytes a slot) per (query, group,
-    key chunk); 4-bit proxies use 8-block chunks up to 1024 blocks (16 for bf16 / fp8), 32
-    beyond, and the one workspace size serves every precision."""
+    key chunk): chunks of 8 blocks up to 1024 blocks, 32 beyond."""
     for max_k, per in ((1000, 8), (1024 * 128, 8), (1025 * 128, 32), (300000, 32)):
         s = msa.make_shape(batch=3, total_q=5, total_k=3 * max_k, max_q=2, max_k=max_k, hq=8,
                            hkv=4, topk=16)
