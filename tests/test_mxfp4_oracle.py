@@ -121,3 +121,38 @@ def test_case_oracle_on_mxfp4_proxies():
     sc = out.scores[0]
     fin = sc[np.isfinite(sc)]
     np.testing.assert_array_equal(fin.astype(np.float32).astype(np.float64), fin)
+
+
+def test_planted_mistakes_fail_a_pin(monkeypatch):
+    """Each plausible slip in the decode (nibble order, scale bias, sign, group width) makes
+    one of the pins above fail."""
+    def pins_hold():
+        try:
+            test_e2m1_values_are_the_formats_published_set()
+            test_e8m0_decode_matches_torch()
+            test_nibble_order_and_scale_groups()
+            test_prepared_vectors_are_nearest_values(0)
+        except AssertionError:
+            return False
+        return True
+
+    assert pins_hold()
+    good_unpack, good_e2m1, good_e8m0 = mxfp4.unpack_codes, mxfp4.e2m1_value, mxfp4.e8m0_value
+
+    def swapped(p):
+        c = good_unpack(p)
+        return np.stack([c[..., 1::2], c[..., 0::2]], axis=-1).reshape(c.shape)
+    monkeypatch.setattr(mxfp4, "unpack_codes", swapped)
+    assert not pins_hold()
+    monkeypatch.setattr(mxfp4, "unpack_codes", good_unpack)
+    monkeypatch.setattr(mxfp4, "e8m0_value", lambda c: good_e8m0(c) * 2.0)
+    assert not pins_hold()
+    monkeypatch.setattr(mxfp4, "e8m0_value", good_e8m0)
+    monkeypatch.setattr(mxfp4, "e2m1_value", lambda c: np.abs(good_e2m1(c)))
+    assert not pins_hold()
+    monkeypatch.setattr(mxfp4, "e2m1_value", good_e2m1)
+    monkeypatch.setattr(mxfp4, "MX_BLOCK", 16)
+    with pytest.raises(AssertionError):
+        mxfp4.dequantize(np.zeros((1, 32), np.uint8), np.zeros((1, 2), np.uint8))
+    monkeypatch.setattr(mxfp4, "MX_BLOCK", 32)
+    assert pins_hold()
